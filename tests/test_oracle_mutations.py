@@ -1,0 +1,87 @@
+"""Plant plausible mistakes in a copy of the oracle and check the pins see them.
+
+Each mutation rewrites one expression of the oracle's source (a dropped term,
+an off-by-one, a wrong sign, index or operand), loads the result as a separate
+module on the CPU and swaps it in for the real oracle.  The fast pins of
+test_oracle_index.py and test_oracle_attention.py then run against the mutant;
+at least one must fail, otherwise the pins do not constrain that expression.
+"""
+
+import os
+import types
+
+import pytest
+
+import oracle.fsa_oracle as O
+import test_oracle_attention as A
+import test_oracle_index as I
+
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "fsa_oracle.py")
+with open(SRC_PATH) as f:
+    SRC = f.read()
+
+MUTATIONS = [
+    # attention: key set
+    ("if 0 <= e <= own})", "if 0 <= e < own})"),
+    ("min(seq_start + (e + 1) * block_size, seq_end, t + 1)", "min(seq_start + (e + 1) * block_size, seq_end, t)"),
+    ("lo = seq_start + e * block_size", "lo = e * block_size"),
+    ("sorted({int(e) for e in np.asarray(sel_row).tolist() if 0 <= e <= own})",
+     "sorted([int(e) for e in np.asarray(sel_row).tolist() if 0 <= e <= own])"),
+    # attention: arithmetic
+    ("scores = scale * (qh @ kh.T)", "scores = (qh @ kh.T)"),
+    ("qh = np.asarray(q[t, h * g : (h + 1) * g, :]", "qh = np.asarray(q[t, h : HQ : H, :]"),
+    ("ls = m + np.log(l)", "ls = m + np.log2(l)"),
+    ("p = np.exp(scores - ls[:, None])", "p = np.exp(scores - m[:, None])"),
+    ("o[i, h * g : (h + 1) * g, :] = p @ vh", "o[i, h * g : (h + 1) * g, :] = p @ kh"),
+    ("row_max[i, h * g : (h + 1) * g] = m", "row_max[i, h * g : (h + 1) * g] = ls"),
+    ("l = np.exp(scores - m[:, None]).sum(axis=1)", "l = np.exp(m[:, None] - scores).sum(axis=1)"),
+    # index
+    ("in_range = (sel >= 0) & (sel <= own[None, :, None])", "in_range = (sel >= 0) & (sel < own[None, :, None])"),
+    ("in_range = (sel >= 0) & (sel <= own[None, :, None])", "in_range = (sel > 0) & (sel <= own[None, :, None])"),
+    ("first[:, :, j] &= sel[:, :, j] != sel[:, :, jj]", "first[:, :, j] &= True"),
+    ("key = hh * NB + gb", "key = gb * H + hh"),
+    ("gb = gboff[seq[tt]] + sel[hh, tt, jj]", "gb = sel[hh, tt, jj]"),
+    ('order = np.argsort(key, kind="stable")', 'order = np.lexsort((-tt, key))'),
+    ("offsets = np.concatenate([[0], np.cumsum(counts)])", "offsets = np.concatenate([np.cumsum(counts), [counts.sum()]])"),
+    ("qidx = tt[order].astype(np.int64)", "qidx = tt.astype(np.int64)"),
+]
+
+
+def fast_pins():
+    pins = [I.test_handworked_example, I.test_row_permutation_moves_slot_with_entry, I.test_shuffled_rows_same_lists]
+    pins += [lambda s=s: I.test_against_brute_force(s) for s in range(6)]
+    pins += [lambda s=s: I.test_invariants(s) for s in range(2)]
+    pins += [lambda n=n: I.test_closed_form_pair_counts(n) for n in ("n1k_h1_g1_d64_t4_bf16", "n8k_h4_g2_d128_t16_bf16")]
+    pins += [A.test_handworked_example, A.test_own_block_only_is_block_diagonal_causal, A.test_order_invariance_bitwise,
+             A.test_duplicates_equal_deduplicated, A.test_zero_queries_give_key_mean, A.test_constant_values_and_first_token,
+             A.test_identical_heads_identical_outputs_and_empty_rows]
+    pins += [lambda s=s: A.test_dense_block_mask_equivalence(s) for s in range(5)]
+    pins += [lambda s=s: A.test_full_selection_is_causal_attention(s) for s in range(3)]
+    return pins
+
+
+def load_mutant(old, new):
+    assert SRC.count(old) == 1, f"mutation anchor must occur exactly once: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(SRC.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def test_unmutated_oracle_passes_fast_pins():
+    for pin in fast_pins():
+        pin()
+
+
+@pytest.mark.parametrize("old,new", MUTATIONS, ids=[f"m{i}" for i in range(len(MUTATIONS))])
+def test_mutant_is_caught(old, new, monkeypatch):
+    mut = load_mutant(old, new)
+    for name in O.__all__:
+        monkeypatch.setattr(O, name, getattr(mut, name))
+    failures = 0
+    for pin in fast_pins():
+        try:
+            pin()
+        except Exception:  # an assertion, or a crash the mutant causes
+            failures += 1
+            break
+    assert failures, f"no pin fails when {old!r} becomes {new!r}"
