@@ -1,0 +1,315 @@
+"""Benchmark: NSA selected-attention forward (FSA order) on one MI355X.
+
+One step = the whole path on one batch of synthetic input already resident in
+HBM: index build (fsa_build_index), softmax statistics (fsa_softmax_stats),
+main kernel (fsa_selected_attn_main) and reduction (fsa_selected_attn_reduce).
+Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--partial input|fp32] [--no-cpu-baseline] [--no-variants]
+
+Throughput is algorithmic TFLOP/s: 4 * g * d * (sum over (token, KV head) of
+the number of keys the token attends to), i.e. QK^T and PV over the visible
+keys only, divided by the step time.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "selected-attn fwd latency (ms) + TFLOP/s at 64K tokens, g=1/2/4; % MFMA peak"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, GB/s
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # dense MFMA
+DEFAULT_WORKLOAD = "n64k_h4_g4_d128_t16_bf16"
+VARIANTS = ["n64k_h4_g2_d128_t16_bf16", "n64k_h4_g1_d128_t16_bf16"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--partial", default="input", choices=["input", "fp32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Work accounting (host bookkeeping for the FLOP and byte counts)
+# ---------------------------------------------------------------------------
+def work_counts(sel, cu, block_size):
+    """Number of selecting entries P and total visible keys over all
+    (KV head, token) rows.  An entry selects block e of the token's sequence
+    iff 0 <= e <= own block and e did not occur earlier in the row; it sees
+    the whole block, or only keys <= t in the own block."""
+    cu = np.asarray(cu, dtype=np.int64)
+    n = int(cu[-1])
+    tok = np.arange(n)
+    seq = np.searchsorted(cu, tok, side="right") - 1
+    local = tok - cu[seq]
+    own = local // block_size
+    H, _, T = sel.shape
+    pairs = 0
+    keys = 0
+    for h in range(H):
+        s = sel[h]
+        ok = (s >= 0) & (s <= own[:, None])
+        for j in range(1, T):
+            ok[:, j] &= ~np.any(s[:, :j] == s[:, j : j + 1], axis=1)
+        pairs += int(ok.sum())
+        full = ok & (s < own[:, None])
+        mine = ok & (s == own[:, None])
+        keys += int(full.sum()) * block_size + int(((local % block_size + 1)[:, None] * mine).sum())
+    return pairs, keys
+
+
+def kernel_bytes(w, P, s_in, s_p):
+    N, H, g, d, T = int(w.cu_seqlens[-1]), w.num_kv_heads, w.gqa_group, w.head_dim, w.topk
+    HQ = H * g
+    q_bytes = N * HQ * d * s_in
+    kv_bytes = 2 * N * H * d * s_in
+    main = q_bytes + kv_bytes + N * HQ * 4 + P * 4 + P * g * d * s_p
+    reduce = P * g * d * s_p + H * N * T * 4 + N * HQ * d * s_in
+    stats = q_bytes + kv_bytes // 2 + P * 4 + 2 * P * g * 8 + H * N * T * 4 + 2 * N * HQ * 4
+    index = 3 * H * N * T * 4 + P * 4
+    return {"index": index, "stats": stats, "main": main, "reduce": reduce}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, on a bounded sample of query tokens
+# ---------------------------------------------------------------------------
+_G = {}
+
+
+def _oracle_shard(tokens):
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    with threadpool_limits(1):
+        oracle.selected_attention(_G["q"], _G["k"], _G["v"], _G["sel"], _G["cu"], _G["B"], _G["scale"], tokens)
+    return len(tokens)
+
+
+def cpu_baseline(w, target_s):
+    import multiprocessing as mp
+
+    q, k, v = (x.float().numpy() for x in (w.q, w.k, w.v))
+    _G.update(q=q, k=k, v=v, sel=w.sel, cu=w.cu_seqlens, B=w.block_size, scale=w.scale)
+    n = int(w.cu_seqlens[-1])
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    rng = np.random.default_rng(12345)
+    # calibrate on one core
+    probe = np.sort(rng.choice(n, size=min(32, n), replace=False))
+    t0 = time.perf_counter()
+    _oracle_shard(probe)
+    per_tok = (time.perf_counter() - t0) / probe.size
+    m = int(min(n, max(cores, target_s * cores / max(per_tok, 1e-9))))
+    sample = np.sort(rng.choice(n, size=m, replace=False))
+    shards = np.array_split(sample, cores * 4)
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        pool.map(_oracle_shard, shards)
+    wall = time.perf_counter() - t0
+    # algorithmic FLOPs of the sampled rows
+    sub = w.sel[:, sample, :]
+    cu = w.cu_seqlens.astype(np.int64)
+    seq = np.searchsorted(cu, sample, side="right") - 1
+    local = sample - cu[seq]
+    own = local // w.block_size
+    keys = 0
+    for h in range(w.num_kv_heads):
+        s = sub[h]
+        ok = (s >= 0) & (s <= own[:, None])
+        for j in range(1, s.shape[1]):
+            ok[:, j] &= ~np.any(s[:, :j] == s[:, j : j + 1], axis=1)
+        keys += int((ok & (s < own[:, None])).sum()) * w.block_size
+        keys += int(((local % w.block_size + 1)[:, None] * (ok & (s == own[:, None]))).sum())
+    flops = 4.0 * w.gqa_group * w.head_dim * keys
+    return {
+        "value": flops / wall / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{m} of {n} query tokens (all KV heads), uniform without replacement, seed 12345; "
+                  f"{wall:.1f} s wall on {cores} worker processes, 1 BLAS thread each",
+        "wall_s": wall,
+    }
+
+
+# ---------------------------------------------------------------------------
+# GPU run
+# ---------------------------------------------------------------------------
+def run_gpu(w, partial, steps, warmup):
+    import torch
+
+    import sparse_attention_sel_amd as fsa
+
+    dev = torch.device("cuda:0")
+    prob = fsa.Problem(
+        w.cu_seqlens, w.num_kv_heads, w.gqa_group, w.head_dim, w.block_size, w.topk,
+        dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float16,
+        partial_dtype=partial, softmax_scale=w.scale, device=dev,
+    )
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    sel = torch.from_numpy(w.sel).to(dev)
+    index = fsa.allocate_index(prob, dev)
+    ws = fsa.Workspaces(prob, dev, index.sizes)
+    n, hq = prob.total_tokens, prob.num_q_heads
+    lse = torch.empty((n, hq), dtype=torch.float32, device=dev)
+    row_max = torch.empty((n, hq), dtype=torch.float32, device=dev)
+    out = torch.empty((n, hq, prob.head_dim), dtype=prob.dtype, device=dev)
+    stream = torch.cuda.current_stream()
+    names = ["index", "stats", "main", "reduce"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fsa.build_index(prob, sel, index, ws.build, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fsa.softmax_stats(prob, q, k, index, row_max, lse, ws.stats, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fsa.selected_attn_main(prob, q, k, v, index, lse, ws.partial, stream)
+        if ev is not None:
+            ev[3].record(stream)
+        fsa.selected_attn_reduce(prob, index, ws.partial, out, stream)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = {nm: 0.0 for nm in names}
+    for ev in events:
+        for i, nm in enumerate(names):
+            stage[nm] += ev[i].elapsed_time(ev[i + 1])
+    stage = {nm: v_ / steps for nm, v_ in stage.items()}
+    counts = index.counts.cpu().numpy()
+    return {
+        "ms_per_step": wall * 1e3 / steps,
+        "stage_ms": stage,
+        "pairs": index.num_pairs(),
+        "n_valid": {"min": int(counts.min()), "median": float(np.median(counts)), "max": int(counts.max())},
+        "partial_bytes": index.num_pairs() * w.gqa_group * w.head_dim * (2 if partial == "input" else 4),
+    }
+
+
+def measure(w, partial, steps, warmup):
+    P_host, keys = work_counts(w.sel, w.cu_seqlens, w.block_size)
+    r = run_gpu(w, partial, steps, warmup)
+    assert r["pairs"] == P_host, (r["pairs"], P_host)
+    f_alg = 4.0 * w.gqa_group * w.head_dim * keys
+    f_main = 4.0 * w.gqa_group * w.block_size * w.head_dim * P_host
+    s_in, s_p = 2, (2 if partial == "input" else 4)
+    byts = kernel_bytes(w, P_host, s_in, s_p)
+    r.update(f_alg=f_alg, f_main=f_main, bytes=byts)
+    return r
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); "
+              "the selected-attention path shards over KV heads without communication, "
+              "so each GPU's throughput is the single-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from sparse_attention_sel_amd.inputs import make_workload
+
+    w = make_workload(args.workload)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)  # before the GPU is touched (fork pool)
+    r = measure(w, args.partial, args.steps, args.warmup)
+    ms = r["ms_per_step"]
+    value = r["f_alg"] / (ms * 1e-3) / 1e12
+    st = r["stage_ms"]
+    dominant = max(("main", "reduce"), key=lambda s: st[s])
+    ach = r["bytes"][dominant] / (st[dominant] * 1e-3) / 1e9
+    main_tflops = r["f_alg"] / (st["main"] * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "tokens": int(w.cu_seqlens[-1]),
+            "kv_heads": w.num_kv_heads,
+            "gqa_group": w.gqa_group,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "topk": w.topk,
+            "partial_dtype": w.dtype if args.partial == "input" else "fp32",
+            "pairs": r["pairs"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_reduce" if dominant == "reduce" else "k_main",
+            "achieved": round(ach, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+        "stages_ms": {k_: round(v_, 4) for k_, v_ in st.items()},
+        "main_kernel": {
+            "tflops_alg": round(main_tflops, 2),
+            "mfma_frac": round(main_tflops / PEAK_MFMA_TFLOPS[w.dtype], 4),
+            "tflops_issued": round(r["f_main"] / (st["main"] * 1e-3) / 1e12, 2),
+            "hbm_gbs": round(r["bytes"]["main"] / (st["main"] * 1e-3) / 1e9, 1),
+        },
+        "reduce_kernel_hbm_gbs": round(r["bytes"]["reduce"] / (st["reduce"] * 1e-3) / 1e9, 1),
+        "index_hbm_gbs": round(r["bytes"]["index"] / (st["index"] * 1e-3) / 1e9, 1),
+        "n_valid": r["n_valid"],
+        "cpu_baseline": cpu,
+    }
+    if cpu is not None:
+        line["cpu_baseline"] = {k_: v_ for k_, v_ in cpu.items() if k_ != "wall_s"}
+    if not args.no_variants and args.workload == DEFAULT_WORKLOAD:
+        var = {}
+        for name in VARIANTS:
+            wv = make_workload(name)
+            rv = measure(wv, args.partial, max(3, args.steps // 2), 2)
+            stv = rv["stage_ms"]
+            var[name] = {
+                "ms_per_step": round(rv["ms_per_step"], 4),
+                "tflops": round(rv["f_alg"] / (rv["ms_per_step"] * 1e-3) / 1e12, 2),
+                "stages_ms": {k_: round(v_, 4) for k_, v_ in stv.items()},
+                "main_mfma_frac": round(rv["f_alg"] / (stv["main"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[wv.dtype], 4),
+            }
+            del wv
+        line["variants"] = var
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * fsa.h - C ABI of the MI355X (gfx950) selected-attention forward library.
+ *
+ * The library computes the forward pass of the token-selection ("selected
+ * attention") branch of Native Sparse Attention in the KV-block-outer loop
+ * order of Flash Sparse Attention (FSA):
+ *
+ *   - "FSA: An Alternative Efficient Implementation of Native Sparse Attention
+ *     Kernel", paper notes (papernotes.org, ICLR 2026): Overall framework
+ *     (flowchart: index precompute -> token-selection kernel -> compact buffer
+ *     -> reduction kernel, with the online-softmax kernel feeding both) and
+ *     Key designs 1-4;
+ *   - Flash-Sparse-Attention README (airanks.app mirror): Method (three
+ *     kernels: main, reduction, online softmax), Features (fp16/bf16, head dim
+ *     up to 256, GQA groups 1..16) and Usage (packed sequences, cu_seqlens,
+ *     block_size, topk).
+ *
+ * Problem.  Packed sequences s = 0..B-1 occupy tokens [cu[s], cu[s+1]).
+ * Q is [N, h_K*g, d], K and V are [N, h_K, d], all row-major, fp16 or bf16.
+ * Query head h*g + j (j < g) belongs to KV head h.  Sel is int32
+ * [h_K, N, T]: for KV head h and query token t, T block indices local to t's
+ * sequence (block e covers tokens cu[s] + [e*B_K, (e+1)*B_K)).  Each of the g
+ * query heads of the group attends to the union of the selected blocks,
+ * restricted causally to keys k <= t.  Entries that are negative, beyond the
+ * token's own block, or repeat an earlier entry of the row select nothing;
+ * such entries are data, not errors.  A query with no keys gets O = 0 and
+ * row max = lse = -inf.
+ *
+ * Calls, in order (each enqueues kernels on `stream`, never synchronises):
+ *   fsa_get_sizes          host only: byte sizes of every buffer below.
+ *   fsa_build_index        Sel -> index tensors I_i / N_valid / O_i.
+ *   fsa_softmax_stats      per-query row max and log-sum-exp.
+ *   fsa_selected_attn_fwd  main kernel (partials) + reduction -> O.
+ *                          (= fsa_selected_attn_main then _reduce.)
+ *
+ * Ownership.  The caller allocates and owns every buffer (device memory
+ * unless marked host).  The library allocates nothing, keeps no pointer
+ * after a call returns, holds no mutable global state and may be called from
+ * several host threads.  Buffers must stay alive until the stream has
+ * executed the enqueued work.  The `fsa_index` buffers and its `aux` blob
+ * belong together: build them once, reuse them for the stats and forward
+ * calls of the same problem and Sel.
+ *
+ * Errors.  Every call returns FSA_OK (0) or a nonzero fsa_status.  Argument
+ * checks run before anything is enqueued: on any status other than
+ * FSA_ERR_HIP nothing has been enqueued.  FSA_ERR_HIP means a kernel launch
+ * failed; earlier kernels of the same call may have been enqueued.
+ */
+#ifndef FSA_H_
+#define FSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FSA_ABI_VERSION 1
+
+typedef enum {
+  FSA_OK = 0,
+  FSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FSA_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes */
+  FSA_ERR_DTYPE = 3,       /* unknown dtype / partial dtype code */
+  FSA_ERR_UNSUPPORTED = 4, /* valid shape, but no compiled kernel for it */
+  FSA_ERR_WORKSPACE = 5,   /* a workspace is smaller than fsa_get_sizes asks */
+  FSA_ERR_HIP = 6,         /* a HIP launch failed */
+  FSA_ERR_ALIGN = 7        /* a pointer is not aligned as documented */
+} fsa_status;
+
+typedef enum { FSA_DTYPE_BF16 = 0, FSA_DTYPE_FP16 = 1 } fsa_dtype;
+
+/* Storage type of the compact partial buffer written by the main kernel. */
+typedef enum {
+  FSA_PARTIAL_FP32 = 0,  /* fp32 partial rows (4 bytes per element) */
+  FSA_PARTIAL_INPUT = 1  /* partial rows in the input dtype (2 bytes) */
+} fsa_partial_dtype;
+
+typedef struct {
+  int32_t num_seqs;               /* B >= 1 packed sequences */
+  const int32_t* cu_seqlens_host; /* host [B+1]: 0 = cu[0] <= cu[1] <= ... = N */
+  const int32_t* cu_seqlens_dev;  /* device [B+1], same values (kernels read it) */
+  int32_t num_kv_heads;           /* h_K >= 1 */
+  int32_t gqa_group;              /* g in [1, 16]; query heads = h_K * g */
+  int32_t head_dim;               /* d: 64, 128 or 256 (same for Q, K, V) */
+  int32_t block_size;             /* B_K: 64 or 128 */
+  int32_t topk;                   /* T in [1, 256] entries per Sel row */
+  float softmax_scale;            /* > 0, or <= 0 for 1/sqrt(d) */
+  int32_t dtype;                  /* fsa_dtype of Q, K, V and O */
+  int32_t partial_dtype;          /* fsa_partial_dtype */
+} fsa_problem;
+
+typedef struct {
+  int64_t total_tokens;   /* N */
+  int64_t num_blocks;     /* NB = sum_s ceil(L_s / B_K) global KV blocks per head */
+  int64_t max_pairs;      /* upper bound of P, the number of selecting entries */
+  int64_t max_work_items; /* upper bound of (KV head, block, query chunk) items */
+  size_t counts_bytes;    /* int32 [h_K * NB] */
+  size_t offsets_bytes;   /* int32 [h_K * NB + 1] */
+  size_t qidx_bytes;      /* int32 [max_pairs] (at least one element) */
+  size_t slot_bytes;      /* int32 [h_K, N, T] */
+  size_t aux_bytes;       /* library-private blob that travels with the index */
+  size_t build_ws_bytes;  /* scratch for fsa_build_index only */
+  size_t stats_ws_bytes;  /* scratch for fsa_softmax_stats only */
+  size_t partial_ws_bytes;/* scratch for fsa_selected_attn_fwd / _main / _reduce */
+} fsa_sizes;
+
+/*
+ * Index tensors (paper notes, Key design 2), in a canonical layout:
+ *   segment f = h * NB + gb, gb = global block = (blocks of earlier sequences) + e;
+ *   counts[f]  = N_valid of segment f: how many query tokens select block gb of KV head h;
+ *   offsets[f] = exclusive prefix sum of counts over f, offsets[h_K*NB] = P
+ *                (the compact output offsets O_i: segment f owns partial rows
+ *                [offsets[f], offsets[f+1]));
+ *   qidx[offsets[f] + r] = the r-th smallest global query token of segment f (I_i);
+ *   slot[h, t, j] = offsets[f] + r for the entry that selects segment f
+ *                   (first occurrence in the row), -1 for entries that select nothing.
+ * All int32, 4-byte aligned; aux 256-byte aligned.
+ */
+typedef struct {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* qidx;
+  int32_t* slot;
+  void* aux;
+} fsa_index;
+
+/* Version of this header's ABI (FSA_ABI_VERSION). */
+int32_t fsa_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* fsa_status_string(int32_t status);
+
+/*
+ * Host-only: validate `prob` and fill `out` with every buffer size.
+ * Touches no device memory and needs no GPU.  cu_seqlens_dev may be NULL here.
+ */
+int32_t fsa_get_sizes(const fsa_problem* prob, fsa_sizes* out);
+
+/*
+ * Index precompute (paper notes, Overall framework: "precompute index tensors
+ * I_i / O_i" from the selection tensor; Key design 2).
+ *   sel  device int32 [h_K, N, T], 4-byte aligned.
+ *   idx  device buffers sized by fsa_get_sizes (counts, offsets, qidx, slot, aux).
+ *   ws   device scratch of at least build_ws_bytes (256-byte aligned); free to
+ *        reuse once the stream has passed this call.
+ * Bit-exact and deterministic: counting sort without order-deciding atomics.
+ */
+int32_t fsa_build_index(const fsa_problem* prob, const int32_t* sel, const fsa_index* idx,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Online-softmax statistics (paper notes, Key design 4; README, Method
+ * "online softmax kernel"): for every query token t and query head hq,
+ *   row_max[t, hq] = max over visible keys of scale * q.k,
+ *   lse[t, hq]     = row_max + ln(sum exp(scale * q.k - row_max)),
+ * natural log, fp32 [N, h_K*g].  q, k: device, 16-byte aligned.
+ *   ws  device scratch of at least stats_ws_bytes (16-byte aligned).
+ */
+int32_t fsa_softmax_stats(const fsa_problem* prob, const void* q, const void* k, const fsa_index* idx,
+                          float* row_max, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Forward output (README, Method: main kernel + reduction kernel; paper
+ * notes, Key designs 1-3): out[t, hq, :] = sum over visible keys of
+ * exp(scale * q.k - lse) * v, in the input dtype (round to nearest even).
+ *   q, k, v, out  device, 16-byte aligned; out is [N, h_K*g, d].
+ *   lse           device fp32 [N, h_K*g] from fsa_softmax_stats.
+ *   partial_ws    device scratch of at least partial_ws_bytes (16-byte aligned).
+ * Equivalent to fsa_selected_attn_main followed by fsa_selected_attn_reduce.
+ */
+int32_t fsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
+                              const fsa_index* idx, const float* lse, void* out, void* partial_ws,
+                              size_t partial_ws_bytes, void* stream);
+
+/*
+ * Main (token-selection) kernel alone (paper notes, Key designs 1-3): one
+ * workgroup per (KV head, KV block, query chunk) stages the block's K and V
+ * once, streams the block's query list, and writes the pre-scaled partial
+ * rows exp(scale*q.k - lse) @ v contiguously to partial_ws rows
+ * [offsets[f] * g, offsets[f+1] * g) (row = pair * g + j, d columns).
+ */
+int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const void* k, const void* v,
+                               const fsa_index* idx, const float* lse, void* partial_ws,
+                               size_t partial_ws_bytes, void* stream);
+
+/*
+ * Reduction kernel alone (paper notes, Key design 3): out[t, h*g + j, :] =
+ * sum over the row's valid slots, in ascending j order, of partial row
+ * slot[h, t, j] * g + j; no atomics.
+ */
+int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, const void* partial_ws,
+                                 size_t partial_ws_bytes, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSA_H_ */

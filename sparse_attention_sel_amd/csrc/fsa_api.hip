@@ -1,0 +1,277 @@
+// C-ABI entry points: argument validation, buffer sizing and kernel dispatch.
+// Every check runs before the first launch, so a call that returns an error
+// other than FSA_ERR_HIP has enqueued nothing.  Nothing here allocates.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "fsa_internal.h"
+
+namespace fsa {
+namespace {
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
+  if (p == nullptr || geo == nullptr || p->cu_seqlens_host == nullptr) return FSA_ERR_NULL;
+  if (p->num_seqs < 1) return FSA_ERR_SHAPE;
+  if (p->dtype != FSA_DTYPE_BF16 && p->dtype != FSA_DTYPE_FP16) return FSA_ERR_DTYPE;
+  if (p->partial_dtype != FSA_PARTIAL_FP32 && p->partial_dtype != FSA_PARTIAL_INPUT) return FSA_ERR_DTYPE;
+  if (p->num_kv_heads < 1 || p->gqa_group < 1 || p->gqa_group > 16) return FSA_ERR_SHAPE;
+  if (p->head_dim < 16 || p->head_dim > 256 || p->head_dim % 16 != 0) return FSA_ERR_SHAPE;
+  if (p->block_size < 1 || p->topk < 1 || p->topk > 256) return FSA_ERR_SHAPE;
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return FSA_ERR_UNSUPPORTED;
+  if (p->block_size != 64 && p->block_size != 128) return FSA_ERR_UNSUPPORTED;
+  if (p->block_size == 128 && p->head_dim == 256) return FSA_ERR_UNSUPPORTED;  // would spill registers
+  float scale = p->softmax_scale;
+  if (std::isnan(scale) || std::isinf(scale)) return FSA_ERR_SHAPE;
+  if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)p->head_dim);
+
+  const int32_t* cu = p->cu_seqlens_host;
+  const int B = p->num_seqs;
+  if (cu[0] != 0) return FSA_ERR_SHAPE;
+  for (int s = 0; s < B; ++s)
+    if (cu[s + 1] < cu[s]) return FSA_ERR_SHAPE;
+  const int64_t N = cu[B];
+  const int64_t H = p->num_kv_heads, g = p->gqa_group, T = p->topk, BK = p->block_size;
+  if (H * N * T >= (int64_t(1) << 31)) return FSA_ERR_SHAPE;  // slot positions are int32
+  if (H * g * N >= (int64_t(1) << 31)) return FSA_ERR_SHAPE;
+
+  std::memset(geo, 0, sizeof(*geo));
+  geo->num_seqs = B;
+  geo->N = (int32_t)N;
+  geo->H = (int32_t)H;
+  geo->g = (int32_t)g;
+  geo->HQ = (int32_t)(H * g);
+  geo->d = p->head_dim;
+  geo->BK = (int32_t)BK;
+  geo->T = (int32_t)T;
+  geo->dtype = p->dtype;
+  geo->partial_dtype = p->partial_dtype;
+  geo->scale = scale;
+  geo->chunk_tokens = (int32_t)((kRowsPerItem + g - 1) / g);
+  const int64_t CT = geo->chunk_tokens;
+
+  // Blocks, the bound on selecting entries (a token of local block e selects
+  // at most min(T, e + 1) distinct blocks) and the bound on work items (block
+  // e of a sequence can be selected by at most the L - e*BK tokens from its
+  // start to the end of the sequence).
+  int64_t NB = 0, pairs = 0, work = 0;
+  for (int s = 0; s < B; ++s) {
+    const int64_t L = cu[s + 1] - cu[s];
+    const int64_t nb = (L + BK - 1) / BK;
+    NB += nb;
+    for (int64_t e = 0; e < nb; ++e) {
+      const int64_t ntok = std::min(BK, L - e * BK);
+      pairs += ntok * std::min(T, e + 1);
+      work += (L - e * BK + CT - 1) / CT;
+    }
+  }
+  if (H * NB >= (int64_t(1) << 30)) return FSA_ERR_SHAPE;
+  geo->NB = (int32_t)NB;
+  geo->max_pairs = H * pairs;
+  geo->max_work = std::min(H * work, (geo->max_pairs + CT - 1) / CT + H * NB);
+  if (geo->max_work >= (int64_t(1) << 31)) return FSA_ERR_SHAPE;
+
+  // Histogram tiles: grow the tile until the tile-by-block histogram is bounded.
+  int64_t TT = kMinTileTokens;
+  while (N > 0 && H * ((N + TT - 1) / TT) * NB > kMaxTileHist) TT *= 2;
+  geo->tile_tokens = (int32_t)TT;
+  geo->ntiles = (int32_t)((N + TT - 1) / TT);
+  // Largest block window of any tile: from the first block of its first
+  // token's sequence to the own block of its last token.
+  {
+    std::vector<int64_t> gboff(B + 1, 0);
+    for (int s = 0; s < B; ++s) gboff[s + 1] = gboff[s] + (cu[s + 1] - cu[s] + BK - 1) / BK;
+    auto seq_of = [&](int64_t t) {
+      int lo = 0, hi = B;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) / 2;
+        if (cu[mid] <= t) lo = mid; else hi = mid;
+      }
+      return lo;
+    };
+    int64_t win_max = 1;
+    for (int64_t tile = 0; tile < geo->ntiles; ++tile) {
+      const int64_t t_lo = tile * TT, t_hi = std::min(t_lo + TT, N);
+      const int s0 = seq_of(t_lo), s1 = seq_of(t_hi - 1);
+      const int64_t win = gboff[s1] + (t_hi - 1 - cu[s1]) / BK - gboff[s0] + 1;
+      win_max = std::max(win_max, win);
+    }
+    if (win_max > kWinMax) return FSA_ERR_UNSUPPORTED;
+    geo->win_max = (int32_t)win_max;
+  }
+
+  size_t off = 0;
+  geo->aux_seq_gboff = off;
+  off = round_up(off + (size_t)(B + 1) * 4, 256);
+  geo->aux_nwork = off;
+  off = round_up(off + 16, 256);
+  geo->aux_work = off;
+  off = round_up(off + (size_t)std::max<int64_t>(geo->max_work, 1) * 16, 256);
+  geo->aux_bytes = off;
+  geo->build_ws_bytes = round_up((size_t)std::max<int64_t>(H * geo->ntiles * NB, 1) * 4, 256);
+  const size_t rows = (size_t)std::max<int64_t>(geo->max_pairs, 1) * (size_t)g;
+  geo->stats_ws_bytes = round_up(rows * 8, 256);
+  geo->partial_ws_bytes = round_up(rows * (size_t)geo->d * (geo->partial_dtype == FSA_PARTIAL_FP32 ? 4 : 2), 256);
+  return FSA_OK;
+}
+
+namespace {
+
+int32_t check_index(const Geometry& geo, const fsa_index* idx) {
+  if (idx == nullptr || idx->counts == nullptr || idx->offsets == nullptr || idx->qidx == nullptr ||
+      idx->slot == nullptr || idx->aux == nullptr)
+    return FSA_ERR_NULL;
+  if (!aligned(idx->counts, 4) || !aligned(idx->offsets, 4) || !aligned(idx->qidx, 4) || !aligned(idx->slot, 4) ||
+      !aligned(idx->aux, 256))
+    return FSA_ERR_ALIGN;
+  return FSA_OK;
+}
+
+int32_t prepare(const fsa_problem* prob, Geometry* geo) {
+  const int32_t st = compute_geometry(prob, geo);
+  if (st != FSA_OK) return st;
+  if (prob->cu_seqlens_dev == nullptr) return FSA_ERR_NULL;
+  if (!aligned(prob->cu_seqlens_dev, 4)) return FSA_ERR_ALIGN;
+  return FSA_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? FSA_OK : FSA_ERR_HIP; }
+
+int32_t check_main_args(const Geometry& geo, const void* q, const void* k, const void* v, const fsa_index* idx,
+                        const float* lse, const void* partial, size_t partial_bytes) {
+  if (q == nullptr || k == nullptr || v == nullptr || lse == nullptr || partial == nullptr) return FSA_ERR_NULL;
+  int32_t st = check_index(geo, idx);
+  if (st != FSA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(lse, 4) || !aligned(partial, 16))
+    return FSA_ERR_ALIGN;
+  if (partial_bytes < geo.partial_ws_bytes) return FSA_ERR_WORKSPACE;
+  return FSA_OK;
+}
+
+int32_t check_reduce_args(const Geometry& geo, const fsa_index* idx, const void* partial, size_t partial_bytes,
+                          const void* out) {
+  if (partial == nullptr || out == nullptr) return FSA_ERR_NULL;
+  int32_t st = check_index(geo, idx);
+  if (st != FSA_OK) return st;
+  if (!aligned(partial, 16) || !aligned(out, 16)) return FSA_ERR_ALIGN;
+  if (partial_bytes < geo.partial_ws_bytes) return FSA_ERR_WORKSPACE;
+  return FSA_OK;
+}
+
+}  // namespace
+}  // namespace fsa
+
+using namespace fsa;
+
+extern "C" {
+
+int32_t fsa_abi_version(void) { return FSA_ABI_VERSION; }
+
+const char* fsa_status_string(int32_t status) {
+  switch (status) {
+    case FSA_OK: return "ok";
+    case FSA_ERR_NULL: return "a required pointer is NULL";
+    case FSA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case FSA_ERR_DTYPE: return "unknown dtype or partial dtype";
+    case FSA_ERR_UNSUPPORTED: return "no compiled kernel for this head dim / block size / sequence length";
+    case FSA_ERR_WORKSPACE: return "workspace smaller than fsa_get_sizes requires";
+    case FSA_ERR_HIP: return "HIP kernel launch failed";
+    case FSA_ERR_ALIGN: return "pointer misaligned";
+    default: return "unknown status";
+  }
+}
+
+int32_t fsa_get_sizes(const fsa_problem* prob, fsa_sizes* out) {
+  if (out == nullptr) return FSA_ERR_NULL;
+  Geometry geo;
+  const int32_t st = compute_geometry(prob, &geo);
+  if (st != FSA_OK) return st;
+  std::memset(out, 0, sizeof(*out));
+  out->total_tokens = geo.N;
+  out->num_blocks = geo.NB;
+  out->max_pairs = geo.max_pairs;
+  out->max_work_items = geo.max_work;
+  const size_t M = (size_t)geo.H * geo.NB;
+  out->counts_bytes = std::max<size_t>(M, 1) * 4;
+  out->offsets_bytes = (M + 1) * 4;
+  out->qidx_bytes = (size_t)std::max<int64_t>(geo.max_pairs, 1) * 4;
+  out->slot_bytes = std::max<size_t>((size_t)geo.H * geo.N * geo.T, 1) * 4;
+  out->aux_bytes = geo.aux_bytes;
+  out->build_ws_bytes = geo.build_ws_bytes;
+  out->stats_ws_bytes = geo.stats_ws_bytes;
+  out->partial_ws_bytes = geo.partial_ws_bytes;
+  return FSA_OK;
+}
+
+int32_t fsa_build_index(const fsa_problem* prob, const int32_t* sel, const fsa_index* idx, void* ws,
+                        size_t ws_bytes, void* stream) {
+  Geometry geo;
+  int32_t st = prepare(prob, &geo);
+  if (st != FSA_OK) return st;
+  if (sel == nullptr || ws == nullptr) return FSA_ERR_NULL;
+  st = check_index(geo, idx);
+  if (st != FSA_OK) return st;
+  if (!aligned(sel, 4) || !aligned(ws, 256)) return FSA_ERR_ALIGN;
+  if (ws_bytes < geo.build_ws_bytes) return FSA_ERR_WORKSPACE;
+  return hip_status(launch_build_index(geo, prob->cu_seqlens_dev, sel, *idx, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t fsa_softmax_stats(const fsa_problem* prob, const void* q, const void* k, const fsa_index* idx,
+                          float* row_max, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Geometry geo;
+  int32_t st = prepare(prob, &geo);
+  if (st != FSA_OK) return st;
+  if (q == nullptr || k == nullptr || row_max == nullptr || lse == nullptr || ws == nullptr) return FSA_ERR_NULL;
+  st = check_index(geo, idx);
+  if (st != FSA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_max, 4) || !aligned(lse, 4) || !aligned(ws, 16))
+    return FSA_ERR_ALIGN;
+  if (ws_bytes < geo.stats_ws_bytes) return FSA_ERR_WORKSPACE;
+  return hip_status(launch_stats(geo, q, k, *idx, row_max, lse, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const void* k, const void* v,
+                               const fsa_index* idx, const float* lse, void* partial_ws, size_t partial_ws_bytes,
+                               void* stream) {
+  Geometry geo;
+  int32_t st = prepare(prob, &geo);
+  if (st != FSA_OK) return st;
+  st = check_main_args(geo, q, k, v, idx, lse, partial_ws, partial_ws_bytes);
+  if (st != FSA_OK) return st;
+  return hip_status(launch_main(geo, q, k, v, *idx, lse, partial_ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, const void* partial_ws,
+                                 size_t partial_ws_bytes, void* out, void* stream) {
+  Geometry geo;
+  int32_t st = prepare(prob, &geo);
+  if (st != FSA_OK) return st;
+  st = check_reduce_args(geo, idx, partial_ws, partial_ws_bytes, out);
+  if (st != FSA_OK) return st;
+  return hip_status(launch_reduce(geo, *idx, partial_ws, out, static_cast<hipStream_t>(stream)));
+}
+
+int32_t fsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
+                              const fsa_index* idx, const float* lse, void* out, void* partial_ws,
+                              size_t partial_ws_bytes, void* stream) {
+  Geometry geo;
+  int32_t st = prepare(prob, &geo);
+  if (st != FSA_OK) return st;
+  st = check_main_args(geo, q, k, v, idx, lse, partial_ws, partial_ws_bytes);
+  if (st != FSA_OK) return st;
+  st = check_reduce_args(geo, idx, partial_ws, partial_ws_bytes, out);
+  if (st != FSA_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(launch_main(geo, q, k, v, *idx, lse, partial_ws, s));
+  if (st != FSA_OK) return st;
+  return hip_status(launch_reduce(geo, *idx, partial_ws, out, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,115 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI host code.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fsa.h"
+
+namespace fsa {
+
+// ---------------------------------------------------------------------------
+// Tunables
+// ---------------------------------------------------------------------------
+constexpr int kBuildThreads = 256;     // workgroup of the index kernels
+constexpr int kScanThreads = 1024;     // single-workgroup offsets scan
+constexpr int kMinTileTokens = 256;    // tokens per histogram tile (grows for long inputs)
+constexpr int64_t kMaxTileHist = int64_t(1) << 24;  // cap on h_K * tiles * NB entries
+constexpr int kWinMax = 7680;          // max global blocks one tile can touch (LDS)
+constexpr int kAttnThreads = 256;      // 4 waves per main / stats workgroup
+constexpr int kRowsPerItem = 1024;     // target query rows (tokens * g) per work item
+constexpr int kReduceThreads = 256;
+
+// ---------------------------------------------------------------------------
+// Problem geometry, computed once on the host from fsa_problem.
+// ---------------------------------------------------------------------------
+struct Geometry {
+  int32_t num_seqs;
+  int32_t N;      // total tokens
+  int32_t H;      // KV heads
+  int32_t g;      // GQA group
+  int32_t HQ;     // query heads
+  int32_t d;      // head dim
+  int32_t BK;     // block size
+  int32_t T;      // Sel entries per row
+  int32_t NB;     // global blocks per head
+  int32_t tile_tokens;   // tokens per index tile
+  int32_t ntiles;        // index tiles
+  int32_t win_max;       // largest block window of any tile
+  int32_t chunk_tokens;  // query tokens per work item
+  int32_t dtype;
+  int32_t partial_dtype;
+  float scale;           // softmax scale (natural units)
+  int64_t max_pairs;
+  int64_t max_work;
+  // aux blob layout (byte offsets)
+  size_t aux_seq_gboff;  // int32 [B+1] exclusive prefix of per-sequence block counts
+  size_t aux_nwork;      // int32 [4]: number of work items, P, spare
+  size_t aux_work;       // int4 [max_work]: (segment, first token, block start, seq end)
+  size_t aux_bytes;
+  size_t build_ws_bytes;
+  size_t stats_ws_bytes;
+  size_t partial_ws_bytes;
+};
+
+int32_t compute_geometry(const fsa_problem* prob, Geometry* geo);
+
+// ---------------------------------------------------------------------------
+// Launchers (defined next to their kernels); all enqueue on `stream` and
+// return hipSuccess or the launch error.
+// ---------------------------------------------------------------------------
+hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const int32_t* sel,
+                              const fsa_index& idx, void* ws, hipStream_t stream);
+hipError_t launch_stats(const Geometry& geo, const void* q, const void* k, const fsa_index& idx,
+                        float* row_max, float* lse, void* ws, hipStream_t stream);
+hipError_t launch_main(const Geometry& geo, const void* q, const void* k, const void* v,
+                       const fsa_index& idx, const float* lse, void* partial, hipStream_t stream);
+hipError_t launch_reduce(const Geometry& geo, const fsa_index& idx, const void* partial, void* out,
+                         hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Vec8;
+template <>
+struct Vec8<__bf16> {
+  using type = bf16x8;
+};
+template <>
+struct Vec8<_Float16> {
+  using type = f16x8;
+};
+
+// D = A * B + C on one 32x32x16 tile (gfx950 MFMA, fp32 accumulate).
+// Lane l supplies A[l % 32][8 * (l / 32) + e] and B[8 * (l / 32) + e][l % 32],
+// e = 0..7; it receives C[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32], r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Sequence that holds global token t: the last s with cu[s] <= t (skips empty
+// sequences).  cu has num_seqs + 1 entries.
+__device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cu, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// Sequence that holds global block gb: the last s with gboff[s] <= gb.
+__device__ __forceinline__ int seq_of_block(const int32_t* __restrict__ gboff, int num_seqs, int gb) {
+  return seq_of_token(gboff, num_seqs, gb);
+}
+
+}  // namespace fsa

@@ -1,0 +1,95 @@
+"""Shared plumbing for the GPU parity tests: run the HIP path through the
+C-ABI binding and bring results back to the host for comparison with the
+oracle.  Holds no attention arithmetic."""
+
+import sys
+
+import numpy as np
+import torch
+
+import sparse_attention_sel_amd as fsa
+from sparse_attention_sel_amd.inputs import Workload, cu_seqlens_of, make_qkv
+
+TOL_O = {"bf16": 2e-2, "fp16": 5e-3}
+TOL_LSE = 1e-3
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def problem_for(w: Workload, partial: str = "fp32", device="cuda") -> fsa.Problem:
+    return fsa.Problem(
+        w.cu_seqlens, w.num_kv_heads, w.gqa_group, w.head_dim, w.block_size, w.topk,
+        dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float16,
+        partial_dtype=partial, softmax_scale=w.scale, device=device,
+    )
+
+
+def run_gpu(w: Workload, partial: str = "fp32", keep_partial: bool = False):
+    """Whole forward on cuda:0.  Returns a dict of host numpy arrays."""
+    prob = problem_for(w, partial)
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    sel = torch.from_numpy(w.sel).to(dev)
+    index = fsa.allocate_index(prob, dev)
+    ws = fsa.Workspaces(prob, dev, index.sizes)
+    n, hq = prob.total_tokens, prob.num_q_heads
+    lse = torch.full((n, hq), float("nan"), dtype=torch.float32, device=dev)
+    row_max = torch.full((n, hq), float("nan"), dtype=torch.float32, device=dev)
+    out = torch.full((n, hq, prob.head_dim), float("nan"), dtype=prob.dtype, device=dev)
+    fsa.build_index(prob, sel, index, ws.build)
+    fsa.softmax_stats(prob, q, k, index, row_max, lse, ws.stats)
+    fsa.selected_attn_fwd(prob, q, k, v, index, lse, out, ws.partial)
+    torch.cuda.synchronize()
+    P = index.num_pairs()
+    res = {
+        "counts": index.counts.cpu().numpy(),
+        "offsets": index.offsets[: index.counts.numel() + 1].cpu().numpy(),
+        "qidx": index.qidx[:P].cpu().numpy(),
+        "slot": index.slot.cpu().numpy(),
+        "pairs": P,
+        "out": out.float().cpu().numpy(),
+        "lse": lse.cpu().numpy(),
+        "row_max": row_max.cpu().numpy(),
+    }
+    if keep_partial:
+        res["partial"] = ws.partial
+        res["index"] = index
+        res["out_dev"] = out
+    return res
+
+
+def sample_tokens(cu, block_size, n_random=96, seed=0):
+    """Tokens that exercise the edges (first tokens of each sequence, block
+    boundaries, last tokens) plus a seeded random spread."""
+    rng = np.random.default_rng(seed)
+    toks = set()
+    for s in range(len(cu) - 1):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        if c1 == c0:
+            continue
+        for off in (0, 1, 2, block_size - 1, block_size, block_size + 1, 2 * block_size + 5):
+            if c0 + off < c1:
+                toks.add(c0 + off)
+        for off in (1, 2, block_size + 1):
+            if c1 - off >= c0:
+                toks.add(c1 - off)
+    n = int(cu[-1])
+    toks.update(int(x) for x in rng.integers(0, n, size=min(n_random, n)))
+    return np.array(sorted(toks), dtype=np.int64)
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().numpy().astype(np.float64)
+
+
+def custom_workload(seqlens, H, g, d, B, T, dtype, sel, seed, scale=None):
+    cu = cu_seqlens_of(seqlens)
+    q, k, v = make_qkv(int(cu[-1]), H, g, d, dtype, seed)
+    return Workload(
+        name="custom", seqlens=list(seqlens), cu_seqlens=cu, num_kv_heads=H, gqa_group=g, head_dim=d,
+        block_size=B, topk=T, dtype=dtype, scale=scale if scale is not None else 1.0 / np.sqrt(d),
+        q=q, k=k, v=v, sel=np.ascontiguousarray(sel.astype(np.int32)), meta={},
+    )

@@ -1,0 +1,187 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fsa.h declares, sizes match closed forms, and every argument error
+returns its documented status before anything is launched (device pointers
+here are never dereferenced: validation fails first)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import sparse_attention_sel_amd as fsa
+from sparse_attention_sel_amd.inputs import WORKLOADS, cu_seqlens_of
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fsa.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIGN = range(8)
+FAKE = 1 << 40  # 256-byte aligned fake device address, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int32_t|const char\*)\s+(fsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = fsa.load_library()
+    names = declared_functions()
+    assert "fsa_build_index" in names and "fsa_softmax_stats" in names and "fsa_selected_attn_fwd" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fsa.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (fsa_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_library_is_gfx950():
+    # the offload bundle of our own build names its only device target
+    blob = open(fsa.library_path(), "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in blob
+    for other in (b"--gfx942", b"--gfx90a", b"--gfx1100"):
+        assert other not in blob
+
+
+def test_version_and_status_strings():
+    lib = fsa.load_library()
+    assert lib.fsa_abi_version() == 1
+    for s in range(8):
+        assert len(fsa.status_string(s)) > 0
+    assert fsa.status_string(99) == "unknown status"
+
+
+def prob(cu=(0, 1000), H=2, g=2, d=128, B=64, T=16, dtype=0, partial=0, scale=0.0, num_seqs=None, dev=True):
+    cu = np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
+    p = fsa._Problem(
+        num_seqs=len(cu) - 1 if num_seqs is None else num_seqs,
+        cu_seqlens_host=cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+        cu_seqlens_dev=FAKE if dev else None,
+        num_kv_heads=H, gqa_group=g, head_dim=d, block_size=B, topk=T,
+        softmax_scale=scale, dtype=dtype, partial_dtype=partial,
+    )
+    p._keep = cu
+    return p
+
+
+def sizes(p):
+    s = fsa._Sizes()
+    st = fsa.load_library().fsa_get_sizes(ctypes.byref(p), ctypes.byref(s))
+    return st, s
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_sizes_closed_form(name):
+    sp = WORKLOADS[name]
+    p = prob(cu_seqlens_of(sp.seqlens), sp.num_kv_heads, sp.gqa_group, sp.head_dim, sp.block_size, sp.topk)
+    st, s = sizes(p)
+    assert st == OK
+    N = sum(sp.seqlens)
+    B, T, H = sp.block_size, sp.topk, sp.num_kv_heads
+    nb = [-(-L // B) for L in sp.seqlens]
+    assert s.total_tokens == N and s.num_blocks == sum(nb)
+    pmax = H * sum(min(B, L - e * B) * min(T, e + 1) for L in sp.seqlens for e in range(-(-L // B)))
+    assert s.max_pairs == pmax
+    assert s.counts_bytes == 4 * H * sum(nb) and s.offsets_bytes == 4 * (H * sum(nb) + 1)
+    assert s.slot_bytes == 4 * H * N * T and s.qidx_bytes == 4 * pmax
+    assert s.partial_ws_bytes >= pmax * sp.gqa_group * sp.head_dim * 4
+    assert s.stats_ws_bytes >= pmax * sp.gqa_group * 8
+
+
+def test_max_pairs_bounds_real_pairs():
+    # the forced-block generators reach the bound exactly (every token keeps
+    # min(T, own block + 1) distinct blocks)
+    from oracle import build_index
+    from sparse_attention_sel_amd.inputs import make_workload
+
+    w = make_workload("n8k_h4_g2_d128_t16_bf16", with_qkv=False)
+    ref = build_index(w.sel, w.cu_seqlens, w.block_size)
+    st, s = sizes(prob(w.cu_seqlens, 4, 2, 128, 64, 16))
+    assert st == OK and s.max_pairs == ref["pairs"]
+    counts = ref["counts"]
+    assert s.max_work_items >= int(np.sum((counts + 1023 // 2) // (1024 // 2)))
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(g=0), SHAPE), (dict(g=17), SHAPE), (dict(H=0), SHAPE),
+        (dict(d=48), UNSUP), (dict(d=100), SHAPE), (dict(d=512), SHAPE),
+        (dict(B=32), UNSUP), (dict(B=0), SHAPE), (dict(B=128, d=256), UNSUP),
+        (dict(T=0), SHAPE), (dict(T=257), SHAPE),
+        (dict(dtype=2), DTYPE), (dict(partial=5), DTYPE),
+        (dict(cu=(1, 100)), SHAPE), (dict(cu=(0, 100, 50)), SHAPE), (dict(num_seqs=0), SHAPE),
+        (dict(scale=float("nan")), SHAPE), (dict(scale=float("inf")), SHAPE),
+        (dict(cu=(0, 2**29), H=8, T=16), SHAPE),
+        (dict(cu=(0, 600000)), UNSUP),
+    ],
+)
+def test_sizes_rejects(kw, status):
+    assert sizes(prob(**kw))[0] == status
+
+
+def test_sizes_accepts_edge_shapes():
+    for kw in (dict(cu=(0, 0)), dict(cu=(0, 0, 5, 5)), dict(T=256), dict(g=16, d=256), dict(B=128, d=64),
+               dict(scale=-1.0), dict(cu=(0, 1))):
+        assert sizes(prob(**kw))[0] == OK, kw
+    assert sizes(prob(cu=(0, 0)))[1].max_pairs == 0
+
+
+def fake_index():
+    return fsa._Index(FAKE, FAKE, FAKE, FAKE, FAKE)
+
+
+def test_entry_points_reject_before_launch():
+    lib = fsa.load_library()
+    p = prob()
+    st, s = sizes(p)
+    assert st == OK
+    P, I = ctypes.byref(p), ctypes.byref(fake_index())
+    null_idx = fsa._Index(FAKE, None, FAKE, FAKE, FAKE)
+    bad_aux = fsa._Index(FAKE, FAKE, FAKE, FAKE, FAKE + 4)
+    # build_index
+    assert lib.fsa_build_index(None, FAKE, I, FAKE, s.build_ws_bytes, None) == NULL
+    assert lib.fsa_build_index(P, None, I, FAKE, s.build_ws_bytes, None) == NULL
+    assert lib.fsa_build_index(P, FAKE, ctypes.byref(null_idx), FAKE, s.build_ws_bytes, None) == NULL
+    assert lib.fsa_build_index(P, FAKE, ctypes.byref(bad_aux), FAKE, s.build_ws_bytes, None) == ALIGN
+    assert lib.fsa_build_index(P, FAKE + 2, I, FAKE, s.build_ws_bytes, None) == ALIGN
+    assert lib.fsa_build_index(P, FAKE, I, FAKE, s.build_ws_bytes - 1, None) == WS
+    assert lib.fsa_build_index(ctypes.byref(prob(dev=False)), FAKE, I, FAKE, s.build_ws_bytes, None) == NULL
+    assert lib.fsa_build_index(ctypes.byref(prob(g=0)), FAKE, I, FAKE, s.build_ws_bytes, None) == SHAPE
+    # softmax_stats
+    f = FAKE
+    assert lib.fsa_softmax_stats(P, None, f, I, f, f, f, s.stats_ws_bytes, None) == NULL
+    assert lib.fsa_softmax_stats(P, f, f, I, f, None, f, s.stats_ws_bytes, None) == NULL
+    assert lib.fsa_softmax_stats(P, f + 8, f, I, f, f, f, s.stats_ws_bytes, None) == ALIGN
+    assert lib.fsa_softmax_stats(P, f, f, I, f, f, f, s.stats_ws_bytes - 1, None) == WS
+    assert lib.fsa_softmax_stats(ctypes.byref(prob(dtype=7)), f, f, I, f, f, f, s.stats_ws_bytes, None) == DTYPE
+    # forward / main / reduce
+    pw = s.partial_ws_bytes
+    assert lib.fsa_selected_attn_fwd(P, f, f, None, I, f, f, f, pw, None) == NULL
+    assert lib.fsa_selected_attn_fwd(P, f, f, f, I, f, None, f, pw, None) == NULL
+    assert lib.fsa_selected_attn_fwd(P, f, f, f, I, f, f + 4, f, pw, None) == ALIGN
+    assert lib.fsa_selected_attn_fwd(P, f, f, f, I, f, f, f, pw - 1, None) == WS
+    assert lib.fsa_selected_attn_main(P, f, f, f, I, None, f, pw, None) == NULL
+    assert lib.fsa_selected_attn_main(P, f, f, f, I, f, f, pw - 256, None) == WS
+    assert lib.fsa_selected_attn_reduce(P, I, f, pw, None, None) == NULL
+    assert lib.fsa_selected_attn_reduce(P, I, f, pw - 1, f, None) == WS
+    assert lib.fsa_selected_attn_reduce(P, ctypes.byref(null_idx), f, pw, f, None) == NULL
+
+
+def test_python_binding_checks_tensors():
+    import torch
+
+    p = fsa.Problem([0, 128], 1, 1, 64, 64, 4)
+    s = fsa.get_sizes(p)
+    assert s["max_pairs"] == 64 * 1 + 64 * 2
+    with pytest.raises(ValueError):
+        fsa.Problem([0, 128], 1, 1, 64, 64, 4, dtype=torch.float32)
+    with pytest.raises(fsa.FsaError) as e:
+        fsa.get_sizes(fsa.Problem([0, 128], 1, 1, 48, 64, 4))
+    assert e.value.status == UNSUP
+    # CPU tensors are refused by the binding before reaching the library
+    idx = fsa.Index(*(torch.zeros(8, dtype=torch.int32) for _ in range(4)), torch.zeros(256, dtype=torch.uint8), s)
+    with pytest.raises(ValueError):
+        fsa.build_index(p, torch.zeros((1, 128, 4), dtype=torch.int32), idx, torch.zeros(s["build_ws_bytes"], dtype=torch.uint8))

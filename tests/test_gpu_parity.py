@@ -1,0 +1,187 @@
+"""GPU parity: the HIP path (through the C-ABI) against the float64 oracle.
+
+Index tensors must match bit-exactly; O within max-abs 2e-2 (bf16) or 5e-3
+(fp16); lse (and row max) within 1e-3.  Small shapes are compared on every
+token, the 64K-token shapes on sampled tokens that include the edges.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.fsa_oracle as O
+from gpu_helpers import TOL_LSE, TOL_O, as_f64, custom_workload, log, run_gpu, sample_tokens
+from sparse_attention_sel_amd.inputs import WORKLOADS, make_workload
+
+pytestmark = pytest.mark.gpu
+
+LARGE = [
+    "n64k_h4_g4_d128_t16_bf16",
+    "n64k_h4_g1_d128_t16_fp16",
+    "b2_n32k_h8_g8_d256_t16_bf16",
+    "n64k_h4_g2_d128_t16_bf16",
+    "n64k_h4_g1_d128_t16_bf16",
+]
+
+
+@functools.lru_cache(maxsize=2)
+def workload(name):
+    log(f"[gen] {name}")
+    return make_workload(name)
+
+
+@functools.lru_cache(maxsize=8)
+def oracle_index(name):
+    w = workload(name)
+    return O.build_index(w.sel, w.cu_seqlens, w.block_size)
+
+
+def check_index(res, ref):
+    assert res["pairs"] == ref["pairs"]
+    np.testing.assert_array_equal(res["counts"], ref["counts"])
+    np.testing.assert_array_equal(res["offsets"], ref["offsets"])
+    np.testing.assert_array_equal(res["qidx"], ref["qidx"])
+    np.testing.assert_array_equal(res["slot"], ref["slot"])
+
+
+def check_attention(res, w, tokens=None):
+    q = w.q.float().numpy()
+    k = w.k.float().numpy()
+    v = w.v.float().numpy()
+    o_ref, m_ref, lse_ref = O.selected_attention(q, k, v, w.sel, w.cu_seqlens, w.block_size, w.scale, tokens)
+    sel = slice(None) if tokens is None else tokens
+    o, lse, m = res["out"][sel], res["lse"][sel], res["row_max"][sel]
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), empty), "empty key sets must give lse = -inf"
+    assert np.array_equal(np.isneginf(m), empty)
+    assert np.all(o[empty] == 0)
+    err_o = float(np.max(np.abs(o - o_ref))) if o.size else 0.0
+    fin = ~empty
+    err_l = float(np.max(np.abs(lse[fin] - lse_ref[fin]))) if fin.any() else 0.0
+    err_m = float(np.max(np.abs(m[fin] - m_ref[fin]))) if fin.any() else 0.0
+    log(f"    max|dO|={err_o:.3e} max|dlse|={err_l:.3e} max|dm|={err_m:.3e}")
+    assert err_o <= TOL_O[w.dtype], f"O error {err_o}"
+    assert err_l <= TOL_LSE and err_m <= TOL_LSE
+
+
+@pytest.mark.parametrize("partial", ["fp32", "input"])
+def test_small_all_tokens(partial):
+    w = workload("n1k_h1_g1_d64_t4_bf16")
+    log(f"[run] n1k partial={partial}")
+    res = run_gpu(w, partial)
+    check_index(res, oracle_index(w.name))
+    check_attention(res, w)
+
+
+@pytest.mark.parametrize("partial", ["fp32", "input"])
+def test_n8k_all_tokens(partial):
+    w = workload("n8k_h4_g2_d128_t16_bf16")
+    log(f"[run] n8k partial={partial}")
+    res = run_gpu(w, partial)
+    check_index(res, oracle_index(w.name))
+    check_attention(res, w)
+
+
+@pytest.mark.parametrize("name", LARGE)
+def test_large_index_and_sampled_outputs(name):
+    w = workload(name)
+    partial = "input" if name.startswith("b2_") else "fp32"
+    log(f"[run] {name} partial={partial}")
+    res = run_gpu(w, partial)
+    log("    index")
+    check_index(res, oracle_index(name))
+    toks = sample_tokens(w.cu_seqlens, w.block_size, n_random=64, seed=1)
+    log(f"    attention on {toks.size} sampled tokens")
+    check_attention(res, w, toks)
+
+
+def adversarial_sel(rng, H, cu, B, T):
+    n = int(cu[-1])
+    sel = np.empty((H, n, T), dtype=np.int32)
+    for s in range(len(cu) - 1):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        nb = (c1 - c0 + B - 1) // B
+        sel[:, c0:c1, :] = rng.integers(-2, nb + 2, size=(H, c1 - c0, T))
+    dup = rng.random(sel.shape) < 0.2
+    sel[dup] = np.roll(sel, 1, axis=2)[dup]
+    return sel
+
+
+CASES = [
+    # seqlens, H, g, d, B, T, dtype
+    ((300, 0, 129, 64), 2, 3, 64, 64, 5, "bf16"),
+    ((513, 77), 1, 16, 128, 64, 3, "fp16"),
+    ((1000,), 2, 1, 128, 128, 8, "bf16"),
+    ((200, 333), 3, 5, 256, 64, 7, "bf16"),
+    ((64, 1, 65), 1, 2, 64, 64, 1, "fp16"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("partial", ["fp32", "input"])
+def test_adversarial_selection(case, partial):
+    seqlens, H, g, d, B, T, dtype = CASES[case]
+    rng = np.random.default_rng(700 + case)
+    from sparse_attention_sel_amd.inputs import cu_seqlens_of
+
+    cu = cu_seqlens_of(seqlens)
+    sel = adversarial_sel(rng, H, cu, B, T)
+    sel[:, ::37, :] = -1  # some rows select nothing
+    w = custom_workload(seqlens, H, g, d, B, T, dtype, sel, seed=900 + case)
+    log(f"[run] adversarial case {case} {CASES[case]} partial={partial}")
+    res = run_gpu(w, partial)
+    check_index(res, O.build_index(w.sel, w.cu_seqlens, B))
+    check_attention(res, w)
+
+
+def test_full_selection_equals_causal_attention():
+    # Sel holding every block (future ones included) is plain causal attention;
+    # compare with torch's float32 SDPA on the CPU as an independent reference.
+    seqlens, H, g, d, B = (700, 300), 2, 2, 64, 64
+    from sparse_attention_sel_amd.inputs import cu_seqlens_of
+
+    cu = cu_seqlens_of(seqlens)
+    nb = max(-(-L // B) for L in seqlens)
+    sel = np.broadcast_to(np.arange(nb, dtype=np.int32), (H, int(cu[-1]), nb)).copy()
+    w = custom_workload(seqlens, H, g, d, B, nb, "bf16", sel, seed=77)
+    res = run_gpu(w, "fp32")
+    for s in range(len(seqlens)):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        qt = w.q[c0:c1].float().permute(1, 0, 2)[None]
+        kt = w.k[c0:c1].float().permute(1, 0, 2).repeat_interleave(g, dim=0)[None]
+        vt = w.v[c0:c1].float().permute(1, 0, 2).repeat_interleave(g, dim=0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=w.scale)
+        ref = ref[0].permute(1, 0, 2).numpy()
+        assert np.max(np.abs(res["out"][c0:c1] - ref)) <= TOL_O["bf16"]
+
+
+def test_deterministic_bitwise():
+    w = workload("n8k_h4_g2_d128_t16_bf16")
+    a = run_gpu(w, "input")
+    b = run_gpu(w, "input")
+    for key in ("counts", "offsets", "qidx", "slot", "out", "lse", "row_max"):
+        assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+def test_partial_rows_sum_to_output():
+    # fp32 partials: summing each query's partial rows (slot order) gives the
+    # output before its final rounding.
+    w = workload("n8k_h4_g2_d128_t16_bf16")
+    res = run_gpu(w, "fp32", keep_partial=True)
+    idx = res["index"]
+    g, d, H = w.gqa_group, w.head_dim, w.num_kv_heads
+    P = res["pairs"]
+    part = res["partial"].view(torch.float32)[: P * g * d].view(P, g, d)
+    slot = idx.slot.long()  # [H, N, T]
+    N = slot.shape[1]
+    acc = torch.zeros((N, H, g, d), dtype=torch.float32, device=part.device)
+    for j in range(slot.shape[2]):
+        s = slot[:, :, j].permute(1, 0)  # [N, H]
+        ok = (s >= 0).unsqueeze(-1).unsqueeze(-1)
+        acc += torch.where(ok, part[s.clamp(min=0)], torch.zeros((), device=part.device))
+    out = res["out_dev"].float().view(N, H, g, d)
+    ulp = torch.clamp(out.abs(), min=2.0**-126)
+    half_ulp = torch.pow(2.0, torch.floor(torch.log2(ulp)) - 8)
+    assert bool(torch.all((acc - out).abs() <= half_ulp * 1.001 + 1e-30))
