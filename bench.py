@@ -31,6 +31,10 @@ DEFAULT_WORKLOAD = "n64k_h4_g4_d128_t16_bf16"
 VARIANTS = ["n64k_h4_g2_d128_t16_bf16", "n64k_h4_g1_d128_t16_bf16"]
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -41,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of 1 GiB (5 times): the known-size kernel "
+                         "against which HBM byte counters are scaled")
     return ap.parse_args()
 
 
@@ -234,13 +241,28 @@ def main():
               "so each GPU's throughput is the single-GPU figure.", file=sys.stderr)
         sys.exit(2)
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    if args.copy_calibration:
+        import torch
+
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4, "launches": 5}))
+        return
     from sparse_attention_sel_amd.inputs import make_workload
 
+    log(f"generating {args.workload}")
     w = make_workload(args.workload)
     cpu = None
     if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
         cpu = cpu_baseline(w, args.cpu_seconds)  # before the GPU is touched (fork pool)
+        log(f"cpu baseline done: {cpu['value']:.4g} TFLOP/s on {cpu['cores']} cores")
+    log("gpu run")
     r = measure(w, args.partial, args.steps, args.warmup)
+    log(f"gpu run done: {r['ms_per_step']:.3f} ms/step")
     ms = r["ms_per_step"]
     value = r["f_alg"] / (ms * 1e-3) / 1e12
     st = r["stage_ms"]
@@ -297,6 +319,7 @@ def main():
     if not args.no_variants and args.workload == DEFAULT_WORKLOAD:
         var = {}
         for name in VARIANTS:
+            log(f"variant {name}")
             wv = make_workload(name)
             rv = measure(wv, args.partial, max(3, args.steps // 2), 2)
             stv = rv["stage_ms"]

@@ -139,38 +139,79 @@ __device__ __forceinline__ Item read_item(const int4* __restrict__ work, const i
   return r;
 }
 
+// One query row of a 32-row tile, as seen by lane l (row = tile*32 + l%32):
+// its position ti in the chunk's query list, its group head j and its token.
+struct Row {
+  int row, ti, j, t;
+  bool valid;
+};
+
+__device__ __forceinline__ Row row_of(int tile, int lr, int nrows, int g, const int32_t* __restrict__ qidx,
+                                      int pair0) {
+  Row r;
+  r.row = tile * 32 + lr;
+  r.valid = r.row < nrows;
+  r.ti = r.row / g;
+  r.j = r.row - r.ti * g;
+  r.t = r.valid ? qidx[pair0 + r.ti] : 0;
+  return r;
+}
+
+// Work-item order.  Workgroup i runs on XCD i % 8 (round-robin dispatch); XCD x
+// takes the contiguous range [x * per, (x + 1) * per) of the work list, in
+// order, so that neighbouring blocks (which share most of their query rows)
+// meet in the same L2.  The grid is a multiple of 8 covering 8 * per items.
+__device__ __forceinline__ int xcd_item(int nwork_total) {
+  const int per = (nwork_total + 7) >> 3;
+  const int i = blockIdx.x;
+  const int k = i >> 3;
+  const int wi = (i & 7) * per + k;
+  return (k < per && wi < nwork_total) ? wi : -1;
+}
+
+// Each wave walks the tiles wave, wave + 4, ...; the Q half-row and lse of the
+// next tile and the token of the tile after it are loaded while the current
+// tile computes, so the gathers overlap the MFMA work.
+constexpr int kWaves = kAttnThreads / 64;
+
+// Waves per SIMD the register budget aims for: two (<= 256 registers) where
+// the tile state fits, one (<= 512) for the wide head dim / long blocks.
+template <int D, int BK>
+constexpr int attn_waves_per_eu() { return (D >= 256 || (D >= 128 && BK >= 128)) ? 1 : 2; }
+
 // ---- statistics -------------------------------------------------------------
 template <typename T, int D, int BK>
-__global__ __launch_bounds__(kAttnThreads) void k_stats(const T* __restrict__ q, const T* __restrict__ k,
-                                                        const int32_t* __restrict__ counts,
-                                                        const int32_t* __restrict__ offsets,
-                                                        const int32_t* __restrict__ qidx,
-                                                        const int4* __restrict__ work,
-                                                        const int32_t* __restrict__ nwork, float2* __restrict__ st,
-                                                        int H, int g, int NB, int CT, float scale_log2) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_stats(
+    const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
+    const int32_t* __restrict__ nwork, float2* __restrict__ st, int H, int g, int NB, int CT, float scale_log2) {
+  using V8 = typename Vec8<T>::type;
+  constexpr int KS = D / 16, KT = BK / 32;
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
-  const int wi = blockIdx.x;
-  if (wi >= nwork[0]) return;
+  const int wi = xcd_item(nwork[0]);
+  if (wi < 0) return;
   const Item it = read_item(work, counts, offsets, wi, NB, CT, BK);
   stage_k<T, D, BK>(Ks, k, it.bs, it.nkeys, H, it.h);
-  __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
   const int HQ = H * g, nrows = it.ntok * g, ntile = (nrows + 31) / 32;
-  for (int tile = wave; tile < ntile; tile += kAttnThreads / 64) {
-    const int row = tile * 32 + lr;
-    const bool valid = row < nrows;
-    const int ti = row / g, j = row - ti * g;
-    const int t = valid ? qidx[it.pair0 + ti] : 0;
-    typename Vec8<T>::type qf[D / 16];
-    load_q_half<T, D>(q, t, it.h * g + j, HQ, hl, valid, qf);
-    f32x16 s[BK / 32];
+  Row r0 = row_of(wave, lr, nrows, g, qidx, it.pair0);
+  Row r1 = row_of(wave + kWaves, lr, nrows, g, qidx, it.pair0);
+  V8 qf[KS];
+  load_q_half<T, D>(q, r0.t, it.h * g + r0.j, HQ, hl, r0.valid, qf);
+  __syncthreads();
+  for (int tile = wave; tile < ntile; tile += kWaves) {
+    V8 qn[KS];
+    load_q_half<T, D>(q, r1.t, it.h * g + r1.j, HQ, hl, r1.valid, qn);
+    const Row r2 = row_of(tile + 2 * kWaves, lr, nrows, g, qidx, it.pair0);
+
+    f32x16 s[KT];
     qk_tile<T, D, BK>(Ks, qf, lr, hl, s);
-    const int lim = valid ? t - it.bs : -1;  // key (block-local) visible iff key <= lim
+    const int lim = r0.valid ? r0.t - it.bs : -1;  // key (block-local) visible iff key <= lim
     float m = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < BK / 32; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
@@ -179,20 +220,27 @@ __global__ __launch_bounds__(kAttnThreads) void k_stats(const T* __restrict__ q,
     m = fmaxf(m, __shfl_xor(m, 32, 64));
     float l = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < BK / 32; ++kt)
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
         if (key <= lim) l += __builtin_amdgcn_exp2f(s[kt][r] * scale_log2 - m);
       }
     l += __shfl_xor(l, 32, 64);
-    if (valid && hl == 0) st[(size_t)it.pair0 * g + row] = make_float2(m, l);
+    if (r0.valid && hl == 0) st[(size_t)it.pair0 * g + r0.row] = make_float2(m, l);
+
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
+    r0 = r1;
+    r1 = r2;
   }
 }
 
 // One thread per (token, query head): merge the per-block (max, sum) pairs of
 // the token's selecting entries, in slot order, into the row max and lse
-// (stored in natural-log units).
+// (stored in natural-log units).  Slots are read 8 at a time and the pairs
+// loaded unconditionally (row 0 stands in for empty slots) so that the loads
+// are independent.
 __global__ __launch_bounds__(256) void k_stats_combine(const int32_t* __restrict__ slot,
                                                        const float2* __restrict__ st, float* __restrict__ row_max,
                                                        float* __restrict__ lse, int N, int H, int g, int T) {
@@ -202,17 +250,21 @@ __global__ __launch_bounds__(256) void k_stats_combine(const int32_t* __restrict
   const int t = (int)(idx / HQ), hq = (int)(idx - (int64_t)t * HQ);
   const int h = hq / g, j = hq - h * g;
   const int32_t* sl = slot + ((size_t)h * N + t) * T;
-  float M = -INFINITY;
-  for (int jj = 0; jj < T; ++jj) {
-    const int s = sl[jj];
-    if (s >= 0) M = fmaxf(M, st[(size_t)s * g + j].x);
-  }
-  float L = 0.f;
-  for (int jj = 0; jj < T; ++jj) {
-    const int s = sl[jj];
-    if (s >= 0) {
-      const float2 v = st[(size_t)s * g + j];
-      L += v.y * __builtin_amdgcn_exp2f(v.x - M);
+  float M = -INFINITY, L = 0.f;
+  for (int j0 = 0; j0 < T; j0 += 8) {
+    int sv[8];
+    float2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sv[u] = j0 + u < T ? sl[j0 + u] : -1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = st[(size_t)max(sv[u], 0) * g + j];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (sv[u] >= 0) {
+        const float mn = fmaxf(M, v[u].x);
+        L = L * __builtin_amdgcn_exp2f(M - mn) + v[u].y * __builtin_amdgcn_exp2f(v[u].x - mn);
+        M = mn;
+      }
     }
   }
   if (L > 0.f) {
@@ -225,58 +277,108 @@ __global__ __launch_bounds__(256) void k_stats_combine(const int32_t* __restrict
 }
 
 // ---- main -------------------------------------------------------------------
+// Output tile epilogue.  The O^T accumulators give each lane 4 consecutive
+// head-dim values of one row, 8 values apart, which would make 8-byte stores
+// 256 bytes apart.  Each wave instead passes its 32 x D tile through a private
+// LDS buffer, 64 columns at a time, and writes it back row-contiguously with
+// 16 bytes per lane: every store instruction covers whole 128-byte lines.
+// Partial rows are written once and read once by the reduction, so the
+// stores are non-temporal (they should not evict the gathered Q rows).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kStageCols = 64;
+
 template <typename PT>
-__device__ __forceinline__ void store4(PT* p, float a, float b, float c, float d);
+constexpr int stage_pitch() { return kStageCols + 16 / (int)sizeof(PT); }
+
+template <typename PT>
+__device__ __forceinline__ void stage_write4(PT* p, float a, float b, float c, float d);
 template <>
-__device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+__device__ __forceinline__ void stage_write4<float>(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 template <>
-__device__ __forceinline__ void store4<__bf16>(__bf16* p, float a, float b, float c, float d) {
+__device__ __forceinline__ void stage_write4<__bf16>(__bf16* p, float a, float b, float c, float d) {
   typedef __bf16 v4 __attribute__((ext_vector_type(4)));
-  *reinterpret_cast<v4*>(p) = v4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d});
 }
 template <>
-__device__ __forceinline__ void store4<_Float16>(_Float16* p, float a, float b, float c, float d) {
+__device__ __forceinline__ void stage_write4<_Float16>(_Float16* p, float a, float b, float c, float d) {
   typedef _Float16 v4 __attribute__((ext_vector_type(4)));
-  *reinterpret_cast<v4*>(p) = v4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d};
+  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d});
+}
+
+// o[mt][r] holds O^T[d = mt*32 + 8*(r/4) + 4*hl + r%4][row = lane % 32].
+// Writes rows [0, rows) of the tile to dst (row-major, pitch D).
+template <typename PT, int D>
+__device__ __forceinline__ void store_tile(PT* __restrict__ stage, const f32x16* o, int lane, int rows,
+                                           PT* __restrict__ dst) {
+  constexpr int P = stage_pitch<PT>();
+  constexpr int EPL = 16 / (int)sizeof(PT);  // elements per 16-byte lane store
+  constexpr int LPR = kStageCols / EPL;      // lanes per staged row
+  constexpr int RPI = 64 / LPR;              // rows per store instruction
+  const int lr = lane & 31, hl = lane >> 5;
+#pragma unroll
+  for (int c = 0; c < D / kStageCols; ++c) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16& acc = o[2 * c + m];
+        stage_write4<PT>(stage + lr * P + m * 32 + 8 * q4 + 4 * hl, acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2],
+                         acc[4 * q4 + 3]);
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = i * RPI + lane / LPR, col = (lane % LPR) * EPL;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * P + col);
+      if (row < rows) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst + (size_t)row * D + c * kStageCols + col));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 }
 
 template <typename T, int D, int BK, typename PT>
-__global__ __launch_bounds__(kAttnThreads) void k_main(const T* __restrict__ q, const T* __restrict__ k,
-                                                       const T* __restrict__ v, const int32_t* __restrict__ counts,
-                                                       const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ qidx,
-                                                       const int4* __restrict__ work,
-                                                       const int32_t* __restrict__ nwork,
-                                                       const float* __restrict__ lse, PT* __restrict__ partial, int H,
-                                                       int g, int NB, int CT, float scale_log2) {
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
+    const int32_t* __restrict__ nwork, const float* __restrict__ lse, PT* __restrict__ partial, int H, int g,
+    int NB, int CT, float scale_log2) {
   using V8 = typename Vec8<T>::type;
-  constexpr int KT = BK / 32, KK = BK / 16, MT = D / 32;
+  constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
   __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
-  const int wi = blockIdx.x;
-  if (wi >= nwork[0]) return;
+  __shared__ __attribute__((aligned(16))) PT Ot[kWaves * 32 * stage_pitch<PT>()];
+  const int wi = xcd_item(nwork[0]);
+  if (wi < 0) return;
   const Item it = read_item(work, counts, offsets, wi, NB, CT, BK);
   stage_k<T, D, BK>(Ks, k, it.bs, it.nkeys, H, it.h);
   stage_vt<T, D, BK>(Vt, v, it.bs, it.nkeys, H, it.h);
-  __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
   const int HQ = H * g, nrows = it.ntok * g, ntile = (nrows + 31) / 32;
-  for (int tile = wave; tile < ntile; tile += kAttnThreads / 64) {
-    const int row = tile * 32 + lr;
-    const bool valid = row < nrows;
-    const int ti = row / g, j = row - ti * g;
-    const int t = valid ? qidx[it.pair0 + ti] : 0;
-    const int hq = it.h * g + j;
-    V8 qf[D / 16];
-    load_q_half<T, D>(q, t, hq, HQ, hl, valid, qf);
+  Row r0 = row_of(wave, lr, nrows, g, qidx, it.pair0);
+  Row r1 = row_of(wave + kWaves, lr, nrows, g, qidx, it.pair0);
+  V8 qf[KS];
+  load_q_half<T, D>(q, r0.t, it.h * g + r0.j, HQ, hl, r0.valid, qf);
+  float l2 = r0.valid ? lse[(size_t)r0.t * HQ + it.h * g + r0.j] * kLog2e : 0.f;
+  __syncthreads();
+  for (int tile = wave; tile < ntile; tile += kWaves) {
+    V8 qn[KS];
+    load_q_half<T, D>(q, r1.t, it.h * g + r1.j, HQ, hl, r1.valid, qn);
+    const float l2n = r1.valid ? lse[(size_t)r1.t * HQ + it.h * g + r1.j] * kLog2e : 0.f;
+    const Row r2 = row_of(tile + 2 * kWaves, lr, nrows, g, qidx, it.pair0);
+
     f32x16 s[KT];
     qk_tile<T, D, BK>(Ks, qf, lr, hl, s);
-    const float l2 = valid ? lse[(size_t)t * HQ + hq] * kLog2e : 0.f;
-    const int lim = valid ? t - it.bs : -1;
+    const int lim = r0.valid ? r0.t - it.bs : -1;
     V8 pb[KK];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
@@ -297,46 +399,52 @@ __global__ __launch_bounds__(kAttnThreads) void k_main(const T* __restrict__ q, 
         o[mt] = mfma32(a, pb[kk], o[mt]);
       }
     }
-    if (valid) {
-      PT* dst = partial + ((size_t)it.pair0 * g + row) * D + 4 * hl;
+    store_tile<PT, D>(Ot + wave * 32 * stage_pitch<PT>(), o, lane, min(32, nrows - tile * 32),
+                      partial + ((size_t)it.pair0 * g + (size_t)tile * 32) * D);
+
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          store4<PT>(dst + mt * 32 + 8 * q4, o[mt][4 * q4], o[mt][4 * q4 + 1], o[mt][4 * q4 + 2], o[mt][4 * q4 + 3]);
-    }
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
+    l2 = l2n;
+    r0 = r1;
+    r1 = r2;
   }
 }
 
 // ---- reduce -----------------------------------------------------------------
 template <typename PT>
-__device__ __forceinline__ void load_acc8(const PT* p, float* acc);
+struct Part8;
 template <>
-__device__ __forceinline__ void load_acc8<float>(const float* p, float* acc) {
-  const f32x4 a = reinterpret_cast<const f32x4*>(p)[0];
-  const f32x4 b = reinterpret_cast<const f32x4*>(p)[1];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc[i] += a[i];
-    acc[4 + i] += b[i];
+struct Part8<float> {
+  struct type {
+    f32x4 a, b;
+  };
+  static __device__ __forceinline__ type load(const float* p) {
+    return type{__builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)),
+                __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1)};
   }
-}
+  static __device__ __forceinline__ float at(const type& x, int i) { return i < 4 ? x.a[i] : x.b[i - 4]; }
+};
 template <>
-__device__ __forceinline__ void load_acc8<__bf16>(const __bf16* p, float* acc) {
-  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] += (float)a[i];
-}
+struct Part8<__bf16> {
+  using type = bf16x8;
+  static __device__ __forceinline__ type load(const __bf16* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+  }
+  static __device__ __forceinline__ float at(const type& x, int i) { return (float)x[i]; }
+};
 template <>
-__device__ __forceinline__ void load_acc8<_Float16>(const _Float16* p, float* acc) {
-  const f16x8 a = *reinterpret_cast<const f16x8*>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] += (float)a[i];
-}
+struct Part8<_Float16> {
+  using type = f16x8;
+  static __device__ __forceinline__ type load(const _Float16* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f16x8*>(p));
+  }
+  static __device__ __forceinline__ float at(const type& x, int i) { return (float)x[i]; }
+};
 
 // Items (token t, KV head h), t-major so that the outputs of consecutive items
 // are adjacent.  TPI threads per item, each owning 8-element vectors of the
-// g*D outputs.
+// g*D outputs.  Slots are taken 8 at a time; the 8 partial loads are issued
+// together (row 0 stands in for empty slots) and summed in slot order.
 template <typename T, typename PT>
 __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __restrict__ slot,
                                                            const PT* __restrict__ partial, T* __restrict__ out,
@@ -353,9 +461,17 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __rest
   T* dst = out + ((size_t)t * H + h) * GD;
   for (int vec = sub; vec < nvec; vec += TPI) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int jj = 0; jj < Tn; ++jj) {
-      const int s = sl[jj];
-      if (s >= 0) load_acc8<PT>(partial + (size_t)s * GD + vec * 8, acc);
+    for (int j0 = 0; j0 < Tn; j0 += 8) {
+      int sv[8];
+      typename Part8<PT>::type x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sv[u] = j0 + u < Tn ? sl[j0 + u] : -1;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = Part8<PT>::load(partial + (size_t)max(sv[u], 0) * GD + vec * 8);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += sv[u] >= 0 ? Part8<PT>::at(x[u], i) : 0.f;
     }
     typename Vec8<T>::type o;
 #pragma unroll
@@ -385,7 +501,7 @@ void stats_typed(const Geometry& geo, const void* q, const void* k, const fsa_in
                  hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
-  hipLaunchKernelGGL((k_stats<T, D, BK>), dim3((unsigned)geo.max_work), dim3(kAttnThreads), 0, stream,
+  hipLaunchKernelGGL((k_stats<T, D, BK>), dim3((unsigned)((geo.max_work + 7) / 8 * 8)), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), p.counts, p.offsets, p.qidx, p.work, p.nwork,
                      st, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
 }
@@ -395,7 +511,7 @@ void main_typed(const Geometry& geo, const void* q, const void* k, const void* v
                 const float* lse, void* partial, hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
-  hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3((unsigned)geo.max_work), dim3(kAttnThreads), 0, stream,
+  hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3((unsigned)((geo.max_work + 7) / 8 * 8)), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), p.counts,
                      p.offsets, p.qidx, p.work, p.nwork, lse, static_cast<PT*>(partial), geo.H, geo.g, geo.NB,
                      geo.chunk_tokens, sl2);
