@@ -114,9 +114,19 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   off = round_up(off + 16, 256);
   geo->aux_work = off;
   off = round_up(off + (size_t)std::max<int64_t>(geo->max_work, 1) * 16, 256);
+  geo->aux_work_sorted = off;
+  off = round_up(off + (size_t)std::max<int64_t>(geo->max_work, 1) * 16, 256);
+  {
+    int shift = 6;
+    while (H * ((N + (int64_t(1) << shift) - 1) >> shift) > kSortBucketsMax) ++shift;
+    geo->sort_shift = shift;
+    geo->sort_buckets_per_head = (int32_t)std::max<int64_t>((N + (int64_t(1) << shift) - 1) >> shift, 1);
+    geo->sort_buckets = (int32_t)(H * geo->sort_buckets_per_head);
+  }
   geo->aux_bytes = off;
   geo->build_ws_bytes = round_up((size_t)std::max<int64_t>(H * geo->ntiles * NB, 1) * 4, 256);
-  const size_t rows = (size_t)std::max<int64_t>(geo->max_pairs, 1) * (size_t)g;
+  geo->dump_row = std::max<int64_t>(geo->max_pairs, 1) * g;
+  const size_t rows = (size_t)geo->dump_row + 32;
   geo->stats_ws_bytes = round_up(rows * 8, 256);
   geo->partial_ws_bytes = round_up(rows * (size_t)geo->d * (geo->partial_dtype == FSA_PARTIAL_FP32 ? 4 : 2), 256);
   return FSA_OK;

@@ -16,18 +16,23 @@
 //
 // Work items come from the index builder: (segment f, first query of the
 // chunk, block start token, sequence end).  Rows of a chunk are
-// (query, group head) pairs, query-major: row = i * g + j.
+// (query, group head) pairs, query-major: row = i * g + j.  A row table in
+// LDS gives each row its Q / lse row index and its token.
+//
+// Q tiles.  A 32-row tile is gathered with coalesced 16-byte loads (lanes in
+// row order, so one load instruction reads whole rows: for g = 4 and d = 128,
+// one token's four head rows, 1 KB), staged in a per-wave LDS tile, and read
+// back in the MFMA operand layout.  The same LDS tile later stages the output
+// tile for row-contiguous stores.
 //
 // MFMA tiling (v_mfma_f32_32x32x16, wave64).  A 32-row query tile meets the
 // block's keys as S^T (keys x rows) so that each lane ends up owning one query
 // row: lane l holds column l % 32 of S^T.  The same registers, cast to 16-bit,
-// are the B operand of O^T = V^T P^T, so P never leaves the registers.  The
-// head dimension is the contraction of S^T; lane half hl = l / 32 supplies
-// d in [hl * D/2, (hl + 1) * D/2), a permutation of the contraction index that
-// A (K from LDS) and B (Q from HBM) share, so each lane reads one contiguous
-// half row of Q.  V is staged transposed (Vt[d][key]) with the keys of every
-// 16-key group permuted so that the 8 keys a lane contributes to one MFMA are
-// adjacent in LDS.
+// are the B operand of O^T = V^T P^T, so P never leaves the registers.  V is
+// staged transposed (Vt[d][key]) with the keys of every 16-key group permuted
+// so that the 8 keys a lane contributes to one MFMA are adjacent in LDS.
+#include <type_traits>
+
 #include "fsa_internal.h"
 
 namespace fsa {
@@ -35,6 +40,12 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kWaves = kAttnThreads / 64;
+constexpr int kRowTable = kRowsPerItem + 32;  // rows of the last tile past the chunk included
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 template <typename T>
 __device__ __forceinline__ typename Vec8<T>::type zero8() {
@@ -54,12 +65,15 @@ __device__ __forceinline__ uint16_t bits16(T x) {
   return __builtin_bit_cast(uint16_t, x);
 }
 
-// LDS layouts (elements).  K: [BK][D + 8]; Vt: [D][BK + 8].  The 8-element
-// pads spread the 16-byte reads of 32 consecutive rows over all banks.
+// LDS layouts (elements).  K: [BK][D + 8]; Vt: [D][BK + 8]; per-wave tile:
+// [32][D + 8].  The 8-element pads spread the 16-byte reads of consecutive
+// rows over all banks.
 template <int D>
 constexpr int k_ld() { return D + 8; }
 template <int BK>
 constexpr int vt_ld() { return BK + 8; }
+template <int D>
+constexpr int tile_ld() { return D + 8; }
 
 // Position of key w (within its 16-key group) in the permuted Vt row: lane half
 // hl contributes keys {4hl..4hl+3, 8+4hl..8+4hl+3} as MFMA elements e = 0..7.
@@ -99,30 +113,6 @@ __device__ __forceinline__ void stage_vt(T* __restrict__ Vt, const T* __restrict
   }
 }
 
-// S^T tile: s[kt][r] = (K Q^T)[key = kt*32 + 8*(r/4) + 4*hl + r%4][row = l%32].
-template <typename T, int D, int BK>
-__device__ __forceinline__ void qk_tile(const T* __restrict__ Ks, const typename Vec8<T>::type* qf, int lr, int hl,
-                                        f32x16* s) {
-  constexpr int KS = D / 16, KT = BK / 32;
-#pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    f32x16 acc = {};
-    const T* kp = Ks + (kt * 32 + lr) * k_ld<D>() + hl * (D / 2);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = mfma32(load8(kp + ks * 8), qf[ks], acc);
-    s[kt] = acc;
-  }
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void load_q_half(const T* __restrict__ q, int t, int hq, int HQ, int hl, bool valid,
-                                            typename Vec8<T>::type* qf) {
-  constexpr int KS = D / 16;
-  const T* qp = q + ((size_t)t * HQ + hq) * D + hl * (D / 2);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) qf[ks] = valid ? load8(qp + ks * 8) : zero8<T>();
-}
-
 struct Item {
   int h, ntok, pair0, bs, nkeys;
 };
@@ -139,28 +129,70 @@ __device__ __forceinline__ Item read_item(const int4* __restrict__ work, const i
   return r;
 }
 
-// One query row of a 32-row tile, as seen by lane l (row = tile*32 + l%32):
-// its position ti in the chunk's query list, its group head j and its token.
-struct Row {
-  int row, ti, j, t;
-  bool valid;
-};
+// Row table of a chunk: rows r < ntile*32 get ridx = the row of Q / lse /
+// row_max (token * HQ + h * g + j) and tok = the query token, or -1 for rows
+// past the chunk (their ridx points at token 0 so that loads stay in bounds).
+__device__ __forceinline__ void stage_rows(int* __restrict__ ridx, int* __restrict__ rtok,
+                                           const int32_t* __restrict__ qidx, const Item& it, int g, int HQ,
+                                           int nrows_padded) {
+  const int nrows = it.ntok * g;
+  for (int r = threadIdx.x; r < nrows_padded; r += kAttnThreads) {
+    const int ti = r / g, j = r - ti * g;
+    const bool valid = r < nrows;
+    const int t = valid ? qidx[it.pair0 + ti] : 0;
+    ridx[r] = t * HQ + it.h * g + (valid ? j : 0);
+    rtok[r] = valid ? t : -1;
+  }
+}
 
-__device__ __forceinline__ Row row_of(int tile, int lr, int nrows, int g, const int32_t* __restrict__ qidx,
-                                      int pair0) {
-  Row r;
-  r.row = tile * 32 + lr;
-  r.valid = r.row < nrows;
-  r.ti = r.row / g;
-  r.j = r.row - r.ti * g;
-  r.t = r.valid ? qidx[pair0 + r.ti] : 0;
-  return r;
+// Coalesced gather of the Q rows of one 32-row tile: vector v of lane l holds
+// tile elements (v*64 + l)*8 .. +8, i.e. row (v*64 + l)*8 / D, column
+// (v*64 + l)*8 % D.
+template <typename T, int D>
+__device__ __forceinline__ void load_q_tile(const T* __restrict__ q, const int* __restrict__ ridx, int tile,
+                                            int lane, typename Vec8<T>::type* qv) {
+#pragma unroll
+  for (int v = 0; v < D / 16; ++v) {
+    const int e = (v * 64 + lane) * 8;
+    const int r = e / D, c = e % D;
+    qv[v] = load8(q + (size_t)ridx[tile * 32 + r] * D + c);
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void put_q_tile(T* __restrict__ qt, int lane, const typename Vec8<T>::type* qv) {
+#pragma unroll
+  for (int v = 0; v < D / 16; ++v) {
+    const int e = (v * 64 + lane) * 8;
+    *reinterpret_cast<typename Vec8<T>::type*>(qt + (e / D) * tile_ld<D>() + e % D) = qv[v];
+  }
+}
+
+// S^T tile from the staged Q tile: s[kt][r] = (K Q^T)[key = kt*32 + 8*(r/4) +
+// 4*hl + r%4][row = l%32].  Lane half hl supplies the contraction elements
+// ks*16 + hl*8 .. +8 of both operands.
+template <typename T, int D, int BK>
+__device__ __forceinline__ void qk_tile(const T* __restrict__ Ks, const T* __restrict__ qt, int lr, int hl,
+                                        f32x16* s) {
+  constexpr int KS = D / 16, KT = BK / 32;
+  typename Vec8<T>::type b[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) b[ks] = load8(qt + lr * tile_ld<D>() + ks * 16 + hl * 8);
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) {
+    f32x16 acc = {};
+    const T* kp = Ks + (kt * 32 + lr) * k_ld<D>() + hl * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = mfma32(load8(kp + ks * 16), b[ks], acc);
+    s[kt] = acc;
+  }
 }
 
 // Work-item order.  Workgroup i runs on XCD i % 8 (round-robin dispatch); XCD x
 // takes the contiguous range [x * per, (x + 1) * per) of the work list, in
-// order, so that neighbouring blocks (which share most of their query rows)
-// meet in the same L2.  The grid is a multiple of 8 covering 8 * per items.
+// order (the list is sorted by query token), so that the items that share an
+// XCD's L2 gather neighbouring query rows.  The grid is a multiple of 8
+// covering 8 * per items.
 __device__ __forceinline__ int xcd_item(int nwork_total) {
   const int per = (nwork_total + 7) >> 3;
   const int i = blockIdx.x;
@@ -169,71 +201,111 @@ __device__ __forceinline__ int xcd_item(int nwork_total) {
   return (k < per && wi < nwork_total) ? wi : -1;
 }
 
-// Each wave walks the tiles wave, wave + 4, ...; the Q half-row and lse of the
-// next tile and the token of the tile after it are loaded while the current
-// tile computes, so the gathers overlap the MFMA work.
-constexpr int kWaves = kAttnThreads / 64;
+// Tile loop with a ring of S register slots: slot (i mod S) holds the
+// prefetched Q vectors (and lse) of the wave's i-th tile.  Before computing
+// tile i the wave issues the loads of tile i + S - 1.  The loop is unrolled by
+// S so that every slot index is a compile-time constant and the slots stay in
+// registers.
+template <int S, typename StepFn>
+__device__ __forceinline__ void tile_ring(int first, int ntile, StepFn&& step) {
+  for (int tile = first; tile < ntile; tile += S * kWaves) {
+    const bool more = [&]<int... I>(std::integer_sequence<int, I...>) {
+      return ((tile + I * kWaves < ntile ? (step(std::integral_constant<int, I>{}, tile + I * kWaves), true) : false) &&
+              ...);
+    }(std::make_integer_sequence<int, S>{});
+    if (!more) break;
+  }
+}
 
 // Waves per SIMD the register budget aims for: two (<= 256 registers) where
 // the tile state fits, one (<= 512) for the wide head dim / long blocks.
 template <int D, int BK>
 constexpr int attn_waves_per_eu() { return (D >= 256 || (D >= 128 && BK >= 128)) ? 1 : 2; }
 
+// Register slots of the Q ring (prefetch depth + 1), per kernel.
+template <int D, int BK>
+constexpr int q_slots_main() { return 2; }
+template <int D, int BK>
+constexpr int q_slots_stats() { return 2; }
+
+// Every key of the block is visible to every row of the tile: the block lies
+// entirely before each row's token (rows of a chunk are in token order, so
+// only the first tiles of a query's own block need the causal mask).
+template <int BK>
+__device__ __forceinline__ bool tile_unmasked(int tok, int bs) {
+  return __all(tok < 0 || tok - bs >= BK - 1);
+}
+
+// scale * max over visible keys and the exp-sum relative to it, in base 2,
+// for the lane's row (lanes l and l + 32 hold the two key halves).
+template <int BK, bool MASKED>
+__device__ __forceinline__ float2 row_stats(const f32x16* s, int hl, int lim, float c) {
+  constexpr int KT = BK / 32;
+  float m = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+      if (!MASKED || key <= lim) m = fmaxf(m, s[kt][r]);
+    }
+  m = fmaxf(m, __shfl_xor(m, 32, 64)) * c;
+  float l = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -m));
+      l += (!MASKED || key <= lim) ? e : 0.f;
+    }
+  l += __shfl_xor(l, 32, 64);
+  return make_float2(m, l);
+}
+
 // ---- statistics -------------------------------------------------------------
 template <typename T, int D, int BK>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_stats(
     const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
-    const int32_t* __restrict__ nwork, float2* __restrict__ st, int H, int g, int NB, int CT, float scale_log2) {
+    const int32_t* __restrict__ nwork, float2* __restrict__ st, size_t dump_row, int H, int g, int NB, int CT,
+    float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32;
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
+  __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
+  __shared__ int ridx[kRowTable], rtok[kRowTable];
   const int wi = xcd_item(nwork[0]);
   if (wi < 0) return;
   const Item it = read_item(work, counts, offsets, wi, NB, CT, BK);
+  const int HQ = H * g, nrows = it.ntok * g, ntile = (nrows + 31) / 32;
   stage_k<T, D, BK>(Ks, k, it.bs, it.nkeys, H, it.h);
+  stage_rows(ridx, rtok, qidx, it, g, HQ, ntile * 32);
+  __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
-  const int HQ = H * g, nrows = it.ntok * g, ntile = (nrows + 31) / 32;
-  Row r0 = row_of(wave, lr, nrows, g, qidx, it.pair0);
-  Row r1 = row_of(wave + kWaves, lr, nrows, g, qidx, it.pair0);
-  V8 qf[KS];
-  load_q_half<T, D>(q, r0.t, it.h * g + r0.j, HQ, hl, r0.valid, qf);
-  __syncthreads();
-  for (int tile = wave; tile < ntile; tile += kWaves) {
-    V8 qn[KS];
-    load_q_half<T, D>(q, r1.t, it.h * g + r1.j, HQ, hl, r1.valid, qn);
-    const Row r2 = row_of(tile + 2 * kWaves, lr, nrows, g, qidx, it.pair0);
+  T* const qt = Qt + wave * 32 * tile_ld<D>();
+  constexpr int S = q_slots_stats<D, BK>();
+  V8 qs[S][KS];
+#pragma unroll
+  for (int i = 0; i + 1 < S; ++i)
+    if (wave + i * kWaves < ntile) load_q_tile<T, D>(q, ridx, wave + i * kWaves, lane, qs[i]);
 
+  tile_ring<S>(wave, ntile, [&](auto slot, int tl) {
+    constexpr int cur = decltype(slot)::value, nxt = (cur + S - 1) % S;
+    if (tl + (S - 1) * kWaves < ntile) load_q_tile<T, D>(q, ridx, tl + (S - 1) * kWaves, lane, qs[nxt]);
+    put_q_tile<T, D>(qt, lane, qs[cur]);
     f32x16 s[KT];
-    qk_tile<T, D, BK>(Ks, qf, lr, hl, s);
-    const int lim = r0.valid ? r0.t - it.bs : -1;  // key (block-local) visible iff key <= lim
-    float m = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (key <= lim) m = fmaxf(m, s[kt][r] * scale_log2);
-      }
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
-    float l = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (key <= lim) l += __builtin_amdgcn_exp2f(s[kt][r] * scale_log2 - m);
-      }
-    l += __shfl_xor(l, 32, 64);
-    if (r0.valid && hl == 0) st[(size_t)it.pair0 * g + r0.row] = make_float2(m, l);
-
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
-    r0 = r1;
-    r1 = r2;
-  }
+    qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
+    const int row = tl * 32 + lr;
+    const int tok = rtok[row];
+    float2 ml;
+    if (tile_unmasked<BK>(tok, it.bs)) ml = row_stats<BK, false>(s, hl, 0, scale_log2);
+    else ml = row_stats<BK, true>(s, hl, tok < 0 ? -1 : tok - it.bs, scale_log2);
+    // lanes l and l + 32 store the same pair; rows past the chunk go to the dump
+    st[tok >= 0 ? (size_t)it.pair0 * g + row : dump_row + lr] = ml;
+  });
 }
 
 // One thread per (token, query head): merge the per-block (max, sum) pairs of
@@ -278,56 +350,57 @@ __global__ __launch_bounds__(256) void k_stats_combine(const int32_t* __restrict
 
 // ---- main -------------------------------------------------------------------
 // Output tile epilogue.  The O^T accumulators give each lane 4 consecutive
-// head-dim values of one row, 8 values apart, which would make 8-byte stores
-// 256 bytes apart.  Each wave instead passes its 32 x D tile through a private
-// LDS buffer, 64 columns at a time, and writes it back row-contiguously with
-// 16 bytes per lane: every store instruction covers whole 128-byte lines.
-// Partial rows are written once and read once by the reduction, so the
-// stores are non-temporal (they should not evict the gathered Q rows).
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kStageCols = 64;
+// head-dim values of one row, 8 values apart.  Each wave passes its 32 x D
+// output tile through its LDS tile (row pitch (D + 8) * 2 bytes: all D
+// columns of 16-bit partials at once, or D/2 columns of fp32 partials twice)
+// and writes it back row-contiguously with 16 bytes per lane, so that every
+// store instruction covers whole rows.  Partial rows are written once and
+// read once by the reduction, so the stores are non-temporal.  Rows past the
+// chunk are written to the dump rows after the last partial row, so every
+// lane stores unconditionally.
+template <typename PT, int D>
+struct Stage {
+  static constexpr int CW = sizeof(PT) == 4 ? D / 2 : D;  // columns per pass
+  static constexpr int P = CW + 16 / (int)sizeof(PT);      // row pitch (elements)
+};
 
 template <typename PT>
-constexpr int stage_pitch() { return kStageCols + 16 / (int)sizeof(PT); }
-
-template <typename PT>
-__device__ __forceinline__ void stage_write4(PT* p, float a, float b, float c, float d);
+__device__ __forceinline__ void stage_write4(PT* p, f32x4 x);
 template <>
-__device__ __forceinline__ void stage_write4<float>(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+__device__ __forceinline__ void stage_write4<float>(float* p, f32x4 x) {
+  *reinterpret_cast<f32x4*>(p) = x;
 }
 template <>
-__device__ __forceinline__ void stage_write4<__bf16>(__bf16* p, float a, float b, float c, float d) {
+__device__ __forceinline__ void stage_write4<__bf16>(__bf16* p, f32x4 x) {
   typedef __bf16 v4 __attribute__((ext_vector_type(4)));
-  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v4{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d});
+  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, __builtin_convertvector(x, v4));
 }
 template <>
-__device__ __forceinline__ void stage_write4<_Float16>(_Float16* p, float a, float b, float c, float d) {
+__device__ __forceinline__ void stage_write4<_Float16>(_Float16* p, f32x4 x) {
   typedef _Float16 v4 __attribute__((ext_vector_type(4)));
-  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, v4{(_Float16)a, (_Float16)b, (_Float16)c, (_Float16)d});
+  *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, __builtin_convertvector(x, v4));
 }
 
 // o[mt][r] holds O^T[d = mt*32 + 8*(r/4) + 4*hl + r%4][row = lane % 32].
-// Writes rows [0, rows) of the tile to dst (row-major, pitch D).
+// Writes rows [0, rows) of the tile to dst (row-major, pitch D), the others
+// to the matching rows of dump.
 template <typename PT, int D>
 __device__ __forceinline__ void store_tile(PT* __restrict__ stage, const f32x16* o, int lane, int rows,
-                                           PT* __restrict__ dst) {
-  constexpr int P = stage_pitch<PT>();
+                                           PT* __restrict__ dst, PT* __restrict__ dump) {
+  constexpr int CW = Stage<PT, D>::CW, P = Stage<PT, D>::P;
   constexpr int EPL = 16 / (int)sizeof(PT);  // elements per 16-byte lane store
-  constexpr int LPR = kStageCols / EPL;      // lanes per staged row
+  constexpr int LPR = CW / EPL;              // lanes per staged row
   constexpr int RPI = 64 / LPR;              // rows per store instruction
   const int lr = lane & 31, hl = lane >> 5;
 #pragma unroll
-  for (int c = 0; c < D / kStageCols; ++c) {
+  for (int c = 0; c < D / CW; ++c) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < CW / 32; ++m)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x16& acc = o[2 * c + m];
-        stage_write4<PT>(stage + lr * P + m * 32 + 8 * q4 + 4 * hl, acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2],
-                         acc[4 * q4 + 3]);
+        const f32x16& acc = o[(CW / 32) * c + m];
+        stage_write4<PT>(stage + lr * P + m * 32 + 8 * q4 + 4 * hl,
+                         f32x4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]});
       }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -336,7 +409,8 @@ __device__ __forceinline__ void store_tile(PT* __restrict__ stage, const f32x16*
     for (int i = 0; i < 32 / RPI; ++i) {
       const int row = i * RPI + lane / LPR, col = (lane % LPR) * EPL;
       const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * P + col);
-      if (row < rows) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst + (size_t)row * D + c * kStageCols + col));
+      PT* base = row < rows ? dst : dump;
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(base + (size_t)row * D + c * CW + col));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -344,70 +418,92 @@ __device__ __forceinline__ void store_tile(PT* __restrict__ stage, const f32x16*
   }
 }
 
+// P = exp2(s * c - lse2) as the 16-bit B operand of O^T = V^T P^T: element e
+// of pb[2*kt + u] is register r = 8*u + e of key tile kt.
+template <typename T, int BK, bool MASKED>
+__device__ __forceinline__ void probs(const f32x16* s, float c, float l2, int hl, int lim,
+                                      typename Vec8<T>::type* pb) {
+#pragma unroll
+  for (int kt = 0; kt < BK / 32; ++kt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * u + e;
+        const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -l2));
+        x[e] = (!MASKED || key <= lim) ? p : 0.f;
+      }
+      pb[2 * kt + u] = __builtin_convertvector(x, typename Vec8<T>::type);
+    }
+}
+
 template <typename T, int D, int BK, typename PT>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
-    const int32_t* __restrict__ nwork, const float* __restrict__ lse, PT* __restrict__ partial, int H, int g,
-    int NB, int CT, float scale_log2) {
+    const int32_t* __restrict__ nwork, const float* __restrict__ lse, PT* __restrict__ partial, size_t dump_row,
+    int H, int g, int NB, int CT, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
+  static_assert(32 * Stage<PT, D>::P * sizeof(PT) <= 32 * tile_ld<D>() * sizeof(T), "stage fits the Q tile");
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
   __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
-  __shared__ __attribute__((aligned(16))) PT Ot[kWaves * 32 * stage_pitch<PT>()];
+  __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
+  __shared__ int ridx[kRowTable], rtok[kRowTable];
   const int wi = xcd_item(nwork[0]);
   if (wi < 0) return;
   const Item it = read_item(work, counts, offsets, wi, NB, CT, BK);
+  const int HQ = H * g, nrows = it.ntok * g, ntile = (nrows + 31) / 32;
   stage_k<T, D, BK>(Ks, k, it.bs, it.nkeys, H, it.h);
   stage_vt<T, D, BK>(Vt, v, it.bs, it.nkeys, H, it.h);
+  stage_rows(ridx, rtok, qidx, it, g, HQ, ntile * 32);
+  __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
-  const int HQ = H * g, nrows = it.ntok * g, ntile = (nrows + 31) / 32;
-  Row r0 = row_of(wave, lr, nrows, g, qidx, it.pair0);
-  Row r1 = row_of(wave + kWaves, lr, nrows, g, qidx, it.pair0);
-  V8 qf[KS];
-  load_q_half<T, D>(q, r0.t, it.h * g + r0.j, HQ, hl, r0.valid, qf);
-  float l2 = r0.valid ? lse[(size_t)r0.t * HQ + it.h * g + r0.j] * kLog2e : 0.f;
-  __syncthreads();
-  for (int tile = wave; tile < ntile; tile += kWaves) {
-    V8 qn[KS];
-    load_q_half<T, D>(q, r1.t, it.h * g + r1.j, HQ, hl, r1.valid, qn);
-    const float l2n = r1.valid ? lse[(size_t)r1.t * HQ + it.h * g + r1.j] * kLog2e : 0.f;
-    const Row r2 = row_of(tile + 2 * kWaves, lr, nrows, g, qidx, it.pair0);
+  T* const qt = Qt + wave * 32 * tile_ld<D>();
+  PT* const stage = reinterpret_cast<PT*>(qt);
+  PT* const dump = partial + dump_row * D;
+  constexpr int S = q_slots_main<D, BK>();
+  V8 qs[S][KS];
+  float ls[S];
+#pragma unroll
+  for (int i = 0; i + 1 < S; ++i) {
+    if (wave + i * kWaves < ntile) {
+      load_q_tile<T, D>(q, ridx, wave + i * kWaves, lane, qs[i]);
+      ls[i] = lse[ridx[(wave + i * kWaves) * 32 + lr]];
+    }
+  }
 
+  tile_ring<S>(wave, ntile, [&](auto slot, int tl) {
+    constexpr int cur = decltype(slot)::value, nxt = (cur + S - 1) % S;
+    if (tl + (S - 1) * kWaves < ntile) {
+      load_q_tile<T, D>(q, ridx, tl + (S - 1) * kWaves, lane, qs[nxt]);
+      ls[nxt] = lse[ridx[(tl + (S - 1) * kWaves) * 32 + lr]];
+    }
+    put_q_tile<T, D>(qt, lane, qs[cur]);
     f32x16 s[KT];
-    qk_tile<T, D, BK>(Ks, qf, lr, hl, s);
-    const int lim = r0.valid ? r0.t - it.bs : -1;
+    qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
+    const int tok = rtok[tl * 32 + lr];
+    const float l2 = ls[cur] * kLog2e;
     V8 pb[KK];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const float p = key <= lim ? __builtin_amdgcn_exp2f(s[kt][r] * scale_log2 - l2) : 0.f;
-        pb[2 * kt + (r >> 3)][r & 7] = (T)p;
-      }
+    if (tile_unmasked<BK>(tok, it.bs)) probs<T, BK, false>(s, scale_log2, l2, hl, 0, pb);
+    else probs<T, BK, true>(s, scale_log2, l2, hl, tok < 0 ? -1 : tok - it.bs, pb);
     f32x16 o[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const V8 a = load8(Vt + (mt * 32 + lr) * vt_ld<BK>() + kk * 16 + hl * 8);
         o[mt] = mfma32(a, pb[kk], o[mt]);
       }
-    }
-    store_tile<PT, D>(Ot + wave * 32 * stage_pitch<PT>(), o, lane, min(32, nrows - tile * 32),
-                      partial + ((size_t)it.pair0 * g + (size_t)tile * 32) * D);
-
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = qn[ks];
-    l2 = l2n;
-    r0 = r1;
-    r1 = r2;
-  }
+    store_tile<PT, D>(stage, o, lane, min(32, nrows - tl * 32), partial + ((size_t)it.pair0 * g + (size_t)tl * 32) * D,
+                      dump);
+  });
 }
 
 // ---- reduce -----------------------------------------------------------------
@@ -492,7 +588,7 @@ struct Ptrs {
 
 inline Ptrs<int> index_ptrs(const Geometry& geo, const fsa_index& idx) {
   const char* aux = static_cast<const char*>(idx.aux);
-  return Ptrs<int>{idx.counts, idx.offsets, idx.qidx, reinterpret_cast<const int4*>(aux + geo.aux_work),
+  return Ptrs<int>{idx.counts, idx.offsets, idx.qidx, reinterpret_cast<const int4*>(aux + geo.aux_work_sorted),
                    reinterpret_cast<const int32_t*>(aux + geo.aux_nwork)};
 }
 
@@ -503,7 +599,7 @@ void stats_typed(const Geometry& geo, const void* q, const void* k, const fsa_in
   const float sl2 = geo.scale * kLog2e;
   hipLaunchKernelGGL((k_stats<T, D, BK>), dim3((unsigned)((geo.max_work + 7) / 8 * 8)), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), p.counts, p.offsets, p.qidx, p.work, p.nwork,
-                     st, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
+                     st, (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
 }
 
 template <typename T, int D, int BK, typename PT>
@@ -513,8 +609,8 @@ void main_typed(const Geometry& geo, const void* q, const void* k, const void* v
   const float sl2 = geo.scale * kLog2e;
   hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3((unsigned)((geo.max_work + 7) / 8 * 8)), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), p.counts,
-                     p.offsets, p.qidx, p.work, p.nwork, lse, static_cast<PT*>(partial), geo.H, geo.g, geo.NB,
-                     geo.chunk_tokens, sl2);
+                     p.offsets, p.qidx, p.work, p.nwork, lse, static_cast<PT*>(partial), (size_t)geo.dump_row, geo.H,
+                     geo.g, geo.NB, geo.chunk_tokens, sl2);
 }
 
 template <typename T, typename PT>

@@ -271,6 +271,65 @@ __global__ __launch_bounds__(kBuildThreads) void k_scatter(
   }
 }
 
+// ---- work order -------------------------------------------------------------
+// One workgroup.  Reorders the work list by (KV head, first query token of the
+// chunk) with a bucket sort (bucket = token >> shift), so that the items that
+// run together on one XCD gather a narrow window of query rows, which then
+// stays in that XCD's L2.  Within a bucket the order depends on atomics; the
+// order only affects scheduling: every item writes its own partial rows and
+// the reduction sums in slot order, so all outputs are unchanged.
+__global__ __launch_bounds__(kScanThreads) void k_work_sort(const int4* __restrict__ work_in,
+                                                            const int32_t* __restrict__ nwork,
+                                                            const int32_t* __restrict__ qidx,
+                                                            const int32_t* __restrict__ offsets, int NB, int shift,
+                                                            int nbh, int nbuckets, int4* __restrict__ work_out) {
+  extern __shared__ int cnt[];
+  __shared__ int64_t wave_tot[kScanThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int W = nwork[0];
+  for (int i = tid; i < nbuckets; i += kScanThreads) cnt[i] = 0;
+  __syncthreads();
+  auto key_of = [&](const int4& it) {
+    const int h = it.x / NB;
+    return h * nbh + (qidx[offsets[it.x] + it.y] >> shift);
+  };
+  for (int w = tid; w < W; w += kScanThreads) atomicAdd(&cnt[key_of(work_in[w])], 1);
+  __syncthreads();
+  // exclusive scan of the bucket counts, kScanItems buckets per thread per pass
+  int64_t carry = 0;
+  for (int base = 0; base < nbuckets; base += kScanThreads * kScanItems) {
+    int c[kScanItems];
+    int64_t local = 0;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+      const int b = base + tid * kScanItems + i;
+      c[i] = b < nbuckets ? cnt[b] : 0;
+      local += c[i];
+    }
+    const int64_t incl = wave_inclusive_scan(local);
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int64_t before = 0, total = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      if (w < wave) before += wave_tot[w];
+      total += wave_tot[w];
+    }
+    int64_t run = carry + before + incl - local;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+      const int b = base + tid * kScanItems + i;
+      if (b < nbuckets) cnt[b] = (int)run;
+      run += c[i];
+    }
+    carry += total;
+    __syncthreads();
+  }
+  for (int w = tid; w < W; w += kScanThreads) {
+    const int4 it = work_in[w];
+    work_out[atomicAdd(&cnt[key_of(it)], 1)] = it;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const int32_t* sel,
@@ -279,6 +338,7 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
   int32_t* gboff = reinterpret_cast<int32_t*>(aux + geo.aux_seq_gboff);
   int32_t* nwork = reinterpret_cast<int32_t*>(aux + geo.aux_nwork);
   int4* work = reinterpret_cast<int4*>(aux + geo.aux_work);
+  int4* work_sorted = reinterpret_cast<int4*>(aux + geo.aux_work_sorted);
   int32_t* tile_hist = static_cast<int32_t*>(ws);
   const int M = geo.H * geo.NB;
 
@@ -301,6 +361,9 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
     hipLaunchKernelGGL(k_scatter, dim3(geo.ntiles, geo.H), dim3(kBuildThreads), lds, stream, sel, cu_dev, gboff,
                        geo.num_seqs, geo.N, geo.T, Tp, tps, geo.BK, geo.tile_tokens, geo.ntiles, geo.NB, geo.win_max,
                        tile_hist, idx.offsets, idx.qidx, idx.slot);
+    hipLaunchKernelGGL(k_work_sort, dim3(1), dim3(kScanThreads), geo.sort_buckets * sizeof(int), stream, work, nwork,
+                       idx.qidx, idx.offsets, geo.NB, geo.sort_shift, geo.sort_buckets_per_head, geo.sort_buckets,
+                       work_sorted);
   }
   return hipGetLastError();
 }

@@ -19,6 +19,7 @@ constexpr int kWinMax = 7680;          // max global blocks one tile can touch (
 constexpr int kAttnThreads = 256;      // 4 waves per main / stats workgroup
 constexpr int kRowsPerItem = 1024;     // target query rows (tokens * g) per work item
 constexpr int kReduceThreads = 256;
+constexpr int kSortBucketsMax = 12288;  // LDS buckets of the work-order sort (48 KB)
 
 // ---------------------------------------------------------------------------
 // Problem geometry, computed once on the host from fsa_problem.
@@ -42,10 +43,16 @@ struct Geometry {
   float scale;           // softmax scale (natural units)
   int64_t max_pairs;
   int64_t max_work;
+  int64_t dump_row;      // first of 32 rows after the partial / stats rows that take the
+                         // stores of rows past a chunk's end (never read)
   // aux blob layout (byte offsets)
   size_t aux_seq_gboff;  // int32 [B+1] exclusive prefix of per-sequence block counts
   size_t aux_nwork;      // int32 [4]: number of work items, P, spare
   size_t aux_work;       // int4 [max_work]: (segment, first token, block start, seq end)
+  size_t aux_work_sorted;// int4 [max_work]: the same items ordered by (KV head, first query token)
+  int32_t sort_shift;    // work-order bucket = query token >> sort_shift
+  int32_t sort_buckets_per_head;
+  int32_t sort_buckets;
   size_t aux_bytes;
   size_t build_ws_bytes;
   size_t stats_ws_bytes;
