@@ -80,6 +80,30 @@ def work_counts(sel, cu, block_size):
     return pairs, keys
 
 
+KERNEL_SOURCES = ("fsa_attn.hip", "fsa_internal.h", "fsa_index.hip", "fsa_api.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the main kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE record of this workload, or None when there is no
+    record or the kernel sources changed since it was taken."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(root, "sparse_attention_sel_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec
+
+
 def kernel_bytes(w, P, s_in, s_p):
     N, H, g, d, T = int(w.cu_seqlens[-1]), w.num_kv_heads, w.gqa_group, w.head_dim, w.topk
     HQ = H * g
@@ -268,6 +292,11 @@ def main():
     st = r["stage_ms"]
     dominant = max(("main", "reduce"), key=lambda s: st[s])
     ach = r["bytes"][dominant] / (st[dominant] * 1e-3) / 1e9
+    traffic = None
+    if dominant == "main" and args.partial == "input":
+        rec = measured_traffic(w.name)
+        if rec is not None:
+            traffic = int(round(rec["fetch_bytes"] + rec["write_bytes"]))
     main_tflops = r["f_alg"] / (st["main"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
@@ -300,7 +329,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(ach / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "algorithmic_bytes": int(r["bytes"][dominant]),
         },
         "stages_ms": {k_: round(v_, 4) for k_, v_ in st.items()},
         "main_kernel": {
