@@ -25,7 +25,7 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++20",
+    "-std=c++17",
     "-fPIC",
     "-Wall",
     "-Wno-unused-function",

@@ -31,7 +31,7 @@
 // are the B operand of O^T = V^T P^T, so P never leaves the registers.  V is
 // staged transposed (Vt[d][key]) with the keys of every 16-key group permuted
 // so that the 8 keys a lane contributes to one MFMA are adjacent in LDS.
-#include <type_traits>
+#include <algorithm>
 
 #include "fsa_internal.h"
 
@@ -46,14 +46,6 @@ constexpr int kRowTable = kRowsPerItem + 32;  // rows of the last tile past the 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
-
-template <typename T>
-__device__ __forceinline__ typename Vec8<T>::type zero8() {
-  typename Vec8<T>::type z;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) z[i] = (T)0.0f;
-  return z;
-}
 
 template <typename T>
 __device__ __forceinline__ typename Vec8<T>::type load8(const T* p) {
@@ -82,37 +74,6 @@ __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~15) + ((w >> 2) & 1) * 8 + (w >> 3) * 4 + (w & 3);
 }
 
-template <typename T, int D, int BK>
-__device__ __forceinline__ void stage_k(T* __restrict__ Ks, const T* __restrict__ k, int bs, int nkeys, int H,
-                                        int h) {
-  constexpr int C8 = D / 8;
-  for (int vi = threadIdx.x; vi < BK * C8; vi += kAttnThreads) {
-    const int key = vi / C8, c = vi - key * C8;
-    typename Vec8<T>::type val = zero8<T>();
-    if (key < nkeys) val = load8(k + ((size_t)(bs + key) * H + h) * D + c * 8);
-    *reinterpret_cast<typename Vec8<T>::type*>(Ks + key * k_ld<D>() + c * 8) = val;
-  }
-}
-
-template <typename T, int D, int BK>
-__device__ __forceinline__ void stage_vt(T* __restrict__ Vt, const T* __restrict__ v, int bs, int nkeys, int H,
-                                         int h) {
-  constexpr int KP = BK / 2;
-  for (int vi = threadIdx.x; vi < KP * (D / 8); vi += kAttnThreads) {
-    const int c = vi / KP, kp = vi - c * KP;
-    const int key = 2 * kp;
-    typename Vec8<T>::type a = zero8<T>(), b = zero8<T>();
-    if (key < nkeys) a = load8(v + ((size_t)(bs + key) * H + h) * D + c * 8);
-    if (key + 1 < nkeys) b = load8(v + ((size_t)(bs + key + 1) * H + h) * D + c * 8);
-    const int pos = vt_pos(key);  // even; key + 1 lands at pos + 1
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t packed = (uint32_t)bits16(a[i]) | ((uint32_t)bits16(b[i]) << 16);
-      *reinterpret_cast<uint32_t*>(Vt + (c * 8 + i) * vt_ld<BK>() + pos) = packed;
-    }
-  }
-}
-
 struct Item {
   int h, ntok, pair0, bs, nkeys;
 };
@@ -127,22 +88,6 @@ __device__ __forceinline__ Item read_item(const int4* __restrict__ work, const i
   r.bs = it.z;
   r.nkeys = min(BK, it.w - it.z);
   return r;
-}
-
-// Row table of a chunk: rows r < ntile*32 get ridx = the row of Q / lse /
-// row_max (token * HQ + h * g + j) and tok = the query token, or -1 for rows
-// past the chunk (their ridx points at token 0 so that loads stay in bounds).
-__device__ __forceinline__ void stage_rows(int* __restrict__ ridx, int* __restrict__ rtok,
-                                           const int32_t* __restrict__ qidx, const Item& it, int g, int HQ,
-                                           int nrows_padded) {
-  const int nrows = it.ntok * g;
-  for (int r = threadIdx.x; r < nrows_padded; r += kAttnThreads) {
-    const int ti = r / g, j = r - ti * g;
-    const bool valid = r < nrows;
-    const int t = valid ? qidx[it.pair0 + ti] : 0;
-    ridx[r] = t * HQ + it.h * g + (valid ? j : 0);
-    rtok[r] = valid ? t : -1;
-  }
 }
 
 // Coalesced gather of the Q rows of one 32-row tile: vector v of lane l holds
@@ -188,45 +133,116 @@ __device__ __forceinline__ void qk_tile(const T* __restrict__ Ks, const T* __res
   }
 }
 
-// Work-item order.  Workgroup i runs on XCD i % 8 (round-robin dispatch); XCD x
-// takes the contiguous range [x * per, (x + 1) * per) of the work list, in
-// order (the list is sorted by query token), so that the items that share an
-// XCD's L2 gather neighbouring query rows.  The grid is a multiple of 8
-// covering 8 * per items.
-__device__ __forceinline__ int xcd_item(int nwork_total) {
-  const int per = (nwork_total + 7) >> 3;
-  const int i = blockIdx.x;
-  const int k = i >> 3;
-  const int wi = (i & 7) * per + k;
-  return (k < per && wi < nwork_total) ? wi : -1;
-}
-
-// Tile loop with a ring of S register slots: slot (i mod S) holds the
-// prefetched Q vectors (and lse) of the wave's i-th tile.  Before computing
-// tile i the wave issues the loads of tile i + S - 1.  The loop is unrolled by
-// S so that every slot index is a compile-time constant and the slots stay in
-// registers.
-template <int S, typename StepFn>
-__device__ __forceinline__ void tile_ring(int first, int ntile, StepFn&& step) {
-  for (int tile = first; tile < ntile; tile += S * kWaves) {
-    const bool more = [&]<int... I>(std::integer_sequence<int, I...>) {
-      return ((tile + I * kWaves < ntile ? (step(std::integral_constant<int, I>{}, tile + I * kWaves), true) : false) &&
-              ...);
-    }(std::make_integer_sequence<int, S>{});
-    if (!more) break;
+// Persistent workgroups.  The grid is a multiple of 8 and workgroup i runs on
+// XCD x = i % 8 (round-robin dispatch).  XCD x owns the contiguous range
+// [x * per, (x + 1) * per) of the token-ordered work list and its G8 = grid / 8
+// workgroups take the range's items round-robin, so the items in flight on one
+// XCD gather neighbouring query rows.  Every workgroup exits when its next
+// index leaves the range.
+struct ItemCursor {
+  int base, per, k, step, total;
+  __device__ __forceinline__ ItemCursor(int nwork_total) {
+    per = (nwork_total + 7) >> 3;
+    base = (blockIdx.x & 7) * per;
+    k = blockIdx.x >> 3;
+    step = gridDim.x >> 3;
+    total = nwork_total;
   }
-}
+  __device__ __forceinline__ int current() const { return (k < per && base + k < total) ? base + k : -1; }
+  __device__ __forceinline__ int next() const {
+    const int kn = k + step;
+    return (kn < per && base + kn < total) ? base + kn : -1;
+  }
+  __device__ __forceinline__ void advance() { k += step; }
+};
+
+// The staging data of one work item held in registers while the previous item
+// computes: this thread's share of the K block (and of V, for the main
+// kernel) and the query tokens of its rows of the row table.  Loads use
+// clamped indices so that they are unconditional: keys past a partial last
+// block are only ever seen by rows that take the causal mask (their values
+// get weight zero), rows past the chunk are marked with token -1.
+template <typename T, int D, int BK, bool WITH_V>
+struct ItemStage {
+  using V8 = typename Vec8<T>::type;
+  static constexpr int KV = BK * D / 8 / kAttnThreads;                          // K vectors per thread
+  static constexpr int VP = WITH_V ? (BK / 2) * (D / 8) / kAttnThreads : 1;    // V key pairs per thread
+  static constexpr int RT = (kRowTable + kAttnThreads - 1) / kAttnThreads;     // table rows per thread
+  static_assert(BK * D / 8 % kAttnThreads == 0 && (BK / 2) * (D / 8) % kAttnThreads == 0, "whole vectors");
+  Item it;
+  V8 k[KV];
+  V8 va[VP], vb[VP];
+  int tok[RT];
+
+  __device__ __forceinline__ void load(const T* __restrict__ kg, const T* __restrict__ vg, const int32_t* __restrict__ qidx,
+                                       const int4* __restrict__ work, const int32_t* __restrict__ counts,
+                                       const int32_t* __restrict__ offsets, int wi, int H, int g, int NB, int CT) {
+    it = read_item(work, counts, offsets, wi, NB, CT, BK);
+    constexpr int C8 = D / 8;
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int vi = threadIdx.x + i * kAttnThreads;
+      const int key = min(vi / C8, it.nkeys - 1), c = vi % C8;
+      k[i] = load8(kg + ((size_t)(it.bs + key) * H + it.h) * D + c * 8);
+    }
+    if constexpr (WITH_V) {
+      constexpr int KP = BK / 2;
+#pragma unroll
+      for (int i = 0; i < VP; ++i) {
+        const int vi = threadIdx.x + i * kAttnThreads;
+        const int c = vi / KP, key = 2 * (vi % KP);
+        va[i] = load8(vg + ((size_t)(it.bs + min(key, it.nkeys - 1)) * H + it.h) * D + c * 8);
+        vb[i] = load8(vg + ((size_t)(it.bs + min(key + 1, it.nkeys - 1)) * H + it.h) * D + c * 8);
+      }
+    }
+    const int nrows = it.ntok * g;
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int r = threadIdx.x + i * kAttnThreads;
+      const int ti = min(r / g, it.ntok - 1);
+      const int t = qidx[it.pair0 + ti];
+      tok[i] = r < nrows ? t : -1;
+    }
+  }
+
+  __device__ __forceinline__ void commit(T* __restrict__ Ks, T* __restrict__ Vt, int* __restrict__ ridx,
+                                         int* __restrict__ rtok, int g, int HQ) const {
+    constexpr int C8 = D / 8;
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int vi = threadIdx.x + i * kAttnThreads;
+      *reinterpret_cast<V8*>(Ks + (vi / C8) * k_ld<D>() + (vi % C8) * 8) = k[i];
+    }
+    if constexpr (WITH_V) {
+      constexpr int KP = BK / 2;
+#pragma unroll
+      for (int i = 0; i < VP; ++i) {
+        const int vi = threadIdx.x + i * kAttnThreads;
+        const int c = vi / KP, key = 2 * (vi % KP);
+        const int pos = vt_pos(key);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t packed = (uint32_t)bits16(va[i][e]) | ((uint32_t)bits16(vb[i][e]) << 16);
+          *reinterpret_cast<uint32_t*>(Vt + (c * 8 + e) * vt_ld<BK>() + pos) = packed;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int r = threadIdx.x + i * kAttnThreads;
+      if (r < kRowTable) {
+        const int t = tok[i];
+        ridx[r] = (t < 0 ? 0 : t) * HQ + it.h * g + (t < 0 ? 0 : r % g);
+        rtok[r] = t;
+      }
+    }
+  }
+};
 
 // Waves per SIMD the register budget aims for: two (<= 256 registers) where
 // the tile state fits, one (<= 512) for the wide head dim / long blocks.
 template <int D, int BK>
 constexpr int attn_waves_per_eu() { return (D >= 256 || (D >= 128 && BK >= 128)) ? 1 : 2; }
-
-// Register slots of the Q ring (prefetch depth + 1), per kernel.
-template <int D, int BK>
-constexpr int q_slots_main() { return 2; }
-template <int D, int BK>
-constexpr int q_slots_stats() { return 2; }
 
 // Every key of the block is visible to every row of the tile: the block lies
 // entirely before each row's token (rows of a chunk are in token order, so
@@ -275,37 +291,43 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
   __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
-  const int wi = xcd_item(nwork[0]);
-  if (wi < 0) return;
-  const Item it = read_item(work, counts, offsets, wi, NB, CT, BK);
-  const int HQ = H * g, nrows = it.ntok * g, ntile = (nrows + 31) / 32;
-  stage_k<T, D, BK>(Ks, k, it.bs, it.nkeys, H, it.h);
-  stage_rows(ridx, rtok, qidx, it, g, HQ, ntile * 32);
-  __syncthreads();
-
+  ItemCursor cur(nwork[0]);
+  if (cur.current() < 0) return;
+  const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
   T* const qt = Qt + wave * 32 * tile_ld<D>();
-  constexpr int S = q_slots_stats<D, BK>();
-  V8 qs[S][KS];
-#pragma unroll
-  for (int i = 0; i + 1 < S; ++i)
-    if (wave + i * kWaves < ntile) load_q_tile<T, D>(q, ridx, wave + i * kWaves, lane, qs[i]);
+  ItemStage<T, D, BK, false> pre;
+  pre.load(k, nullptr, qidx, work, counts, offsets, cur.current(), H, g, NB, CT);
+  for (; cur.current() >= 0; cur.advance()) {
+    __syncthreads();  // the previous item's LDS reads are done
+    pre.commit(Ks, nullptr, ridx, rtok, g, HQ);
+    const Item it = pre.it;
+    __syncthreads();
+    const int nrows = it.ntok * g, ntile = (nrows + 31) / 32;
 
-  tile_ring<S>(wave, ntile, [&](auto slot, int tl) {
-    constexpr int cur = decltype(slot)::value, nxt = (cur + S - 1) % S;
-    if (tl + (S - 1) * kWaves < ntile) load_q_tile<T, D>(q, ridx, tl + (S - 1) * kWaves, lane, qs[nxt]);
-    put_q_tile<T, D>(qt, lane, qs[cur]);
-    f32x16 s[KT];
-    qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
-    const int row = tl * 32 + lr;
-    const int tok = rtok[row];
-    float2 ml;
-    if (tile_unmasked<BK>(tok, it.bs)) ml = row_stats<BK, false>(s, hl, 0, scale_log2);
-    else ml = row_stats<BK, true>(s, hl, tok < 0 ? -1 : tok - it.bs, scale_log2);
-    // lanes l and l + 32 store the same pair; rows past the chunk go to the dump
-    st[tok >= 0 ? (size_t)it.pair0 * g + row : dump_row + lr] = ml;
-  });
+    // Q pipeline: one register set plus the wave's LDS tile.  At each tile the
+    // registers (tile i, loaded during tile i - 1) go to LDS and are refilled
+    // with tile i + 1 while tile i computes from LDS.  The next item's staging
+    // loads are issued after the first Q tile's.
+    V8 qv[KS];
+    if (wave < ntile) load_q_tile<T, D>(q, ridx, wave, lane, qv);
+    const int wn = cur.next();
+    if (wn >= 0) pre.load(k, nullptr, qidx, work, counts, offsets, wn, H, g, NB, CT);
+    for (int tl = wave; tl < ntile; tl += kWaves) {
+      put_q_tile<T, D>(qt, lane, qv);
+      if (tl + kWaves < ntile) load_q_tile<T, D>(q, ridx, tl + kWaves, lane, qv);
+      f32x16 s[KT];
+      qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
+      const int row = tl * 32 + lr;
+      const int tok = rtok[row];
+      float2 ml;
+      if (tile_unmasked<BK>(tok, it.bs)) ml = row_stats<BK, false>(s, hl, 0, scale_log2);
+      else ml = row_stats<BK, true>(s, hl, tok < 0 ? -1 : tok - it.bs, scale_log2);
+      // lanes l and l + 32 store the same pair; rows past the chunk go to the dump
+      st[tok >= 0 ? (size_t)it.pair0 * g + row : dump_row + lr] = ml;
+    }
+  }
 }
 
 // One thread per (token, query head): merge the per-block (max, sum) pairs of
@@ -452,58 +474,60 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
   __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
-  const int wi = xcd_item(nwork[0]);
-  if (wi < 0) return;
-  const Item it = read_item(work, counts, offsets, wi, NB, CT, BK);
-  const int HQ = H * g, nrows = it.ntok * g, ntile = (nrows + 31) / 32;
-  stage_k<T, D, BK>(Ks, k, it.bs, it.nkeys, H, it.h);
-  stage_vt<T, D, BK>(Vt, v, it.bs, it.nkeys, H, it.h);
-  stage_rows(ridx, rtok, qidx, it, g, HQ, ntile * 32);
-  __syncthreads();
-
+  ItemCursor cur(nwork[0]);
+  if (cur.current() < 0) return;
+  const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
   T* const qt = Qt + wave * 32 * tile_ld<D>();
   PT* const stage = reinterpret_cast<PT*>(qt);
   PT* const dump = partial + dump_row * D;
-  constexpr int S = q_slots_main<D, BK>();
-  V8 qs[S][KS];
-  float ls[S];
+  ItemStage<T, D, BK, true> pre;
+  pre.load(k, v, qidx, work, counts, offsets, cur.current(), H, g, NB, CT);
+  for (; cur.current() >= 0; cur.advance()) {
+    __syncthreads();  // the previous item's LDS reads are done
+    pre.commit(Ks, Vt, ridx, rtok, g, HQ);
+    const Item it = pre.it;
+    __syncthreads();
+    const int nrows = it.ntok * g, ntile = (nrows + 31) / 32;
+
+    // Q pipeline: one register set plus the wave's LDS tile (as in k_stats);
+    // the lse of tile i + 1 is loaded with its Q rows.
+    V8 qv[KS];
+    float lnext = 0.f;
+    if (wave < ntile) {
+      load_q_tile<T, D>(q, ridx, wave, lane, qv);
+      lnext = lse[ridx[wave * 32 + lr]];
+    }
+    const int wn = cur.next();
+    if (wn >= 0) pre.load(k, v, qidx, work, counts, offsets, wn, H, g, NB, CT);
+    for (int tl = wave; tl < ntile; tl += kWaves) {
+      put_q_tile<T, D>(qt, lane, qv);
+      const float l2 = lnext * kLog2e;
+      if (tl + kWaves < ntile) {
+        load_q_tile<T, D>(q, ridx, tl + kWaves, lane, qv);
+        lnext = lse[ridx[(tl + kWaves) * 32 + lr]];
+      }
+      f32x16 s[KT];
+      qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
+      const int tok = rtok[tl * 32 + lr];
+      V8 pb[KK];
+      if (tile_unmasked<BK>(tok, it.bs)) probs<T, BK, false>(s, scale_log2, l2, hl, 0, pb);
+      else probs<T, BK, true>(s, scale_log2, l2, hl, tok < 0 ? -1 : tok - it.bs, pb);
+      f32x16 o[MT];
 #pragma unroll
-  for (int i = 0; i + 1 < S; ++i) {
-    if (wave + i * kWaves < ntile) {
-      load_q_tile<T, D>(q, ridx, wave + i * kWaves, lane, qs[i]);
-      ls[i] = lse[ridx[(wave + i * kWaves) * 32 + lr]];
+      for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const V8 a = load8(Vt + (mt * 32 + lr) * vt_ld<BK>() + kk * 16 + hl * 8);
+          o[mt] = mfma32(a, pb[kk], o[mt]);
+        }
+      store_tile<PT, D>(stage, o, lane, min(32, nrows - tl * 32),
+                        partial + ((size_t)it.pair0 * g + (size_t)tl * 32) * D, dump);
     }
   }
-
-  tile_ring<S>(wave, ntile, [&](auto slot, int tl) {
-    constexpr int cur = decltype(slot)::value, nxt = (cur + S - 1) % S;
-    if (tl + (S - 1) * kWaves < ntile) {
-      load_q_tile<T, D>(q, ridx, tl + (S - 1) * kWaves, lane, qs[nxt]);
-      ls[nxt] = lse[ridx[(tl + (S - 1) * kWaves) * 32 + lr]];
-    }
-    put_q_tile<T, D>(qt, lane, qs[cur]);
-    f32x16 s[KT];
-    qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
-    const int tok = rtok[tl * 32 + lr];
-    const float l2 = ls[cur] * kLog2e;
-    V8 pb[KK];
-    if (tile_unmasked<BK>(tok, it.bs)) probs<T, BK, false>(s, scale_log2, l2, hl, 0, pb);
-    else probs<T, BK, true>(s, scale_log2, l2, hl, tok < 0 ? -1 : tok - it.bs, pb);
-    f32x16 o[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const V8 a = load8(Vt + (mt * 32 + lr) * vt_ld<BK>() + kk * 16 + hl * 8);
-        o[mt] = mfma32(a, pb[kk], o[mt]);
-      }
-    store_tile<PT, D>(stage, o, lane, min(32, nrows - tl * 32), partial + ((size_t)it.pair0 * g + (size_t)tl * 32) * D,
-                      dump);
-  });
 }
 
 // ---- reduce -----------------------------------------------------------------
@@ -592,12 +616,28 @@ inline Ptrs<int> index_ptrs(const Geometry& geo, const fsa_index& idx) {
                    reinterpret_cast<const int32_t*>(aux + geo.aux_nwork)};
 }
 
+// Persistent grid: as many workgroups as fit on the device at once (a
+// multiple of 8, one share per XCD), at most one per work item.
+template <typename K>
+unsigned persistent_grid(K kernel, int64_t max_work) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kAttnThreads, 0) != hipSuccess || cus <= 0 ||
+      per_cu <= 0) {
+    cus = 256;
+    per_cu = 1;
+  }
+  const int64_t want = std::min<int64_t>((int64_t)cus * per_cu, (max_work + 7) / 8 * 8);
+  return (unsigned)std::max<int64_t>(8, (want + 7) / 8 * 8);
+}
+
 template <typename T, int D, int BK>
 void stats_typed(const Geometry& geo, const void* q, const void* k, const fsa_index& idx, float2* st,
                  hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
-  hipLaunchKernelGGL((k_stats<T, D, BK>), dim3((unsigned)((geo.max_work + 7) / 8 * 8)), dim3(kAttnThreads), 0, stream,
+  hipLaunchKernelGGL((k_stats<T, D, BK>), dim3(persistent_grid(k_stats<T, D, BK>, geo.max_work)), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), p.counts, p.offsets, p.qidx, p.work, p.nwork,
                      st, (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
 }
@@ -607,7 +647,7 @@ void main_typed(const Geometry& geo, const void* q, const void* k, const void* v
                 const float* lse, void* partial, hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
-  hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3((unsigned)((geo.max_work + 7) / 8 * 8)), dim3(kAttnThreads), 0, stream,
+  hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3(persistent_grid(k_main<T, D, BK, PT>, geo.max_work)), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), p.counts,
                      p.offsets, p.qidx, p.work, p.nwork, lse, static_cast<PT*>(partial), (size_t)geo.dump_row, geo.H,
                      geo.g, geo.NB, geo.chunk_tokens, sl2);
