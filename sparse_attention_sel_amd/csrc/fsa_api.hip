@@ -124,7 +124,8 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
     geo->sort_buckets = (int32_t)(H * geo->sort_buckets_per_head);
   }
   geo->aux_bytes = off;
-  geo->build_ws_bytes = round_up((size_t)std::max<int64_t>(H * geo->ntiles * NB, 1) * 4, 256);
+  geo->build_ws_buckets = round_up((size_t)std::max<int64_t>(H * geo->ntiles * NB, 1) * 4, 256);
+  geo->build_ws_bytes = round_up(geo->build_ws_buckets + (size_t)std::max(geo->sort_buckets, 1) * 4, 256);
   geo->dump_row = std::max<int64_t>(geo->max_pairs, 1) * g;
   const size_t rows = (size_t)geo->dump_row + 32;
   geo->stats_ws_bytes = round_up(rows * 8, 256);

@@ -11,6 +11,7 @@
 //              work-item list (segment, query chunk) for the attention kernels
 //   scatter    per (KV head, token tile): walks its tokens in order and places
 //              each selecting entry at offsets + tile base + rank in the tile
+//   work order bucket sort of the work list by (KV head, first query token)
 //
 // Integer atomics only count (their result does not depend on order); ranks
 // come from per-step bit masks, so the output is bit-exact and deterministic.
@@ -62,31 +63,42 @@ __device__ __forceinline__ TileWindow tile_window(const int32_t* __restrict__ cu
 }
 
 // ---- hist -------------------------------------------------------------------
-// grid (ntiles, H); dynamic LDS: win_max ints.
+// grid (ntiles, H); dynamic LDS: win_max ints of histogram, then a staging
+// buffer of kHistStage ints for the Sel rows of kHistStage / T tokens at a time
+// (the first-occurrence check reads earlier entries of the row from LDS).
+constexpr int kHistStage = 4096;
+
 __global__ __launch_bounds__(kBuildThreads) void k_hist(const int32_t* __restrict__ sel,
                                                         const int32_t* __restrict__ cu,
                                                         const int32_t* __restrict__ gboff, int num_seqs, int N,
-                                                        int T, int BK, int TT, int ntiles, int NB,
+                                                        int T, int BK, int TT, int ntiles, int NB, int win_max,
                                                         int32_t* __restrict__ tile_hist) {
-  extern __shared__ int hist[];
+  extern __shared__ int lds[];
+  int* hist = lds;
+  int* rows = lds + win_max;
   const int tile = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const TileWindow w = tile_window(cu, gboff, num_seqs, N, TT, BK, tile);
   for (int i = tid; i < w.win; i += kBuildThreads) hist[i] = 0;
-  __syncthreads();
-  const int n_entries = (w.t_hi - w.t_lo) * T;
-  const int32_t* rows = sel + ((size_t)h * N + w.t_lo) * T;
-  for (int i = tid; i < n_entries; i += kBuildThreads) {
-    const int tl = i / T, j = i - tl * T;
-    const int t = w.t_lo + tl;
-    const int32_t* row = rows + (size_t)tl * T;
-    const int e = row[j];
-    if (e < 0) continue;
-    const int s = seq_of_token(cu, num_seqs, t);
-    if (e > (t - cu[s]) / BK) continue;
-    bool dup = false;
-    for (int jj = 0; jj < j; ++jj) dup |= (row[jj] == e);
-    if (dup) continue;
-    atomicAdd(&hist[gboff[s] + e - w.gb_lo], 1);
+  const int chunk = max(1, kHistStage / T);  // tokens per staging round
+  for (int c0 = w.t_lo; c0 < w.t_hi; c0 += chunk) {
+    const int nt = min(chunk, w.t_hi - c0);
+    const int32_t* src = sel + ((size_t)h * N + c0) * T;
+    __syncthreads();  // previous round's reads done (and the histogram zeroed)
+    for (int i = tid; i < nt * T; i += kBuildThreads) rows[i] = src[i];
+    __syncthreads();
+    for (int i = tid; i < nt * T; i += kBuildThreads) {
+      const int tl = i / T, j = i - tl * T;
+      const int t = c0 + tl;
+      const int* row = rows + tl * T;
+      const int e = row[j];
+      if (e < 0) continue;
+      const int s = seq_of_token(cu, num_seqs, t);
+      if (e > (t - cu[s]) / BK) continue;
+      bool dup = false;
+      for (int jj = 0; jj < j; ++jj) dup |= (row[jj] == e);
+      if (dup) continue;
+      atomicAdd(&hist[gboff[s] + e - w.gb_lo], 1);
+    }
   }
   __syncthreads();
   int32_t* out = tile_hist + ((size_t)h * ntiles + tile) * NB + w.gb_lo;
@@ -94,42 +106,53 @@ __global__ __launch_bounds__(kBuildThreads) void k_hist(const int32_t* __restric
 }
 
 // ---- tile_scan --------------------------------------------------------------
-// One thread per (h, gb).  Tiles outside [tile of the block's first token, tile
-// of the sequence's last token] hold no entries for gb and are not touched;
-// every tile inside that range has gb in its window, so its entry was written
-// by k_hist.
+// Exclusive scan over tiles of each (h, gb) column of the tile histograms ->
+// tile bases, totals -> counts.  Tiles outside [tile of the block's first
+// token, tile of the sequence's last token] hold no entries for gb and are not
+// touched; every tile inside that range has gb in its window, so its entry was
+// written by k_hist.  A workgroup takes 16 columns; 16 threads split each
+// column's tile range into segments, scan them, and add the segment prefixes.
+constexpr int kScanSegs = 16;
+
 __global__ __launch_bounds__(kBuildThreads) void k_tile_scan(int32_t* __restrict__ tile_hist,
                                                              const int32_t* __restrict__ cu,
                                                              const int32_t* __restrict__ gboff, int num_seqs,
                                                              int H, int NB, int BK, int TT, int ntiles,
                                                              int32_t* __restrict__ counts) {
-  const int idx = blockIdx.x * kBuildThreads + threadIdx.x;
-  if (idx >= H * NB) return;
-  const int h = idx / NB, gb = idx - h * NB;
-  const int s = seq_of_block(gboff, num_seqs, gb);
-  const int bs = cu[s] + (gb - gboff[s]) * BK;
-  const int se = cu[s + 1];
-  const int tau0 = bs / TT, tau1 = (se - 1) / TT;
-  int32_t* p = tile_hist + ((size_t)h * ntiles) * NB + gb;
-  int run = 0;
-  int tau = tau0;
-  constexpr int U = 8;
-  for (; tau + U - 1 <= tau1; tau += U) {
-    int v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = p[(size_t)(tau + u) * NB];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      p[(size_t)(tau + u) * NB] = run;
-      run += v[u];
-    }
+  __shared__ int seg_tot[kBuildThreads / kScanSegs][kScanSegs];
+  const int col_local = threadIdx.x / kScanSegs, seg = threadIdx.x % kScanSegs;
+  const int idx = blockIdx.x * (kBuildThreads / kScanSegs) + col_local;
+  const bool active = idx < H * NB;
+  int tau0 = 0, len = 0;
+  int32_t* p = tile_hist;
+  if (active) {
+    const int h = idx / NB, gb = idx - h * NB;
+    const int s = seq_of_block(gboff, num_seqs, gb);
+    const int bs = cu[s] + (gb - gboff[s]) * BK;
+    const int se = cu[s + 1];
+    const int t0 = bs / TT, t1 = (se - 1) / TT;
+    const int per = (t1 - t0 + kScanSegs) / kScanSegs;
+    tau0 = t0 + seg * per;
+    len = max(0, min(per, t1 + 1 - tau0));
+    p = tile_hist + ((size_t)h * ntiles) * NB + gb;
   }
-  for (; tau <= tau1; ++tau) {
-    const int v = p[(size_t)tau * NB];
-    p[(size_t)tau * NB] = run;
+  int run = 0;
+  for (int i = 0; i < len; ++i) run += p[(size_t)(tau0 + i) * NB];
+  seg_tot[col_local][seg] = run;
+  __syncthreads();
+  int base = 0, total = 0;
+  for (int k = 0; k < kScanSegs; ++k) {
+    const int v = seg_tot[col_local][k];
+    if (k < seg) base += v;
+    total += v;
+  }
+  run = base;
+  for (int i = 0; i < len; ++i) {
+    const int v = p[(size_t)(tau0 + i) * NB];
+    p[(size_t)(tau0 + i) * NB] = run;
     run += v;
   }
-  counts[idx] = run;
+  if (active && seg == 0) counts[idx] = total;
 }
 
 // ---- offsets + work list ------------------------------------------------------
@@ -152,9 +175,11 @@ __global__ __launch_bounds__(kScanThreads) void k_offsets(const int32_t* __restr
                                                           int CT, const int32_t* __restrict__ cu,
                                                           const int32_t* __restrict__ gboff, int num_seqs,
                                                           int NB, int BK, int32_t* __restrict__ offsets,
-                                                          int4* __restrict__ work, int32_t* __restrict__ nwork) {
+                                                          int4* __restrict__ work, int32_t* __restrict__ nwork,
+                                                          int32_t* __restrict__ buckets, int nbuckets) {
   __shared__ int64_t wave_tot[kScanThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int b = tid; b < nbuckets; b += kScanThreads) buckets[b] = 0;
   int64_t carry = 0;
   for (int base = 0; base < M; base += kScanThreads * kScanItems) {
     int c[kScanItems];
@@ -272,30 +297,32 @@ __global__ __launch_bounds__(kBuildThreads) void k_scatter(
 }
 
 // ---- work order -------------------------------------------------------------
-// One workgroup.  Reorders the work list by (KV head, first query token of the
-// chunk) with a bucket sort (bucket = token >> shift), so that the items that
-// run together on one XCD gather a narrow window of query rows, which then
-// stays in that XCD's L2.  Within a bucket the order depends on atomics; the
-// order only affects scheduling: every item writes its own partial rows and
-// the reduction sums in slot order, so all outputs are unchanged.
-__global__ __launch_bounds__(kScanThreads) void k_work_sort(const int4* __restrict__ work_in,
-                                                            const int32_t* __restrict__ nwork,
-                                                            const int32_t* __restrict__ qidx,
-                                                            const int32_t* __restrict__ offsets, int NB, int shift,
-                                                            int nbh, int nbuckets, int4* __restrict__ work_out) {
-  extern __shared__ int cnt[];
+// Reorders the work list by (KV head, first query token of the chunk) with a
+// bucket sort (bucket = token >> shift), so that the items that run together
+// on one XCD gather a narrow window of query rows, which then stays in that
+// XCD's L2.  Three grid-wide steps: count items per bucket, exclusive scan of
+// the bucket counts (one workgroup), place items at their bucket's cursor.
+// Within a bucket the order depends on atomics; the order only affects
+// scheduling: every item writes its own partial rows and the reduction sums
+// in slot order, so all outputs are unchanged.
+__device__ __forceinline__ int work_key(const int4& it, const int32_t* __restrict__ qidx,
+                                        const int32_t* __restrict__ offsets, int NB, int shift, int nbh) {
+  return (it.x / NB) * nbh + (qidx[offsets[it.x] + it.y] >> shift);
+}
+
+__global__ __launch_bounds__(kBuildThreads) void k_work_count(const int4* __restrict__ work,
+                                                              const int32_t* __restrict__ nwork,
+                                                              const int32_t* __restrict__ qidx,
+                                                              const int32_t* __restrict__ offsets, int NB, int shift,
+                                                              int nbh, int32_t* __restrict__ buckets) {
+  const int w = blockIdx.x * kBuildThreads + threadIdx.x;
+  if (w >= nwork[0]) return;
+  atomicAdd(&buckets[work_key(work[w], qidx, offsets, NB, shift, nbh)], 1);
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_bucket_scan(int32_t* __restrict__ buckets, int nbuckets) {
   __shared__ int64_t wave_tot[kScanThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int W = nwork[0];
-  for (int i = tid; i < nbuckets; i += kScanThreads) cnt[i] = 0;
-  __syncthreads();
-  auto key_of = [&](const int4& it) {
-    const int h = it.x / NB;
-    return h * nbh + (qidx[offsets[it.x] + it.y] >> shift);
-  };
-  for (int w = tid; w < W; w += kScanThreads) atomicAdd(&cnt[key_of(work_in[w])], 1);
-  __syncthreads();
-  // exclusive scan of the bucket counts, kScanItems buckets per thread per pass
   int64_t carry = 0;
   for (int base = 0; base < nbuckets; base += kScanThreads * kScanItems) {
     int c[kScanItems];
@@ -303,7 +330,7 @@ __global__ __launch_bounds__(kScanThreads) void k_work_sort(const int4* __restri
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
       const int b = base + tid * kScanItems + i;
-      c[i] = b < nbuckets ? cnt[b] : 0;
+      c[i] = b < nbuckets ? buckets[b] : 0;
       local += c[i];
     }
     const int64_t incl = wave_inclusive_scan(local);
@@ -318,16 +345,24 @@ __global__ __launch_bounds__(kScanThreads) void k_work_sort(const int4* __restri
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
       const int b = base + tid * kScanItems + i;
-      if (b < nbuckets) cnt[b] = (int)run;
+      if (b < nbuckets) buckets[b] = (int32_t)run;
       run += c[i];
     }
     carry += total;
     __syncthreads();
   }
-  for (int w = tid; w < W; w += kScanThreads) {
-    const int4 it = work_in[w];
-    work_out[atomicAdd(&cnt[key_of(it)], 1)] = it;
-  }
+}
+
+__global__ __launch_bounds__(kBuildThreads) void k_work_place(const int4* __restrict__ work,
+                                                              const int32_t* __restrict__ nwork,
+                                                              const int32_t* __restrict__ qidx,
+                                                              const int32_t* __restrict__ offsets, int NB, int shift,
+                                                              int nbh, int32_t* __restrict__ buckets,
+                                                              int4* __restrict__ work_out) {
+  const int w = blockIdx.x * kBuildThreads + threadIdx.x;
+  if (w >= nwork[0]) return;
+  const int4 it = work[w];
+  work_out[atomicAdd(&buckets[work_key(it, qidx, offsets, NB, shift, nbh)], 1)] = it;
 }
 
 }  // namespace
@@ -340,19 +375,22 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
   int4* work = reinterpret_cast<int4*>(aux + geo.aux_work);
   int4* work_sorted = reinterpret_cast<int4*>(aux + geo.aux_work_sorted);
   int32_t* tile_hist = static_cast<int32_t*>(ws);
+  int32_t* buckets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + geo.build_ws_buckets);
   const int M = geo.H * geo.NB;
 
   hipLaunchKernelGGL(k_seq_table, dim3(1), dim3(kBuildThreads), 0, stream, cu_dev, geo.num_seqs, geo.BK, gboff);
   if (geo.N > 0) {
-    hipLaunchKernelGGL(k_hist, dim3(geo.ntiles, geo.H), dim3(kBuildThreads), geo.win_max * sizeof(int), stream,
-                       sel, cu_dev, gboff, geo.num_seqs, geo.N, geo.T, geo.BK, geo.tile_tokens, geo.ntiles, geo.NB,
-                       tile_hist);
-    hipLaunchKernelGGL(k_tile_scan, dim3((M + kBuildThreads - 1) / kBuildThreads), dim3(kBuildThreads), 0, stream,
+    hipLaunchKernelGGL(k_hist, dim3(geo.ntiles, geo.H), dim3(kBuildThreads),
+                       (geo.win_max + kHistStage) * sizeof(int), stream, sel, cu_dev, gboff, geo.num_seqs, geo.N, geo.T,
+                       geo.BK, geo.tile_tokens, geo.ntiles, geo.NB, geo.win_max, tile_hist);
+    constexpr int cols = kBuildThreads / kScanSegs;
+    hipLaunchKernelGGL(k_tile_scan, dim3((M + cols - 1) / cols), dim3(kBuildThreads), 0, stream,
                        tile_hist, cu_dev, gboff, geo.num_seqs, geo.H, geo.NB, geo.BK, geo.tile_tokens, geo.ntiles,
                        idx.counts);
   }
   hipLaunchKernelGGL(k_offsets, dim3(1), dim3(kScanThreads), 0, stream, idx.counts, M, geo.chunk_tokens, cu_dev,
-                     gboff, geo.num_seqs, geo.NB > 0 ? geo.NB : 1, geo.BK, idx.offsets, work, nwork);
+                     gboff, geo.num_seqs, geo.NB > 0 ? geo.NB : 1, geo.BK, idx.offsets, work, nwork, buckets,
+                     geo.N > 0 ? geo.sort_buckets : 0);
   if (geo.N > 0) {
     int Tp = 1;
     while (Tp < geo.T) Tp <<= 1;
@@ -361,9 +399,14 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
     hipLaunchKernelGGL(k_scatter, dim3(geo.ntiles, geo.H), dim3(kBuildThreads), lds, stream, sel, cu_dev, gboff,
                        geo.num_seqs, geo.N, geo.T, Tp, tps, geo.BK, geo.tile_tokens, geo.ntiles, geo.NB, geo.win_max,
                        tile_hist, idx.offsets, idx.qidx, idx.slot);
-    hipLaunchKernelGGL(k_work_sort, dim3(1), dim3(kScanThreads), geo.sort_buckets * sizeof(int), stream, work, nwork,
-                       idx.qidx, idx.offsets, geo.NB, geo.sort_shift, geo.sort_buckets_per_head, geo.sort_buckets,
-                       work_sorted);
+    const unsigned wg = (unsigned)((geo.max_work + kBuildThreads - 1) / kBuildThreads);
+    if (wg > 0) {
+      hipLaunchKernelGGL(k_work_count, dim3(wg), dim3(kBuildThreads), 0, stream, work, nwork, idx.qidx, idx.offsets,
+                         geo.NB, geo.sort_shift, geo.sort_buckets_per_head, buckets);
+      hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(kScanThreads), 0, stream, buckets, geo.sort_buckets);
+      hipLaunchKernelGGL(k_work_place, dim3(wg), dim3(kBuildThreads), 0, stream, work, nwork, idx.qidx, idx.offsets,
+                         geo.NB, geo.sort_shift, geo.sort_buckets_per_head, buckets, work_sorted);
+    }
   }
   return hipGetLastError();
 }

@@ -19,7 +19,7 @@ constexpr int kWinMax = 7680;          // max global blocks one tile can touch (
 constexpr int kAttnThreads = 256;      // 4 waves per main / stats workgroup
 constexpr int kRowsPerItem = 1024;     // target query rows (tokens * g) per work item
 constexpr int kReduceThreads = 256;
-constexpr int kSortBucketsMax = 12288;  // LDS buckets of the work-order sort (48 KB)
+constexpr int kSortBucketsMax = 16384;  // buckets of the work-order sort
 
 // ---------------------------------------------------------------------------
 // Problem geometry, computed once on the host from fsa_problem.
@@ -55,6 +55,7 @@ struct Geometry {
   int32_t sort_buckets;
   size_t aux_bytes;
   size_t build_ws_bytes;
+  size_t build_ws_buckets;  // byte offset of the work-order bucket counters in the build workspace
   size_t stats_ws_bytes;
   size_t partial_ws_bytes;
 };
