@@ -186,12 +186,31 @@ int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const voi
                                size_t partial_ws_bytes, void* stream);
 
 /*
- * Reduction kernel alone (paper notes, Key design 3): out[t, h*g + j, :] =
- * sum over the row's valid slots, in ascending j order, of partial row
- * slot[h, t, j] * g + j; no atomics.
+ * Reduction kernel alone (paper notes, Key design 3): out[t, h*g + r, :] =
+ * sum, over the Sel entries j of row (h, t) in ascending j order whose slot
+ * is valid, of partial row slot[h, t, j] * g + r; no atomics.
  */
 int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, const void* partial_ws,
                                  size_t partial_ws_bytes, void* out, void* stream);
+
+/*
+ * Query-outer forward, the loop order of vanilla NSA selected attention
+ * (paper notes, Background and motivation; Key design 1 names the loop order
+ * this path is compared with).  One wave per (token, KV head, up to 16 query
+ * heads) walks the token's selected blocks with an online softmax; the query
+ * heads of a group are padded to 16 MFMA rows.  Needs no index and no
+ * workspace.  Computes the same function as fsa_softmax_stats +
+ * fsa_selected_attn_fwd:
+ *   out[t, hq, :] in the input dtype, [N, h_K*g, d];
+ *   lse[t, hq]    natural-log log-sum-exp, fp32 [N, h_K*g] (-inf and a zero
+ *                 output row for a row with no valid Sel entry).
+ *   q, k, v, out  device, 16-byte aligned;  sel  device int32 [h_K, N, T],
+ *                 4-byte aligned;  lse  device, 4-byte aligned.
+ * Returns FSA_ERR_NULL / _ALIGN / _SHAPE / _UNSUPPORTED before any launch,
+ * FSA_ERR_HIP if the launch fails.
+ */
+int32_t fsa_nsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
+                                  const int32_t* sel, float* lse, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -37,6 +37,7 @@ __all__ = [
     "selected_attn_fwd",
     "selected_attn_main",
     "selected_attn_reduce",
+    "nsa_selected_attn_fwd",
     "selected_attention",
     "status_string",
 ]
@@ -135,6 +136,8 @@ def load_library():
     lib.fsa_selected_attn_main.argtypes = [P, vp, vp, vp, I, vp, vp, sz, vp]
     lib.fsa_selected_attn_reduce.restype = i32
     lib.fsa_selected_attn_reduce.argtypes = [P, I, vp, sz, vp, vp]
+    lib.fsa_nsa_selected_attn_fwd.restype = i32
+    lib.fsa_nsa_selected_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     if lib.fsa_abi_version() != 1:
         raise RuntimeError("libfsa.so ABI version mismatch")
     _LIB = lib
@@ -348,6 +351,21 @@ class Workspaces:
         self.build = torch.empty(sizes["build_ws_bytes"], **u8)
         self.stats = torch.empty(sizes["stats_ws_bytes"], **u8)
         self.partial = torch.empty(sizes["partial_ws_bytes"], **u8)
+
+
+def nsa_selected_attn_fwd(prob: Problem, q, k, v, sel, lse, out, stream=None):
+    """fsa_nsa_selected_attn_fwd: query-outer forward straight from Sel
+    [h_K, N, T] into out [N, h_q, d] and lse [N, h_q]; no index or workspace."""
+    qs, ks = _qkv_shapes(prob)
+    args = (
+        _ptr(q, "q", prob.dtype, qs),
+        _ptr(k, "k", prob.dtype, ks),
+        _ptr(v, "v", prob.dtype, ks),
+        _ptr(sel, "sel", torch.int32, (prob.num_kv_heads, prob.total_tokens, prob.topk)),
+        _ptr(lse, "lse", torch.float32, (prob.total_tokens, prob.num_q_heads)),
+        _ptr(out, "out", prob.dtype, qs),
+    )
+    _check(load_library().fsa_nsa_selected_attn_fwd(prob.c(), *args, _stream(stream)), "fsa_nsa_selected_attn_fwd")
 
 
 def selected_attention(prob: Problem, q, k, v, sel, stream=None):

@@ -285,4 +285,17 @@ int32_t fsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void
   return hip_status(launch_reduce(geo, *idx, partial_ws, out, s));
 }
 
+int32_t fsa_nsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
+                                  const int32_t* sel, float* lse, void* out, void* stream) {
+  Geometry geo;
+  const int32_t st = prepare(prob, &geo);
+  if (st != FSA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || sel == nullptr || lse == nullptr || out == nullptr)
+    return FSA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(sel, 4) ||
+      !aligned(lse, 4))
+    return FSA_ERR_ALIGN;
+  return hip_status(launch_nsa(geo, prob->cu_seqlens_dev, q, k, v, sel, out, lse, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

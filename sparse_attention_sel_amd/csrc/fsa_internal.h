@@ -74,6 +74,8 @@ hipError_t launch_main(const Geometry& geo, const void* q, const void* k, const 
                        const fsa_index& idx, const float* lse, void* partial, hipStream_t stream);
 hipError_t launch_reduce(const Geometry& geo, const fsa_index& idx, const void* partial, void* out,
                          hipStream_t stream);
+hipError_t launch_nsa(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
+                      const int32_t* sel, void* out, float* lse, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Device helpers

@@ -61,6 +61,21 @@ def run_gpu(w: Workload, partial: str = "fp32", keep_partial: bool = False):
     return res
 
 
+def run_gpu_nsa(w: Workload):
+    """Query-outer forward on cuda:0 straight from Sel.  Returns host numpy
+    arrays out [N, h_q, d] (float32) and lse [N, h_q]."""
+    prob = problem_for(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    sel = torch.from_numpy(w.sel).to(dev)
+    n, hq = prob.total_tokens, prob.num_q_heads
+    lse = torch.full((n, hq), float("nan"), dtype=torch.float32, device=dev)
+    out = torch.full((n, hq, prob.head_dim), float("nan"), dtype=prob.dtype, device=dev)
+    fsa.nsa_selected_attn_fwd(prob, q, k, v, sel, lse, out)
+    torch.cuda.synchronize()
+    return {"out": out.float().cpu().numpy(), "lse": lse.cpu().numpy()}
+
+
 def sample_tokens(cu, block_size, n_random=96, seed=0):
     """Tokens that exercise the edges (first tokens of each sequence, block
     boundaries, last tokens) plus a seeded random spread."""

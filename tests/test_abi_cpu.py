@@ -168,6 +168,16 @@ def test_entry_points_reject_before_launch():
     assert lib.fsa_selected_attn_reduce(P, I, f, pw, None, None) == NULL
     assert lib.fsa_selected_attn_reduce(P, I, f, pw - 1, f, None) == WS
     assert lib.fsa_selected_attn_reduce(P, ctypes.byref(null_idx), f, pw, f, None) == NULL
+    # query-outer forward (no index, no workspace)
+    assert lib.fsa_nsa_selected_attn_fwd(None, f, f, f, f, f, f, None) == NULL
+    assert lib.fsa_nsa_selected_attn_fwd(P, f, f, f, None, f, f, None) == NULL
+    assert lib.fsa_nsa_selected_attn_fwd(P, f, f, f, f, None, f, None) == NULL
+    assert lib.fsa_nsa_selected_attn_fwd(P, f, f, f, f, f, None, None) == NULL
+    assert lib.fsa_nsa_selected_attn_fwd(P, f, f + 8, f, f, f, f, None) == ALIGN
+    assert lib.fsa_nsa_selected_attn_fwd(P, f, f, f, f + 2, f, f, None) == ALIGN
+    assert lib.fsa_nsa_selected_attn_fwd(P, f, f, f, f, f, f + 4, None) == ALIGN
+    assert lib.fsa_nsa_selected_attn_fwd(ctypes.byref(prob(dev=False)), f, f, f, f, f, f, None) == NULL
+    assert lib.fsa_nsa_selected_attn_fwd(ctypes.byref(prob(d=48)), f, f, f, f, f, f, None) == UNSUP
 
 
 def test_python_binding_checks_tensors():
