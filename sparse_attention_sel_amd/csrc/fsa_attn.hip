@@ -133,6 +133,27 @@ __device__ __forceinline__ void qk_tile(const T* __restrict__ Ks, const T* __res
   }
 }
 
+// x combined with the same register of lane l ^ 32 by a commutative op:
+// v_permlane32_swap of x with itself hands each lane the values of lanes
+// l % 32 (first result) and l % 32 + 32 (second result).  The compiler treats
+// the two results of a swap of one value with itself as equal and would fold
+// the combination away, so they pass through an empty asm statement first.
+__device__ __forceinline__ float2 xhalf_pair(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                  false, false);
+  uint32_t lo = r[0], hi = r[1];
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  return make_float2(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+__device__ __forceinline__ float xhalf_max(float x) {
+  const float2 p = xhalf_pair(x);
+  return fmaxf(p.x, p.y);
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const float2 p = xhalf_pair(x);
+  return p.x + p.y;
+}
+
 // Persistent workgroups.  The grid is a multiple of 8 and workgroup i runs on
 // XCD x = i % 8 (round-robin dispatch).  XCD x owns the contiguous range
 // [x * per, (x + 1) * per) of the token-ordered work list and its G8 = grid / 8
@@ -195,13 +216,12 @@ struct ItemStage {
         vb[i] = load8(vg + ((size_t)(it.bs + min(key + 1, it.nkeys - 1)) * H + it.h) * D + c * 8);
       }
     }
-    const int nrows = it.ntok * g;
+    // Nothing here consumes the loaded values (the row bound is applied at
+    // commit), so the loads stay in flight while the current item computes.
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
       const int r = threadIdx.x + i * kAttnThreads;
-      const int ti = min(r / g, it.ntok - 1);
-      const int t = qidx[it.pair0 + ti];
-      tok[i] = r < nrows ? t : -1;
+      tok[i] = qidx[it.pair0 + min(r / g, it.ntok - 1)];
     }
   }
 
@@ -227,13 +247,14 @@ struct ItemStage {
         }
       }
     }
+    const int nrows = it.ntok * g;
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
       const int r = threadIdx.x + i * kAttnThreads;
       if (r < kRowTable) {
-        const int t = tok[i];
-        ridx[r] = (t < 0 ? 0 : t) * HQ + it.h * g + (t < 0 ? 0 : r % g);
-        rtok[r] = t;
+        const bool ok = r < nrows;
+        ridx[r] = (ok ? tok[i] : 0) * HQ + it.h * g + (ok ? r % g : 0);
+        rtok[r] = ok ? tok[i] : -1;
       }
     }
   }
@@ -265,7 +286,7 @@ __device__ __forceinline__ float2 row_stats(const f32x16* s, int hl, int lim, fl
       const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
       if (!MASKED || key <= lim) m = fmaxf(m, s[kt][r]);
     }
-  m = fmaxf(m, __shfl_xor(m, 32, 64)) * c;
+  m = xhalf_max(m) * c;
   float l = 0.f;
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt)
@@ -275,7 +296,7 @@ __device__ __forceinline__ float2 row_stats(const f32x16* s, int hl, int lim, fl
       const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -m));
       l += (!MASKED || key <= lim) ? e : 0.f;
     }
-  l += __shfl_xor(l, 32, 64);
+  l = xhalf_sum(l);
   return make_float2(m, l);
 }
 
