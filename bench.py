@@ -7,6 +7,11 @@ Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--partial input|fp32] [--no-cpu-baseline] [--no-variants]
+                    [--no-query-outer]
+
+The query-outer forward (fsa_nsa_selected_attn_fwd, the vanilla NSA loop
+order) is timed on the same inputs and reported beside the step, with the
+FSA-order speedup over it.
 
 Throughput is algorithmic TFLOP/s: 4 * g * d * (sum over (token, KV head) of
 the number of keys the token attends to), i.e. QK^T and PV over the visible
@@ -44,6 +49,8 @@ def parse():
     ap.add_argument("--partial", default="input", choices=["input", "fp32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-query-outer", action="store_true",
+                    help="skip timing the query-outer (vanilla NSA order) forward")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB (5 times): the known-size kernel "
@@ -182,7 +189,7 @@ def cpu_baseline(w, target_s):
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
-def run_gpu(w, partial, steps, warmup):
+def run_gpu(w, partial, steps, warmup, query_outer=False):
     import torch
 
     import sparse_attention_sel_amd as fsa
@@ -235,9 +242,23 @@ def run_gpu(w, partial, steps, warmup):
         for i, nm in enumerate(names):
             stage[nm] += ev[i].elapsed_time(ev[i + 1])
     stage = {nm: v_ / steps for nm, v_ in stage.items()}
+    # the query-outer (vanilla NSA loop order) forward on the same inputs,
+    # timed the same way, for the loop-order comparison
+    qo_ms = None
+    if query_outer:
+        for _ in range(2):
+            fsa.nsa_selected_attn_fwd(prob, q, k, v, sel, lse, out, stream)
+        qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+        for a, b in qev:
+            a.record(stream)
+            fsa.nsa_selected_attn_fwd(prob, q, k, v, sel, lse, out, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        qo_ms = sum(a.elapsed_time(b) for a, b in qev) / len(qev)
     counts = index.counts.cpu().numpy()
     return {
         "ms_per_step": wall * 1e3 / steps,
+        "query_outer_ms": qo_ms,
         "stage_ms": stage,
         "pairs": index.num_pairs(),
         "n_valid": {"min": int(counts.min()), "median": float(np.median(counts)), "max": int(counts.max())},
@@ -245,9 +266,9 @@ def run_gpu(w, partial, steps, warmup):
     }
 
 
-def measure(w, partial, steps, warmup):
+def measure(w, partial, steps, warmup, query_outer=False):
     P_host, keys = work_counts(w.sel, w.cu_seqlens, w.block_size)
-    r = run_gpu(w, partial, steps, warmup)
+    r = run_gpu(w, partial, steps, warmup, query_outer)
     assert r["pairs"] == P_host, (r["pairs"], P_host)
     f_alg = 4.0 * w.gqa_group * w.head_dim * keys
     f_main = 4.0 * w.gqa_group * w.block_size * w.head_dim * P_host
@@ -285,7 +306,7 @@ def main():
         cpu = cpu_baseline(w, args.cpu_seconds)  # before the GPU is touched (fork pool)
         log(f"cpu baseline done: {cpu['value']:.4g} TFLOP/s on {cpu['cores']} cores")
     log("gpu run")
-    r = measure(w, args.partial, args.steps, args.warmup)
+    r = measure(w, args.partial, args.steps, args.warmup, not args.no_query_outer)
     log(f"gpu run done: {r['ms_per_step']:.3f} ms/step")
     ms = r["ms_per_step"]
     value = r["f_alg"] / (ms * 1e-3) / 1e12
@@ -344,6 +365,11 @@ def main():
         "n_valid": r["n_valid"],
         "cpu_baseline": cpu,
     }
+    if r["query_outer_ms"] is not None:
+        line["query_outer"] = {
+            "ms": round(r["query_outer_ms"], 4),
+            "fsa_speedup": round(r["query_outer_ms"] / ms, 3),
+        }
     if cpu is not None:
         line["cpu_baseline"] = {k_: v_ for k_, v_ in cpu.items() if k_ != "wall_s"}
     if not args.no_variants and args.workload == DEFAULT_WORKLOAD:
@@ -351,10 +377,11 @@ def main():
         for name in VARIANTS:
             log(f"variant {name}")
             wv = make_workload(name)
-            rv = measure(wv, args.partial, max(3, args.steps // 2), 2)
+            rv = measure(wv, args.partial, max(3, args.steps // 2), 2, not args.no_query_outer)
             stv = rv["stage_ms"]
             var[name] = {
                 "ms_per_step": round(rv["ms_per_step"], 4),
+                "query_outer_ms": None if rv["query_outer_ms"] is None else round(rv["query_outer_ms"], 4),
                 "tflops": round(rv["f_alg"] / (rv["ms_per_step"] * 1e-3) / 1e12, 2),
                 "stages_ms": {k_: round(v_, 4) for k_, v_ in stv.items()},
                 "main_mfma_frac": round(rv["f_alg"] / (stv["main"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[wv.dtype], 4),

@@ -3,8 +3,8 @@
 // README, Method).  It is the baseline the KV-block-outer path is measured
 // against and a second, independent GPU implementation of the same forward.
 //
-// One wave per (query token, KV head).  The g <= 16 query heads of the group
-// (fsa_problem limits g to 16) are the rows of a 16-row MFMA tile
+// One wave per (query token, KV head), head-major.  The g <= 16 query heads
+// of the group (fsa_problem limits g to 16) are the rows of a 16-row MFMA tile
 // (v_mfma_f32_16x16x32), padded with zero rows when g < 16: this padding is
 // the waste the KV-block-outer order removes for small g.  The wave walks the
 // token's selected blocks (valid entries, first occurrence) with an online
@@ -78,6 +78,90 @@ __device__ __forceinline__ unsigned long long nsa_keep_mask(const int32_t* __res
   return __ballot(ok);
 }
 
+// Walk over the kept Sel entries of one row in order: the current 64-entry
+// group and its remaining keep bits.
+struct NsaCursor {
+  int j0;
+  unsigned long long kb;
+};
+
+// Next kept entry index, or -1 after the last (wave-uniform).
+__device__ __forceinline__ int nsa_next(NsaCursor& c, const int32_t* __restrict__ row, int Tn, int own, int lane) {
+  while (c.kb == 0) {
+    c.j0 += 64;
+    if (c.j0 >= Tn) return -1;
+    c.kb = nsa_keep_mask(row, Tn, c.j0, own, lane);
+  }
+  const int jl = __builtin_ctzll(c.kb);
+  c.kb &= c.kb - 1;
+  return c.j0 + jl;
+}
+
+// One block's K (in the A-operand layout of S^T = K Q^T) and V (the lane's
+// share of the key pairs of the transposed staging) in registers.  Key
+// indices are clamped to the sequence (nkeys keys exist from bs on); clamped
+// keys are masked by causality.
+template <typename T, int D, int BK>
+struct NsaKV {
+  using V8 = typename Vec8<T>::type;
+  static constexpr int KS = D / 32, KT = BK / 16;
+  static constexpr int VI = (BK / 2) * (D / 8) / 64;  // key pairs x 8-column chunks per lane
+  static_assert((BK / 2) * (D / 8) % 64 == 0, "whole iterations");
+  V8 kf[KT][KS];
+  V8 va[VI], vb[VI];
+  int bs;
+
+  __device__ __forceinline__ void load_k(const T* __restrict__ k, int nkeys, int H, int h, int lane) {
+    const int lr = lane & 15, hu = lane >> 4;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const T* kp = k + ((size_t)(bs + min(kt * 16 + lr, nkeys - 1)) * H + h) * D + 8 * hu;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kf[kt][ks] = nsa_ld8(kp + ks * 32);
+    }
+  }
+
+  __device__ __forceinline__ void load_v(const T* __restrict__ v, int nkeys, int H, int h, int lane) {
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int vi = lane + 64 * i;
+      const int c = vi / (BK / 2), key = 2 * (vi - c * (BK / 2));
+      va[i] = nsa_ld8(v + ((size_t)(bs + min(key, nkeys - 1)) * H + h) * D + c * 8);
+      vb[i] = nsa_ld8(v + ((size_t)(bs + min(key + 1, nkeys - 1)) * H + h) * D + c * 8);
+    }
+  }
+
+  __device__ __forceinline__ void put_vt(T* __restrict__ Vt, int lane) const {
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int vi = lane + 64 * i;
+      const int c = vi / (BK / 2), key = 2 * (vi - c * (BK / 2));
+      const int pos = nsa_vt_pos(key);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint32_t*>(Vt + (c * 8 + e) * nsa_vt_ld<BK>() + pos) =
+            nsa_bits(va[i][e]) | (nsa_bits(vb[i][e]) << 16);
+    }
+  }
+};
+
+// V block -> the wave's LDS, transposed (Vt[d][pos(key)], key pairs packed),
+// one key pair and 8-column chunk per lane and iteration.
+template <typename T, int D, int BK>
+__device__ __forceinline__ void nsa_stage_vt(const T* __restrict__ v, int bs, int nkeys, int H, int h, int lane,
+                                             T* __restrict__ Vt) {
+  using V8 = typename Vec8<T>::type;
+  for (int vi = lane; vi < (BK / 2) * (D / 8); vi += 64) {
+    const int c = vi / (BK / 2), key = 2 * (vi - c * (BK / 2));
+    const V8 a = nsa_ld8(v + ((size_t)(bs + min(key, nkeys - 1)) * H + h) * D + c * 8);
+    const V8 b = nsa_ld8(v + ((size_t)(bs + min(key + 1, nkeys - 1)) * H + h) * D + c * 8);
+    const int pos = nsa_vt_pos(key);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<uint32_t*>(Vt + (c * 8 + e) * nsa_vt_ld<BK>() + pos) = nsa_bits(a[e]) | (nsa_bits(b[e]) << 16);
+  }
+}
+
 template <typename T, int D, int BK>
 __global__ __launch_bounds__(kNsaWaves * 64) void k_nsa(const T* __restrict__ q, const T* __restrict__ k,
                                                         const T* __restrict__ v, const int32_t* __restrict__ sel,
@@ -96,7 +180,9 @@ __global__ __launch_bounds__(kNsaWaves * 64) void k_nsa(const T* __restrict__ q,
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t item = (int64_t)blockIdx.x * kNsaWaves + wave;
   if (item >= (int64_t)N * H) return;  // wave-uniform; the kernel has no workgroup barrier
-  const int t = (int)(item / H), h = (int)(item - (int64_t)t * H);
+  // head-major: neighbouring waves take consecutive tokens of one KV head,
+  // which select mostly the same blocks, so their K / V reads share the caches
+  const int h = (int)(item / N), t = (int)(item - (int64_t)h * N);
   const int lr = lane & 15, hu = lane >> 4;
   const int HQ = H * g;
   const bool row_ok = lr < g;  // row lr is query head h*g + lr
@@ -124,86 +210,84 @@ __global__ __launch_bounds__(kNsaWaves * 64) void k_nsa(const T* __restrict__ q,
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{};
 
-  for (int j0 = 0; j0 < Tn; j0 += 64) {
-    unsigned long long kb = nsa_keep_mask(srow, Tn, j0, own, lane);
-    while (kb) {
-      const int jl = __builtin_ctzll(kb);
-      kb &= kb - 1;
-      const int bs = c0 + srow[j0 + jl] * BK;
-      const int nkeys = min(BK, c1 - bs);
-      const int lim = t - bs;  // block-local key visible iff key <= lim
-
-      // V block -> this wave's LDS, transposed: Vt[d][pos(key)], key pairs packed.
-      for (int vi = lane; vi < (BK / 2) * (D / 8); vi += 64) {
-        const int c = vi / (BK / 2), kp = vi - c * (BK / 2);
-        const int key = 2 * kp;
-        const V8 a = nsa_ld8(v + ((size_t)(bs + min(key, nkeys - 1)) * H + h) * D + c * 8);
-        const V8 b = nsa_ld8(v + ((size_t)(bs + min(key + 1, nkeys - 1)) * H + h) * D + c * 8);
-        const int pos = nsa_vt_pos(key);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          *reinterpret_cast<uint32_t*>(Vt + (c * 8 + i) * LD + pos) = nsa_bits(a[i]) | (nsa_bits(b[i]) << 16);
-      }
-
-      // S^T = K Q^T: lane supplies K[key kt*16 + lr][ks*32 + 8*hu + e].
-      f32x4 st[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const int key = min(kt * 16 + lr, nkeys - 1);
-        const T* kp = k + ((size_t)(bs + key) * H + h) * D + 8 * hu;
-        f32x4 acc = {};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16(nsa_ld8(kp + ks * 32), qb[ks], acc);
-        st[kt] = acc;
-      }
-
-      // Online softmax update for row lr over keys kt*16 + 4*hu + r.
-      float mb = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (kt * 16 + 4 * hu + r <= lim) mb = fmaxf(mb, st[kt][r]);
-      mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-      // key 0 of a valid block is always visible, so mb is finite
-      const float m_new = fmaxf(m_run, mb * scale_log2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      float ls = 0.f;
-      V8 pb[KK];
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        f32x8 x;
-#pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) {
-          const int kt = 2 * kk + (e8 >> 2), r = e8 & 3;
-          const int key = kt * 16 + 4 * hu + r;
-          const float p = key <= lim ? __builtin_amdgcn_exp2f(fmaf(st[kt][r], scale_log2, -m_new)) : 0.f;
-          ls += p;
-          x[e8] = p;
-        }
-        pb[kk] = __builtin_convertvector(x, V8);
-      }
-      ls += __shfl_xor(ls, 16, 64);
-      ls += __shfl_xor(ls, 32, 64);
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      // O^T = alpha O^T + V^T P^T: lane supplies Vt[mt*16 + lr][kk*32 + 8*hu + e].
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        f32x4 acc = o[mt] * alpha;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) acc = mfma16(nsa_ld8(Vt + (mt * 16 + lr) * LD + kk * 32 + hu * 8), pb[kk], acc);
-        o[mt] = acc;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // Blocks in Sel order.  Per block: V is loaded and staged transposed in
+  // the wave's LDS, then K is loaded in the A-operand layout next to the
+  // MFMAs.  For d = 256 the K loads are issued together with V (one memory
+  // round trip per block), which measured faster there; for the smaller head
+  // dims the later K loads measured faster.
+  NsaCursor cur{0, nsa_keep_mask(srow, Tn, 0, own, lane)};
+  for (int j = nsa_next(cur, srow, Tn, own, lane); j >= 0; j = nsa_next(cur, srow, Tn, own, lane)) {
+    NsaKV<T, D, BK> cb;
+    cb.bs = c0 + srow[j] * BK;
+    const int nkeys = min(BK, c1 - cb.bs);
+    const int lim = t - cb.bs;  // block-local key visible iff key <= lim
+    if constexpr (D >= 256) {
+      cb.load_k(k, nkeys, H, h, lane);
+      cb.load_v(v, nkeys, H, h, lane);
+      cb.put_vt(Vt, lane);
+    } else {
+      nsa_stage_vt<T, D, BK>(v, cb.bs, nkeys, H, h, lane, Vt);
     }
+
+    // S^T = K Q^T: lane supplies K[key kt*16 + lr][ks*32 + 8*hu + e] (for
+    // d < 256 loaded here, next to the MFMAs that consume it).
+    f32x4 st[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const T* kp = k + ((size_t)(cb.bs + min(kt * 16 + lr, nkeys - 1)) * H + h) * D + 8 * hu;
+      f32x4 acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma16(D >= 256 ? cb.kf[kt][ks] : nsa_ld8(kp + ks * 32), qb[ks], acc);
+      st[kt] = acc;
+    }
+
+    // Online softmax update for row lr over keys kt*16 + 4*hu + r.
+    float mb = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (kt * 16 + 4 * hu + r <= lim) mb = fmaxf(mb, st[kt][r]);
+    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
+    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    // key 0 of a valid block is always visible, so mb is finite
+    const float m_new = fmaxf(m_run, mb * scale_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float ls = 0.f;
+    V8 pb[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      f32x8 x;
+#pragma unroll
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const int kt = 2 * kk + (e8 >> 2), r = e8 & 3;
+        const int key = kt * 16 + 4 * hu + r;
+        const float p = key <= lim ? __builtin_amdgcn_exp2f(fmaf(st[kt][r], scale_log2, -m_new)) : 0.f;
+        ls += p;
+        x[e8] = p;
+      }
+      pb[kk] = __builtin_convertvector(x, V8);
+    }
+    ls += __shfl_xor(ls, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O^T = alpha O^T + V^T P^T: lane supplies Vt[mt*16 + lr][kk*32 + 8*hu + e].
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      f32x4 acc = o[mt] * alpha;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) acc = mfma16(nsa_ld8(Vt + (mt * 16 + lr) * LD + kk * 32 + hu * 8), pb[kk], acc);
+      o[mt] = acc;
+    }
+    // the next block's staging writes come after these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
   // O = O^T / l for rows lr < g (lane holds d = mt*16 + 4*hu + r); lse = (m + log2 l) ln 2.
