@@ -25,6 +25,9 @@ the plain definition of that attention:
   row maximum m and the log-sum-exp lse (natural log) of the scaled scores;
 * an empty key set gives O = 0 and m = lse = -inf.
 
+``selected_attention_backward`` is the derivative of that forward for a given
+output gradient (dQ, dK, dV), Sel held constant.
+
 The index oracle produces the canonical layout: segment f = h*NB + global
 block, counts[f] = N_valid (number of queries that select the block), offsets =
 exclusive prefix of counts (the compact output offsets O_i), qidx = the query
@@ -47,6 +50,7 @@ __all__ = [
     "build_index",
     "key_indices",
     "selected_attention",
+    "selected_attention_backward",
 ]
 
 
@@ -176,3 +180,70 @@ def selected_attention(
             row_max[i, h * g : (h + 1) * g] = m
             lse[i, h * g : (h + 1) * g] = ls
     return o, row_max, lse
+
+
+def selected_attention_backward(
+    q,
+    k,
+    v,
+    sel,
+    cu_seqlens,
+    block_size: int,
+    dout,
+    scale: Optional[float] = None,
+):
+    """Gradients of ``selected_attention`` for an output gradient ``dout``, in
+    float64, one (token, KV head) at a time.
+
+    The pages give the forward only and state that the module trains (README,
+    Usage: ``loss.backward()``; Evaluation: the unit tests compare forward and
+    backward outputs).  The gradient is therefore the plain derivative of the
+    forward definition above, with Sel a constant.  For the g query rows of
+    (t, h) with key set K_t: P = softmax(scale * Q K^T), O = P V, and for an
+    output gradient dO:
+
+        dP = dO V^T,   D = rowsum(dO * O),   dS = P * (dP - D),
+        dQ = scale * dS K,   dK += scale * dS^T Q,   dV += P^T dO,
+
+    dK and dV summed over every (t, h) whose key set holds the key.  Rows with
+    an empty key set contribute nothing.
+
+    Returns (dq [N, h_q, d], dk [N, h_K, d], dv [N, h_K, d]) in float64.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    sel = np.asarray(sel)
+    dout = np.asarray(dout)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    N, HQ, D = q.shape
+    H = k.shape[1]
+    g = HQ // H
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = np.zeros((N, HQ, D), dtype=np.float64)
+    dk = np.zeros((N, H, D), dtype=np.float64)
+    dv = np.zeros((N, H, v.shape[2]), dtype=np.float64)
+    for t in range(N):
+        s = int(np.searchsorted(cu, t, side="right") - 1)
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        for h in range(H):
+            keys = key_indices(sel[h, t], t, c0, c1, block_size)
+            if keys.size == 0:
+                continue
+            qh = np.asarray(q[t, h * g : (h + 1) * g, :], dtype=np.float64)  # [g, d]
+            kh = np.asarray(k[keys, h, :], dtype=np.float64)  # [nk, d]
+            vh = np.asarray(v[keys, h, :], dtype=np.float64)  # [nk, d]
+            doh = np.asarray(dout[t, h * g : (h + 1) * g, :], dtype=np.float64)  # [g, d]
+            scores = scale * (qh @ kh.T)  # [g, nk]
+            m = scores.max(axis=1)
+            p = np.exp(scores - m[:, None])
+            p /= p.sum(axis=1, keepdims=True)
+            o = p @ vh
+            dp = doh @ vh.T
+            delta = (doh * o).sum(axis=1)
+            ds = p * (dp - delta[:, None])
+            dq[t, h * g : (h + 1) * g, :] = scale * (ds @ kh)
+            dk[keys, h, :] += scale * (ds.T @ qh)
+            dv[keys, h, :] += p.T @ doh
+    return dq, dk, dv

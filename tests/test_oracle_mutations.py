@@ -14,6 +14,7 @@ import pytest
 
 import oracle.fsa_oracle as O
 import test_oracle_attention as A
+import test_oracle_backward as BW
 import test_oracle_index as I
 
 SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "fsa_oracle.py")
@@ -60,15 +61,37 @@ def fast_pins():
     return pins
 
 
+# backward: dropped term, wrong scale / operand / axis / head grouping,
+# overwrite instead of accumulate
+BWD_MUTATIONS = [
+    ("ds = p * (dp - delta[:, None])", "ds = p * dp"),
+    ("dq[t, h * g : (h + 1) * g, :] = scale * (ds @ kh)", "dq[t, h * g : (h + 1) * g, :] = ds @ kh"),
+    ("dk[keys, h, :] += scale * (ds.T @ qh)", "dk[keys, h, :] += scale * (ds.T @ doh)"),
+    ("dk[keys, h, :] += scale * (ds.T @ qh)", "dk[keys, h, :] = scale * (ds.T @ qh)"),
+    ("dv[keys, h, :] += p.T @ doh", "dv[keys, h, :] += ds.T @ doh"),
+    ("dp = doh @ vh.T", "dp = doh @ kh.T"),
+    ("p /= p.sum(axis=1, keepdims=True)", "p /= p.sum(axis=0, keepdims=True)"),
+    ("doh = np.asarray(dout[t, h * g : (h + 1) * g, :]", "doh = np.asarray(dout[t, h : HQ : H, :]"),
+    ("delta = (doh * o).sum(axis=1)", "delta = (doh * vh[:1]).sum(axis=1)"),
+]
+
+
+def fast_pins_bwd():
+    return [lambda: BW.test_finite_differences(0), lambda: BW.test_torch_autograd_dense_mask(0),
+            BW.test_zero_output_gradient, BW.test_constant_values_give_no_score_gradient,
+            BW.test_value_gradient_column_sums]
+
+
 def load_mutant(old, new):
-    assert SRC.count(old) == 1, f"mutation anchor must occur exactly once: {old!r}"
+    # an expression shared by the forward and the backward is mutated in both
+    assert SRC.count(old) >= 1, f"mutation anchor not found: {old!r}"
     mod = types.ModuleType("oracle_mutant")
     exec(compile(SRC.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
     return mod
 
 
 def test_unmutated_oracle_passes_fast_pins():
-    for pin in fast_pins():
+    for pin in fast_pins() + fast_pins_bwd():
         pin()
 
 
@@ -85,3 +108,18 @@ def test_mutant_is_caught(old, new, monkeypatch):
             failures += 1
             break
     assert failures, f"no pin fails when {old!r} becomes {new!r}"
+
+
+@pytest.mark.parametrize("old,new", BWD_MUTATIONS, ids=[f"b{i}" for i in range(len(BWD_MUTATIONS))])
+def test_backward_mutant_is_caught(old, new, monkeypatch):
+    mut = load_mutant(old, new)
+    for name in O.__all__:
+        monkeypatch.setattr(O, name, getattr(mut, name))
+    failures = 0
+    for pin in fast_pins_bwd():
+        try:
+            pin()
+        except Exception:  # an assertion, or a crash the mutant causes
+            failures += 1
+            break
+    assert failures, f"no backward pin fails when {old!r} becomes {new!r}"
