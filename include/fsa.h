@@ -1,9 +1,9 @@
 /*
- * fsa.h - C ABI of the MI355X (gfx950) selected-attention forward library.
+ * fsa.h - C ABI of the MI355X (gfx950) selected-attention library.
  *
- * The library computes the forward pass of the token-selection ("selected
- * attention") branch of Native Sparse Attention in the KV-block-outer loop
- * order of Flash Sparse Attention (FSA):
+ * The library computes the forward pass (and its gradient) of the
+ * token-selection ("selected attention") branch of Native Sparse Attention in
+ * the KV-block-outer loop order of Flash Sparse Attention (FSA):
  *
  *   - "FSA: An Alternative Efficient Implementation of Native Sparse Attention
  *     Kernel", paper notes (papernotes.org, ICLR 2026): Overall framework
@@ -32,6 +32,10 @@
  *   fsa_softmax_stats      per-query row max and log-sum-exp.
  *   fsa_selected_attn_fwd  main kernel (partials) + reduction -> O.
  *                          (= fsa_selected_attn_main then _reduce.)
+ *   fsa_selected_attn_bwd  dQ, dK, dV for an output gradient dO, from the
+ *                          same index, O and lse.
+ *   fsa_nsa_selected_attn_fwd  the same forward in the query-outer order of
+ *                          vanilla NSA (baseline; needs no index).
  *
  * Ownership.  The caller allocates and owns every buffer (device memory
  * unless marked host).  The library allocates nothing, keeps no pointer
@@ -56,7 +60,7 @@
 extern "C" {
 #endif
 
-#define FSA_ABI_VERSION 1
+#define FSA_ABI_VERSION 2
 
 typedef enum {
   FSA_OK = 0,
@@ -104,6 +108,8 @@ typedef struct {
   size_t build_ws_bytes;  /* scratch for fsa_build_index only */
   size_t stats_ws_bytes;  /* scratch for fsa_softmax_stats only */
   size_t partial_ws_bytes;/* scratch for fsa_selected_attn_fwd / _main / _reduce */
+  size_t bwd_ws_bytes;    /* scratch for fsa_selected_attn_bwd; 0 where no backward
+                             kernel is compiled for the shape (see that call) */
 } fsa_sizes;
 
 /*
@@ -192,6 +198,30 @@ int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const voi
  */
 int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, const void* partial_ws,
                                  size_t partial_ws_bytes, void* out, void* stream);
+
+/*
+ * Backward pass (gradient of the forward above for an output gradient dO;
+ * README, Usage and Evaluation: the module trains and its tests compare
+ * backward outputs).  With P = exp(scale * q.k - lse) over each row's visible
+ * keys:  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+ *        dQ = scale * dS K,  dK = scale * sum dS^T Q,  dV = sum P^T dO.
+ * KV-block-outer like the forward: per (KV head, block, query chunk) the
+ * block's K and V are staged once; dK and dV of the block accumulate in
+ * registers over the chunk's queries and are summed over the chunks in chunk
+ * order; dQ goes through the compact partial rows and the forward's ordered
+ * reduction.  No atomics; deterministic.
+ *   q, k, v, out, dout  device, input dtype, 16-byte aligned (out and lse as
+ *                       returned by the forward for this problem and index);
+ *   lse                 device fp32 [N, h_K*g], 4-byte aligned;
+ *   dq                  device [N, h_K*g, d]; dk, dv device [N, h_K, d]; input
+ *                       dtype, 16-byte aligned, fully written;
+ *   ws                  device scratch of at least bwd_ws_bytes, 256-byte aligned.
+ * Compiled for B_K = 64 and d in {64, 128}; other shapes return
+ * FSA_ERR_UNSUPPORTED (and fsa_get_sizes reports bwd_ws_bytes = 0).
+ */
+int32_t fsa_selected_attn_bwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
+                              const void* out, const void* dout, const float* lse, const fsa_index* idx,
+                              void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Query-outer forward, the loop order of vanilla NSA selected attention

@@ -191,9 +191,14 @@ def selected_attention_backward(
     block_size: int,
     dout,
     scale: Optional[float] = None,
+    tokens: Optional[Iterable[int]] = None,
 ):
     """Gradients of ``selected_attention`` for an output gradient ``dout``, in
     float64, one (token, KV head) at a time.
+
+    ``tokens`` restricts the loop to those query tokens: dq is then exact for
+    them (a row's dQ depends on that row only) and zero elsewhere, while dk
+    and dv hold only their contributions.
 
     The pages give the forward only and state that the module trains (README,
     Usage: ``loss.backward()``; Evaluation: the unit tests compare forward and
@@ -224,7 +229,8 @@ def selected_attention_backward(
     dq = np.zeros((N, HQ, D), dtype=np.float64)
     dk = np.zeros((N, H, D), dtype=np.float64)
     dv = np.zeros((N, H, v.shape[2]), dtype=np.float64)
-    for t in range(N):
+    toks = range(N) if tokens is None else [int(x) for x in tokens]
+    for t in toks:
         s = int(np.searchsorted(cu, t, side="right") - 1)
         c0, c1 = int(cu[s]), int(cu[s + 1])
         for h in range(H):

@@ -38,6 +38,8 @@ __all__ = [
     "selected_attn_main",
     "selected_attn_reduce",
     "nsa_selected_attn_fwd",
+    "selected_attn_bwd",
+    "selected_attention_backward",
     "selected_attention",
     "status_string",
 ]
@@ -83,6 +85,7 @@ class _Sizes(ctypes.Structure):
         ("build_ws_bytes", ctypes.c_size_t),
         ("stats_ws_bytes", ctypes.c_size_t),
         ("partial_ws_bytes", ctypes.c_size_t),
+        ("bwd_ws_bytes", ctypes.c_size_t),
     ]
 
     def as_dict(self):
@@ -100,6 +103,7 @@ class _Index(ctypes.Structure):
 
 
 _LIB = None
+ABI_VERSION = 2  # FSA_ABI_VERSION of include/fsa.h
 
 
 def library_path() -> str:
@@ -136,9 +140,11 @@ def load_library():
     lib.fsa_selected_attn_main.argtypes = [P, vp, vp, vp, I, vp, vp, sz, vp]
     lib.fsa_selected_attn_reduce.restype = i32
     lib.fsa_selected_attn_reduce.argtypes = [P, I, vp, sz, vp, vp]
+    lib.fsa_selected_attn_bwd.restype = i32
+    lib.fsa_selected_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, I, vp, vp, vp, vp, sz, vp]
     lib.fsa_nsa_selected_attn_fwd.restype = i32
     lib.fsa_nsa_selected_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
-    if lib.fsa_abi_version() != 1:
+    if lib.fsa_abi_version() != ABI_VERSION:
         raise RuntimeError("libfsa.so ABI version mismatch")
     _LIB = lib
     return lib
@@ -344,13 +350,53 @@ def selected_attn_reduce(prob, index: Index, partial_ws, out, stream=None):
 
 
 class Workspaces:
-    """Scratch buffers for one problem (plumbing: plain torch allocations)."""
+    """Scratch buffers for one problem (plumbing: plain torch allocations).
+    The backward workspace is allocated only with ``backward=True``."""
 
-    def __init__(self, prob: Problem, device, sizes: dict):
+    def __init__(self, prob: Problem, device, sizes: dict, backward: bool = False):
         u8 = dict(dtype=torch.uint8, device=device)
         self.build = torch.empty(sizes["build_ws_bytes"], **u8)
         self.stats = torch.empty(sizes["stats_ws_bytes"], **u8)
         self.partial = torch.empty(sizes["partial_ws_bytes"], **u8)
+        self.bwd = None
+        if backward:
+            if sizes["bwd_ws_bytes"] == 0:
+                raise FsaError(4, "Workspaces(backward=True)")
+            self.bwd = torch.empty(sizes["bwd_ws_bytes"], **u8)
+
+
+def selected_attn_bwd(prob: Problem, q, k, v, out, dout, lse, index: Index, dq, dk, dv, ws, stream=None):
+    """fsa_selected_attn_bwd: dq [N, h_q, d], dk and dv [N, h_K, d] from the
+    output gradient dout, the forward's out and lse, and the same index."""
+    qs, ks = _qkv_shapes(prob)
+    w, wb = _ws(ws, "backward workspace", index.sizes["bwd_ws_bytes"])
+    args = (
+        _ptr(q, "q", prob.dtype, qs),
+        _ptr(k, "k", prob.dtype, ks),
+        _ptr(v, "v", prob.dtype, ks),
+        _ptr(out, "out", prob.dtype, qs),
+        _ptr(dout, "dout", prob.dtype, qs),
+        _ptr(lse, "lse", torch.float32, (prob.total_tokens, prob.num_q_heads)),
+        index.c(),
+        _ptr(dq, "dq", prob.dtype, qs),
+        _ptr(dk, "dk", prob.dtype, ks),
+        _ptr(dv, "dv", prob.dtype, ks),
+        w,
+        wb,
+    )
+    _check(load_library().fsa_selected_attn_bwd(prob.c(), *args, _stream(stream)), "fsa_selected_attn_bwd")
+
+
+def selected_attention_backward(prob: Problem, q, k, v, out, dout, lse, index: Index, stream=None):
+    """Gradients with torch-allocated outputs and workspace; returns (dq, dk, dv)."""
+    dev = q.device
+    ws = Workspaces(prob, dev, index.sizes, backward=True)
+    qs, ks = _qkv_shapes(prob)
+    dq = torch.empty(qs, dtype=prob.dtype, device=dev)
+    dk = torch.empty(ks, dtype=prob.dtype, device=dev)
+    dv = torch.empty(ks, dtype=prob.dtype, device=dev)
+    selected_attn_bwd(prob, q, k, v, out, dout, lse, index, dq, dk, dv, ws.bwd, stream)
+    return dq, dk, dv
 
 
 def nsa_selected_attn_fwd(prob: Problem, q, k, v, sel, lse, out, stream=None):

@@ -130,6 +130,14 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   const size_t rows = (size_t)geo->dump_row + 32;
   geo->stats_ws_bytes = round_up(rows * 8, 256);
   geo->partial_ws_bytes = round_up(rows * (size_t)geo->d * (geo->partial_dtype == FSA_PARTIAL_FP32 ? 4 : 2), 256);
+  // Backward: the chunk slot offsets[f] / CT + f + c (c < ceil(count_f / CT))
+  // is injective and below max_pairs / CT + M + 2.
+  geo->bwd_ok = BK == 64 && (geo->d == 64 || geo->d == 128);
+  geo->kv_slots = geo->max_pairs / geo->chunk_tokens + H * NB + 2;
+  geo->bwd_dq_off = round_up((size_t)N * H * g * 4, 256);
+  geo->bwd_kv_off = round_up(geo->bwd_dq_off + geo->partial_ws_bytes, 256);
+  geo->bwd_ws_bytes =
+      geo->bwd_ok ? round_up(geo->bwd_kv_off + (size_t)geo->kv_slots * 2 * BK * geo->d * 4, 256) : 0;
   return FSA_OK;
 }
 
@@ -218,6 +226,7 @@ int32_t fsa_get_sizes(const fsa_problem* prob, fsa_sizes* out) {
   out->build_ws_bytes = geo.build_ws_bytes;
   out->stats_ws_bytes = geo.stats_ws_bytes;
   out->partial_ws_bytes = geo.partial_ws_bytes;
+  out->bwd_ws_bytes = geo.bwd_ws_bytes;
   return FSA_OK;
 }
 
@@ -283,6 +292,26 @@ int32_t fsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void
   st = hip_status(launch_main(geo, q, k, v, *idx, lse, partial_ws, s));
   if (st != FSA_OK) return st;
   return hip_status(launch_reduce(geo, *idx, partial_ws, out, s));
+}
+
+int32_t fsa_selected_attn_bwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
+                              const void* out, const void* dout, const float* lse, const fsa_index* idx,
+                              void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+  Geometry geo;
+  int32_t st = prepare(prob, &geo);
+  if (st != FSA_OK) return st;
+  if (!geo.bwd_ok) return FSA_ERR_UNSUPPORTED;
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
+      dq == nullptr || dk == nullptr || dv == nullptr || ws == nullptr)
+    return FSA_ERR_NULL;
+  st = check_index(geo, idx);
+  if (st != FSA_OK) return st;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(ws, 256))
+    return FSA_ERR_ALIGN;
+  if (ws_bytes < geo.bwd_ws_bytes) return FSA_ERR_WORKSPACE;
+  return hip_status(launch_bwd(geo, prob->cu_seqlens_dev, q, k, v, out, dout, lse, *idx, dq, dk, dv, ws,
+                               static_cast<hipStream_t>(stream)));
 }
 
 int32_t fsa_nsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,

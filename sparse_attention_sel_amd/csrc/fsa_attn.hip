@@ -74,22 +74,6 @@ __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~15) + ((w >> 2) & 1) * 8 + (w >> 3) * 4 + (w & 3);
 }
 
-struct Item {
-  int h, ntok, pair0, bs, nkeys;
-};
-
-__device__ __forceinline__ Item read_item(const int4* __restrict__ work, const int32_t* __restrict__ counts,
-                                          const int32_t* __restrict__ offsets, int wi, int NB, int CT, int BK) {
-  const int4 it = work[wi];
-  Item r;
-  r.h = it.x / NB;
-  r.ntok = min(CT, counts[it.x] - it.y);
-  r.pair0 = offsets[it.x] + it.y;
-  r.bs = it.z;
-  r.nkeys = min(BK, it.w - it.z);
-  return r;
-}
-
 // Coalesced gather of the Q rows of one 32-row tile: vector v of lane l holds
 // tile elements (v*64 + l)*8 .. +8, i.e. row (v*64 + l)*8 / D, column
 // (v*64 + l)*8 % D.
@@ -153,29 +137,6 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   const float2 p = xhalf_pair(x);
   return p.x + p.y;
 }
-
-// Persistent workgroups.  The grid is a multiple of 8 and workgroup i runs on
-// XCD x = i % 8 (round-robin dispatch).  XCD x owns the contiguous range
-// [x * per, (x + 1) * per) of the token-ordered work list and its G8 = grid / 8
-// workgroups take the range's items round-robin, so the items in flight on one
-// XCD gather neighbouring query rows.  Every workgroup exits when its next
-// index leaves the range.
-struct ItemCursor {
-  int base, per, k, step, total;
-  __device__ __forceinline__ ItemCursor(int nwork_total) {
-    per = (nwork_total + 7) >> 3;
-    base = (blockIdx.x & 7) * per;
-    k = blockIdx.x >> 3;
-    step = gridDim.x >> 3;
-    total = nwork_total;
-  }
-  __device__ __forceinline__ int current() const { return (k < per && base + k < total) ? base + k : -1; }
-  __device__ __forceinline__ int next() const {
-    const int kn = k + step;
-    return (kn < per && base + kn < total) ? base + kn : -1;
-  }
-  __device__ __forceinline__ void advance() { k += step; }
-};
 
 // The staging data of one work item held in registers while the previous item
 // computes: this thread's share of the K block (and of V, for the main
@@ -637,28 +598,13 @@ inline Ptrs<int> index_ptrs(const Geometry& geo, const fsa_index& idx) {
                    reinterpret_cast<const int32_t*>(aux + geo.aux_nwork)};
 }
 
-// Persistent grid: as many workgroups as fit on the device at once (a
-// multiple of 8, one share per XCD), at most one per work item.
-template <typename K>
-unsigned persistent_grid(K kernel, int64_t max_work) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kAttnThreads, 0) != hipSuccess || cus <= 0 ||
-      per_cu <= 0) {
-    cus = 256;
-    per_cu = 1;
-  }
-  const int64_t want = std::min<int64_t>((int64_t)cus * per_cu, (max_work + 7) / 8 * 8);
-  return (unsigned)std::max<int64_t>(8, (want + 7) / 8 * 8);
-}
 
 template <typename T, int D, int BK>
 void stats_typed(const Geometry& geo, const void* q, const void* k, const fsa_index& idx, float2* st,
                  hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
-  hipLaunchKernelGGL((k_stats<T, D, BK>), dim3(persistent_grid(k_stats<T, D, BK>, geo.max_work)), dim3(kAttnThreads), 0, stream,
+  hipLaunchKernelGGL((k_stats<T, D, BK>), dim3(persistent_grid(k_stats<T, D, BK>, kAttnThreads, geo.max_work)), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), p.counts, p.offsets, p.qidx, p.work, p.nwork,
                      st, (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
 }
@@ -668,7 +614,7 @@ void main_typed(const Geometry& geo, const void* q, const void* k, const void* v
                 const float* lse, void* partial, hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
-  hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3(persistent_grid(k_main<T, D, BK, PT>, geo.max_work)), dim3(kAttnThreads), 0, stream,
+  hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3(persistent_grid(k_main<T, D, BK, PT>, kAttnThreads, geo.max_work)), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), p.counts,
                      p.offsets, p.qidx, p.work, p.nwork, lse, static_cast<PT*>(partial), (size_t)geo.dump_row, geo.H,
                      geo.g, geo.NB, geo.chunk_tokens, sl2);

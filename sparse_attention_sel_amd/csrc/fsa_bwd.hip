@@ -1,0 +1,445 @@
+// Backward pass of selected attention on gfx950, in the KV-block-outer order
+// of the forward (FSA paper notes, Key designs 1-3: per KV block, the block
+// is loaded once and the queries that select it stream through; the README's
+// Usage and Evaluation sections train the module and check its gradients).
+//
+//   k_bwd_delta      D[t, hq] = sum_d dO * O  (fp32).
+//   k_bwd_main       per work item (KV head, block, query chunk): K, V and
+//                    K^T of the 64-key block are staged in LDS once; the
+//                    item's query rows stream through in 16-row tiles.  Wave
+//                    w owns keys 16w .. 16w+15: it forms S = Q K^T and
+//                    dP = dO V^T for its keys, P = exp(S - lse), dS = P (dP -
+//                    D), and accumulates dV^T += dO^T P and dK^T += Q^T dS in
+//                    registers over the chunk.  dS of all 64 keys meets in
+//                    LDS and dQ^T = K^T dS^T (split over d across the waves) is
+//                    written to the compact partial rows of the forward.  At
+//                    the end of the item the block's dK / dV partial goes to
+//                    the item's slot offsets[f] / CT + f + chunk.
+//   k_reduce         (the forward's reduction) sums each (token, KV head)'s dQ
+//                    partial rows in slot order.
+//   k_bwd_kv_reduce  per key row of every block: dK, dV = sum over the
+//                    block's chunk slots in chunk order.
+// No atomics; every sum has a fixed order, so the gradients are deterministic.
+//
+// MFMA layouts (wave64, l = lane, u = l / 16).  v_mfma_f32_16x16x32: lane l
+// supplies A[l % 16][8u + e] and B[8u + e][l % 16] (e < 8) and receives
+// C[4u + r][l % 16] (r < 4).  v_mfma_f32_16x16x16: A[l % 16][4u + e],
+// B[4u + e][l % 16] (e < 4), same C.  S = Q K^T (rows x keys) therefore leaves
+// lane l with key l % 16 and rows 4u + r, which is exactly the B operand of a
+// 16x16x16 product that contracts over the rows: dV^T = dO^T P and
+// dK^T = Q^T dS need no transpose of P or dS.
+#include <math.h>
+
+#include "fsa_internal.h"
+
+namespace fsa {
+namespace {
+
+constexpr float kBwdLog2e = 1.4426950408889634f;
+constexpr int kBwdThreads = 256;  // 4 waves x 16 keys = the 64-key block
+constexpr int kBwdBK = 64;
+constexpr int kBwdRows = 16;  // query rows per tile
+constexpr int kBwdRowTable = kRowsPerItem + kBwdRows;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Vec4;
+template <>
+struct Vec4<__bf16> {
+  using type = bf16x4;
+};
+template <>
+struct Vec4<_Float16> {
+  using type = f16x4;
+};
+
+__device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
+                                                   0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_k16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Vec8<T>::type bld8(const T* p) {
+  return *reinterpret_cast<const typename Vec8<T>::type*>(p);
+}
+template <typename T>
+__device__ __forceinline__ typename Vec4<T>::type bld4(const T* p) {
+  return *reinterpret_cast<const typename Vec4<T>::type*>(p);
+}
+template <typename T>
+__device__ __forceinline__ uint32_t bbits(T x) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, x);
+}
+
+// LDS pitches (elements).  K, V: [64][D + 8]; K^T: [D][64 + 8]; Q, dO tiles:
+// [16][D + 8]; their transposes: [D][16 + 4]; dS: [16][64 + 8].
+template <int D>
+constexpr int b_kld() { return D + 8; }
+constexpr int kKtLd = kBwdBK + 8;
+constexpr int kTLd = kBwdRows + 4;
+constexpr int kSLd = kBwdBK + 8;
+
+// ---- D = rowsum(dO * O) -------------------------------------------------------
+// D / 8 lanes per row, 16-byte loads, a butterfly over those lanes.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ out, const T* __restrict__ dout,
+                                                   float* __restrict__ delta, int64_t rows) {
+  constexpr int LPR = D / 8;  // lanes per row (8, 16 or 32)
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / LPR;
+  const int c = (int)(idx % LPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const auto o = bld8(out + row * D + c * 8);
+    const auto g = bld8(dout + row * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+  if (row < rows && c == 0) delta[row] = acc;
+}
+
+// ---- main ---------------------------------------------------------------------
+// One item's staging data held in registers while the previous item computes:
+// K as key pairs (row-major copy and packed transposed copy), V row-major, the
+// query tokens of the item's row table, and the raw work entry.
+template <typename T, int D>
+struct BwdStage {
+  using V8 = typename Vec8<T>::type;
+  static constexpr int C8 = D / 8;
+  static constexpr int KP = (kBwdBK / 2) * C8 / kBwdThreads;  // K key-pair vectors per thread
+  static constexpr int VV = kBwdBK * C8 / kBwdThreads;        // V vectors per thread
+  static constexpr int RT = (kBwdRowTable + kBwdThreads - 1) / kBwdThreads;
+  static_assert((kBwdBK / 2) * C8 % kBwdThreads == 0 && kBwdBK * C8 % kBwdThreads == 0, "whole vectors");
+  int4 w;
+  Item it;
+  V8 ka[KP], kb[KP], vv[VV];
+  int tok[RT];
+
+  __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
+                                       const int32_t* __restrict__ qidx, const int4* __restrict__ work,
+                                       const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+                                       int wi, int H, int g, int NB, int CT) {
+    w = work[wi];
+    it = read_item(work, counts, offsets, wi, NB, CT, kBwdBK);
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int vi = threadIdx.x + i * kBwdThreads;
+      const int c = vi / (kBwdBK / 2), key = 2 * (vi % (kBwdBK / 2));
+      ka[i] = bld8(k + ((size_t)(it.bs + min(key, it.nkeys - 1)) * H + it.h) * D + c * 8);
+      kb[i] = bld8(k + ((size_t)(it.bs + min(key + 1, it.nkeys - 1)) * H + it.h) * D + c * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VV; ++i) {
+      const int vi = threadIdx.x + i * kBwdThreads;
+      vv[i] = bld8(v + ((size_t)(it.bs + min(vi / C8, it.nkeys - 1)) * H + it.h) * D + (vi % C8) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int r = threadIdx.x + i * kBwdThreads;
+      tok[i] = qidx[it.pair0 + min(r / g, it.ntok - 1)];
+    }
+  }
+
+  __device__ __forceinline__ void commit(T* __restrict__ Ks, T* __restrict__ Vs, T* __restrict__ Kt,
+                                         int* __restrict__ rtok, int g) const {
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int vi = threadIdx.x + i * kBwdThreads;
+      const int c = vi / (kBwdBK / 2), key = 2 * (vi % (kBwdBK / 2));
+      *reinterpret_cast<V8*>(Ks + key * b_kld<D>() + c * 8) = ka[i];
+      *reinterpret_cast<V8*>(Ks + (key + 1) * b_kld<D>() + c * 8) = kb[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint32_t*>(Kt + (c * 8 + e) * kKtLd + key) = bbits(ka[i][e]) | (bbits(kb[i][e]) << 16);
+    }
+#pragma unroll
+    for (int i = 0; i < VV; ++i) {
+      const int vi = threadIdx.x + i * kBwdThreads;
+      *reinterpret_cast<V8*>(Vs + (vi / C8) * b_kld<D>() + (vi % C8) * 8) = vv[i];
+    }
+    const int nrows = it.ntok * g;
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int r = threadIdx.x + i * kBwdThreads;
+      if (r < kBwdRowTable) rtok[r] = r < nrows ? tok[i] : -1;
+    }
+  }
+};
+
+// One 16-row tile's gather data in registers: this thread's Q / dO vectors
+// (zero for rows past the chunk) and, for threads < 16, its row's lse (base 2)
+// and D.
+template <typename T, int D>
+struct BwdTile {
+  using V8 = typename Vec8<T>::type;
+  static constexpr int NV = 4 * D / kBwdThreads;  // 16 rows x D/8 chunks x 2 tensors over the threads
+  V8 x[NV];
+  float l2, dd;
+
+  __device__ __forceinline__ void load(const T* __restrict__ q, const T* __restrict__ dout,
+                                       const float* __restrict__ lse, const float* __restrict__ delta,
+                                       const int* __restrict__ rtok, int tile, int h, int g, int HQ) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = threadIdx.x + i * kBwdThreads;
+      const int tensor = vi / (2 * D), e = vi % (2 * D);
+      const int row = e / (D / 8), c = e % (D / 8);
+      const int r = tile * kBwdRows + row;
+      const int t = rtok[r];
+      const size_t qrow = t >= 0 ? (size_t)t * HQ + h * g + r % g : 0;
+      const V8 val = bld8((tensor == 0 ? q : dout) + qrow * D + c * 8);
+      x[i] = t >= 0 ? val : V8{};
+    }
+    l2 = 0.f;
+    dd = 0.f;
+    if (threadIdx.x < kBwdRows) {
+      const int r = tile * kBwdRows + threadIdx.x;
+      const int t = rtok[r];
+      if (t >= 0) {
+        const size_t qrow = (size_t)t * HQ + h * g + r % g;
+        l2 = lse[qrow] * kBwdLog2e;
+        dd = delta[qrow];
+      }
+    }
+  }
+
+  __device__ __forceinline__ void put(T* __restrict__ Qs, T* __restrict__ Ds, T* __restrict__ Qt,
+                                      T* __restrict__ Dt, float* __restrict__ tab_l, float* __restrict__ tab_d) const {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int vi = threadIdx.x + i * kBwdThreads;
+      const int tensor = vi / (2 * D), e = vi % (2 * D);
+      const int row = e / (D / 8), c = e % (D / 8);
+      T* rm = tensor == 0 ? Qs : Ds;
+      T* tr = tensor == 0 ? Qt : Dt;
+      *reinterpret_cast<V8*>(rm + row * b_kld<D>() + c * 8) = x[i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tr[(c * 8 + j) * kTLd + row] = x[i][j];
+    }
+    if (threadIdx.x < kBwdRows) {
+      tab_l[threadIdx.x] = l2;
+      tab_d[threadIdx.x] = dd;
+    }
+  }
+};
+
+template <typename T, int D, typename PT>
+__global__ __launch_bounds__(kBwdThreads) void k_bwd_main(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
+    const int32_t* __restrict__ nwork, PT* __restrict__ dq_part, float* __restrict__ kv_part, int H, int g, int NB,
+    int CT, float scale, float scale_log2) {
+  using V4 = typename Vec4<T>::type;
+  constexpr int KS = D / 32;  // 32-wide contraction steps over d
+  constexpr int MT = D / 16;  // 16-wide d tiles
+  __shared__ __attribute__((aligned(16))) T Ks[kBwdBK * b_kld<D>()];
+  __shared__ __attribute__((aligned(16))) T Vs[kBwdBK * b_kld<D>()];
+  __shared__ __attribute__((aligned(16))) T Kt[D * kKtLd];
+  __shared__ __attribute__((aligned(16))) T Qs[kBwdRows * b_kld<D>()];
+  __shared__ __attribute__((aligned(16))) T Ds[kBwdRows * b_kld<D>()];
+  __shared__ __attribute__((aligned(16))) T Qt[D * kTLd];
+  __shared__ __attribute__((aligned(16))) T Dt[D * kTLd];
+  __shared__ __attribute__((aligned(16))) T Ss[kBwdRows * kSLd];
+  __shared__ __attribute__((aligned(16))) int rtok[kBwdRowTable];
+  __shared__ __attribute__((aligned(16))) float tab_l[kBwdRows];
+  __shared__ __attribute__((aligned(16))) float tab_d[kBwdRows];
+
+  ItemCursor cur(nwork[0]);
+  if (cur.current() < 0) return;
+  const int HQ = H * g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kl = lane & 15, u = lane >> 4;
+  const int key = wave * 16 + kl;  // this lane's key within the block (S, dP, dK, dV)
+  BwdStage<T, D> pre;
+  pre.load(k, v, qidx, work, counts, offsets, cur.current(), H, g, NB, CT);
+  for (; cur.current() >= 0; cur.advance()) {
+    __syncthreads();  // the previous item's LDS reads are done
+    pre.commit(Ks, Vs, Kt, rtok, g);
+    const Item it = pre.it;
+    const int4 wraw = pre.w;
+    __syncthreads();
+    const int nrows = it.ntok * g, ntile = (nrows + kBwdRows - 1) / kBwdRows;
+    BwdTile<T, D> tl;
+    tl.load(q, dout, lse, delta, rtok, 0, it.h, g, HQ);
+    const int wn = cur.next();
+    if (wn >= 0) pre.load(k, v, qidx, work, counts, offsets, wn, H, g, NB, CT);
+
+    f32x4 dk[MT], dv[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) dk[mt] = dv[mt] = f32x4{};
+
+    for (int tile = 0; tile < ntile; ++tile) {
+      tl.put(Qs, Ds, Qt, Dt, tab_l, tab_d);
+      __syncthreads();  // tile in LDS; every wave is past the previous tile's dQ
+      if (tile + 1 < ntile) tl.load(q, dout, lse, delta, rtok, tile + 1, it.h, g, HQ);
+
+      // S = Q K^T and dP = dO V^T for rows 4u + r and this lane's key.
+      f32x4 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s = mfma_k32(bld8(Qs + kl * b_kld<D>() + 32 * ks + 8 * u), bld8(Ks + key * b_kld<D>() + 32 * ks + 8 * u), s);
+        dp = mfma_k32(bld8(Ds + kl * b_kld<D>() + 32 * ks + 8 * u), bld8(Vs + key * b_kld<D>() + 32 * ks + 8 * u), dp);
+      }
+      const int4 tk = *reinterpret_cast<const int4*>(rtok + tile * kBwdRows + 4 * u);
+      const f32x4 l2 = *reinterpret_cast<const f32x4*>(tab_l + 4 * u);
+      const f32x4 dd = *reinterpret_cast<const f32x4*>(tab_d + 4 * u);
+      const int tks[4] = {tk.x, tk.y, tk.z, tk.w};
+      f32x4 p, ds;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // key visible iff it is in the row's causal past (rows past the chunk: token -1)
+        const bool vis = tks[r] >= 0 && key <= tks[r] - it.bs;
+        p[r] = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -l2[r])) : 0.f;
+        ds[r] = p[r] * (dp[r] - dd[r]);
+      }
+      const V4 p4 = __builtin_convertvector(p, V4);
+      const V4 ds4 = __builtin_convertvector(ds, V4);
+      // dV^T += dO^T P and dK^T += Q^T dS (contraction over the tile's 16 rows)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        dv[mt] = mfma_k16(bld4(Dt + (16 * mt + kl) * kTLd + 4 * u), p4, dv[mt]);
+        dk[mt] = mfma_k16(bld4(Qt + (16 * mt + kl) * kTLd + 4 * u), ds4, dk[mt]);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ss[(4 * u + r) * kSLd + key] = ds4[r];
+      __syncthreads();  // dS of all 64 keys in LDS
+
+      // dQ^T = K^T dS^T for the d tiles of this wave; lane: row kl, d = 16mt + 4u + r.
+      const int row = tile * kBwdRows + kl;
+      PT* const dst = dq_part + ((size_t)it.pair0 * g + row) * D + 4 * u;
+      for (int mt = wave; mt < MT; mt += kBwdThreads / 64) {
+        f32x4 acc = {};
+#pragma unroll
+        for (int ks = 0; ks < kBwdBK / 32; ++ks)
+          acc = mfma_k32(bld8(Kt + (16 * mt + kl) * kKtLd + 32 * ks + 8 * u), bld8(Ss + kl * kSLd + 32 * ks + 8 * u),
+                         acc);
+        if (row < nrows) {
+          if constexpr (sizeof(PT) == 4) {
+            *reinterpret_cast<f32x4*>(dst + 16 * mt) = acc * scale;
+          } else {
+            typedef PT P4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<P4*>(dst + 16 * mt) = __builtin_convertvector(acc * scale, P4);
+          }
+        }
+      }
+    }
+
+    // The block's dK (scaled) / dV partial of this chunk: slot [2][64][D] fp32.
+    const int64_t slot = (int64_t)(offsets[wraw.x] / CT) + wraw.x + wraw.y / CT;
+    float* const kvp = kv_part + slot * 2 * kBwdBK * D + (size_t)key * D + 4 * u;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      *reinterpret_cast<f32x4*>(kvp + 16 * mt) = dk[mt] * scale;
+      *reinterpret_cast<f32x4*>(kvp + kBwdBK * D + 16 * mt) = dv[mt];
+    }
+  }
+}
+
+// ---- dK, dV = ordered sum of the block's chunk slots --------------------------
+// One thread per (segment f, key, 4 columns); keys past the sequence end are
+// skipped, keys of blocks nobody selects get zero.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_bwd_kv_reduce(const int32_t* __restrict__ counts,
+                                                       const int32_t* __restrict__ offsets,
+                                                       const int32_t* __restrict__ gboff,
+                                                       const int32_t* __restrict__ cu, int num_seqs,
+                                                       const float* __restrict__ kv_part, T* __restrict__ dk,
+                                                       T* __restrict__ dv, int H, int NB, int CT) {
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  constexpr int C4 = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)H * NB * kBwdBK * C4) return;
+  const int c4 = (int)(idx % C4);
+  const int key = (int)((idx / C4) % kBwdBK);
+  const int f = (int)(idx / ((int64_t)C4 * kBwdBK));
+  const int h = f / NB, gb = f - h * NB;
+  const int s = seq_of_block(gboff, num_seqs, gb);
+  const int token = cu[s] + (gb - gboff[s]) * kBwdBK + key;
+  if (token >= cu[s + 1]) return;
+  const int nch = (counts[f] + CT - 1) / CT;
+  const int64_t slot0 = (int64_t)(offsets[f] / CT) + f;
+  f32x4 sk = {}, sv = {};
+  for (int c = 0; c < nch; ++c) {
+    const float* p = kv_part + (slot0 + c) * 2 * kBwdBK * D + (size_t)key * D + 4 * c4;
+    sk += *reinterpret_cast<const f32x4*>(p);
+    sv += *reinterpret_cast<const f32x4*>(p + kBwdBK * D);
+  }
+  const size_t o = ((size_t)token * H + h) * D + 4 * c4;
+  *reinterpret_cast<T4*>(dk + o) = __builtin_convertvector(sk, T4);
+  *reinterpret_cast<T4*>(dv + o) = __builtin_convertvector(sv, T4);
+}
+
+template <typename T, int D, typename PT>
+hipError_t bwd_typed(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
+                     const void* out, const void* dout, const float* lse, const fsa_index& idx, void* dq, void* dk,
+                     void* dv, void* ws, hipStream_t stream) {
+  char* wsb = static_cast<char*>(ws);
+  float* delta = reinterpret_cast<float*>(wsb);
+  PT* dq_part = reinterpret_cast<PT*>(wsb + geo.bwd_dq_off);
+  float* kv_part = reinterpret_cast<float*>(wsb + geo.bwd_kv_off);
+  const char* aux = static_cast<const char*>(idx.aux);
+  const int4* work = reinterpret_cast<const int4*>(aux + geo.aux_work_sorted);
+  const int32_t* nwork = reinterpret_cast<const int32_t*>(aux + geo.aux_nwork);
+  const int32_t* gboff = reinterpret_cast<const int32_t*>(aux + geo.aux_seq_gboff);
+
+  const int64_t rows = (int64_t)geo.N * geo.HQ;
+  const int64_t dthreads = rows * (D / 8);
+  hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((unsigned)((dthreads + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const T*>(out), static_cast<const T*>(dout), delta, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_bwd_main<T, D, PT>),
+                     dim3(persistent_grid(k_bwd_main<T, D, PT>, kBwdThreads, geo.max_work)), dim3(kBwdThreads), 0,
+                     stream, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                     static_cast<const T*>(dout), lse, delta, idx.counts, idx.offsets, idx.qidx, work, nwork, dq_part,
+                     kv_part, geo.H, geo.g, geo.NB, geo.chunk_tokens, geo.scale, geo.scale * kBwdLog2e);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_reduce(geo, idx, dq_part, dq, stream);
+  if (e != hipSuccess) return e;
+  const int64_t kthreads = (int64_t)geo.H * geo.NB * kBwdBK * (D / 4);
+  if (kthreads > 0)
+    hipLaunchKernelGGL((k_bwd_kv_reduce<T, D>), dim3((unsigned)((kthreads + 255) / 256)), dim3(256), 0, stream,
+                       idx.counts, idx.offsets, gboff, cu_dev, geo.num_seqs, kv_part, static_cast<T*>(dk),
+                       static_cast<T*>(dv), geo.H, geo.NB, geo.chunk_tokens);
+  return hipGetLastError();
+}
+
+template <typename T, typename PT>
+hipError_t bwd_d(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
+                 const void* out, const void* dout, const float* lse, const fsa_index& idx, void* dq, void* dk,
+                 void* dv, void* ws, hipStream_t s) {
+  if (geo.d == 64) return bwd_typed<T, 64, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
+  return bwd_typed<T, 128, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
+                      const void* out, const void* dout, const float* lse, const fsa_index& idx, void* dq, void* dk,
+                      void* dv, void* ws, hipStream_t stream) {
+  if (geo.N == 0) return hipSuccess;
+  const bool f32 = geo.partial_dtype == FSA_PARTIAL_FP32;
+  if (geo.dtype == FSA_DTYPE_BF16)
+    return f32 ? bwd_d<__bf16, float>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, stream)
+               : bwd_d<__bf16, __bf16>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, stream);
+  return f32 ? bwd_d<_Float16, float>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, stream)
+             : bwd_d<_Float16, _Float16>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, stream);
+}
+
+}  // namespace fsa

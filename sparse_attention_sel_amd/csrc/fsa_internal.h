@@ -58,6 +58,11 @@ struct Geometry {
   size_t build_ws_buckets;  // byte offset of the work-order bucket counters in the build workspace
   size_t stats_ws_bytes;
   size_t partial_ws_bytes;
+  // backward workspace: delta [N, HQ] fp32 | dQ partial rows (as partial_ws) |
+  // dK / dV slots: fp32 [kv_slots][2][BK][d], slot = offsets[f] / CT + f + chunk
+  bool bwd_ok;           // a backward kernel is compiled for (d, BK)
+  int64_t kv_slots;
+  size_t bwd_dq_off, bwd_kv_off, bwd_ws_bytes;
 };
 
 int32_t compute_geometry(const fsa_problem* prob, Geometry* geo);
@@ -74,6 +79,9 @@ hipError_t launch_main(const Geometry& geo, const void* q, const void* k, const 
                        const fsa_index& idx, const float* lse, void* partial, hipStream_t stream);
 hipError_t launch_reduce(const Geometry& geo, const fsa_index& idx, const void* partial, void* out,
                          hipStream_t stream);
+hipError_t launch_bwd(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
+                      const void* out, const void* dout, const float* lse, const fsa_index& idx, void* dq, void* dk,
+                      void* dv, void* ws, hipStream_t stream);
 hipError_t launch_nsa(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
                       const int32_t* sel, void* out, float* lse, hipStream_t stream);
 
@@ -120,6 +128,67 @@ __device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cu, int 
 // Sequence that holds global block gb: the last s with gboff[s] <= gb.
 __device__ __forceinline__ int seq_of_block(const int32_t* __restrict__ gboff, int num_seqs, int gb) {
   return seq_of_token(gboff, num_seqs, gb);
+}
+
+// One work item of the attention kernels: KV head, number of query tokens,
+// first pair (position in qidx), block start token and keys in the block.
+struct Item {
+  int h, ntok, pair0, bs, nkeys;
+};
+
+// Work item wi = (segment f, first query of the chunk within the segment,
+// block start token, sequence end) of the index builder's work list.
+__device__ __forceinline__ Item read_item(const int4* __restrict__ work, const int32_t* __restrict__ counts,
+                                          const int32_t* __restrict__ offsets, int wi, int NB, int CT, int BK) {
+  const int4 it = work[wi];
+  Item r;
+  r.h = it.x / NB;
+  r.ntok = min(CT, counts[it.x] - it.y);
+  r.pair0 = offsets[it.x] + it.y;
+  r.bs = it.z;
+  r.nkeys = min(BK, it.w - it.z);
+  return r;
+}
+
+// Persistent workgroups.  The grid is a multiple of 8 and workgroup i runs on
+// XCD x = i % 8 (round-robin dispatch).  XCD x owns the contiguous range
+// [x * per, (x + 1) * per) of the token-ordered work list and its G8 = grid / 8
+// workgroups take the range's items round-robin, so the items in flight on one
+// XCD gather neighbouring query rows.  Every workgroup exits when its next
+// index leaves the range.
+struct ItemCursor {
+  int base, per, k, step, total;
+  __device__ __forceinline__ ItemCursor(int nwork_total) {
+    per = (nwork_total + 7) >> 3;
+    base = (blockIdx.x & 7) * per;
+    k = blockIdx.x >> 3;
+    step = gridDim.x >> 3;
+    total = nwork_total;
+  }
+  __device__ __forceinline__ int current() const { return (k < per && base + k < total) ? base + k : -1; }
+  __device__ __forceinline__ int next() const {
+    const int kn = k + step;
+    return (kn < per && base + kn < total) ? base + kn : -1;
+  }
+  __device__ __forceinline__ void advance() { k += step; }
+};
+
+// Persistent grid: as many workgroups of `threads` as fit on the device at
+// once (a multiple of 8, one share per XCD), at most one per work item.
+template <typename K>
+inline unsigned persistent_grid(K kernel, int threads, int64_t max_work) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || cus <= 0 ||
+      per_cu <= 0) {
+    cus = 256;
+    per_cu = 1;
+  }
+  int64_t want = (int64_t)cus * per_cu;
+  if (want > (max_work + 7) / 8 * 8) want = (max_work + 7) / 8 * 8;
+  want = (want + 7) / 8 * 8;
+  return (unsigned)(want < 8 ? 8 : want);
 }
 
 }  // namespace fsa

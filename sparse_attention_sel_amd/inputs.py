@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for NSA selected attention.
 
-This module produces inputs only: Q/K/V tensors and the per-KV-head block
-selection tensor Sel[h_K, N, T].  It holds none of the attention arithmetic and
+This module produces inputs only: Q/K/V tensors, an output gradient dO for the
+backward, and the per-KV-head block selection tensor Sel[h_K, N, T].  It holds none of the attention arithmetic and
 is shared by the oracle tests, the GPU tests and the benchmark, so that both
 sides of every parity check see the same bytes.
 
@@ -30,6 +30,7 @@ __all__ = [
     "Workload",
     "make_workload",
     "make_qkv",
+    "make_dout",
     "make_sel",
     "shuffle_rows",
     "cu_seqlens_of",
@@ -111,6 +112,17 @@ def make_qkv(num_tokens: int, num_kv_heads: int, gqa_group: int, head_dim: int, 
         x = torch.randn((num_tokens, heads, head_dim), generator=g, dtype=torch.float32)
         out.append(x.to(td))
     return tuple(out)
+
+
+def make_dout(num_tokens: int, num_q_heads: int, head_dim: int, dtype: str, seed: int):
+    """An output gradient dO ~ N(0, 1) of shape [N, h_q, d] for the backward,
+    from its own seeded CPU generator (stream 3 of the workload's seed), cast
+    to the storage dtype with round-to-nearest-even."""
+    import torch
+
+    g = torch.Generator(device="cpu").manual_seed(int(seed) * 8 + 3)
+    x = torch.randn((num_tokens, num_q_heads, head_dim), generator=g, dtype=torch.float32)
+    return x.to(_torch_dtype(dtype))
 
 
 def _forced_blocks(kind: str, b: int) -> List[int]:

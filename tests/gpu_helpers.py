@@ -61,6 +61,33 @@ def run_gpu(w: Workload, partial: str = "fp32", keep_partial: bool = False):
     return res
 
 
+def run_gpu_bwd(w: Workload, dout, partial: str = "fp32"):
+    """FSA forward then backward on cuda:0 for the output gradient ``dout``
+    (torch CPU tensor, input dtype).  Returns host float32 numpy arrays
+    dq, dk, dv (and out, lse of the forward)."""
+    prob = problem_for(w, partial)
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    do = dout.to(dev)
+    sel = torch.from_numpy(w.sel).to(dev)
+    index = fsa.allocate_index(prob, dev)
+    ws = fsa.Workspaces(prob, dev, index.sizes, backward=True)
+    n, hq, d = prob.total_tokens, prob.num_q_heads, prob.head_dim
+    lse = torch.empty((n, hq), dtype=torch.float32, device=dev)
+    row_max = torch.empty((n, hq), dtype=torch.float32, device=dev)
+    out = torch.empty((n, hq, d), dtype=prob.dtype, device=dev)
+    fsa.build_index(prob, sel, index, ws.build)
+    fsa.softmax_stats(prob, q, k, index, row_max, lse, ws.stats)
+    fsa.selected_attn_fwd(prob, q, k, v, index, lse, out, ws.partial)
+    dq = torch.full((n, hq, d), float("nan"), dtype=prob.dtype, device=dev)
+    dk = torch.full((n, prob.num_kv_heads, d), float("nan"), dtype=prob.dtype, device=dev)
+    dv = torch.full_like(dk, float("nan"))
+    fsa.selected_attn_bwd(prob, q, k, v, out, do, lse, index, dq, dk, dv, ws.bwd)
+    torch.cuda.synchronize()
+    return {"dq": dq.float().cpu().numpy(), "dk": dk.float().cpu().numpy(), "dv": dv.float().cpu().numpy(),
+            "out": out.float().cpu().numpy(), "lse": lse.cpu().numpy()}
+
+
 def run_gpu_nsa(w: Workload):
     """Query-outer forward on cuda:0 straight from Sel.  Returns host numpy
     arrays out [N, h_q, d] (float32) and lse [N, h_q]."""

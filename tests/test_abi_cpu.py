@@ -47,7 +47,7 @@ def test_library_is_gfx950():
 
 def test_version_and_status_strings():
     lib = fsa.load_library()
-    assert lib.fsa_abi_version() == 1
+    assert lib.fsa_abi_version() == fsa.ABI_VERSION == 2
     for s in range(8):
         assert len(fsa.status_string(s)) > 0
     assert fsa.status_string(99) == "unknown status"
@@ -88,6 +88,13 @@ def test_sizes_closed_form(name):
     assert s.slot_bytes == 4 * H * N * T and s.qidx_bytes == 4 * pmax
     assert s.partial_ws_bytes >= pmax * sp.gqa_group * sp.head_dim * 4
     assert s.stats_ws_bytes >= pmax * sp.gqa_group * 8
+    # backward: delta [N, h_q] fp32 + dQ partial rows + fp32 dK/dV slots of [2][B_K][d]
+    if B == 64 and sp.head_dim in (64, 128):
+        CT = -(-1024 // sp.gqa_group)
+        slots = pmax // CT + H * sum(nb) + 2
+        assert s.bwd_ws_bytes >= 4 * N * H * sp.gqa_group + s.partial_ws_bytes + slots * 2 * B * sp.head_dim * 4
+    else:
+        assert s.bwd_ws_bytes == 0
 
 
 def test_max_pairs_bounds_real_pairs():
@@ -168,6 +175,20 @@ def test_entry_points_reject_before_launch():
     assert lib.fsa_selected_attn_reduce(P, I, f, pw, None, None) == NULL
     assert lib.fsa_selected_attn_reduce(P, I, f, pw - 1, f, None) == WS
     assert lib.fsa_selected_attn_reduce(P, ctypes.byref(null_idx), f, pw, f, None) == NULL
+    # backward
+    bw = s.bwd_ws_bytes
+    assert bw > 0
+    assert lib.fsa_selected_attn_bwd(P, f, f, f, None, f, f, I, f, f, f, f, bw, None) == NULL
+    assert lib.fsa_selected_attn_bwd(P, f, f, f, f, None, f, I, f, f, f, f, bw, None) == NULL
+    assert lib.fsa_selected_attn_bwd(P, f, f, f, f, f, f, I, f, f, None, f, bw, None) == NULL
+    assert lib.fsa_selected_attn_bwd(P, f, f, f, f, f, f, ctypes.byref(null_idx), f, f, f, f, bw, None) == NULL
+    assert lib.fsa_selected_attn_bwd(P, f, f, f, f, f + 8, f, I, f, f, f, f, bw, None) == ALIGN
+    assert lib.fsa_selected_attn_bwd(P, f, f, f, f, f, f, I, f, f, f, f + 16, bw, None) == ALIGN
+    assert lib.fsa_selected_attn_bwd(P, f, f, f, f, f, f, I, f, f, f, f, bw - 1, None) == WS
+    assert lib.fsa_selected_attn_bwd(ctypes.byref(prob(B=128)), f, f, f, f, f, f, I, f, f, f, f, bw,
+                                     None) == UNSUP
+    assert lib.fsa_selected_attn_bwd(ctypes.byref(prob(d=256)), f, f, f, f, f, f, I, f, f, f, f, bw,
+                                     None) == UNSUP
     # query-outer forward (no index, no workspace)
     assert lib.fsa_nsa_selected_attn_fwd(None, f, f, f, f, f, f, None) == NULL
     assert lib.fsa_nsa_selected_attn_fwd(P, f, f, f, None, f, f, None) == NULL
