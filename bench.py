@@ -7,11 +7,12 @@ Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--partial input|fp32] [--no-cpu-baseline] [--no-variants]
-                    [--no-query-outer]
+                    [--no-query-outer] [--no-backward]
 
 The query-outer forward (fsa_nsa_selected_attn_fwd, the vanilla NSA loop
 order) is timed on the same inputs and reported beside the step, with the
-FSA-order speedup over it.
+FSA-order speedup over it; so is the backward (fsa_selected_attn_bwd) from the
+step's O and lse, with its algorithmic TFLOP/s (10 g d flops per visible key).
 
 Throughput is algorithmic TFLOP/s: 4 * g * d * (sum over (token, KV head) of
 the number of keys the token attends to), i.e. QK^T and PV over the visible
@@ -33,7 +34,7 @@ METRIC = "selected-attn fwd latency (ms) + TFLOP/s at 64K tokens, g=1/2/4; % MFM
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # dense MFMA
 DEFAULT_WORKLOAD = "n64k_h4_g4_d128_t16_bf16"
-VARIANTS = ["n64k_h4_g2_d128_t16_bf16", "n64k_h4_g1_d128_t16_bf16"]
+VARIANTS = ["n64k_h4_g2_d128_t16_bf16", "n64k_h4_g1_d128_t16_bf16", "n64k_h4_g4_d128_b128_t8_bf16"]
 
 
 def log(msg):
@@ -51,6 +52,7 @@ def parse():
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-query-outer", action="store_true",
                     help="skip timing the query-outer (vanilla NSA order) forward")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB (5 times): the known-size kernel "
@@ -189,7 +191,7 @@ def cpu_baseline(w, target_s):
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
-def run_gpu(w, partial, steps, warmup, query_outer=False):
+def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False):
     import torch
 
     import sparse_attention_sel_amd as fsa
@@ -255,10 +257,32 @@ def run_gpu(w, partial, steps, warmup, query_outer=False):
             b.record(stream)
         torch.cuda.synchronize()
         qo_ms = sum(a.elapsed_time(b) for a, b in qev) / len(qev)
+    # the backward (fsa_selected_attn_bwd) from this forward's O and lse, for
+    # a seeded output gradient, timed the same way
+    bwd_ms = None
+    if backward and index.sizes["bwd_ws_bytes"] > 0:
+        from sparse_attention_sel_amd.inputs import make_dout
+
+        do = make_dout(n, hq, prob.head_dim, w.dtype, 7).to(dev)
+        wsb = fsa.Workspaces(prob, dev, index.sizes, backward=True)
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        for _ in range(2):
+            fsa.selected_attn_bwd(prob, q, k, v, out, do, lse, index, dq, dk, dv, wsb.bwd, stream)
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in bev:
+            a.record(stream)
+            fsa.selected_attn_bwd(prob, q, k, v, out, do, lse, index, dq, dk, dv, wsb.bwd, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = sum(a.elapsed_time(b) for a, b in bev) / len(bev)
+        del wsb, dq, dk, dv, do
     counts = index.counts.cpu().numpy()
     return {
         "ms_per_step": wall * 1e3 / steps,
         "query_outer_ms": qo_ms,
+        "backward_ms": bwd_ms,
         "stage_ms": stage,
         "pairs": index.num_pairs(),
         "n_valid": {"min": int(counts.min()), "median": float(np.median(counts)), "max": int(counts.max())},
@@ -266,9 +290,9 @@ def run_gpu(w, partial, steps, warmup, query_outer=False):
     }
 
 
-def measure(w, partial, steps, warmup, query_outer=False):
+def measure(w, partial, steps, warmup, query_outer=False, backward=False):
     P_host, keys = work_counts(w.sel, w.cu_seqlens, w.block_size)
-    r = run_gpu(w, partial, steps, warmup, query_outer)
+    r = run_gpu(w, partial, steps, warmup, query_outer, backward)
     assert r["pairs"] == P_host, (r["pairs"], P_host)
     f_alg = 4.0 * w.gqa_group * w.head_dim * keys
     f_main = 4.0 * w.gqa_group * w.block_size * w.head_dim * P_host
@@ -306,7 +330,7 @@ def main():
         cpu = cpu_baseline(w, args.cpu_seconds)  # before the GPU is touched (fork pool)
         log(f"cpu baseline done: {cpu['value']:.4g} TFLOP/s on {cpu['cores']} cores")
     log("gpu run")
-    r = measure(w, args.partial, args.steps, args.warmup, not args.no_query_outer)
+    r = measure(w, args.partial, args.steps, args.warmup, not args.no_query_outer, not args.no_backward)
     log(f"gpu run done: {r['ms_per_step']:.3f} ms/step")
     ms = r["ms_per_step"]
     value = r["f_alg"] / (ms * 1e-3) / 1e12
@@ -365,6 +389,14 @@ def main():
         "n_valid": r["n_valid"],
         "cpu_baseline": cpu,
     }
+    if r["backward_ms"] is not None:
+        # algorithmic backward work: S, dP, dV, dK, dQ over the visible keys
+        f_bwd = r["f_alg"] * 10.0 / 4.0
+        line["backward"] = {
+            "ms": round(r["backward_ms"], 4),
+            "tflops_alg": round(f_bwd / (r["backward_ms"] * 1e-3) / 1e12, 2),
+            "ratio_to_forward": round(r["backward_ms"] / ms, 3),
+        }
     if r["query_outer_ms"] is not None:
         line["query_outer"] = {
             "ms": round(r["query_outer_ms"], 4),
@@ -377,10 +409,11 @@ def main():
         for name in VARIANTS:
             log(f"variant {name}")
             wv = make_workload(name)
-            rv = measure(wv, args.partial, max(3, args.steps // 2), 2, not args.no_query_outer)
+            rv = measure(wv, args.partial, max(3, args.steps // 2), 2, not args.no_query_outer, not args.no_backward)
             stv = rv["stage_ms"]
             var[name] = {
                 "ms_per_step": round(rv["ms_per_step"], 4),
+                "backward_ms": None if rv["backward_ms"] is None else round(rv["backward_ms"], 4),
                 "query_outer_ms": None if rv["query_outer_ms"] is None else round(rv["query_outer_ms"], 4),
                 "tflops": round(rv["f_alg"] / (rv["ms_per_step"] * 1e-3) / 1e12, 2),
                 "stages_ms": {k_: round(v_, 4) for k_, v_ in stv.items()},

@@ -62,6 +62,10 @@ WORKLOADS: Dict[str, WorkloadSpec] = {
     # 64K-token bf16 latency shape at the two smaller group sizes.
     "n64k_h4_g2_d128_t16_bf16": WorkloadSpec((65536,), 4, 2, 128, 64, 16, "bf16", "init_local_zipf", 3200),
     "n64k_h4_g1_d128_t16_bf16": WorkloadSpec((65536,), 4, 1, 128, 64, 16, "bf16", "init_local_zipf", 3100),
+    # the same 64K g = 4 shape with 128-key blocks and 8 selected blocks (the
+    # same 1024 selected keys per token; the README's Performance section
+    # benchmarks both (B_K, T) = (64, 16) and (128, 8))
+    "n64k_h4_g4_d128_b128_t8_bf16": WorkloadSpec((65536,), 4, 4, 128, 128, 8, "bf16", "init_local_zipf", 3300),
 }
 
 

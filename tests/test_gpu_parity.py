@@ -26,6 +26,7 @@ LARGE = [
     ("b2_n32k_h8_g8_d256_t16_bf16", "input"),
     ("n64k_h4_g2_d128_t16_bf16", "fp32"),
     ("n64k_h4_g1_d128_t16_bf16", "fp32"),
+    ("n64k_h4_g4_d128_b128_t8_bf16", "input"),
 ]
 
 
