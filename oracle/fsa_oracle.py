@@ -26,7 +26,8 @@ the plain definition of that attention:
 * an empty key set gives O = 0 and m = lse = -inf.
 
 ``selected_attention_backward`` is the derivative of that forward for a given
-output gradient (dQ, dK, dV), Sel held constant.
+output gradient (dQ, dK, dV), Sel held constant.  ``select_blocks`` produces
+the Sel rows from per-block scores (top-k with forced initial / local blocks).
 
 The index oracle produces the canonical layout: segment f = h*NB + global
 block, counts[f] = N_valid (number of queries that select the block), offsets =
@@ -51,6 +52,7 @@ __all__ = [
     "key_indices",
     "selected_attention",
     "selected_attention_backward",
+    "select_blocks",
 ]
 
 
@@ -253,3 +255,45 @@ def selected_attention_backward(
             dk[keys, h, :] += scale * (ds.T @ qh)
             dv[keys, h, :] += p.T @ doh
     return dq, dk, dv
+
+
+def select_blocks(scores, cu_seqlens, block_size: int, topk: int, init_blocks: int, local_blocks: int):
+    """NSA block selection: the Sel rows the attention consumes, from per-block
+    importance scores, in int32 [h_K, N, T].
+
+    The pages give the selection's hyper-parameters (README, Usage:
+    ``topk=16, init_blocks=1, local_blocks=2``) and say that each query token
+    picks T KV blocks per KV head (paper notes, Background and motivation);
+    the scores themselves (NSA's compressed attention) are not described and
+    are an input here: ``scores[h, t, e]`` for the local blocks e of t's
+    sequence (entries e > own block are ignored).  For query token t (own
+    block b) and KV head h the row is
+
+      * the forced blocks: initial blocks 0 .. init_blocks-1, then the local
+        blocks b, b-1, .. b-local_blocks+1, each kept once and only if
+        0 <= e <= b, truncated to T entries;
+      * then the remaining candidates e in [0, b] ranked by score, highest
+        first, ties to the smaller e (NaN counts as -inf), as many as fit;
+      * then -1 padding.
+    """
+    scores = np.asarray(scores)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    H, N = scores.shape[0], scores.shape[1]
+    sel = np.full((H, N, topk), -1, dtype=np.int32)
+    for t in range(N):
+        s = int(np.searchsorted(cu, t, side="right") - 1)
+        own = (t - int(cu[s])) // block_size
+        forced = []
+        for e in list(range(init_blocks)) + [own - i for i in range(local_blocks)]:
+            if 0 <= e <= own and e not in forced:
+                forced.append(e)
+        forced = forced[:topk]
+        free = [e for e in range(own + 1) if e not in forced]
+        for h in range(H):
+            sc = np.asarray(scores[h, t, : own + 1], dtype=np.float64)
+            sc = np.where(np.isnan(sc), -np.inf, sc)
+            # rank by (score descending, block ascending)
+            order = sorted(free, key=lambda e: (-sc[e], e))
+            row = forced + order[: topk - len(forced)]
+            sel[h, t, : len(row)] = row
+    return sel

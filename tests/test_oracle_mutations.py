@@ -16,6 +16,7 @@ import oracle.fsa_oracle as O
 import test_oracle_attention as A
 import test_oracle_backward as BW
 import test_oracle_index as I
+import test_oracle_select as SEL
 
 SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "fsa_oracle.py")
 with open(SRC_PATH) as f:
@@ -76,6 +77,24 @@ BWD_MUTATIONS = [
 ]
 
 
+# block selection: ranking direction, tie order, forced set, truncation, NaN
+SEL_MUTATIONS = [
+    ("order = sorted(free, key=lambda e: (-sc[e], e))", "order = sorted(free, key=lambda e: (sc[e], e))"),
+    ("order = sorted(free, key=lambda e: (-sc[e], e))", "order = sorted(free, key=lambda e: (-sc[e], -e))"),
+    ("[own - i for i in range(local_blocks)]", "[own - i - 1 for i in range(local_blocks)]"),
+    ("if 0 <= e <= own and e not in forced:", "if 0 <= e <= own:"),
+    ("forced = forced[:topk]", "forced = forced"),
+    ("sc = np.where(np.isnan(sc), -np.inf, sc)", "sc = np.where(np.isnan(sc), np.inf, sc)"),
+    ("own = (t - int(cu[s])) // block_size", "own = t // block_size"),
+    ("free = [e for e in range(own + 1) if e not in forced]", "free = [e for e in range(own) if e not in forced]"),
+]
+
+
+def fast_pins_sel():
+    return [SEL.test_handworked_example] + [lambda s=s: SEL.test_against_brute_force(s) for s in range(3)] + [
+        lambda: SEL.test_invariants(0)]
+
+
 def fast_pins_bwd():
     return [lambda: BW.test_finite_differences(0), lambda: BW.test_torch_autograd_dense_mask(0),
             BW.test_zero_output_gradient, BW.test_constant_values_give_no_score_gradient,
@@ -91,7 +110,7 @@ def load_mutant(old, new):
 
 
 def test_unmutated_oracle_passes_fast_pins():
-    for pin in fast_pins() + fast_pins_bwd():
+    for pin in fast_pins() + fast_pins_bwd() + fast_pins_sel():
         pin()
 
 
@@ -123,3 +142,18 @@ def test_backward_mutant_is_caught(old, new, monkeypatch):
             failures += 1
             break
     assert failures, f"no backward pin fails when {old!r} becomes {new!r}"
+
+
+@pytest.mark.parametrize("old,new", SEL_MUTATIONS, ids=[f"s{i}" for i in range(len(SEL_MUTATIONS))])
+def test_selection_mutant_is_caught(old, new, monkeypatch):
+    mut = load_mutant(old, new)
+    for name in O.__all__:
+        monkeypatch.setattr(O, name, getattr(mut, name))
+    failures = 0
+    for pin in fast_pins_sel():
+        try:
+            pin()
+        except Exception:  # an assertion, or a crash the mutant causes
+            failures += 1
+            break
+    assert failures, f"no selection pin fails when {old!r} becomes {new!r}"
