@@ -36,6 +36,8 @@
  *                          same index, O and lse.
  *   fsa_nsa_selected_attn_fwd  the same forward in the query-outer order of
  *                          vanilla NSA (baseline; needs no index).
+ *   fsa_select_blocks      Sel from per-block scores (top-k with forced
+ *                          initial and local blocks), the step before the path.
  *
  * Ownership.  The caller allocates and owns every buffer (device memory
  * unless marked host).  The library allocates nothing, keeps no pointer
@@ -222,6 +224,24 @@ int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, 
 int32_t fsa_selected_attn_bwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
                               const void* out, const void* dout, const float* lse, const fsa_index* idx,
                               void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Block selection, the step that produces Sel (README, Usage: topk,
+ * init_blocks, local_blocks; paper notes, Background and motivation: every
+ * query token picks T KV blocks per KV head).  The scores are an input (the
+ * pages do not describe NSA's compressed-attention scoring):
+ *   scores  device fp32 [h_K, N, score_stride]: scores[h, t, e] for the local
+ *           blocks e of t's sequence; entries e > t's own block are ignored.
+ *           score_stride >= the block count of the longest sequence.
+ *   sel     device int32 [h_K, N, T], written: for own block b, the forced
+ *           blocks (0 .. init_blocks-1 that are <= b, then b, b-1, .. for
+ *           local_blocks, each once, truncated to T), then the other blocks
+ *           e <= b by score descending with ties to the smaller e (NaN counts
+ *           as -inf, -0 as +0), then -1.
+ * init_blocks, local_blocks >= 0.  Bit-exact and deterministic.
+ */
+int32_t fsa_select_blocks(const fsa_problem* prob, const float* scores, int64_t score_stride, int32_t init_blocks,
+                          int32_t local_blocks, int32_t* sel, void* stream);
 
 /*
  * Query-outer forward, the loop order of vanilla NSA selected attention

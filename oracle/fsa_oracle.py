@@ -257,7 +257,8 @@ def selected_attention_backward(
     return dq, dk, dv
 
 
-def select_blocks(scores, cu_seqlens, block_size: int, topk: int, init_blocks: int, local_blocks: int):
+def select_blocks(scores, cu_seqlens, block_size: int, topk: int, init_blocks: int, local_blocks: int,
+                  tokens: Optional[Iterable[int]] = None):
     """NSA block selection: the Sel rows the attention consumes, from per-block
     importance scores, in int32 [h_K, N, T].
 
@@ -275,12 +276,15 @@ def select_blocks(scores, cu_seqlens, block_size: int, topk: int, init_blocks: i
       * then the remaining candidates e in [0, b] ranked by score, highest
         first, ties to the smaller e (NaN counts as -inf), as many as fit;
       * then -1 padding.
+
+    ``tokens`` restricts the evaluation to those query tokens (the other rows
+    stay -1).
     """
     scores = np.asarray(scores)
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     H, N = scores.shape[0], scores.shape[1]
     sel = np.full((H, N, topk), -1, dtype=np.int32)
-    for t in range(N):
+    for t in range(N) if tokens is None else [int(x) for x in tokens]:
         s = int(np.searchsorted(cu, t, side="right") - 1)
         own = (t - int(cu[s])) // block_size
         forced = []

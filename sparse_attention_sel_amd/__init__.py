@@ -40,6 +40,7 @@ __all__ = [
     "nsa_selected_attn_fwd",
     "selected_attn_bwd",
     "selected_attention_backward",
+    "select_blocks",
     "selected_attention",
     "status_string",
 ]
@@ -142,6 +143,8 @@ def load_library():
     lib.fsa_selected_attn_reduce.argtypes = [P, I, vp, sz, vp, vp]
     lib.fsa_selected_attn_bwd.restype = i32
     lib.fsa_selected_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, I, vp, vp, vp, vp, sz, vp]
+    lib.fsa_select_blocks.restype = i32
+    lib.fsa_select_blocks.argtypes = [P, vp, ctypes.c_int64, i32, i32, vp, vp]
     lib.fsa_nsa_selected_attn_fwd.restype = i32
     lib.fsa_nsa_selected_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     if lib.fsa_abi_version() != ABI_VERSION:
@@ -397,6 +400,18 @@ def selected_attention_backward(prob: Problem, q, k, v, out, dout, lse, index: I
     dv = torch.empty(ks, dtype=prob.dtype, device=dev)
     selected_attn_bwd(prob, q, k, v, out, dout, lse, index, dq, dk, dv, ws.bwd, stream)
     return dq, dk, dv
+
+
+def select_blocks(prob: Problem, scores, init_blocks: int, local_blocks: int, sel, stream=None):
+    """fsa_select_blocks: scores fp32 [h_K, N, S] (S >= blocks of the longest
+    sequence) -> sel int32 [h_K, N, T]."""
+    if scores.dim() != 3:
+        raise ValueError("scores must be [h_K, N, S]")
+    S = int(scores.shape[2])
+    p = _ptr(scores, "scores", torch.float32, (prob.num_kv_heads, prob.total_tokens, S))
+    o = _ptr(sel, "sel", torch.int32, (prob.num_kv_heads, prob.total_tokens, prob.topk))
+    _check(load_library().fsa_select_blocks(prob.c(), p, S, int(init_blocks), int(local_blocks), o, _stream(stream)),
+           "fsa_select_blocks")
 
 
 def nsa_selected_attn_fwd(prob: Problem, q, k, v, sel, lse, out, stream=None):

@@ -61,11 +61,12 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   // at most min(T, e + 1) distinct blocks) and the bound on work items (block
   // e of a sequence can be selected by at most the L - e*BK tokens from its
   // start to the end of the sequence).
-  int64_t NB = 0, pairs = 0, work = 0;
+  int64_t NB = 0, pairs = 0, work = 0, max_nb = 0;
   for (int s = 0; s < B; ++s) {
     const int64_t L = cu[s + 1] - cu[s];
     const int64_t nb = (L + BK - 1) / BK;
     NB += nb;
+    max_nb = std::max(max_nb, nb);
     for (int64_t e = 0; e < nb; ++e) {
       const int64_t ntok = std::min(BK, L - e * BK);
       pairs += ntok * std::min(T, e + 1);
@@ -74,6 +75,8 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   }
   if (H * NB >= (int64_t(1) << 30)) return FSA_ERR_SHAPE;
   geo->NB = (int32_t)NB;
+  geo->max_seq_blocks = max_nb;
+  geo->select_long_rows = max_nb > kSelRegBlocks;
   geo->max_pairs = H * pairs;
   geo->max_work = std::min(H * work, (geo->max_pairs + CT - 1) / CT + H * NB);
   if (geo->max_work >= (int64_t(1) << 31)) return FSA_ERR_SHAPE;
@@ -312,6 +315,19 @@ int32_t fsa_selected_attn_bwd(const fsa_problem* prob, const void* q, const void
   if (ws_bytes < geo.bwd_ws_bytes) return FSA_ERR_WORKSPACE;
   return hip_status(launch_bwd(geo, prob->cu_seqlens_dev, q, k, v, out, dout, lse, *idx, dq, dk, dv, ws,
                                static_cast<hipStream_t>(stream)));
+}
+
+int32_t fsa_select_blocks(const fsa_problem* prob, const float* scores, int64_t score_stride, int32_t init_blocks,
+                          int32_t local_blocks, int32_t* sel, void* stream) {
+  Geometry geo;
+  const int32_t st = prepare(prob, &geo);
+  if (st != FSA_OK) return st;
+  if (scores == nullptr || sel == nullptr) return FSA_ERR_NULL;
+  if (init_blocks < 0 || local_blocks < 0 || score_stride < geo.max_seq_blocks || score_stride < 1)
+    return FSA_ERR_SHAPE;
+  if (!aligned(scores, 4) || !aligned(sel, 4)) return FSA_ERR_ALIGN;
+  return hip_status(launch_select(geo, prob->cu_seqlens_dev, scores, score_stride, init_blocks, local_blocks, sel,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 int32_t fsa_nsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,

@@ -20,6 +20,7 @@ constexpr int kAttnThreads = 256;      // 4 waves per main / stats workgroup
 constexpr int kRowsPerItem = 1024;     // target query rows (tokens * g) per work item
 constexpr int kReduceThreads = 256;
 constexpr int kSortBucketsMax = 16384;  // buckets of the work-order sort
+constexpr int kSelRegBlocks = 1024;     // block selection keeps rows up to this many blocks in registers
 
 // ---------------------------------------------------------------------------
 // Problem geometry, computed once on the host from fsa_problem.
@@ -34,6 +35,8 @@ struct Geometry {
   int32_t BK;     // block size
   int32_t T;      // Sel entries per row
   int32_t NB;     // global blocks per head
+  int64_t max_seq_blocks;  // blocks of the longest sequence
+  bool select_long_rows;   // some sequence has more than kSelRegBlocks blocks
   int32_t tile_tokens;   // tokens per index tile
   int32_t ntiles;        // index tiles
   int32_t win_max;       // largest block window of any tile
@@ -82,6 +85,8 @@ hipError_t launch_reduce(const Geometry& geo, const fsa_index& idx, const void* 
 hipError_t launch_bwd(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
                       const void* out, const void* dout, const float* lse, const fsa_index& idx, void* dq, void* dk,
                       void* dv, void* ws, hipStream_t stream);
+hipError_t launch_select(const Geometry& geo, const int32_t* cu_dev, const float* scores, int64_t S, int init_blocks,
+                         int local_blocks, int32_t* sel, hipStream_t stream);
 hipError_t launch_nsa(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
                       const int32_t* sel, void* out, float* lse, hipStream_t stream);
 

@@ -31,6 +31,7 @@ __all__ = [
     "make_workload",
     "make_qkv",
     "make_dout",
+    "make_block_scores",
     "make_sel",
     "shuffle_rows",
     "cu_seqlens_of",
@@ -127,6 +128,30 @@ def make_dout(num_tokens: int, num_q_heads: int, head_dim: int, dtype: str, seed
     g = torch.Generator(device="cpu").manual_seed(int(seed) * 8 + 3)
     x = torch.randn((num_tokens, num_q_heads, head_dim), generator=g, dtype=torch.float32)
     return x.to(_torch_dtype(dtype))
+
+
+def make_block_scores(seqlens: Sequence[int], num_kv_heads: int, block_size: int, seed: int) -> np.ndarray:
+    """Synthetic block-importance scores for the selection step, float32
+    [h_K, N, S] with S = blocks of the longest sequence: a recency term
+    -log(b - e + 1) for query token t of local block b and block e, plus
+    standard Gumbel noise (PCG64, seeded).  Entries e > b are noise only (the
+    selection ignores them).  A stand-in for NSA's compressed-attention
+    scores, which the pages do not describe."""
+    rng = np.random.Generator(np.random.PCG64(int(seed)))
+    seqlens = [int(x) for x in seqlens]
+    S = max([-(-L // block_size) for L in seqlens] + [1])
+    N = sum(seqlens)
+    out = np.empty((num_kv_heads, N, S), dtype=np.float32)
+    e = np.arange(S, dtype=np.float64)
+    t0 = 0
+    for L in seqlens:
+        b = np.arange(L) // block_size
+        rec = -np.log(np.maximum(b[:, None] - e[None, :], 0.0) + 1.0)
+        for h in range(num_kv_heads):
+            g = rng.gumbel(size=(L, S))
+            out[h, t0 : t0 + L] = (rec + g).astype(np.float32)
+        t0 += L
+    return out
 
 
 def _forced_blocks(kind: str, b: int) -> List[int]:

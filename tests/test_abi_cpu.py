@@ -189,6 +189,14 @@ def test_entry_points_reject_before_launch():
                                      None) == UNSUP
     assert lib.fsa_selected_attn_bwd(ctypes.byref(prob(d=256)), f, f, f, f, f, f, I, f, f, f, f, bw,
                                      None) == UNSUP
+    # block selection
+    assert lib.fsa_select_blocks(P, None, 16, 1, 2, f, None) == NULL
+    assert lib.fsa_select_blocks(P, f, 16, 1, 2, None, None) == NULL
+    assert lib.fsa_select_blocks(P, f, 15, 1, 2, f, None) == SHAPE  # 1000 tokens / 64 = 16 blocks
+    assert lib.fsa_select_blocks(P, f, 16, -1, 2, f, None) == SHAPE
+    assert lib.fsa_select_blocks(P, f, 16, 1, -2, f, None) == SHAPE
+    assert lib.fsa_select_blocks(P, f + 2, 16, 1, 2, f, None) == ALIGN
+    assert lib.fsa_select_blocks(ctypes.byref(prob(dev=False)), f, 16, 1, 2, f, None) == NULL
     # query-outer forward (no index, no workspace)
     assert lib.fsa_nsa_selected_attn_fwd(None, f, f, f, f, f, f, None) == NULL
     assert lib.fsa_nsa_selected_attn_fwd(P, f, f, f, None, f, f, None) == NULL
