@@ -7,12 +7,14 @@ Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--partial input|fp32] [--no-cpu-baseline] [--no-variants]
-                    [--no-query-outer] [--no-backward]
+                    [--no-query-outer] [--no-backward] [--no-selection]
 
 The query-outer forward (fsa_nsa_selected_attn_fwd, the vanilla NSA loop
 order) is timed on the same inputs and reported beside the step, with the
 FSA-order speedup over it; so is the backward (fsa_selected_attn_bwd) from the
-step's O and lse, with its algorithmic TFLOP/s (10 g d flops per visible key).
+step's O and lse, with its algorithmic TFLOP/s (10 g d flops per visible key),
+and block selection (fsa_select_blocks, the step that produces Sel) on
+synthetic scores of the same shape, with its HBM rate on the causal scores read.
 
 Throughput is algorithmic TFLOP/s: 4 * g * d * (sum over (token, KV head) of
 the number of keys the token attends to), i.e. QK^T and PV over the visible
@@ -53,6 +55,7 @@ def parse():
     ap.add_argument("--no-query-outer", action="store_true",
                     help="skip timing the query-outer (vanilla NSA order) forward")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
+    ap.add_argument("--no-selection", action="store_true", help="skip timing block selection")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB (5 times): the known-size kernel "
@@ -191,7 +194,7 @@ def cpu_baseline(w, target_s):
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
-def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False):
+def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, selection=False):
     import torch
 
     import sparse_attention_sel_amd as fsa
@@ -278,9 +281,30 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False):
         torch.cuda.synchronize()
         bwd_ms = sum(a.elapsed_time(b) for a, b in bev) / len(bev)
         del wsb, dq, dk, dv, do
+    # block selection (fsa_select_blocks) on synthetic recency-weighted scores
+    # of this shape, init_blocks = 1, local_blocks = 2
+    sel_ms = sel_bytes = None
+    if selection:
+        from sparse_attention_sel_amd.inputs import make_block_scores
+
+        scores = torch.from_numpy(make_block_scores(w.seqlens, w.num_kv_heads, w.block_size, 17)).to(dev)
+        sel_out = torch.empty_like(sel)
+        fsa.select_blocks(prob, scores, 1, 2, sel_out, stream)
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(5)]
+        for a, b in sev:
+            a.record(stream)
+            fsa.select_blocks(prob, scores, 1, 2, sel_out, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        sel_ms = sum(a.elapsed_time(b) for a, b in sev) / len(sev)
+        own_blocks = sum(int(((np.arange(L) // w.block_size) + 1).sum()) for L in w.seqlens)
+        sel_bytes = w.num_kv_heads * (4 * own_blocks + 4 * int(w.cu_seqlens[-1]) * w.topk)
+        del scores, sel_out
     counts = index.counts.cpu().numpy()
     return {
         "ms_per_step": wall * 1e3 / steps,
+        "selection_ms": sel_ms,
+        "selection_bytes": sel_bytes,
         "query_outer_ms": qo_ms,
         "backward_ms": bwd_ms,
         "stage_ms": stage,
@@ -290,9 +314,9 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False):
     }
 
 
-def measure(w, partial, steps, warmup, query_outer=False, backward=False):
+def measure(w, partial, steps, warmup, query_outer=False, backward=False, selection=False):
     P_host, keys = work_counts(w.sel, w.cu_seqlens, w.block_size)
-    r = run_gpu(w, partial, steps, warmup, query_outer, backward)
+    r = run_gpu(w, partial, steps, warmup, query_outer, backward, selection)
     assert r["pairs"] == P_host, (r["pairs"], P_host)
     f_alg = 4.0 * w.gqa_group * w.head_dim * keys
     f_main = 4.0 * w.gqa_group * w.block_size * w.head_dim * P_host
@@ -330,7 +354,8 @@ def main():
         cpu = cpu_baseline(w, args.cpu_seconds)  # before the GPU is touched (fork pool)
         log(f"cpu baseline done: {cpu['value']:.4g} TFLOP/s on {cpu['cores']} cores")
     log("gpu run")
-    r = measure(w, args.partial, args.steps, args.warmup, not args.no_query_outer, not args.no_backward)
+    r = measure(w, args.partial, args.steps, args.warmup, not args.no_query_outer, not args.no_backward,
+                not args.no_selection)
     log(f"gpu run done: {r['ms_per_step']:.3f} ms/step")
     ms = r["ms_per_step"]
     value = r["f_alg"] / (ms * 1e-3) / 1e12
@@ -389,6 +414,14 @@ def main():
         "n_valid": r["n_valid"],
         "cpu_baseline": cpu,
     }
+    if r["selection_ms"] is not None:
+        gbs = r["selection_bytes"] / (r["selection_ms"] * 1e-3) / 1e9
+        line["selection"] = {
+            "ms": round(r["selection_ms"], 4),
+            "hbm_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": int(r["selection_bytes"]),
+        }
     if r["backward_ms"] is not None:
         # algorithmic backward work: S, dP, dV, dK, dQ over the visible keys
         f_bwd = r["f_alg"] * 10.0 / 4.0
