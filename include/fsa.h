@@ -51,6 +51,12 @@
  * checks run before anything is enqueued: on any status other than
  * FSA_ERR_HIP nothing has been enqueued.  FSA_ERR_HIP means a kernel launch
  * failed; earlier kernels of the same call may have been enqueued.
+ *
+ * Empty problems.  With no tokens (N = 0) the per-token data buffers (Q, K,
+ * V, O, dO, lse, row max, Sel, scores, dQ, dK, dV) are empty and may be NULL;
+ * workspaces and index buffers are never empty (fsa_get_sizes reports at
+ * least one element) and stay required.  fsa_build_index still writes
+ * offsets[0] = 0 (P = 0).
  */
 #ifndef FSA_H_
 #define FSA_H_

@@ -228,10 +228,14 @@ class Index:
     """Device buffers of the index tensors (fsa_index): counts, offsets, qidx,
     slot and the library-private aux blob that travels with them."""
 
-    def __init__(self, counts, offsets, qidx, slot, aux, sizes):
+    def __init__(self, counts, offsets, qidx, slot, aux, sizes, buffers=None):
+        """``counts`` and ``slot`` may be shaped views; ``buffers`` (the five
+        underlying allocations, in the same order) supplies the addresses
+        handed to the library, which stay valid when a view is empty."""
         self.counts, self.offsets, self.qidx, self.slot, self.aux = counts, offsets, qidx, slot, aux
         self.sizes = sizes
-        self._c = _Index(counts.data_ptr(), offsets.data_ptr(), qidx.data_ptr(), slot.data_ptr(), aux.data_ptr())
+        self._bufs = buffers if buffers is not None else (counts, offsets, qidx, slot, aux)
+        self._c = _Index(*(b.data_ptr() for b in self._bufs))
 
     def c(self):
         return ctypes.byref(self._c)
@@ -243,16 +247,17 @@ class Index:
 def allocate_index(prob: Problem, device) -> Index:
     s = get_sizes(prob)
     i32 = dict(dtype=torch.int32, device=device)
-    return Index(
-        torch.empty(s["counts_bytes"] // 4, **i32)[: prob.num_kv_heads * s["num_blocks"]],
+    bufs = (
+        torch.empty(s["counts_bytes"] // 4, **i32),
         torch.empty(s["offsets_bytes"] // 4, **i32),
         torch.empty(s["qidx_bytes"] // 4, **i32),
-        torch.empty(s["slot_bytes"] // 4, **i32)[: prob.num_kv_heads * prob.total_tokens * prob.topk].view(
-            prob.num_kv_heads, prob.total_tokens, prob.topk
-        ),
+        torch.empty(s["slot_bytes"] // 4, **i32),
         torch.empty(s["aux_bytes"], dtype=torch.uint8, device=device),
-        s,
     )
+    counts = bufs[0][: prob.num_kv_heads * s["num_blocks"]]
+    slot = bufs[3][: prob.num_kv_heads * prob.total_tokens * prob.topk].view(
+        prob.num_kv_heads, prob.total_tokens, prob.topk)
+    return Index(counts, bufs[1], bufs[2], slot, bufs[4], s, buffers=bufs)
 
 
 def _stream(stream) -> int:

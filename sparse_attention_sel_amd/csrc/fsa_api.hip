@@ -166,9 +166,14 @@ int32_t prepare(const fsa_problem* prob, Geometry* geo) {
 
 int32_t hip_status(hipError_t e) { return e == hipSuccess ? FSA_OK : FSA_ERR_HIP; }
 
+// A per-token data buffer (Q, K, V, O, lse, Sel, scores, gradients) is
+// required unless the problem has no tokens, where it is empty and may be
+// NULL (workspaces and index buffers are never empty and stay required).
+bool data(const void* p, const Geometry& geo) { return p != nullptr || geo.N == 0; }
+
 int32_t check_main_args(const Geometry& geo, const void* q, const void* k, const void* v, const fsa_index* idx,
                         const float* lse, const void* partial, size_t partial_bytes) {
-  if (q == nullptr || k == nullptr || v == nullptr || lse == nullptr || partial == nullptr) return FSA_ERR_NULL;
+  if (!data(q, geo) || !data(k, geo) || !data(v, geo) || !data(lse, geo) || partial == nullptr) return FSA_ERR_NULL;
   int32_t st = check_index(geo, idx);
   if (st != FSA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(lse, 4) || !aligned(partial, 16))
@@ -179,7 +184,7 @@ int32_t check_main_args(const Geometry& geo, const void* q, const void* k, const
 
 int32_t check_reduce_args(const Geometry& geo, const fsa_index* idx, const void* partial, size_t partial_bytes,
                           const void* out) {
-  if (partial == nullptr || out == nullptr) return FSA_ERR_NULL;
+  if (partial == nullptr || !data(out, geo)) return FSA_ERR_NULL;
   int32_t st = check_index(geo, idx);
   if (st != FSA_OK) return st;
   if (!aligned(partial, 16) || !aligned(out, 16)) return FSA_ERR_ALIGN;
@@ -238,7 +243,7 @@ int32_t fsa_build_index(const fsa_problem* prob, const int32_t* sel, const fsa_i
   Geometry geo;
   int32_t st = prepare(prob, &geo);
   if (st != FSA_OK) return st;
-  if (sel == nullptr || ws == nullptr) return FSA_ERR_NULL;
+  if (!data(sel, geo) || ws == nullptr) return FSA_ERR_NULL;
   st = check_index(geo, idx);
   if (st != FSA_OK) return st;
   if (!aligned(sel, 4) || !aligned(ws, 256)) return FSA_ERR_ALIGN;
@@ -251,7 +256,7 @@ int32_t fsa_softmax_stats(const fsa_problem* prob, const void* q, const void* k,
   Geometry geo;
   int32_t st = prepare(prob, &geo);
   if (st != FSA_OK) return st;
-  if (q == nullptr || k == nullptr || row_max == nullptr || lse == nullptr || ws == nullptr) return FSA_ERR_NULL;
+  if (!data(q, geo) || !data(k, geo) || !data(row_max, geo) || !data(lse, geo) || ws == nullptr) return FSA_ERR_NULL;
   st = check_index(geo, idx);
   if (st != FSA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_max, 4) || !aligned(lse, 4) || !aligned(ws, 16))
@@ -304,8 +309,8 @@ int32_t fsa_selected_attn_bwd(const fsa_problem* prob, const void* q, const void
   int32_t st = prepare(prob, &geo);
   if (st != FSA_OK) return st;
   if (!geo.bwd_ok) return FSA_ERR_UNSUPPORTED;
-  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr || dout == nullptr || lse == nullptr ||
-      dq == nullptr || dk == nullptr || dv == nullptr || ws == nullptr)
+  if (!data(q, geo) || !data(k, geo) || !data(v, geo) || !data(out, geo) || !data(dout, geo) || !data(lse, geo) ||
+      !data(dq, geo) || !data(dk, geo) || !data(dv, geo) || ws == nullptr)
     return FSA_ERR_NULL;
   st = check_index(geo, idx);
   if (st != FSA_OK) return st;
@@ -322,7 +327,7 @@ int32_t fsa_select_blocks(const fsa_problem* prob, const float* scores, int64_t 
   Geometry geo;
   const int32_t st = prepare(prob, &geo);
   if (st != FSA_OK) return st;
-  if (scores == nullptr || sel == nullptr) return FSA_ERR_NULL;
+  if (!data(scores, geo) || !data(sel, geo)) return FSA_ERR_NULL;
   if (init_blocks < 0 || local_blocks < 0 || score_stride < geo.max_seq_blocks || score_stride < 1)
     return FSA_ERR_SHAPE;
   if (!aligned(scores, 4) || !aligned(sel, 4)) return FSA_ERR_ALIGN;
@@ -335,7 +340,7 @@ int32_t fsa_nsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const 
   Geometry geo;
   const int32_t st = prepare(prob, &geo);
   if (st != FSA_OK) return st;
-  if (q == nullptr || k == nullptr || v == nullptr || sel == nullptr || lse == nullptr || out == nullptr)
+  if (!data(q, geo) || !data(k, geo) || !data(v, geo) || !data(sel, geo) || !data(lse, geo) || !data(out, geo))
     return FSA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(sel, 4) ||
       !aligned(lse, 4))

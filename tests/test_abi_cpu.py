@@ -224,3 +224,25 @@ def test_python_binding_checks_tensors():
     idx = fsa.Index(*(torch.zeros(8, dtype=torch.int32) for _ in range(4)), torch.zeros(256, dtype=torch.uint8), s)
     with pytest.raises(ValueError):
         fsa.build_index(p, torch.zeros((1, 128, 4), dtype=torch.int32), idx, torch.zeros(s["build_ws_bytes"], dtype=torch.uint8))
+
+
+def test_empty_problem_accepts_null_data_pointers():
+    # N = 0: the per-token buffers may be NULL; calls that launch nothing
+    # for an empty problem succeed without a GPU (the index build launches
+    # its offsets kernel and is exercised by the GPU tests instead)
+    lib = fsa.load_library()
+    p = prob(cu=(0, 0))
+    st, s = sizes(p)
+    assert st == OK and s.total_tokens == 0 and s.max_pairs == 0
+    P, I = ctypes.byref(p), ctypes.byref(fake_index())
+    f = FAKE
+    assert lib.fsa_softmax_stats(P, None, None, I, None, None, f, s.stats_ws_bytes, None) == OK
+    assert lib.fsa_selected_attn_main(P, None, None, None, I, None, f, s.partial_ws_bytes, None) == OK
+    assert lib.fsa_selected_attn_reduce(P, I, f, s.partial_ws_bytes, None, None) == OK
+    assert lib.fsa_selected_attn_fwd(P, None, None, None, I, None, None, f, s.partial_ws_bytes, None) == OK
+    assert lib.fsa_selected_attn_bwd(P, None, None, None, None, None, None, I, None, None, None, f, s.bwd_ws_bytes,
+                                     None) == OK
+    assert lib.fsa_nsa_selected_attn_fwd(P, None, None, None, None, None, None, None) == OK
+    assert lib.fsa_select_blocks(P, None, 1, 1, 2, None, None) == OK
+    # workspaces stay required
+    assert lib.fsa_selected_attn_main(P, None, None, None, I, None, None, s.partial_ws_bytes, None) == NULL

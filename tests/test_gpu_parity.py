@@ -188,3 +188,32 @@ def test_partial_rows_sum_to_output():
     ulp = torch.clamp(out.abs(), min=2.0**-126)
     half_ulp = torch.pow(2.0, torch.floor(torch.log2(ulp)) - 8)
     assert bool(torch.all((acc - out).abs() <= half_ulp * 1.001 + 1e-30))
+
+
+def test_empty_problem_through_every_entry_point():
+    # no tokens at all: every call succeeds, writes nothing per token, and the
+    # index reports zero pairs
+    import sparse_attention_sel_amd as fsa
+
+    dev = torch.device("cuda:0")
+    H, g, d, B, T = 2, 2, 128, 64, 4
+    prob = fsa.Problem([0, 0], H, g, d, B, T, device=dev)
+    index = fsa.allocate_index(prob, dev)
+    ws = fsa.Workspaces(prob, dev, index.sizes, backward=True)
+    q = torch.empty((0, H * g, d), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((0, H, d), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    sel = torch.empty((H, 0, T), dtype=torch.int32, device=dev)
+    lse = torch.empty((0, H * g), dtype=torch.float32, device=dev)
+    row_max = torch.empty_like(lse)
+    out = torch.empty_like(q)
+    fsa.build_index(prob, sel, index, ws.build)
+    fsa.softmax_stats(prob, q, k, index, row_max, lse, ws.stats)
+    fsa.selected_attn_fwd(prob, q, k, v, index, lse, out, ws.partial)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fsa.selected_attn_bwd(prob, q, k, v, out, q, lse, index, dq, dk, dv, ws.bwd)
+    fsa.nsa_selected_attn_fwd(prob, q, k, v, sel, lse, out)
+    fsa.select_blocks(prob, torch.empty((H, 0, 1), dtype=torch.float32, device=dev), 1, 2, sel)
+    torch.cuda.synchronize()
+    assert index.num_pairs() == 0
+    assert int(index.offsets[0].item()) == 0
