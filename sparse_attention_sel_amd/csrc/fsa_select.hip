@@ -16,10 +16,12 @@
 // image of the float score << 32 | ~e), so the wanted order is the unsigned
 // integer order and no floating-point operation touches the scores (-0 is
 // folded into +0 and NaN into -inf on the bit pattern).  A lane holds the
-// keys of blocks lane, lane + 64, ..; each round takes the wave-wide maximum
-// of the lanes' current bests, emits its block, and only the lane that owned
-// it rescans for its best key below the winner.  Rows of up to 64 * kSelRegs
-// candidates keep their keys in registers; longer rows rescan from memory.
+// keys of blocks lane, lane + 64, .. and tracks its two best.  Each round
+// takes the wave-wide maximum of the lanes' bests (DPP on the score half, a
+// ballot for the owning lane, no LDS), emits its block, and the owner moves
+// to its second best; it rescans below the winner only when it wins again
+// after that.  Rows of up to 64 * kSelRegs candidates keep their keys in
+// registers; longer rows rescan from memory.
 #include "fsa_internal.h"
 
 namespace fsa {
@@ -41,13 +43,26 @@ __device__ __forceinline__ uint64_t cand_key(const float* __restrict__ row_score
   return ((uint64_t)score_order(u) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint64_t y = __shfl_xor(x, m, 64);
-    x = y > x ? y : x;
-  }
-  return x;
+// One step of a wave-wide unsigned maximum: the DPP-moved neighbour's value
+// (0, the identity, in rows outside ROW_MASK) against the lane's own; the
+// compiler folds the move into a DPP-modified v_max_u32.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_max_step(uint32_t x) {
+  const uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, false);
+  return x > y ? x : y;
+}
+
+// Maximum over the wave, returned as a scalar: quad swaps, half-row and row
+// mirrors (each 16-lane row then holds its maximum), row_bcast15 /
+// row_bcast31 carry rows 0-2 into row 3, and lane 63 is read back.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = dpp_max_step<0xB1, 0xF>(x);   // quad_perm [1, 0, 3, 2]
+  x = dpp_max_step<0x4E, 0xF>(x);   // quad_perm [2, 3, 0, 1]
+  x = dpp_max_step<0x141, 0xF>(x);  // row_half_mirror
+  x = dpp_max_step<0x140, 0xF>(x);  // row_mirror
+  x = dpp_max_step<0x142, 0xA>(x);  // row_bcast15 into rows 1, 3
+  x = dpp_max_step<0x143, 0xC>(x);  // row_bcast31 into rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 template <bool IN_REGS>
@@ -56,7 +71,10 @@ __global__ __launch_bounds__(kSelWaves * 64) void k_select(const float* __restri
                                                            int H, int BK, int T, int init_blocks, int local_blocks,
                                                            int32_t* __restrict__ sel) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kSelWaves + (threadIdx.x >> 6);
+  // wave-uniform row, held in scalar registers so the sequence lookup uses
+  // scalar loads; below 2^32 since rows < 2^31
+  const int64_t row =
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(blockIdx.x * kSelWaves + (threadIdx.x >> 6)));
   if (row >= (int64_t)H * N) return;  // wave-uniform; no barrier in this kernel
   const int t = (int)(row % N);
   const int s = seq_of_token(cu, num_seqs, t);
@@ -75,39 +93,58 @@ __global__ __launch_bounds__(kSelWaves * 64) void k_select(const float* __restri
   const int want = T - kf;
   int picked = 0;
   if (want > 0) {
+    // Each lane tracks its two best keys below `limit`; `second` is exact
+    // until the lane's best is taken twice, then the lane rescans.
     uint64_t keys[IN_REGS ? kSelRegs : 1];
-    uint64_t best = 0;
+    uint64_t best = 0, second = 0;
+    auto offer = [&](uint64_t k) {  // selects only: no branch per key
+      const uint64_t lo = k < best ? k : best;
+      second = lo > second ? lo : second;
+      best = k > best ? k : best;
+    };
     if constexpr (IN_REGS) {
 #pragma unroll
       for (int j = 0; j < kSelRegs; ++j) {
         const int e = lane + 64 * j;
         keys[j] = candidate(e) ? cand_key(rs, e) : 0;
-        best = keys[j] > best ? keys[j] : best;
+        offer(keys[j]);
       }
     } else {
       for (int e = lane; e <= own; e += 64)
-        if (candidate(e)) {
-          const uint64_t k = cand_key(rs, e);
-          best = k > best ? k : best;
-        }
+        if (candidate(e)) offer(cand_key(rs, e));
     }
+    bool second_exact = true;
     for (; picked < want; ++picked) {
-      const uint64_t win = wave_max_u64(best);
-      if (win == 0) break;  // no candidate left (wave-uniform)
-      if (lane == 0) out[kf + picked] = (int32_t)(0xFFFFFFFFu - (uint32_t)win);
+      // the wave's largest key: maximum of the score halves, then among the
+      // lanes holding that score (nearly always one) the largest index half
+      const uint32_t best_hi = (uint32_t)(best >> 32);
+      const uint32_t win_hi = wave_max_u32(best_hi);
+      if (win_hi == 0) break;  // no candidate left (wave-uniform)
+      const uint64_t tied = __ballot(best_hi == win_hi);
+      const uint32_t win_lo = __popcll(tied) == 1
+                                  ? (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)best, __ffsll((long long)tied) - 1)
+                                  : wave_max_u32(best_hi == win_hi ? (uint32_t)best : 0u);
+      const uint64_t win = ((uint64_t)win_hi << 32) | win_lo;
+      if (lane == 0) out[kf + picked] = (int32_t)(0xFFFFFFFFu - win_lo);
       if (best == win) {  // keys are unique: exactly one lane owned the winner
-        uint64_t nb = 0;
-        if constexpr (IN_REGS) {
-#pragma unroll
-          for (int j = 0; j < kSelRegs; ++j) nb = (keys[j] < win && keys[j] > nb) ? keys[j] : nb;
+        if (second_exact) {
+          best = second;
+          second = 0;
+          second_exact = false;
         } else {
-          for (int e = lane; e <= own; e += 64)
-            if (candidate(e)) {
-              const uint64_t k = cand_key(rs, e);
-              nb = (k < win && k > nb) ? k : nb;
-            }
+          best = second = 0;
+          if constexpr (IN_REGS) {
+#pragma unroll
+            for (int j = 0; j < kSelRegs; ++j) offer(keys[j] < win ? keys[j] : 0);
+          } else {
+            for (int e = lane; e <= own; e += 64)
+              if (candidate(e)) {
+                const uint64_t k = cand_key(rs, e);
+                offer(k < win ? k : 0);
+              }
+          }
+          second_exact = true;
         }
-        best = nb;
       }
     }
   }
