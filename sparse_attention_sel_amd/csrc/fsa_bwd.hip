@@ -4,17 +4,20 @@
 // Usage and Evaluation sections train the module and check its gradients).
 //
 //   k_bwd_delta      D[t, hq] = sum_d dO * O  (fp32).
-//   k_bwd_main       per work item (KV head, block, query chunk): K, V and
-//                    K^T of the 64-key block are staged in LDS once; the
-//                    item's query rows stream through in 16-row tiles.  Wave
-//                    w owns keys 16w .. 16w+15: it forms S = Q K^T and
-//                    dP = dO V^T for its keys, P = exp(S - lse), dS = P (dP -
-//                    D), and accumulates dV^T += dO^T P and dK^T += Q^T dS in
-//                    registers over the chunk.  dS of all 64 keys meets in
-//                    LDS and dQ^T = K^T dS^T (split over d across the waves) is
-//                    written to the compact partial rows of the forward.  At
-//                    the end of the item the block's dK / dV partial goes to
-//                    the item's slot offsets[f] / CT + f + chunk.
+//   k_bwd_main       per work item (KV head, block, query chunk): each lane
+//                    keeps the K and V fragments of its key and the K^T
+//                    fragments of its dQ d tiles in registers for the whole
+//                    item; the item's query rows stream through in 16-row
+//                    tiles staged row-major in LDS.  Wave w owns keys
+//                    16w .. 16w+15: it forms S = Q K^T and dP = dO V^T for its
+//                    keys, P = exp(S - lse), dS = P (dP - D), and accumulates
+//                    dV^T += dO^T P and dK^T += Q^T dS in registers over the
+//                    chunk, reading dO^T and Q^T with LDS transpose reads.
+//                    dS of all 64 keys meets in LDS and dQ^T = K^T dS^T
+//                    (split over d across the waves) is written to the
+//                    compact partial rows of the forward.  At the end of the
+//                    item the block's dK / dV partial goes to the item's slot
+//                    offsets[f] / CT + f + chunk.
 //   k_reduce         (the forward's reduction) sums each (token, KV head)'s dQ
 //                    partial rows in slot order.
 //   k_bwd_kv_reduce  per key row of every block: dK, dV = sum over the
@@ -37,6 +40,7 @@ namespace {
 
 constexpr float kBwdLog2e = 1.4426950408889634f;
 constexpr int kBwdThreads = 256;  // 4 waves x 16 keys = the 64-key block
+constexpr int kBwdWaves = kBwdThreads / 64;
 constexpr int kBwdBK = 64;
 constexpr int kBwdRows = 16;  // query rows per tile
 constexpr int kBwdRowTable = kRowsPerItem + kBwdRows;
@@ -78,17 +82,27 @@ template <typename T>
 __device__ __forceinline__ typename Vec4<T>::type bld4(const T* p) {
   return *reinterpret_cast<const typename Vec4<T>::type*>(p);
 }
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte chunks addressed by lanes i / 4, i / 4 + 4, i / 4 + 8
+// and i / 4 + 12 of the group.  When lane n of group u addresses row
+// 4u + n / 4, columns c0 + 4 (n % 4) .. +3 of a row-major tile, lane i gets
+// rows 4u .. 4u + 3 of column c0 + i: the A operand of a 16x16x16 MFMA that
+// contracts over the rows of the transposed tile.
+template <typename T>
+__device__ __forceinline__ typename Vec4<T>::type read_tr4(const T* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(typename Vec4<T>::type, r);
+}
 template <typename T>
 __device__ __forceinline__ uint32_t bbits(T x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x);
 }
 
-// LDS pitches (elements).  K, V: [64][D + 8]; K^T: [D][64 + 8]; Q, dO tiles:
-// [16][D + 8]; their transposes: [D][16 + 4]; dS: [16][64 + 8].
+// LDS pitches (elements).  K: [64][D + 8]; Q, dO tiles: [16][D + 8]; dS:
+// [16][64 + 8].
 template <int D>
 constexpr int b_kld() { return D + 8; }
-constexpr int kKtLd = kBwdBK + 8;
-constexpr int kTLd = kBwdRows + 4;
 constexpr int kSLd = kBwdBK + 8;
 
 // ---- D = rowsum(dO * O) -------------------------------------------------------
@@ -113,82 +127,20 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ out, co
 }
 
 // ---- main ---------------------------------------------------------------------
-// One item's staging data held in registers while the previous item computes:
-// K as key pairs (row-major copy and packed transposed copy), V row-major, the
-// query tokens of the item's row table, and the raw work entry.
-template <typename T, int D>
-struct BwdStage {
-  using V8 = typename Vec8<T>::type;
-  static constexpr int C8 = D / 8;
-  static constexpr int KP = (kBwdBK / 2) * C8 / kBwdThreads;  // K key-pair vectors per thread
-  static constexpr int VV = kBwdBK * C8 / kBwdThreads;        // V vectors per thread
-  static constexpr int RT = (kBwdRowTable + kBwdThreads - 1) / kBwdThreads;
-  static_assert((kBwdBK / 2) * C8 % kBwdThreads == 0 && kBwdBK * C8 % kBwdThreads == 0, "whole vectors");
-  int4 w;
-  Item it;
-  V8 ka[KP], kb[KP], vv[VV];
-  int tok[RT];
-
-  __device__ __forceinline__ void load(const T* __restrict__ k, const T* __restrict__ v,
-                                       const int32_t* __restrict__ qidx, const int4* __restrict__ work,
-                                       const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-                                       int wi, int H, int g, int NB, int CT) {
-    w = work[wi];
-    it = read_item(work, counts, offsets, wi, NB, CT, kBwdBK);
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      const int vi = threadIdx.x + i * kBwdThreads;
-      const int c = vi / (kBwdBK / 2), key = 2 * (vi % (kBwdBK / 2));
-      ka[i] = bld8(k + ((size_t)(it.bs + min(key, it.nkeys - 1)) * H + it.h) * D + c * 8);
-      kb[i] = bld8(k + ((size_t)(it.bs + min(key + 1, it.nkeys - 1)) * H + it.h) * D + c * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < VV; ++i) {
-      const int vi = threadIdx.x + i * kBwdThreads;
-      vv[i] = bld8(v + ((size_t)(it.bs + min(vi / C8, it.nkeys - 1)) * H + it.h) * D + (vi % C8) * 8);
-    }
-#pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const int r = threadIdx.x + i * kBwdThreads;
-      tok[i] = qidx[it.pair0 + min(r / g, it.ntok - 1)];
-    }
-  }
-
-  __device__ __forceinline__ void commit(T* __restrict__ Ks, T* __restrict__ Vs, T* __restrict__ Kt,
-                                         int* __restrict__ rtok, int g) const {
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
-      const int vi = threadIdx.x + i * kBwdThreads;
-      const int c = vi / (kBwdBK / 2), key = 2 * (vi % (kBwdBK / 2));
-      *reinterpret_cast<V8*>(Ks + key * b_kld<D>() + c * 8) = ka[i];
-      *reinterpret_cast<V8*>(Ks + (key + 1) * b_kld<D>() + c * 8) = kb[i];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint32_t*>(Kt + (c * 8 + e) * kKtLd + key) = bbits(ka[i][e]) | (bbits(kb[i][e]) << 16);
-    }
-#pragma unroll
-    for (int i = 0; i < VV; ++i) {
-      const int vi = threadIdx.x + i * kBwdThreads;
-      *reinterpret_cast<V8*>(Vs + (vi / C8) * b_kld<D>() + (vi % C8) * 8) = vv[i];
-    }
-    const int nrows = it.ntok * g;
-#pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const int r = threadIdx.x + i * kBwdThreads;
-      if (r < kBwdRowTable) rtok[r] = r < nrows ? tok[i] : -1;
-    }
-  }
-};
-
 // One 16-row tile's gather data in registers: this thread's Q / dO vectors
-// (zero for rows past the chunk) and, for threads < 16, its row's lse (base 2)
-// and D.
+// (zero for rows past the chunk) and, for threads < 16, its row's lse and D.
+// Every load is unconditional (rows past the chunk read row 0) and nothing
+// consumes a loaded value before put(), so the loads stay in flight while
+// the previous tile computes; the row mask and the base-2 scaling of lse are
+// applied in put().
 template <typename T, int D>
 struct BwdTile {
   using V8 = typename Vec8<T>::type;
   static constexpr int NV = 4 * D / kBwdThreads;  // 16 rows x D/8 chunks x 2 tensors over the threads
   V8 x[NV];
-  float l2, dd;
+  bool ok[NV];  // the vector's row is a row of the chunk
+  float lraw, draw;
+  bool live;
 
   __device__ __forceinline__ void load(const T* __restrict__ q, const T* __restrict__ dout,
                                        const float* __restrict__ lse, const float* __restrict__ delta,
@@ -201,38 +153,30 @@ struct BwdTile {
       const int r = tile * kBwdRows + row;
       const int t = rtok[r];
       const size_t qrow = t >= 0 ? (size_t)t * HQ + h * g + r % g : 0;
-      const V8 val = bld8((tensor == 0 ? q : dout) + qrow * D + c * 8);
-      x[i] = t >= 0 ? val : V8{};
+      x[i] = bld8((tensor == 0 ? q : dout) + qrow * D + c * 8);
+      ok[i] = t >= 0;
     }
-    l2 = 0.f;
-    dd = 0.f;
-    if (threadIdx.x < kBwdRows) {
-      const int r = tile * kBwdRows + threadIdx.x;
-      const int t = rtok[r];
-      if (t >= 0) {
-        const size_t qrow = (size_t)t * HQ + h * g + r % g;
-        l2 = lse[qrow] * kBwdLog2e;
-        dd = delta[qrow];
-      }
-    }
+    // threads >= 16 load row 0's values too (unused): no branch around the loads
+    const int r = tile * kBwdRows + (threadIdx.x & (kBwdRows - 1));
+    const int t = rtok[r];
+    live = t >= 0;
+    const size_t qrow = live ? (size_t)t * HQ + h * g + r % g : 0;
+    lraw = lse[qrow];
+    draw = delta[qrow];
   }
 
-  __device__ __forceinline__ void put(T* __restrict__ Qs, T* __restrict__ Ds, T* __restrict__ Qt,
-                                      T* __restrict__ Dt, float* __restrict__ tab_l, float* __restrict__ tab_d) const {
+  __device__ __forceinline__ void put(T* __restrict__ Qs, T* __restrict__ Ds, float* __restrict__ tab_l,
+                                      float* __restrict__ tab_d) const {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int vi = threadIdx.x + i * kBwdThreads;
       const int tensor = vi / (2 * D), e = vi % (2 * D);
       const int row = e / (D / 8), c = e % (D / 8);
-      T* rm = tensor == 0 ? Qs : Ds;
-      T* tr = tensor == 0 ? Qt : Dt;
-      *reinterpret_cast<V8*>(rm + row * b_kld<D>() + c * 8) = x[i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) tr[(c * 8 + j) * kTLd + row] = x[i][j];
+      *reinterpret_cast<V8*>((tensor == 0 ? Qs : Ds) + row * b_kld<D>() + c * 8) = ok[i] ? x[i] : V8{};
     }
     if (threadIdx.x < kBwdRows) {
-      tab_l[threadIdx.x] = l2;
-      tab_d[threadIdx.x] = dd;
+      tab_l[threadIdx.x] = live ? lraw * kBwdLog2e : 0.f;
+      tab_d[threadIdx.x] = live ? draw : 0.f;
     }
   }
 };
@@ -244,47 +188,88 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_main(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
     const int32_t* __restrict__ nwork, PT* __restrict__ dq_part, float* __restrict__ kv_part, int H, int g, int NB,
     int CT, float scale, float scale_log2) {
+  using V8 = typename Vec8<T>::type;
   using V4 = typename Vec4<T>::type;
-  constexpr int KS = D / 32;  // 32-wide contraction steps over d
-  constexpr int MT = D / 16;  // 16-wide d tiles
+  constexpr int KS = D / 32;           // 32-wide contraction steps over d
+  constexpr int MT = D / 16;           // 16-wide d tiles
+  constexpr int MW = MT / kBwdWaves;   // d tiles of dQ per wave
+  constexpr int C8 = D / 8;
+  constexpr int KV = kBwdBK * C8 / kBwdThreads;  // K vectors staged per thread
+  constexpr int RT = (kBwdRowTable + kBwdThreads - 1) / kBwdThreads;
+  static_assert(MT % kBwdWaves == 0 && kBwdBK * C8 % kBwdThreads == 0, "whole tiles");
   __shared__ __attribute__((aligned(16))) T Ks[kBwdBK * b_kld<D>()];
-  __shared__ __attribute__((aligned(16))) T Vs[kBwdBK * b_kld<D>()];
-  __shared__ __attribute__((aligned(16))) T Kt[D * kKtLd];
   __shared__ __attribute__((aligned(16))) T Qs[kBwdRows * b_kld<D>()];
   __shared__ __attribute__((aligned(16))) T Ds[kBwdRows * b_kld<D>()];
-  __shared__ __attribute__((aligned(16))) T Qt[D * kTLd];
-  __shared__ __attribute__((aligned(16))) T Dt[D * kTLd];
   __shared__ __attribute__((aligned(16))) T Ss[kBwdRows * kSLd];
   __shared__ __attribute__((aligned(16))) int rtok[kBwdRowTable];
   __shared__ __attribute__((aligned(16))) float tab_l[kBwdRows];
   __shared__ __attribute__((aligned(16))) float tab_d[kBwdRows];
 
   ItemCursor cur(nwork[0]);
-  if (cur.current() < 0) return;
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kl = lane & 15, u = lane >> 4;
   const int key = wave * 16 + kl;  // this lane's key within the block (S, dP, dK, dV)
-  BwdStage<T, D> pre;
-  pre.load(k, v, qidx, work, counts, offsets, cur.current(), H, g, NB, CT);
+  // transposed-read address of this lane in a [16][D + 8] tile (see read_tr4)
+  const int tr_off = (4 * u + (kl >> 2)) * b_kld<D>() + 4 * (kl & 3);
   for (; cur.current() >= 0; cur.advance()) {
-    __syncthreads();  // the previous item's LDS reads are done
-    pre.commit(Ks, Vs, Kt, rtok, g);
-    const Item it = pre.it;
-    const int4 wraw = pre.w;
-    __syncthreads();
+    const int wi = cur.current();
+    const int4 wraw = work[wi];
+    const Item it = read_item(work, counts, offsets, wi, NB, CT, kBwdBK);
     const int nrows = it.ntok * g, ntile = (nrows + kBwdRows - 1) / kBwdRows;
+    // Item operands that stay in registers for all of its tiles: the B
+    // fragments of this lane's key for S = Q K^T and dP = dO V^T (16-byte
+    // loads straight from K / V; keys past a partial last block repeat the
+    // last key and are masked), and below, the K^T fragments of dQ.
+    const size_t krow = ((size_t)(it.bs + min(key, it.nkeys - 1)) * H + it.h) * D;
+    V8 kb[KS], vb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      kb[ks] = bld8(k + krow + 32 * ks + 8 * u);
+      vb[ks] = bld8(v + krow + 32 * ks + 8 * u);
+    }
+    V8 kst[KV];
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int vi = threadIdx.x + i * kBwdThreads;
+      kst[i] = bld8(k + ((size_t)(it.bs + min(vi / C8, it.nkeys - 1)) * H + it.h) * D + (vi % C8) * 8);
+    }
+    int tk[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int r = threadIdx.x + i * kBwdThreads;
+      tk[i] = qidx[it.pair0 + min(r / g, it.ntok - 1)];
+    }
+    __syncthreads();  // every wave is done with the previous item's K and row table
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int vi = threadIdx.x + i * kBwdThreads;
+      *reinterpret_cast<V8*>(Ks + (vi / C8) * b_kld<D>() + (vi % C8) * 8) = kst[i];
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int r = threadIdx.x + i * kBwdThreads;
+      if (r < kBwdRowTable) rtok[r] = r < nrows ? tk[i] : -1;
+    }
+    __syncthreads();
+    // K^T fragments of dQ^T = K^T dS^T: lane (kl, u) of d tile mt holds
+    // K[32 ks + 8u + e][16 mt + kl], e < 8.
+    V8 kt[MW][2];
+#pragma unroll
+    for (int m = 0; m < MW; ++m)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kt[m][ks][e] = Ks[(32 * ks + 8 * u + e) * b_kld<D>() + 16 * (wave + kBwdWaves * m) + kl];
+
     BwdTile<T, D> tl;
     tl.load(q, dout, lse, delta, rtok, 0, it.h, g, HQ);
-    const int wn = cur.next();
-    if (wn >= 0) pre.load(k, v, qidx, work, counts, offsets, wn, H, g, NB, CT);
-
     f32x4 dk[MT], dv[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) dk[mt] = dv[mt] = f32x4{};
 
     for (int tile = 0; tile < ntile; ++tile) {
-      tl.put(Qs, Ds, Qt, Dt, tab_l, tab_d);
+      tl.put(Qs, Ds, tab_l, tab_d);
       __syncthreads();  // tile in LDS; every wave is past the previous tile's dQ
       if (tile + 1 < ntile) tl.load(q, dout, lse, delta, rtok, tile + 1, it.h, g, HQ);
 
@@ -292,13 +277,13 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_main(
       f32x4 s = {}, dp = {};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s = mfma_k32(bld8(Qs + kl * b_kld<D>() + 32 * ks + 8 * u), bld8(Ks + key * b_kld<D>() + 32 * ks + 8 * u), s);
-        dp = mfma_k32(bld8(Ds + kl * b_kld<D>() + 32 * ks + 8 * u), bld8(Vs + key * b_kld<D>() + 32 * ks + 8 * u), dp);
+        s = mfma_k32(bld8(Qs + kl * b_kld<D>() + 32 * ks + 8 * u), kb[ks], s);
+        dp = mfma_k32(bld8(Ds + kl * b_kld<D>() + 32 * ks + 8 * u), vb[ks], dp);
       }
-      const int4 tk = *reinterpret_cast<const int4*>(rtok + tile * kBwdRows + 4 * u);
+      const int4 tq = *reinterpret_cast<const int4*>(rtok + tile * kBwdRows + 4 * u);
       const f32x4 l2 = *reinterpret_cast<const f32x4*>(tab_l + 4 * u);
       const f32x4 dd = *reinterpret_cast<const f32x4*>(tab_d + 4 * u);
-      const int tks[4] = {tk.x, tk.y, tk.z, tk.w};
+      const int tks[4] = {tq.x, tq.y, tq.z, tq.w};
       f32x4 p, ds;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -309,11 +294,12 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_main(
       }
       const V4 p4 = __builtin_convertvector(p, V4);
       const V4 ds4 = __builtin_convertvector(ds, V4);
-      // dV^T += dO^T P and dK^T += Q^T dS (contraction over the tile's 16 rows)
+      // dV^T += dO^T P and dK^T += Q^T dS (contraction over the tile's 16
+      // rows); the A operands come transposed out of the row-major tiles.
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        dv[mt] = mfma_k16(bld4(Dt + (16 * mt + kl) * kTLd + 4 * u), p4, dv[mt]);
-        dk[mt] = mfma_k16(bld4(Qt + (16 * mt + kl) * kTLd + 4 * u), ds4, dk[mt]);
+        dv[mt] = mfma_k16(read_tr4(Ds + tr_off + 16 * mt), p4, dv[mt]);
+        dk[mt] = mfma_k16(read_tr4(Qs + tr_off + 16 * mt), ds4, dk[mt]);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) Ss[(4 * u + r) * kSLd + key] = ds4[r];
@@ -322,18 +308,18 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_main(
       // dQ^T = K^T dS^T for the d tiles of this wave; lane: row kl, d = 16mt + 4u + r.
       const int row = tile * kBwdRows + kl;
       PT* const dst = dq_part + ((size_t)it.pair0 * g + row) * D + 4 * u;
-      for (int mt = wave; mt < MT; mt += kBwdThreads / 64) {
+#pragma unroll
+      for (int m = 0; m < MW; ++m) {
         f32x4 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < kBwdBK / 32; ++ks)
-          acc = mfma_k32(bld8(Kt + (16 * mt + kl) * kKtLd + 32 * ks + 8 * u), bld8(Ss + kl * kSLd + 32 * ks + 8 * u),
-                         acc);
+        for (int ks = 0; ks < 2; ++ks) acc = mfma_k32(kt[m][ks], bld8(Ss + kl * kSLd + 32 * ks + 8 * u), acc);
         if (row < nrows) {
+          PT* const o = dst + 16 * (wave + kBwdWaves * m);
           if constexpr (sizeof(PT) == 4) {
-            *reinterpret_cast<f32x4*>(dst + 16 * mt) = acc * scale;
+            *reinterpret_cast<f32x4*>(o) = acc * scale;
           } else {
             typedef PT P4 __attribute__((ext_vector_type(4)));
-            *reinterpret_cast<P4*>(dst + 16 * mt) = __builtin_convertvector(acc * scale, P4);
+            *reinterpret_cast<P4*>(o) = __builtin_convertvector(acc * scale, P4);
           }
         }
       }
