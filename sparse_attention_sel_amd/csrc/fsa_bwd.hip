@@ -7,7 +7,7 @@
 //   k_bwd_main       per work item (KV head, block, query chunk): each lane
 //                    keeps the K and V fragments of its key and the K^T
 //                    fragments of its dQ d tiles in registers for the whole
-//                    item; the item's query rows stream through in 16-row
+//                    item; the item's query rows stream through in 32-row
 //                    tiles staged row-major in LDS.  Wave w owns keys
 //                    16w .. 16w+15: it forms S = Q K^T and dP = dO V^T for its
 //                    keys, P = exp(S - lse), dS = P (dP - D), and accumulates
@@ -26,11 +26,12 @@
 //
 // MFMA layouts (wave64, l = lane, u = l / 16).  v_mfma_f32_16x16x32: lane l
 // supplies A[l % 16][8u + e] and B[8u + e][l % 16] (e < 8) and receives
-// C[4u + r][l % 16] (r < 4).  v_mfma_f32_16x16x16: A[l % 16][4u + e],
-// B[4u + e][l % 16] (e < 4), same C.  S = Q K^T (rows x keys) therefore leaves
-// lane l with key l % 16 and rows 4u + r, which is exactly the B operand of a
-// 16x16x16 product that contracts over the rows: dV^T = dO^T P and
-// dK^T = Q^T dS need no transpose of P or dS.
+// C[4u + r][l % 16] (r < 4).  S = Q K^T over a 16-row block therefore leaves
+// lane l with key l % 16 and rows 4u + r.  For dV^T = dO^T P and
+// dK^T = Q^T dS, which contract over a 32-row tile, the lane's k range 8u + e
+// is taken to mean row 4u + e of the first 16-row block (e < 4) and row
+// 4u + e - 4 of the second: the lane's own P / dS values of both blocks form
+// the B operand as they are, with no transpose.
 #include <math.h>
 
 #include "fsa_internal.h"
@@ -42,7 +43,7 @@ constexpr float kBwdLog2e = 1.4426950408889634f;
 constexpr int kBwdThreads = 256;  // 4 waves x 16 keys = the 64-key block
 constexpr int kBwdWaves = kBwdThreads / 64;
 constexpr int kBwdBK = 64;
-constexpr int kBwdRows = 16;  // query rows per tile
+constexpr int kBwdRows = 32;  // query rows per tile: two 16-row MFMA blocks
 constexpr int kBwdRowTable = kRowsPerItem + kBwdRows;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -94,13 +95,17 @@ __device__ __forceinline__ typename Vec4<T>::type read_tr4(const T* p) {
   const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(typename Vec4<T>::type, r);
 }
+template <typename V4>
+__device__ __forceinline__ auto cat8(V4 a, V4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 template <typename T>
 __device__ __forceinline__ uint32_t bbits(T x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x);
 }
 
-// LDS pitches (elements).  K: [64][D + 8]; Q, dO tiles: [16][D + 8]; dS:
-// [16][64 + 8].
+// LDS pitches (elements).  K: [64][D + 8]; Q, dO tiles: [32][D + 8]; dS:
+// [32][64 + 8].
 template <int D>
 constexpr int b_kld() { return D + 8; }
 constexpr int kSLd = kBwdBK + 8;
@@ -127,8 +132,9 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ out, co
 }
 
 // ---- main ---------------------------------------------------------------------
-// One 16-row tile's gather data in registers: this thread's Q / dO vectors
-// (zero for rows past the chunk) and, for threads < 16, its row's lse and D.
+// One row tile's gather data in registers: this thread's Q / dO vectors
+// (zero for rows past the chunk) and, for threads < kBwdRows, its row's lse
+// and D.
 // Every load is unconditional (rows past the chunk read row 0) and nothing
 // consumes a loaded value before put(), so the loads stay in flight while
 // the previous tile computes; the row mask and the base-2 scaling of lse are
@@ -136,7 +142,9 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ out, co
 template <typename T, int D>
 struct BwdTile {
   using V8 = typename Vec8<T>::type;
-  static constexpr int NV = 4 * D / kBwdThreads;  // 16 rows x D/8 chunks x 2 tensors over the threads
+  static constexpr int PER = kBwdRows * D / 8;               // vectors of one tensor's tile
+  static constexpr int NV = 2 * PER / kBwdThreads;           // Q and dO tiles over the threads
+  static_assert(2 * PER % kBwdThreads == 0 && PER % kBwdThreads == 0, "whole vectors, one tensor per vector slot");
   V8 x[NV];
   bool ok[NV];  // the vector's row is a row of the chunk
   float lraw, draw;
@@ -148,7 +156,7 @@ struct BwdTile {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int vi = threadIdx.x + i * kBwdThreads;
-      const int tensor = vi / (2 * D), e = vi % (2 * D);
+      const int tensor = vi / PER, e = vi % PER;
       const int row = e / (D / 8), c = e % (D / 8);
       const int r = tile * kBwdRows + row;
       const int t = rtok[r];
@@ -170,7 +178,7 @@ struct BwdTile {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int vi = threadIdx.x + i * kBwdThreads;
-      const int tensor = vi / (2 * D), e = vi % (2 * D);
+      const int tensor = vi / PER, e = vi % PER;
       const int row = e / (D / 8), c = e % (D / 8);
       *reinterpret_cast<V8*>((tensor == 0 ? Qs : Ds) + row * b_kld<D>() + c * 8) = ok[i] ? x[i] : V8{};
     }
@@ -182,7 +190,7 @@ struct BwdTile {
 };
 
 template <typename T, int D, typename PT>
-__global__ __launch_bounds__(kBwdThreads) void k_bwd_main(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_main(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_main(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kl = lane & 15, u = lane >> 4;
   const int key = wave * 16 + kl;  // this lane's key within the block (S, dP, dK, dV)
-  // transposed-read address of this lane in a [16][D + 8] tile (see read_tr4)
+  // transposed-read address of this lane in a 16-row block of a tile (see read_tr4)
   const int tr_off = (4 * u + (kl >> 2)) * b_kld<D>() + 4 * (kl & 3);
   for (; cur.current() >= 0; cur.advance()) {
     const int wi = cur.current();
@@ -273,53 +281,70 @@ __global__ __launch_bounds__(kBwdThreads) void k_bwd_main(
       __syncthreads();  // tile in LDS; every wave is past the previous tile's dQ
       if (tile + 1 < ntile) tl.load(q, dout, lse, delta, rtok, tile + 1, it.h, g, HQ);
 
-      // S = Q K^T and dP = dO V^T for rows 4u + r and this lane's key.
-      f32x4 s = {}, dp = {};
+      // S = Q K^T and dP = dO V^T for rows 16 rb + 4u + r and this lane's key.
+      f32x4 s[2] = {}, dp[2] = {};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        s = mfma_k32(bld8(Qs + kl * b_kld<D>() + 32 * ks + 8 * u), kb[ks], s);
-        dp = mfma_k32(bld8(Ds + kl * b_kld<D>() + 32 * ks + 8 * u), vb[ks], dp);
-      }
-      const int4 tq = *reinterpret_cast<const int4*>(rtok + tile * kBwdRows + 4 * u);
-      const f32x4 l2 = *reinterpret_cast<const f32x4*>(tab_l + 4 * u);
-      const f32x4 dd = *reinterpret_cast<const f32x4*>(tab_d + 4 * u);
-      const int tks[4] = {tq.x, tq.y, tq.z, tq.w};
-      f32x4 p, ds;
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // key visible iff it is in the row's causal past (rows past the chunk: token -1)
-        const bool vis = tks[r] >= 0 && key <= tks[r] - it.bs;
-        p[r] = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -l2[r])) : 0.f;
-        ds[r] = p[r] * (dp[r] - dd[r]);
+        for (int ks = 0; ks < KS; ++ks) {
+          s[rb] = mfma_k32(bld8(Qs + (16 * rb + kl) * b_kld<D>() + 32 * ks + 8 * u), kb[ks], s[rb]);
+          dp[rb] = mfma_k32(bld8(Ds + (16 * rb + kl) * b_kld<D>() + 32 * ks + 8 * u), vb[ks], dp[rb]);
+        }
+      V4 p4[2], ds4[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int4 tq = *reinterpret_cast<const int4*>(rtok + tile * kBwdRows + 16 * rb + 4 * u);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(tab_l + 16 * rb + 4 * u);
+        const f32x4 dd = *reinterpret_cast<const f32x4*>(tab_d + 16 * rb + 4 * u);
+        const int tks[4] = {tq.x, tq.y, tq.z, tq.w};
+        f32x4 p, ds;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // key visible iff it is in the row's causal past (rows past the chunk: token -1)
+          const bool vis = tks[r] >= 0 && key <= tks[r] - it.bs;
+          p[r] = vis ? __builtin_amdgcn_exp2f(fmaf(s[rb][r], scale_log2, -l2[r])) : 0.f;
+          ds[r] = p[r] * (dp[rb][r] - dd[r]);
+        }
+        p4[rb] = __builtin_convertvector(p, V4);
+        ds4[rb] = __builtin_convertvector(ds, V4);
       }
-      const V4 p4 = __builtin_convertvector(p, V4);
-      const V4 ds4 = __builtin_convertvector(ds, V4);
-      // dV^T += dO^T P and dK^T += Q^T dS (contraction over the tile's 16
-      // rows); the A operands come transposed out of the row-major tiles.
+      // dV^T += dO^T P and dK^T += Q^T dS, contracting over the tile's 32
+      // rows: element e of a lane's k range is row 4u + e of block 0 (e < 4)
+      // or of block 1 (e >= 4), for the transposed reads and P / dS alike.
+      const V8 pb = cat8(p4[0], p4[1]), dsb = cat8(ds4[0], ds4[1]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        dv[mt] = mfma_k16(read_tr4(Ds + tr_off + 16 * mt), p4, dv[mt]);
-        dk[mt] = mfma_k16(read_tr4(Qs + tr_off + 16 * mt), ds4, dk[mt]);
+        const V8 a_do = cat8(read_tr4(Ds + tr_off + 16 * mt), read_tr4(Ds + 16 * b_kld<D>() + tr_off + 16 * mt));
+        const V8 a_q = cat8(read_tr4(Qs + tr_off + 16 * mt), read_tr4(Qs + 16 * b_kld<D>() + tr_off + 16 * mt));
+        dv[mt] = mfma_k32(a_do, pb, dv[mt]);
+        dk[mt] = mfma_k32(a_q, dsb, dk[mt]);
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Ss[(4 * u + r) * kSLd + key] = ds4[r];
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ss[(16 * rb + 4 * u + r) * kSLd + key] = ds4[rb][r];
       __syncthreads();  // dS of all 64 keys in LDS
 
-      // dQ^T = K^T dS^T for the d tiles of this wave; lane: row kl, d = 16mt + 4u + r.
-      const int row = tile * kBwdRows + kl;
-      PT* const dst = dq_part + ((size_t)it.pair0 * g + row) * D + 4 * u;
+      // dQ^T = K^T dS^T for the d tiles of this wave; lane: row 16 rb + kl,
+      // d = 16mt + 4u + r.
 #pragma unroll
-      for (int m = 0; m < MW; ++m) {
-        f32x4 acc = {};
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row = tile * kBwdRows + 16 * rb + kl;
+        PT* const dst = dq_part + ((size_t)it.pair0 * g + row) * D + 4 * u;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) acc = mfma_k32(kt[m][ks], bld8(Ss + kl * kSLd + 32 * ks + 8 * u), acc);
-        if (row < nrows) {
-          PT* const o = dst + 16 * (wave + kBwdWaves * m);
-          if constexpr (sizeof(PT) == 4) {
-            *reinterpret_cast<f32x4*>(o) = acc * scale;
-          } else {
-            typedef PT P4 __attribute__((ext_vector_type(4)));
-            *reinterpret_cast<P4*>(o) = __builtin_convertvector(acc * scale, P4);
+        for (int m = 0; m < MW; ++m) {
+          f32x4 acc = {};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            acc = mfma_k32(kt[m][ks], bld8(Ss + (16 * rb + kl) * kSLd + 32 * ks + 8 * u), acc);
+          if (row < nrows) {
+            PT* const o = dst + 16 * (wave + kBwdWaves * m);
+            if constexpr (sizeof(PT) == 4) {
+              *reinterpret_cast<f32x4*>(o) = acc * scale;
+            } else {
+              typedef PT P4 __attribute__((ext_vector_type(4)));
+              *reinterpret_cast<P4*>(o) = __builtin_convertvector(acc * scale, P4);
+            }
           }
         }
       }
