@@ -14,8 +14,9 @@
 //                    dV^T += dO^T P and dK^T += Q^T dS in registers over the
 //                    chunk, reading dO^T and Q^T with LDS transpose reads.
 //                    dS of all 64 keys meets in LDS and dQ^T = K^T dS^T
-//                    (split over d across the waves) is written to the
-//                    compact partial rows of the forward.  At the end of the
+//                    (split over d across the waves) is staged in LDS and
+//                    written as whole rows to the compact partial rows of
+//                    the forward.  At the end of the
 //                    item the block's dK / dV partial goes to the item's slot
 //                    offsets[f] / CT + f + chunk.
 //   k_reduce         (the forward's reduction) sums each (token, KV head)'s dQ
@@ -47,6 +48,7 @@ constexpr int kBwdRows = 32;  // query rows per tile: two 16-row MFMA blocks
 constexpr int kBwdRowTable = kRowsPerItem + kBwdRows;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
@@ -209,6 +211,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
   __shared__ __attribute__((aligned(16))) T Qs[kBwdRows * b_kld<D>()];
   __shared__ __attribute__((aligned(16))) T Ds[kBwdRows * b_kld<D>()];
   __shared__ __attribute__((aligned(16))) T Ss[kBwdRows * kSLd];
+  constexpr int QOLD = D + 16 / (int)sizeof(PT);  // dQ stage pitch (elements): rows 16 bytes apart in banks
+  __shared__ __attribute__((aligned(16))) PT Qo[kBwdRows * QOLD];
   __shared__ __attribute__((aligned(16))) int rtok[kBwdRowTable];
   __shared__ __attribute__((aligned(16))) float tab_l[kBwdRows];
   __shared__ __attribute__((aligned(16))) float tab_d[kBwdRows];
@@ -218,6 +222,21 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kl = lane & 15, u = lane >> 4;
   const int key = wave * 16 + kl;  // this lane's key within the block (S, dP, dK, dV)
+  // Writes the staged dQ rows of tile `tl` of the current item as whole rows
+  // (consecutive threads, consecutive 16-byte pieces; non-temporal).
+  auto flush_dq = [&](int tl, int pair0, int nrows) {
+    constexpr int CPR = D * (int)sizeof(PT) / 16;  // 16-byte pieces per row
+    constexpr int EPC = 16 / (int)sizeof(PT);      // elements per piece
+#pragma unroll
+    for (int j = 0; j < kBwdRows * CPR / kBwdThreads; ++j) {
+      const int pc = threadIdx.x + j * kBwdThreads;
+      const int row = pc / CPR, col = pc % CPR;
+      const int r = tl * kBwdRows + row;
+      if (r < nrows)
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(Qo + row * QOLD + col * EPC),
+                                    reinterpret_cast<u32x4*>(dq_part + ((size_t)pair0 * g + r) * D + col * EPC));
+    }
+  };
   // transposed-read address of this lane in a 16-row block of a tile (see read_tr4)
   const int tr_off = (4 * u + (kl >> 2)) * b_kld<D>() + 4 * (kl & 3);
   for (; cur.current() >= 0; cur.advance()) {
@@ -280,6 +299,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
       tl.put(Qs, Ds, tab_l, tab_d);
       __syncthreads();  // tile in LDS; every wave is past the previous tile's dQ
       if (tile + 1 < ntile) tl.load(q, dout, lse, delta, rtok, tile + 1, it.h, g, HQ);
+      if (tile > 0) flush_dq(tile - 1, it.pair0, nrows);  // the stage is rewritten only after the next barrier
 
       // S = Q K^T and dP = dO V^T for rows 16 rb + 4u + r and this lane's key.
       f32x4 s[2] = {}, dp[2] = {};
@@ -325,30 +345,27 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
         for (int r = 0; r < 4; ++r) Ss[(16 * rb + 4 * u + r) * kSLd + key] = ds4[rb][r];
       __syncthreads();  // dS of all 64 keys in LDS
 
-      // dQ^T = K^T dS^T for the d tiles of this wave; lane: row 16 rb + kl,
-      // d = 16mt + 4u + r.
+      // dQ^T = K^T dS^T for the d tiles of this wave, staged in LDS; lane:
+      // row 16 rb + kl, d = 16mt + 4u + r.
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const int row = tile * kBwdRows + 16 * rb + kl;
-        PT* const dst = dq_part + ((size_t)it.pair0 * g + row) * D + 4 * u;
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int m = 0; m < MW; ++m) {
           f32x4 acc = {};
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
             acc = mfma_k32(kt[m][ks], bld8(Ss + (16 * rb + kl) * kSLd + 32 * ks + 8 * u), acc);
-          if (row < nrows) {
-            PT* const o = dst + 16 * (wave + kBwdWaves * m);
-            if constexpr (sizeof(PT) == 4) {
-              *reinterpret_cast<f32x4*>(o) = acc * scale;
-            } else {
-              typedef PT P4 __attribute__((ext_vector_type(4)));
-              *reinterpret_cast<P4*>(o) = __builtin_convertvector(acc * scale, P4);
-            }
+          PT* const o = Qo + (16 * rb + kl) * QOLD + 16 * (wave + kBwdWaves * m) + 4 * u;
+          if constexpr (sizeof(PT) == 4) {
+            *reinterpret_cast<f32x4*>(o) = acc * scale;
+          } else {
+            typedef PT P4 __attribute__((ext_vector_type(4)));
+            *reinterpret_cast<P4*>(o) = __builtin_convertvector(acc * scale, P4);
           }
         }
-      }
     }
+    __syncthreads();  // the last tile's dQ is staged
+    flush_dq(ntile - 1, it.pair0, nrows);
 
     // The block's dK (scaled) / dV partial of this chunk: slot [2][64][D] fp32.
     const int64_t slot = (int64_t)(offsets[wraw.x] / CT) + wraw.x + wraw.y / CT;
