@@ -8,6 +8,7 @@ Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--partial input|fp32] [--no-cpu-baseline] [--no-variants]
                     [--no-query-outer] [--no-backward] [--no-selection]
+                    [--cold-reps R]
 
 The query-outer forward (fsa_nsa_selected_attn_fwd, the vanilla NSA loop
 order) is timed on the same inputs and reported beside the step, with the
@@ -15,6 +16,12 @@ FSA-order speedup over it; so is the backward (fsa_selected_attn_bwd) from the
 step's O and lse, with its algorithmic TFLOP/s (10 g d flops per visible key),
 and block selection (fsa_select_blocks, the step that produces Sel) on
 synthetic scores of the same shape, with its HBM rate on the causal scores read.
+
+Besides the mean over back-to-back steps (`value`, `stages_ms`), the line
+carries the median and minimum step time, the same step timed R more times
+each after a 1 GiB fill that evicts the L2s and the MALL (`cold_cache`), and
+what this GPU reaches on a plain device copy and a large GEMM
+(`measured_peaks`), with the main kernel's fractions of both.
 
 Throughput is algorithmic TFLOP/s: 4 * g * d * (sum over (token, KV head) of
 the number of keys the token attends to), i.e. QK^T and PV over the visible
@@ -57,6 +64,8 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--no-selection", action="store_true", help="skip timing block selection")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="extra steps timed after a 1 GiB cache-evicting fill each (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of 1 GiB (5 times): the known-size kernel "
                          "against which HBM byte counters are scaled")
@@ -194,7 +203,7 @@ def cpu_baseline(w, target_s):
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
-def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, selection=False):
+def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, selection=False, cold_reps=0):
     import torch
 
     import sparse_attention_sel_amd as fsa
@@ -247,6 +256,28 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
         for i, nm in enumerate(names):
             stage[nm] += ev[i].elapsed_time(ev[i + 1])
     stage = {nm: v_ / steps for nm, v_ in stage.items()}
+    warm_steps = sorted(ev[0].elapsed_time(ev[4]) for ev in events)
+    # cold caches: before each rep a 1 GiB fill evicts the L2s and the MALL,
+    # so every input of the step comes from HBM
+    cold = None
+    if cold_reps:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(cold_reps)]
+        for i in range(cold_reps):
+            scratch.fill_(float(i))
+            step(cev[i])
+        torch.cuda.synchronize()
+        per = {nm: sorted(ev[j].elapsed_time(ev[j + 1]) for ev in cev) for j, nm in enumerate(names)}
+        tot = sorted(ev[0].elapsed_time(ev[4]) for ev in cev)
+        cold = {
+            "reps": cold_reps,
+            "flush_bytes": scratch.numel() * 4,
+            "step_ms_median": round(float(np.median(tot)), 4),
+            "step_ms_min": round(tot[0], 4),
+            "stages_ms_median": {nm: round(float(np.median(v_)), 4) for nm, v_ in per.items()},
+            "stages_ms_min": {nm: round(v_[0], 4) for nm, v_ in per.items()},
+        }
+        del scratch
     # the query-outer (vanilla NSA loop order) forward on the same inputs,
     # timed the same way, for the loop-order comparison
     qo_ms = None
@@ -303,6 +334,9 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
     counts = index.counts.cpu().numpy()
     return {
         "ms_per_step": wall * 1e3 / steps,
+        "step_ms_median": float(np.median(warm_steps)),
+        "step_ms_min": warm_steps[0],
+        "cold": cold,
         "selection_ms": sel_ms,
         "selection_bytes": sel_bytes,
         "query_outer_ms": qo_ms,
@@ -314,9 +348,45 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
     }
 
 
-def measure(w, partial, steps, warmup, query_outer=False, backward=False, selection=False):
+def measured_peaks(dtype):
+    """What this GPU reaches on plain work: a 1 GiB device copy (bytes read +
+    written per second) and an 8192^3 GEMM in the workload's dtype through
+    torch (hipBLASLt), each the median of 10 timed runs."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    n = 8192
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    a = torch.randn((n, n), device=dev, dtype=tdt)
+    b = torch.randn((n, n), device=dev, dtype=tdt)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for s, e in ev:
+            s.record()
+            fn()
+            e.record()
+        torch.cuda.synchronize()
+        return float(np.median([s.elapsed_time(e) for s, e in ev])) * 1e-3
+
+    t_copy = timed(lambda: dst.copy_(src))
+    t_gemm = timed(lambda: torch.matmul(a, b))
+    out = {
+        "copy_gbs": round(2 * src.numel() * 4 / t_copy / 1e9, 1),
+        "gemm_tflops": round(2.0 * n ** 3 / t_gemm / 1e12, 1),
+        "gemm_dtype": dtype,
+    }
+    del src, dst, a, b
+    return out
+
+
+def measure(w, partial, steps, warmup, query_outer=False, backward=False, selection=False, cold_reps=0):
     P_host, keys = work_counts(w.sel, w.cu_seqlens, w.block_size)
-    r = run_gpu(w, partial, steps, warmup, query_outer, backward, selection)
+    r = run_gpu(w, partial, steps, warmup, query_outer, backward, selection, cold_reps)
     assert r["pairs"] == P_host, (r["pairs"], P_host)
     f_alg = 4.0 * w.gqa_group * w.head_dim * keys
     f_main = 4.0 * w.gqa_group * w.block_size * w.head_dim * P_host
@@ -355,7 +425,8 @@ def main():
         log(f"cpu baseline done: {cpu['value']:.4g} TFLOP/s on {cpu['cores']} cores")
     log("gpu run")
     r = measure(w, args.partial, args.steps, args.warmup, not args.no_query_outer, not args.no_backward,
-                not args.no_selection)
+                not args.no_selection, cold_reps=args.cold_reps)
+    peaks = measured_peaks(w.dtype)
     log(f"gpu run done: {r['ms_per_step']:.3f} ms/step")
     ms = r["ms_per_step"]
     value = r["f_alg"] / (ms * 1e-3) / 1e12
@@ -408,7 +479,13 @@ def main():
             "mfma_frac": round(main_tflops / PEAK_MFMA_TFLOPS[w.dtype], 4),
             "tflops_issued": round(r["f_main"] / (st["main"] * 1e-3) / 1e12, 2),
             "hbm_gbs": round(r["bytes"]["main"] / (st["main"] * 1e-3) / 1e9, 1),
+            "hbm_frac_of_measured_copy": round(r["bytes"]["main"] / (st["main"] * 1e-3) / 1e9 / peaks["copy_gbs"], 4),
+            "mfma_frac_of_measured_gemm": round(main_tflops / peaks["gemm_tflops"], 4),
         },
+        "measured_peaks": peaks,
+        "step_ms_median": round(r["step_ms_median"], 4),
+        "step_ms_min": round(r["step_ms_min"], 4),
+        "cold_cache": r["cold"],
         "reduce_kernel_hbm_gbs": round(r["bytes"]["reduce"] / (st["reduce"] * 1e-3) / 1e9, 1),
         "index_hbm_gbs": round(r["bytes"]["index"] / (st["index"] * 1e-3) / 1e9, 1),
         "n_valid": r["n_valid"],
