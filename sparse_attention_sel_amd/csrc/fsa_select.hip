@@ -16,11 +16,12 @@
 // image of the float score << 32 | ~e), so the wanted order is the unsigned
 // integer order and no floating-point operation touches the scores (-0 is
 // folded into +0 and NaN into -inf on the bit pattern).  A lane holds the
-// keys of blocks lane, lane + 64, .. and tracks its two best.  Each round
+// keys of blocks lane, lane + 64, .. and tracks its three best.  Each round
 // takes the wave-wide maximum of the lanes' bests (DPP on the score half, a
 // ballot for the owning lane, no LDS), emits its block, and the owner moves
-// to its second best; it rescans below the winner only when it wins again
-// after that.  Rows of up to 64 * kSelRegs candidates keep their keys in
+// to its next best; it rescans below the winner only when it wins a fourth
+// time.  Groups of 64 blocks wholly past the own block are skipped
+// (wave-uniform).  Rows of up to 64 * kSelRegs candidates keep their keys in
 // registers; longer rows rescan from memory.
 #include "fsa_internal.h"
 
@@ -88,32 +89,43 @@ __global__ __launch_bounds__(kSelWaves * 64) void k_select(const float* __restri
   const int n_loc = max(0, min(local_blocks, own - init_blocks + 1));
   const int kf = min(n_init + n_loc, T);
   for (int p = lane; p < kf; p += 64) out[p] = p < n_init ? p : own - (p - n_init);
-  auto candidate = [&](int e) { return e <= own && e >= init_blocks && own - e >= local_blocks; };
+  // A candidate is a causal block that is neither initial nor local:
+  // init <= e <= own - local (own - e >= local already implies e <= own),
+  // tested with one unsigned compare when the range is not empty.
+  const int cand_hi = own - local_blocks;
+  const uint32_t cand_span = (uint32_t)(cand_hi - init_blocks);
+  const bool any_cand = cand_hi >= init_blocks;
+  auto candidate = [&](int e) { return any_cand && (uint32_t)(e - init_blocks) <= cand_span; };
 
   const int want = T - kf;
   int picked = 0;
   if (want > 0) {
-    // Each lane tracks its two best keys below `limit`; `second` is exact
-    // until the lane's best is taken twice, then the lane rescans.
+    // Each lane tracks its three best keys; after its best is taken, the
+    // next ones move up, and only when all three are gone does it rescan.
     uint64_t keys[IN_REGS ? kSelRegs : 1];
-    uint64_t best = 0, second = 0;
+    uint64_t best = 0, second = 0, third = 0;
     auto offer = [&](uint64_t k) {  // selects only: no branch per key
-      const uint64_t lo = k < best ? k : best;
-      second = lo > second ? lo : second;
+      const uint64_t lo1 = k < best ? k : best;
       best = k > best ? k : best;
+      const uint64_t lo2 = lo1 < second ? lo1 : second;
+      second = lo1 > second ? lo1 : second;
+      third = lo2 > third ? lo2 : third;
     };
     if constexpr (IN_REGS) {
 #pragma unroll
       for (int j = 0; j < kSelRegs; ++j) {
-        const int e = lane + 64 * j;
-        keys[j] = candidate(e) ? cand_key(rs, e) : 0;
-        offer(keys[j]);
+        keys[j] = 0;
+        if (64 * j <= own) {  // wave-uniform: groups wholly past the own block cost nothing
+          const int e = lane + 64 * j;
+          keys[j] = candidate(e) ? cand_key(rs, e) : 0;
+          offer(keys[j]);
+        }
       }
     } else {
       for (int e = lane; e <= own; e += 64)
         if (candidate(e)) offer(cand_key(rs, e));
     }
-    bool second_exact = true;
+    int exact = 2;  // how many of (second, third) are the lane's next keys below best
     for (; picked < want; ++picked) {
       // the wave's largest key: maximum of the score halves, then among the
       // lanes holding that score (nearly always one) the largest index half
@@ -127,15 +139,17 @@ __global__ __launch_bounds__(kSelWaves * 64) void k_select(const float* __restri
       const uint64_t win = ((uint64_t)win_hi << 32) | win_lo;
       if (lane == 0) out[kf + picked] = (int32_t)(0xFFFFFFFFu - win_lo);
       if (best == win) {  // keys are unique: exactly one lane owned the winner
-        if (second_exact) {
+        if (exact > 0) {
           best = second;
-          second = 0;
-          second_exact = false;
+          second = third;
+          third = 0;
+          --exact;
         } else {
-          best = second = 0;
+          best = second = third = 0;
           if constexpr (IN_REGS) {
 #pragma unroll
-            for (int j = 0; j < kSelRegs; ++j) offer(keys[j] < win ? keys[j] : 0);
+            for (int j = 0; j < kSelRegs; ++j)
+              if (64 * j <= own) offer(keys[j] < win ? keys[j] : 0);
           } else {
             for (int e = lane; e <= own; e += 64)
               if (candidate(e)) {
@@ -143,7 +157,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void k_select(const float* __restri
                 offer(k < win ? k : 0);
               }
           }
-          second_exact = true;
+          exact = 2;
         }
       }
     }
