@@ -401,11 +401,24 @@ __global__ __launch_bounds__(256) void k_bwd_kv_reduce(const int32_t* __restrict
   if (token >= cu[s + 1]) return;
   const int nch = (counts[f] + CT - 1) / CT;
   const int64_t slot0 = (int64_t)(offsets[f] / CT) + f;
+  // Eight chunks' loads are issued together (indices clamped to the last
+  // chunk), then added in chunk order; the order of the sum is unchanged.
+  constexpr int U = 8;
   f32x4 sk = {}, sv = {};
-  for (int c = 0; c < nch; ++c) {
-    const float* p = kv_part + (slot0 + c) * 2 * kBwdBK * D + (size_t)key * D + 4 * c4;
-    sk += *reinterpret_cast<const f32x4*>(p);
-    sv += *reinterpret_cast<const f32x4*>(p + kBwdBK * D);
+  for (int c = 0; c < nch; c += U) {
+    f32x4 xk[U], xv[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const float* p = kv_part + (slot0 + min(c + j, nch - 1)) * 2 * kBwdBK * D + (size_t)key * D + 4 * c4;
+      xk[j] = *reinterpret_cast<const f32x4*>(p);
+      xv[j] = *reinterpret_cast<const f32x4*>(p + kBwdBK * D);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+      if (c + j < nch) {
+        sk += xk[j];
+        sv += xv[j];
+      }
   }
   const size_t o = ((size_t)token * H + h) * D + 4 * c4;
   *reinterpret_cast<T4*>(dk + o) = __builtin_convertvector(sk, T4);
