@@ -45,7 +45,11 @@
  * several host threads.  Buffers must stay alive until the stream has
  * executed the enqueued work.  The `fsa_index` buffers and its `aux` blob
  * belong together: build them once, reuse them for the stats and forward
- * calls of the same problem and Sel.
+ * calls of the same problem and Sel.  The compute calls (stats, forward,
+ * backward) claim their work items through counters in the `aux` blob, which
+ * fsa_build_index clears and every such call leaves cleared when it ends: the
+ * calls that take one index must run one after another (as on one stream),
+ * never overlapping in time.
  *
  * Errors.  Every call returns FSA_OK (0) or a nonzero fsa_status.  Argument
  * checks run before anything is enqueued: on any status other than

@@ -115,6 +115,8 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   off = round_up(off + (size_t)(B + 1) * 4, 256);
   geo->aux_nwork = off;
   off = round_up(off + 16, 256);
+  geo->aux_queue = off;
+  off = round_up(off + (size_t)kQueueKinds * kQueueInts * 4, 256);
   geo->aux_work = off;
   off = round_up(off + (size_t)std::max<int64_t>(geo->max_work, 1) * 16, 256);
   geo->aux_work_sorted = off;

@@ -266,26 +266,32 @@ template <typename T, int D, int BK>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_stats(
     const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
-    const int32_t* __restrict__ nwork, float2* __restrict__ st, size_t dump_row, int H, int g, int NB, int CT,
-    float scale_log2) {
+    const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, float2* __restrict__ st, size_t dump_row, int H,
+    int g, int NB, int CT, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32;
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
   __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
-  ItemCursor cur(nwork[0]);
-  if (cur.current() < 0) return;
+  __shared__ int s_items[2];
+  ItemChain ch(queue, nwork[0], s_items);
+  if (ch.cur < 0) {
+    ch.finish();
+    return;
+  }
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
   T* const qt = Qt + wave * 32 * tile_ld<D>();
   ItemStage<T, D, BK, false> pre;
-  pre.load(k, nullptr, qidx, work, counts, offsets, cur.current(), H, g, NB, CT);
-  for (; cur.current() >= 0; cur.advance()) {
+  pre.load(k, nullptr, qidx, work, counts, offsets, ch.cur, H, g, NB, CT);
+  while (ch.cur >= 0) {
     __syncthreads();  // the previous item's LDS reads are done
     pre.commit(Ks, nullptr, ridx, rtok, g, HQ);
+    ch.publish(s_items);
     const Item it = pre.it;
     __syncthreads();
+    const int after = ch.after(s_items);
     const int nrows = it.ntok * g, ntile = (nrows + 31) / 32;
 
     // Q pipeline: one register set plus the wave's LDS tile.  At each tile the
@@ -294,8 +300,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     // loads are issued after the first Q tile's.
     V8 qv[KS];
     if (wave < ntile) load_q_tile<T, D>(q, ridx, wave, lane, qv);
-    const int wn = cur.next();
-    if (wn >= 0) pre.load(k, nullptr, qidx, work, counts, offsets, wn, H, g, NB, CT);
+    if (ch.nxt >= 0) pre.load(k, nullptr, qidx, work, counts, offsets, ch.nxt, H, g, NB, CT);
     for (int tl = wave; tl < ntile; tl += kWaves) {
       put_q_tile<T, D>(qt, lane, qv);
       if (tl + kWaves < ntile) load_q_tile<T, D>(q, ridx, tl + kWaves, lane, qv);
@@ -309,7 +314,9 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
       // lanes l and l + 32 store the same pair; rows past the chunk go to the dump
       st[tok >= 0 ? (size_t)it.pair0 * g + row : dump_row + lr] = ml;
     }
+    ch.advance(after);
   }
+  ch.finish();
 }
 
 // One thread per (token, query head): merge the per-block (max, sum) pairs of
@@ -447,8 +454,8 @@ template <typename T, int D, int BK, typename PT>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
-    const int32_t* __restrict__ nwork, const float* __restrict__ lse, PT* __restrict__ partial, size_t dump_row,
-    int H, int g, int NB, int CT, float scale_log2) {
+    const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
+    PT* __restrict__ partial, size_t dump_row, int H, int g, int NB, int CT, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
   static_assert(32 * Stage<PT, D>::P * sizeof(PT) <= 32 * tile_ld<D>() * sizeof(T), "stage fits the Q tile");
@@ -456,8 +463,12 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
   __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
-  ItemCursor cur(nwork[0]);
-  if (cur.current() < 0) return;
+  __shared__ int s_items[2];
+  ItemChain ch(queue, nwork[0], s_items);
+  if (ch.cur < 0) {
+    ch.finish();
+    return;
+  }
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
@@ -465,12 +476,14 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   PT* const stage = reinterpret_cast<PT*>(qt);
   PT* const dump = partial + dump_row * D;
   ItemStage<T, D, BK, true> pre;
-  pre.load(k, v, qidx, work, counts, offsets, cur.current(), H, g, NB, CT);
-  for (; cur.current() >= 0; cur.advance()) {
+  pre.load(k, v, qidx, work, counts, offsets, ch.cur, H, g, NB, CT);
+  while (ch.cur >= 0) {
     __syncthreads();  // the previous item's LDS reads are done
     pre.commit(Ks, Vt, ridx, rtok, g, HQ);
+    ch.publish(s_items);
     const Item it = pre.it;
     __syncthreads();
+    const int after = ch.after(s_items);
     const int nrows = it.ntok * g, ntile = (nrows + 31) / 32;
 
     // Q pipeline: one register set plus the wave's LDS tile (as in k_stats);
@@ -481,8 +494,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
       load_q_tile<T, D>(q, ridx, wave, lane, qv);
       lnext = lse[ridx[wave * 32 + lr]];
     }
-    const int wn = cur.next();
-    if (wn >= 0) pre.load(k, v, qidx, work, counts, offsets, wn, H, g, NB, CT);
+    if (ch.nxt >= 0) pre.load(k, v, qidx, work, counts, offsets, ch.nxt, H, g, NB, CT);
     for (int tl = wave; tl < ntile; tl += kWaves) {
       put_q_tile<T, D>(qt, lane, qv);
       const float l2 = lnext * kLog2e;
@@ -509,7 +521,9 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
       store_tile<PT, D>(stage, o, lane, min(32, nrows - tl * 32),
                         partial + ((size_t)it.pair0 * g + (size_t)tl * 32) * D, dump);
     }
+    ch.advance(after);
   }
+  ch.finish();
 }
 
 // ---- reduce -----------------------------------------------------------------
@@ -590,12 +604,14 @@ struct Ptrs {
   const int32_t* qidx;
   const int4* work;
   const int32_t* nwork;
+  int32_t* queue;
 };
 
 inline Ptrs<int> index_ptrs(const Geometry& geo, const fsa_index& idx) {
   const char* aux = static_cast<const char*>(idx.aux);
   return Ptrs<int>{idx.counts, idx.offsets, idx.qidx, reinterpret_cast<const int4*>(aux + geo.aux_work_sorted),
-                   reinterpret_cast<const int32_t*>(aux + geo.aux_nwork)};
+                   reinterpret_cast<const int32_t*>(aux + geo.aux_nwork),
+                   reinterpret_cast<int32_t*>(static_cast<char*>(idx.aux) + geo.aux_queue)};
 }
 
 
@@ -606,7 +622,7 @@ void stats_typed(const Geometry& geo, const void* q, const void* k, const fsa_in
   const float sl2 = geo.scale * kLog2e;
   hipLaunchKernelGGL((k_stats<T, D, BK>), dim3(persistent_grid(k_stats<T, D, BK>, kAttnThreads, geo.max_work)), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), p.counts, p.offsets, p.qidx, p.work, p.nwork,
-                     st, (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
+                     p.queue, st, (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
 }
 
 template <typename T, int D, int BK, typename PT>
@@ -616,7 +632,7 @@ void main_typed(const Geometry& geo, const void* q, const void* k, const void* v
   const float sl2 = geo.scale * kLog2e;
   hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3(persistent_grid(k_main<T, D, BK, PT>, kAttnThreads, geo.max_work)), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), p.counts,
-                     p.offsets, p.qidx, p.work, p.nwork, lse, static_cast<PT*>(partial), (size_t)geo.dump_row, geo.H,
+                     p.offsets, p.qidx, p.work, p.nwork, p.queue + kQueueInts, lse, static_cast<PT*>(partial), (size_t)geo.dump_row, geo.H,
                      geo.g, geo.NB, geo.chunk_tokens, sl2);
 }
 

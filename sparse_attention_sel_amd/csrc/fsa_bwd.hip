@@ -196,8 +196,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
-    const int32_t* __restrict__ nwork, PT* __restrict__ dq_part, float* __restrict__ kv_part, int H, int g, int NB,
-    int CT, float scale, float scale_log2) {
+    const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, PT* __restrict__ dq_part,
+    float* __restrict__ kv_part, int H, int g, int NB, int CT, float scale, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   using V4 = typename Vec4<T>::type;
   constexpr int KS = D / 32;           // 32-wide contraction steps over d
@@ -217,7 +217,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
   __shared__ __attribute__((aligned(16))) float tab_l[kBwdRows];
   __shared__ __attribute__((aligned(16))) float tab_d[kBwdRows];
 
-  ItemCursor cur(nwork[0]);
+  __shared__ int s_items[2];
+  ItemChain ch(queue, nwork[0], s_items);
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kl = lane & 15, u = lane >> 4;
@@ -239,8 +240,8 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
   };
   // transposed-read address of this lane in a 16-row block of a tile (see read_tr4)
   const int tr_off = (4 * u + (kl >> 2)) * b_kld<D>() + 4 * (kl & 3);
-  for (; cur.current() >= 0; cur.advance()) {
-    const int wi = cur.current();
+  while (ch.cur >= 0) {
+    const int wi = ch.cur;
     const int4 wraw = work[wi];
     const Item it = read_item(work, counts, offsets, wi, NB, CT, kBwdBK);
     const int nrows = it.ntok * g, ntile = (nrows + kBwdRows - 1) / kBwdRows;
@@ -278,7 +279,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
       const int r = threadIdx.x + i * kBwdThreads;
       if (r < kBwdRowTable) rtok[r] = r < nrows ? tk[i] : -1;
     }
+    ch.publish(s_items);
     __syncthreads();
+    const int after = ch.after(s_items);
     // K^T fragments of dQ^T = K^T dS^T: lane (kl, u) of d tile mt holds
     // K[32 ks + 8u + e][16 mt + kl], e < 8.
     V8 kt[MW][2];
@@ -375,7 +378,9 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))
       *reinterpret_cast<f32x4*>(kvp + 16 * mt) = dk[mt] * scale;
       *reinterpret_cast<f32x4*>(kvp + kBwdBK * D + 16 * mt) = dv[mt];
     }
+    ch.advance(after);
   }
+  ch.finish();
 }
 
 // ---- dK, dV = ordered sum of the block's chunk slots --------------------------
@@ -437,6 +442,7 @@ hipError_t bwd_typed(const Geometry& geo, const int32_t* cu_dev, const void* q, 
   const int4* work = reinterpret_cast<const int4*>(aux + geo.aux_work_sorted);
   const int32_t* nwork = reinterpret_cast<const int32_t*>(aux + geo.aux_nwork);
   const int32_t* gboff = reinterpret_cast<const int32_t*>(aux + geo.aux_seq_gboff);
+  int32_t* queue = reinterpret_cast<int32_t*>(static_cast<char*>(idx.aux) + geo.aux_queue) + 2 * kQueueInts;
 
   const int64_t rows = (int64_t)geo.N * geo.HQ;
   const int64_t dthreads = rows * (D / 8);
@@ -447,7 +453,7 @@ hipError_t bwd_typed(const Geometry& geo, const int32_t* cu_dev, const void* q, 
   hipLaunchKernelGGL((k_bwd_main<T, D, PT>),
                      dim3(persistent_grid(k_bwd_main<T, D, PT>, kBwdThreads, geo.max_work)), dim3(kBwdThreads), 0,
                      stream, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
-                     static_cast<const T*>(dout), lse, delta, idx.counts, idx.offsets, idx.qidx, work, nwork, dq_part,
+                     static_cast<const T*>(dout), lse, delta, idx.counts, idx.offsets, idx.qidx, work, nwork, queue, dq_part,
                      kv_part, geo.H, geo.g, geo.NB, geo.chunk_tokens, geo.scale, geo.scale * kBwdLog2e);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

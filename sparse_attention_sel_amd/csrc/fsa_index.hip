@@ -22,9 +22,11 @@ namespace {
 
 // ---- seq_table ------------------------------------------------------------
 __global__ __launch_bounds__(kBuildThreads) void k_seq_table(const int32_t* __restrict__ cu, int num_seqs,
-                                                             int BK, int32_t* __restrict__ gboff) {
+                                                             int BK, int32_t* __restrict__ gboff,
+                                                             int32_t* __restrict__ queue) {
   __shared__ int buf[kBuildThreads];
   const int tid = threadIdx.x;
+  for (int i = tid; i < kQueueKinds * kQueueInts; i += kBuildThreads) queue[i] = 0;
   int carry = 0;
   for (int base = 0; base < num_seqs; base += kBuildThreads) {
     const int s = base + tid;
@@ -378,7 +380,8 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
   int32_t* buckets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + geo.build_ws_buckets);
   const int M = geo.H * geo.NB;
 
-  hipLaunchKernelGGL(k_seq_table, dim3(1), dim3(kBuildThreads), 0, stream, cu_dev, geo.num_seqs, geo.BK, gboff);
+  hipLaunchKernelGGL(k_seq_table, dim3(1), dim3(kBuildThreads), 0, stream, cu_dev, geo.num_seqs, geo.BK, gboff,
+                     reinterpret_cast<int32_t*>(aux + geo.aux_queue));
   if (geo.N > 0) {
     hipLaunchKernelGGL(k_hist, dim3(geo.ntiles, geo.H), dim3(kBuildThreads),
                        (geo.win_max + kHistStage) * sizeof(int), stream, sel, cu_dev, gboff, geo.num_seqs, geo.N, geo.T,

@@ -51,6 +51,7 @@ struct Geometry {
   // aux blob layout (byte offsets)
   size_t aux_seq_gboff;  // int32 [B+1] exclusive prefix of per-sequence block counts
   size_t aux_nwork;      // int32 [4]: number of work items, P, spare
+  size_t aux_queue;      // int32 [kQueueKinds][kQueueInts]: work-queue counters
   size_t aux_work;       // int4 [max_work]: (segment, first token, block start, seq end)
   size_t aux_work_sorted;// int4 [max_work]: the same items ordered by (KV head, first query token)
   int32_t sort_shift;    // work-order bucket = query token >> sort_shift
@@ -155,27 +156,91 @@ __device__ __forceinline__ Item read_item(const int4* __restrict__ work, const i
   return r;
 }
 
-// Persistent workgroups.  The grid is a multiple of 8 and workgroup i runs on
-// XCD x = i % 8 (round-robin dispatch).  XCD x owns the contiguous range
-// [x * per, (x + 1) * per) of the token-ordered work list and its G8 = grid / 8
-// workgroups take the range's items round-robin, so the items in flight on one
-// XCD gather neighbouring query rows.  Every workgroup exits when its next
-// index leaves the range.
-struct ItemCursor {
-  int base, per, k, step, total;
-  __device__ __forceinline__ ItemCursor(int nwork_total) {
-    per = (nwork_total + 7) >> 3;
-    base = (blockIdx.x & 7) * per;
-    k = blockIdx.x >> 3;
-    step = gridDim.x >> 3;
-    total = nwork_total;
+// Persistent workgroups take their items from dynamic work queues.  The grid
+// is a multiple of 8 and workgroup i runs on XCD x = i % 8 (round-robin
+// dispatch).  Queue x covers the contiguous range [x * per, min((x + 1) * per,
+// total)) of the token-ordered work list, so the items in flight on one XCD
+// gather neighbouring query rows into that XCD's L2.  The workgroups of XCD x
+// claim the items of queue x in order with an atomic counter, then move on to
+// the other queues in turn, so every workgroup stays busy while any item is
+// left (item sizes vary, and a static split left some XCDs a quarter more rows
+// than others).  Which workgroup takes an item changes no output.  The
+// counters live in the index's aux blob: the index builder clears them and the
+// last workgroup of each launch sets them back to zero, so launches that use
+// one index must not overlap.
+constexpr int kQueues = 8;
+constexpr int kQueueStride = 32;  // ints between counters: one 128-byte line each
+constexpr int kQueueInts = (kQueues + 1) * kQueueStride;
+constexpr int kQueueKinds = 3;    // 0: statistics, 1: main, 2: backward
+
+struct WorkQueue {
+  int32_t* q;
+  int per, total, x, tried;
+  __device__ __forceinline__ WorkQueue(int32_t* counters, int total_items) : q(counters), total(total_items) {
+    per = (total + kQueues - 1) / kQueues;
+    x = blockIdx.x & (kQueues - 1);
+    tried = 0;
   }
-  __device__ __forceinline__ int current() const { return (k < per && base + k < total) ? base + k : -1; }
-  __device__ __forceinline__ int next() const {
-    const int kn = k + step;
-    return (kn < per && base + kn < total) ? base + kn : -1;
+  // One thread per workgroup: the next item, or -1 once every queue is empty.
+  __device__ __forceinline__ int claim() {
+    while (tried < kQueues) {
+      const int qq = (x + tried) & (kQueues - 1);
+      const int base = qq * per;
+      const int n = min(per, total - base);
+      if (n > 0) {
+        const int i = atomicAdd(q + qq * kQueueStride, 1);
+        if (i < n) return base + i;
+      }
+      ++tried;
+    }
+    return -1;
   }
-  __device__ __forceinline__ void advance() { k += step; }
+  // One thread per workgroup, after its last claim.
+  __device__ __forceinline__ void finish() {
+    __threadfence();
+    if (atomicAdd(q + kQueues * kQueueStride, 1) == (int)gridDim.x - 1) {
+      for (int i = 0; i < kQueues; ++i) atomicExch(q + i * kQueueStride, 0);
+      atomicExch(q + kQueues * kQueueStride, 0);
+    }
+  }
+};
+
+// The item chain of one persistent workgroup: every thread knows the current
+// item and the next one (whose staging loads run during the current item);
+// thread 0 keeps the claim of the item after those in flight across a whole
+// item, so the atomic's latency is hidden.  `s` is a __shared__ int[2].
+struct ItemChain {
+  WorkQueue wq;
+  int cur, nxt, pending;
+  __device__ __forceinline__ ItemChain(int32_t* counters, int total, int* s) : wq(counters, total) {
+    if (threadIdx.x == 0) {
+      const int a = wq.claim();
+      s[0] = a;
+      s[1] = a >= 0 ? wq.claim() : -1;
+    }
+    __syncthreads();
+    cur = __builtin_amdgcn_readfirstlane(s[0]);
+    nxt = __builtin_amdgcn_readfirstlane(s[1]);
+    pending = -1;
+    if (threadIdx.x == 0 && nxt >= 0) pending = wq.claim();
+  }
+  // Between the two barriers at the top of an item.
+  __device__ __forceinline__ void publish(int* s) const {
+    if (threadIdx.x == 0) s[0] = pending;
+  }
+  // After the second barrier: the item after `nxt`; thread 0 claims the next.
+  __device__ __forceinline__ int after(const int* s) {
+    const int a = __builtin_amdgcn_readfirstlane(s[0]);
+    if (threadIdx.x == 0) pending = a >= 0 ? wq.claim() : -1;
+    return a;
+  }
+  __device__ __forceinline__ void advance(int a) {
+    cur = nxt;
+    nxt = a;
+  }
+  __device__ __forceinline__ void finish() {
+    if (threadIdx.x == 0) wq.finish();
+  }
 };
 
 // Persistent grid: as many workgroups of `threads` as fit on the device at

@@ -168,6 +168,48 @@ def test_deterministic_bitwise():
         assert np.array_equal(a[key], b[key], equal_nan=True), key
 
 
+def test_repeated_calls_on_one_index():
+    # The compute calls claim their work items through counters kept with the
+    # index.  Calls that reuse one index without rebuilding it must each cover
+    # every item: three rounds of stats + forward and two backward calls on one
+    # index give bitwise the results of a freshly built index.
+    import sparse_attention_sel_amd as fsa
+    from sparse_attention_sel_amd.inputs import make_dout
+
+    w = workload("n8k_h4_g2_d128_t16_bf16")
+    ref = run_gpu(w, "input")
+    prob = fsa.Problem(w.cu_seqlens, w.num_kv_heads, w.gqa_group, w.head_dim, w.block_size, w.topk,
+                       dtype=torch.bfloat16, partial_dtype="input", softmax_scale=w.scale, device="cuda:0")
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    sel = torch.from_numpy(w.sel).to(dev)
+    index = fsa.allocate_index(prob, dev)
+    ws = fsa.Workspaces(prob, dev, index.sizes, backward=True)
+    fsa.build_index(prob, sel, index, ws.build)
+    n, hq = prob.total_tokens, prob.num_q_heads
+    for rnd in range(3):
+        log(f"    round {rnd}")
+        lse = torch.full((n, hq), float("nan"), dtype=torch.float32, device=dev)
+        row_max = torch.full_like(lse, float("nan"))
+        out = torch.full((n, hq, prob.head_dim), float("nan"), dtype=prob.dtype, device=dev)
+        fsa.softmax_stats(prob, q, k, index, row_max, lse, ws.stats)
+        fsa.selected_attn_fwd(prob, q, k, v, index, lse, out, ws.partial)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.float().cpu().numpy(), ref["out"])
+        assert np.array_equal(lse.cpu().numpy(), ref["lse"])
+        assert np.array_equal(row_max.cpu().numpy(), ref["row_max"])
+    do = make_dout(n, hq, prob.head_dim, "bf16", 11).to(dev)
+    grads = []
+    for _ in range(2):
+        dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+        fsa.selected_attn_bwd(prob, q, k, v, out, do, lse, index, dq, dk, dv, ws.bwd)
+        torch.cuda.synchronize()
+        grads.append([x.float().cpu() for x in (dq, dk, dv)])
+    for a, b in zip(*grads):
+        assert torch.isfinite(a).all()
+        assert torch.equal(a, b)
+
+
 def test_partial_rows_sum_to_output():
     # fp32 partials: summing each query's partial rows (slot order) gives the
     # output before its final rounding.
