@@ -76,10 +76,12 @@ def parse():
 # Work accounting (host bookkeeping for the FLOP and byte counts)
 # ---------------------------------------------------------------------------
 def work_counts(sel, cu, block_size):
-    """Number of selecting entries P and total visible keys over all
-    (KV head, token) rows.  An entry selects block e of the token's sequence
-    iff 0 <= e <= own block and e did not occur earlier in the row; it sees
-    the whole block, or only keys <= t in the own block."""
+    """Number of selecting entries P, the local ones among them (entries of
+    the token's own, previous or first block, which the forward computes per
+    query block) and total visible keys over all (KV head, token) rows.  An
+    entry selects block e of the token's sequence iff 0 <= e <= own block and
+    e did not occur earlier in the row; it sees the whole block, or only keys
+    <= t in the own block."""
     cu = np.asarray(cu, dtype=np.int64)
     n = int(cu[-1])
     tok = np.arange(n)
@@ -88,6 +90,7 @@ def work_counts(sel, cu, block_size):
     own = local // block_size
     H, _, T = sel.shape
     pairs = 0
+    local_pairs = 0
     keys = 0
     for h in range(H):
         s = sel[h]
@@ -95,10 +98,11 @@ def work_counts(sel, cu, block_size):
         for j in range(1, T):
             ok[:, j] &= ~np.any(s[:, :j] == s[:, j : j + 1], axis=1)
         pairs += int(ok.sum())
+        local_pairs += int((ok & ((s == own[:, None]) | (s == own[:, None] - 1) | (s == 0))).sum())
         full = ok & (s < own[:, None])
         mine = ok & (s == own[:, None])
         keys += int(full.sum()) * block_size + int(((local % block_size + 1)[:, None] * mine).sum())
-    return pairs, keys
+    return pairs, local_pairs, keys
 
 
 KERNEL_SOURCES = ("fsa_attn.hip", "fsa_internal.h", "fsa_index.hip", "fsa_api.hip")
@@ -125,15 +129,23 @@ def measured_traffic(workload):
     return rec
 
 
-def kernel_bytes(w, P, s_in, s_p):
+def kernel_bytes(w, P, P_loc, s_in, s_p):
+    """Compulsory HBM bytes of each stage (each input read once, each output
+    written once).  Block-outer kernels take the P - P_loc non-local pairs;
+    the local entries of a (KV head, token) give one partial row group and one
+    (max, sum) pair per query head."""
     N, H, g, d, T = int(w.cu_seqlens[-1]), w.num_kv_heads, w.gqa_group, w.head_dim, w.topk
     HQ = H * g
+    Pn = P - P_loc
     q_bytes = N * HQ * d * s_in
     kv_bytes = 2 * N * H * d * s_in
-    main = q_bytes + kv_bytes + N * HQ * 4 + P * 4 + P * g * d * s_p
-    reduce = P * g * d * s_p + H * N * T * 4 + N * HQ * d * s_in
-    stats = q_bytes + kv_bytes // 2 + P * 4 + 2 * P * g * 8 + H * N * T * 4 + 2 * N * HQ * 4
-    index = 3 * H * N * T * 4 + P * 4
+    loc = 4 * H * N
+    local_rows = N * HQ * d * s_p
+    main = q_bytes + kv_bytes + N * HQ * 4 + Pn * 4 + Pn * g * d * s_p + local_rows + loc
+    reduce = Pn * g * d * s_p + local_rows + H * N * T * 4 + loc + N * HQ * d * s_in
+    stats = (q_bytes + kv_bytes // 2 + Pn * 4 + 2 * Pn * g * 8 + 2 * N * HQ * 8 + H * N * T * 4 + loc
+             + 2 * N * HQ * 4)
+    index = 3 * H * N * T * 4 + P * 4 + loc
     return {"index": index, "stats": stats, "main": main, "reduce": reduce}
 
 
@@ -344,7 +356,6 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
         "stage_ms": stage,
         "pairs": index.num_pairs(),
         "n_valid": {"min": int(counts.min()), "median": float(np.median(counts)), "max": int(counts.max())},
-        "partial_bytes": index.num_pairs() * w.gqa_group * w.head_dim * (2 if partial == "input" else 4),
     }
 
 
@@ -385,14 +396,14 @@ def measured_peaks(dtype):
 
 
 def measure(w, partial, steps, warmup, query_outer=False, backward=False, selection=False, cold_reps=0):
-    P_host, keys = work_counts(w.sel, w.cu_seqlens, w.block_size)
+    P_host, P_loc, keys = work_counts(w.sel, w.cu_seqlens, w.block_size)
     r = run_gpu(w, partial, steps, warmup, query_outer, backward, selection, cold_reps)
     assert r["pairs"] == P_host, (r["pairs"], P_host)
     f_alg = 4.0 * w.gqa_group * w.head_dim * keys
     f_main = 4.0 * w.gqa_group * w.block_size * w.head_dim * P_host
     s_in, s_p = 2, (2 if partial == "input" else 4)
-    byts = kernel_bytes(w, P_host, s_in, s_p)
-    r.update(f_alg=f_alg, f_main=f_main, bytes=byts)
+    byts = kernel_bytes(w, P_host, P_loc, s_in, s_p)
+    r.update(f_alg=f_alg, f_main=f_main, bytes=byts, local_pairs=P_loc)
     return r
 
 
@@ -462,10 +473,11 @@ def main():
             "topk": w.topk,
             "partial_dtype": w.dtype if args.partial == "input" else "fp32",
             "pairs": r["pairs"],
+            "local_pairs": r["local_pairs"],
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_reduce" if dominant == "reduce" else "k_main",
+            "kernel": "k_reduce" if dominant == "reduce" else "k_main+k_main_local",
             "achieved": round(ach, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -56,6 +56,7 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   geo->scale = scale;
   geo->chunk_tokens = (int32_t)((kRowsPerItem + g - 1) / g);
   const int64_t CT = geo->chunk_tokens;
+  geo->local = BK == 64 && g >= 2;
 
   // Blocks, the bound on selecting entries (a token of local block e selects
   // at most min(T, e + 1) distinct blocks) and the bound on work items (block
@@ -117,10 +118,14 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   off = round_up(off + 16, 256);
   geo->aux_queue = off;
   off = round_up(off + (size_t)kQueueKinds * kQueueInts * 4, 256);
-  geo->aux_work = off;
-  off = round_up(off + (size_t)std::max<int64_t>(geo->max_work, 1) * 16, 256);
+  geo->aux_loc = off;
+  off = round_up(off + (size_t)std::max<int64_t>(H * N, 1) * 4, 256);
+  geo->aux_nloc = off;
+  off = round_up(off + (size_t)std::max<int64_t>(H * NB, 1) * 4, 256);
+  // full and forward lists: the forward list's chunks of a segment are no
+  // more than its full list's, so both fit max_work
   geo->aux_work_sorted = off;
-  off = round_up(off + (size_t)std::max<int64_t>(geo->max_work, 1) * 16, 256);
+  off = round_up(off + 2 * (size_t)std::max<int64_t>(geo->max_work, 1) * 16, 256);
   {
     int shift = 6;
     while (H * ((N + (int64_t(1) << shift) - 1) >> shift) > kSortBucketsMax) ++shift;
@@ -130,17 +135,22 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   }
   geo->aux_bytes = off;
   geo->build_ws_buckets = round_up((size_t)std::max<int64_t>(H * geo->ntiles * NB, 1) * 4, 256);
-  geo->build_ws_bytes = round_up(geo->build_ws_buckets + (size_t)std::max(geo->sort_buckets, 1) * 4, 256);
+  geo->build_ws_cb = round_up(geo->build_ws_buckets + 2 * (size_t)std::max(geo->sort_buckets, 1) * 4, 256);
+  geo->build_ws_bytes = round_up(geo->build_ws_cb + 2 * (size_t)(H * NB + 1) * 4, 256);
   geo->dump_row = std::max<int64_t>(geo->max_pairs, 1) * g;
   const size_t rows = (size_t)geo->dump_row + 32;
-  geo->stats_ws_bytes = round_up(rows * 8, 256);
-  geo->partial_ws_bytes = round_up(rows * (size_t)geo->d * (geo->partial_dtype == FSA_PARTIAL_FP32 ? 4 : 2), 256);
+  const size_t local_rows = (size_t)std::max<int64_t>(H * N * g, 1);
+  const size_t s_p = geo->partial_dtype == FSA_PARTIAL_FP32 ? 4 : 2;
+  geo->stats_local_off = round_up(rows * 8, 256);
+  geo->stats_ws_bytes = round_up(geo->stats_local_off + local_rows * 8, 256);
+  geo->partial_local_off = round_up(rows * (size_t)geo->d * s_p, 256);
+  geo->partial_ws_bytes = round_up(geo->partial_local_off + local_rows * (size_t)geo->d * s_p, 256);
   // Backward: the chunk slot offsets[f] / CT + f + c (c < ceil(count_f / CT))
   // is injective and below max_pairs / CT + M + 2.
   geo->bwd_ok = BK == 64 && (geo->d == 64 || geo->d == 128);
   geo->kv_slots = geo->max_pairs / geo->chunk_tokens + H * NB + 2;
   geo->bwd_dq_off = round_up((size_t)N * H * g * 4, 256);
-  geo->bwd_kv_off = round_up(geo->bwd_dq_off + geo->partial_ws_bytes, 256);
+  geo->bwd_kv_off = round_up(geo->bwd_dq_off + geo->partial_local_off, 256);  // dQ rows: no local region
   geo->bwd_ws_bytes =
       geo->bwd_ok ? round_up(geo->bwd_kv_off + (size_t)geo->kv_slots * 2 * BK * geo->d * 4, 256) : 0;
   return FSA_OK;
@@ -264,7 +274,8 @@ int32_t fsa_softmax_stats(const fsa_problem* prob, const void* q, const void* k,
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_max, 4) || !aligned(lse, 4) || !aligned(ws, 16))
     return FSA_ERR_ALIGN;
   if (ws_bytes < geo.stats_ws_bytes) return FSA_ERR_WORKSPACE;
-  return hip_status(launch_stats(geo, q, k, *idx, row_max, lse, ws, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_stats(geo, prob->cu_seqlens_dev, q, k, *idx, row_max, lse, ws,
+                                 static_cast<hipStream_t>(stream)));
 }
 
 int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const void* k, const void* v,
@@ -275,7 +286,8 @@ int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const voi
   if (st != FSA_OK) return st;
   st = check_main_args(geo, q, k, v, idx, lse, partial_ws, partial_ws_bytes);
   if (st != FSA_OK) return st;
-  return hip_status(launch_main(geo, q, k, v, *idx, lse, partial_ws, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      launch_main(geo, prob->cu_seqlens_dev, q, k, v, *idx, lse, partial_ws, static_cast<hipStream_t>(stream)));
 }
 
 int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, const void* partial_ws,
@@ -285,7 +297,7 @@ int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, 
   if (st != FSA_OK) return st;
   st = check_reduce_args(geo, idx, partial_ws, partial_ws_bytes, out);
   if (st != FSA_OK) return st;
-  return hip_status(launch_reduce(geo, *idx, partial_ws, out, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_reduce(geo, *idx, partial_ws, out, true, static_cast<hipStream_t>(stream)));
 }
 
 int32_t fsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
@@ -299,9 +311,9 @@ int32_t fsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void
   st = check_reduce_args(geo, idx, partial_ws, partial_ws_bytes, out);
   if (st != FSA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(launch_main(geo, q, k, v, *idx, lse, partial_ws, s));
+  st = hip_status(launch_main(geo, prob->cu_seqlens_dev, q, k, v, *idx, lse, partial_ws, s));
   if (st != FSA_OK) return st;
-  return hip_status(launch_reduce(geo, *idx, partial_ws, out, s));
+  return hip_status(launch_reduce(geo, *idx, partial_ws, out, true, s));
 }
 
 int32_t fsa_selected_attn_bwd(const fsa_problem* prob, const void* q, const void* k, const void* v,

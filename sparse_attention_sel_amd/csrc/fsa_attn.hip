@@ -117,6 +117,18 @@ __device__ __forceinline__ void qk_tile(const T* __restrict__ Ks, const T* __res
   }
 }
 
+// O^T += V^T P^T over one key block: o[mt] holds O^T rows (d) mt*32.. of the
+// lane's query row; pb are the 16-bit probabilities of probs().
+template <typename T, int D, int BK>
+__device__ __forceinline__ void pv_tile(const T* __restrict__ Vt, const typename Vec8<T>::type* pb, int lr, int hl,
+                                        f32x16* o) {
+  constexpr int KK = BK / 16, MT = D / 32;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[mt] = mfma32(load8(Vt + (mt * 32 + lr) * vt_ld<BK>() + kk * 16 + hl * 8), pb[kk], o[mt]);
+}
+
 // x combined with the same register of lane l ^ 32 by a commutative op:
 // v_permlane32_swap of x with itself hands each lane the values of lanes
 // l % 32 (first result) and l % 32 + 32 (second result).  The compiler treats
@@ -274,7 +286,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
   __shared__ int s_items[2];
-  ItemChain ch(queue, nwork[0], s_items);
+  ItemChain ch(queue, nwork[2], s_items);  // the forward list
+  const int4* const wl = work + nwork[0];
   if (ch.cur < 0) {
     ch.finish();
     return;
@@ -284,7 +297,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   const int lr = lane & 31, hl = lane >> 5;
   T* const qt = Qt + wave * 32 * tile_ld<D>();
   ItemStage<T, D, BK, false> pre;
-  pre.load(k, nullptr, qidx, work, counts, offsets, ch.cur, H, g, NB, CT);
+  pre.load(k, nullptr, qidx, wl, counts, offsets, ch.cur, H, g, NB, CT);
   while (ch.cur >= 0) {
     __syncthreads();  // the previous item's LDS reads are done
     pre.commit(Ks, nullptr, ridx, rtok, g, HQ);
@@ -300,7 +313,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     // loads are issued after the first Q tile's.
     V8 qv[KS];
     if (wave < ntile) load_q_tile<T, D>(q, ridx, wave, lane, qv);
-    if (ch.nxt >= 0) pre.load(k, nullptr, qidx, work, counts, offsets, ch.nxt, H, g, NB, CT);
+    if (ch.nxt >= 0) pre.load(k, nullptr, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
     for (int tl = wave; tl < ntile; tl += kWaves) {
       put_q_tile<T, D>(qt, lane, qv);
       if (tl + kWaves < ntile) load_q_tile<T, D>(q, ridx, tl + kWaves, lane, qv);
@@ -319,26 +332,35 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   ch.finish();
 }
 
-// One thread per (token, query head): merge the per-block (max, sum) pairs of
-// the token's selecting entries, in slot order, into the row max and lse
-// (stored in natural-log units).  Slots are read 8 at a time and the pairs
-// loaded unconditionally (row 0 stands in for empty slots) so that the loads
-// are independent.
+// One thread per (token, query head): merge the token's local (max, sum) pair
+// and the per-block pairs of its other selecting entries, in slot order, into
+// the row max and lse (stored in natural-log units).  Slots are read 8 at a
+// time and the pairs loaded unconditionally (row 0 stands in for empty and
+// local slots) so that the loads are independent.
 __global__ __launch_bounds__(256) void k_stats_combine(const int32_t* __restrict__ slot,
-                                                       const float2* __restrict__ st, float* __restrict__ row_max,
-                                                       float* __restrict__ lse, int N, int H, int g, int T) {
+                                                       const float2* __restrict__ st,
+                                                       const int32_t* __restrict__ loc,
+                                                       const float2* __restrict__ st_local,
+                                                       float* __restrict__ row_max, float* __restrict__ lse, int N,
+                                                       int H, int g, int T) {
   const int HQ = H * g;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)N * HQ) return;
   const int t = (int)(idx / HQ), hq = (int)(idx - (int64_t)t * HQ);
   const int h = hq / g, j = hq - h * g;
   const int32_t* sl = slot + ((size_t)h * N + t) * T;
+  const unsigned word = (unsigned)loc[(size_t)h * N + t];
   float M = -INFINITY, L = 0.f;
+  if (word != 0u) {
+    const float2 v = st_local[idx];
+    M = v.x;
+    L = v.y;
+  }
   for (int j0 = 0; j0 < T; j0 += 8) {
     int sv[8];
     float2 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sv[u] = j0 + u < T ? sl[j0 + u] : -1;
+    for (int u = 0; u < 8; ++u) sv[u] = j0 + u < T && !local_entry(word, j0 + u) ? sl[j0 + u] : -1;
 #pragma unroll
     for (int u = 0; u < 8; ++u) v[u] = st[(size_t)max(sv[u], 0) * g + j];
 #pragma unroll
@@ -464,7 +486,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
   __shared__ int s_items[2];
-  ItemChain ch(queue, nwork[0], s_items);
+  ItemChain ch(queue, nwork[2], s_items);  // the forward list
+  const int4* const wl = work + nwork[0];
   if (ch.cur < 0) {
     ch.finish();
     return;
@@ -476,7 +499,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   PT* const stage = reinterpret_cast<PT*>(qt);
   PT* const dump = partial + dump_row * D;
   ItemStage<T, D, BK, true> pre;
-  pre.load(k, v, qidx, work, counts, offsets, ch.cur, H, g, NB, CT);
+  pre.load(k, v, qidx, wl, counts, offsets, ch.cur, H, g, NB, CT);
   while (ch.cur >= 0) {
     __syncthreads();  // the previous item's LDS reads are done
     pre.commit(Ks, Vt, ridx, rtok, g, HQ);
@@ -494,7 +517,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
       load_q_tile<T, D>(q, ridx, wave, lane, qv);
       lnext = lse[ridx[wave * 32 + lr]];
     }
-    if (ch.nxt >= 0) pre.load(k, v, qidx, work, counts, offsets, ch.nxt, H, g, NB, CT);
+    if (ch.nxt >= 0) pre.load(k, v, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
     for (int tl = wave; tl < ntile; tl += kWaves) {
       put_q_tile<T, D>(qt, lane, qv);
       const float l2 = lnext * kLog2e;
@@ -511,19 +534,236 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
       f32x16 o[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const V8 a = load8(Vt + (mt * 32 + lr) * vt_ld<BK>() + kk * 16 + hl * 8);
-          o[mt] = mfma32(a, pb[kk], o[mt]);
-        }
+      pv_tile<T, D, BK>(Vt, pb, lr, hl, o);
       store_tile<PT, D>(stage, o, lane, min(32, nrows - tl * 32),
                         partial + ((size_t)it.pair0 * g + (size_t)tl * 32) * D, dump);
     }
     ch.advance(after);
   }
   ch.finish();
+}
+
+// ---- local entries, per query block ---------------------------------------------
+// The entries of a query's own, previous and first block (its local entries)
+// are computed per query block: one workgroup per (KV head, query block, group
+// of kLocalTiles 32-row tiles of the block's rows), wave w taking tile w of the
+// group.  The block's queries are contiguous, so their Q rows are gathered
+// once and kept in registers (the B operand of S^T = K Q^T) while the block's
+// local key blocks (kinds 0 .. min(e, 2): own, previous, first) are staged in
+// LDS one after another; a row uses the key blocks its token selects (its
+// local word), the own block causally.  Statistics: the rows' (max, sum) over
+// those blocks, merged, go to one (max, sum) pair per row.  Main: the rows'
+// exp(s - lse) V over those blocks, summed in registers, go to one partial row
+// per row.  Both land at row (h N + token) g + j of a local region, so the
+// combine and the reduction read one local row instead of up to three.
+constexpr int kLocalTiles = kWaves;
+constexpr int kLocalRows = 32 * kLocalTiles;
+
+struct LocalItem {
+  int h, e, bs, ntok, seq_lo, seq_hi, row0, rows;
+};
+
+// Local item i = (KV head, global block, row group); rows = 0 when the group
+// lies past the block's rows.
+__device__ __forceinline__ LocalItem local_item(int i, const int32_t* __restrict__ cu,
+                                                const int32_t* __restrict__ gboff, int num_seqs, int NB, int BK, int g,
+                                                int groups) {
+  LocalItem it;
+  const int grp = i % groups, f = i / groups;
+  it.h = f / NB;
+  const int gb = f - it.h * NB;
+  const int sq = seq_of_block(gboff, num_seqs, gb);
+  it.e = gb - gboff[sq];
+  it.seq_lo = cu[sq];
+  it.seq_hi = cu[sq + 1];
+  it.bs = it.seq_lo + it.e * BK;
+  it.ntok = min(BK, it.seq_hi - it.bs);
+  it.row0 = grp * kLocalRows;
+  it.rows = max(0, min(kLocalRows, it.ntok * g - it.row0));
+  return it;
+}
+
+// Q / lse row of row r (within the item) of a local item; rows past the
+// item map to its first row, so that every gather stays in bounds.
+__device__ __forceinline__ int local_qrow(const LocalItem& it, int r, int g, int HQ) {
+  const int row = it.row0 + (r < it.rows ? r : 0);
+  return (it.bs + row / g) * HQ + it.h * g + row % g;
+}
+
+// The wave's Q tile of a local item (item rows 32 * wave + 0..31), in the
+// row-contiguous layout of load_q_tile.
+template <typename T, int D>
+__device__ __forceinline__ void load_q_local(const T* __restrict__ q, const LocalItem& it, int wave, int lane, int g,
+                                             int HQ, typename Vec8<T>::type* qv) {
+#pragma unroll
+  for (int v = 0; v < D / 16; ++v) {
+    const int e = (v * 64 + lane) * 8;
+    qv[v] = load8(q + (size_t)local_qrow(it, wave * 32 + e / D, g, HQ) * D + e % D);
+  }
+}
+
+// One key block of head h in registers, then in LDS: K as [key][D + 8] and,
+// WITH_V, V transposed and key-permuted as in ItemStage.  Keys past nk repeat
+// the last key (only the own block can be short, and there the causal mask
+// hides them).  load() only issues the loads, so they stay in flight while the
+// previous block computes; commit() writes them to LDS.
+template <typename T, int D, int BK, bool WITH_V>
+struct BlockStage {
+  using V8 = typename Vec8<T>::type;
+  static constexpr int C8 = D / 8, KV = BK * C8 / kAttnThreads, KP = BK / 2;
+  static constexpr int VP = WITH_V ? KP * C8 / kAttnThreads : 1;
+  V8 kr[KV], va[VP], vb[VP];
+
+  __device__ __forceinline__ void load(const T* __restrict__ kg, const T* __restrict__ vg, int H, int h, int kbs,
+                                       int nk) {
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int vi = threadIdx.x + i * kAttnThreads;
+      kr[i] = load8(kg + ((size_t)(kbs + min(vi / C8, nk - 1)) * H + h) * D + (vi % C8) * 8);
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < VP; ++i) {
+        const int vi = threadIdx.x + i * kAttnThreads;
+        const int c = vi / KP, key = 2 * (vi % KP);
+        va[i] = load8(vg + ((size_t)(kbs + min(key, nk - 1)) * H + h) * D + c * 8);
+        vb[i] = load8(vg + ((size_t)(kbs + min(key + 1, nk - 1)) * H + h) * D + c * 8);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void commit(T* __restrict__ Ks, T* __restrict__ Vt) const {
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int vi = threadIdx.x + i * kAttnThreads;
+      *reinterpret_cast<V8*>(Ks + (vi / C8) * k_ld<D>() + (vi % C8) * 8) = kr[i];
+    }
+    if constexpr (WITH_V) {
+#pragma unroll
+      for (int i = 0; i < VP; ++i) {
+        const int vi = threadIdx.x + i * kAttnThreads;
+        const int c = vi / KP, key = 2 * (vi % KP);
+        const int pos = vt_pos(key);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t packed = (uint32_t)bits16(va[i][e]) | ((uint32_t)bits16(vb[i][e]) << 16);
+          *reinterpret_cast<uint32_t*>(Vt + (c * 8 + e) * vt_ld<BK>() + pos) = packed;
+        }
+      }
+    }
+  }
+};
+
+// Visible-key limit of a row for local kind `kind`: -1 when the row's token
+// does not select that block (or the row is past the item), the key offset
+// of the token in its own block for kind 0, the whole block otherwise.
+template <int BK>
+__device__ __forceinline__ int local_lim(int tok, unsigned word, int kind, int kbs) {
+  if (tok < 0 || !local_has(word, kind)) return -1;
+  return kind == 0 ? tok - kbs : BK - 1;
+}
+
+template <typename T, int D, int BK>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_stats_local(
+    const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc, float2* __restrict__ st_local,
+    int N, int H, int g, int NB, int groups, float scale_log2) {
+  using V8 = typename Vec8<T>::type;
+  constexpr int KS = D / 16, KT = BK / 32;
+  __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
+  __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
+  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups);
+  if (it.rows == 0) return;
+  const int HQ = H * g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 31, hl = lane >> 5;
+  const bool busy = wave * 32 < it.rows;
+  T* const qt = Qt + wave * 32 * tile_ld<D>();
+  const int kinds = min(it.e, 2) + 1;
+  // every load of the item's start goes out here: the own block's K, the Q
+  // tile and the row's local word
+  BlockStage<T, D, BK, false> pre;
+  pre.load(k, nullptr, H, it.h, it.bs, it.ntok);
+  V8 qv[KS];
+  if (busy) load_q_local<T, D>(q, it, wave, lane, g, HQ, qv);
+  const int row = wave * 32 + lr;
+  const int qrow = local_qrow(it, row, g, HQ);
+  const int tok = row < it.rows ? qrow / HQ : -1;
+  const unsigned word = tok >= 0 ? (unsigned)loc[(size_t)it.h * N + tok] : 0u;
+  float M = -INFINITY, L = 0.f;
+  for (int kind = 0; kind < kinds; ++kind) {
+    const int kbs = it.seq_lo + local_block(kind, it.e) * BK;
+    __syncthreads();  // the previous block's K reads are done
+    pre.commit(Ks, nullptr);
+    __syncthreads();
+    if (kind + 1 < kinds) pre.load(k, nullptr, H, it.h, it.seq_lo + local_block(kind + 1, it.e) * BK, BK);
+    if (!busy) continue;
+    if (kind == 0) put_q_tile<T, D>(qt, lane, qv);
+    f32x16 s[KT];
+    qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
+    const int lim = local_lim<BK>(tok, word, kind, kbs);
+    const float2 ml = kind == 0 ? row_stats<BK, true>(s, hl, lim, scale_log2)
+                                : row_stats<BK, false>(s, hl, 0, scale_log2);
+    if (lim >= 0) {
+      const float mn = fmaxf(M, ml.x);
+      L = L * __builtin_amdgcn_exp2f(M - mn) + ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
+      M = mn;
+    }
+  }
+  if (busy && hl == 0 && tok >= 0) st_local[qrow] = make_float2(M, L);
+}
+
+template <typename T, int D, int BK, typename PT>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main_local(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc, const float* __restrict__ lse,
+    PT* __restrict__ local_part, PT* __restrict__ dump, int N, int H, int g, int NB, int groups, float scale_log2) {
+  using V8 = typename Vec8<T>::type;
+  constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
+  __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
+  __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
+  __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
+  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups);
+  if (it.rows == 0) return;
+  const int HQ = H * g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 31, hl = lane >> 5;
+  const bool busy = wave * 32 < it.rows;
+  T* const qt = Qt + wave * 32 * tile_ld<D>();
+  const int kinds = min(it.e, 2) + 1;
+  // every load of the item's start goes out here: the own block's K and V,
+  // the Q tile, the row's local word and lse
+  BlockStage<T, D, BK, true> pre;
+  pre.load(k, v, H, it.h, it.bs, it.ntok);
+  V8 qv[KS];
+  if (busy) load_q_local<T, D>(q, it, wave, lane, g, HQ, qv);
+  const int row = wave * 32 + lr;
+  const int qrow = local_qrow(it, row, g, HQ);
+  const int tok = row < it.rows ? qrow / HQ : -1;
+  const unsigned word = tok >= 0 ? (unsigned)loc[(size_t)it.h * N + tok] : 0u;
+  const float l2 = tok >= 0 ? lse[qrow] * kLog2e : 0.f;
+  f32x16 o[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
+  for (int kind = 0; kind < kinds; ++kind) {
+    const int kbs = it.seq_lo + local_block(kind, it.e) * BK;
+    __syncthreads();  // the previous block's K / V reads are done
+    pre.commit(Ks, Vt);
+    __syncthreads();
+    if (kind + 1 < kinds) pre.load(k, v, H, it.h, it.seq_lo + local_block(kind + 1, it.e) * BK, BK);
+    if (!busy) continue;
+    if (kind == 0) put_q_tile<T, D>(qt, lane, qv);
+    f32x16 s[KT];
+    qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
+    const int lim = local_lim<BK>(tok, word, kind, kbs);
+    V8 pb[KK];
+    if (__all(lim == BK - 1)) probs<T, BK, false>(s, scale_log2, l2, hl, 0, pb);
+    else probs<T, BK, true>(s, scale_log2, l2, hl, lim, pb);
+    pv_tile<T, D, BK>(Vt, pb, lr, hl, o);
+  }
+  if (busy)
+    store_tile<PT, D>(reinterpret_cast<PT*>(qt), o, lane, min(32, it.rows - wave * 32),
+                      local_part + ((size_t)(it.h * N + it.bs) * g + it.row0 + wave * 32) * D, dump);
 }
 
 // ---- reduce -----------------------------------------------------------------
@@ -559,11 +799,15 @@ struct Part8<_Float16> {
 
 // Items (token t, KV head h), t-major so that the outputs of consecutive items
 // are adjacent.  TPI threads per item, each owning 8-element vectors of the
-// g*D outputs.  Slots are taken 8 at a time; the 8 partial loads are issued
-// together (row 0 stands in for empty slots) and summed in slot order.
-template <typename T, typename PT>
+// g*D outputs.  With LOCAL (the forward), the sum starts from the item's local
+// partial row group and skips the local slots; the backward's dQ reduction
+// sums every slot.  Slots are taken 8 at a time; the 8 partial loads are
+// issued together (row 0 stands in for empty slots) and summed in slot order.
+template <typename T, typename PT, bool LOCAL>
 __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __restrict__ slot,
-                                                           const PT* __restrict__ partial, T* __restrict__ out,
+                                                           const PT* __restrict__ partial,
+                                                           const int32_t* __restrict__ loc,
+                                                           const PT* __restrict__ local_part, T* __restrict__ out,
                                                            int N, int H, int g, int D, int Tn, int TPI) {
   const int ipb = kReduceThreads / TPI;
   const int local = threadIdx.x / TPI;
@@ -574,14 +818,20 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __rest
   const int sub = threadIdx.x - local * TPI;
   const int GD = g * D, nvec = GD / 8;
   const int32_t* sl = slot + ((size_t)h * N + t) * Tn;
+  const unsigned word = LOCAL ? (unsigned)loc[(size_t)h * N + t] : 0u;
   T* dst = out + ((size_t)t * H + h) * GD;
   for (int vec = sub; vec < nvec; vec += TPI) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (LOCAL && word != 0u) {
+      const auto x = Part8<PT>::load(local_part + ((size_t)h * N + t) * GD + vec * 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = Part8<PT>::at(x, i);
+    }
     for (int j0 = 0; j0 < Tn; j0 += 8) {
       int sv[8];
       typename Part8<PT>::type x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sv[u] = j0 + u < Tn ? sl[j0 + u] : -1;
+      for (int u = 0; u < 8; ++u) sv[u] = j0 + u < Tn && !(LOCAL && local_entry(word, j0 + u)) ? sl[j0 + u] : -1;
 #pragma unroll
       for (int u = 0; u < 8; ++u) x[u] = Part8<PT>::load(partial + (size_t)max(sv[u], 0) * GD + vec * 8);
 #pragma unroll
@@ -605,124 +855,166 @@ struct Ptrs {
   const int4* work;
   const int32_t* nwork;
   int32_t* queue;
+  const int32_t* gboff;
+  const int32_t* loc;
 };
 
 inline Ptrs<int> index_ptrs(const Geometry& geo, const fsa_index& idx) {
-  const char* aux = static_cast<const char*>(idx.aux);
-  return Ptrs<int>{idx.counts, idx.offsets, idx.qidx, reinterpret_cast<const int4*>(aux + geo.aux_work_sorted),
+  char* aux = static_cast<char*>(idx.aux);
+  return Ptrs<int>{idx.counts,
+                   idx.offsets,
+                   idx.qidx,
+                   reinterpret_cast<const int4*>(aux + geo.aux_work_sorted),
                    reinterpret_cast<const int32_t*>(aux + geo.aux_nwork),
-                   reinterpret_cast<int32_t*>(static_cast<char*>(idx.aux) + geo.aux_queue)};
+                   reinterpret_cast<int32_t*>(aux + geo.aux_queue),
+                   reinterpret_cast<const int32_t*>(aux + geo.aux_seq_gboff),
+                   reinterpret_cast<const int32_t*>(aux + geo.aux_loc)};
 }
 
+// Workgroups of the local kernels, one per item (KV head, global block, row group).
+inline unsigned local_grid(const Geometry& geo, int* groups) {
+  *groups = (geo.BK * geo.g + kLocalRows - 1) / kLocalRows;
+  return (unsigned)((int64_t)geo.H * geo.NB * *groups);
+}
 
 template <typename T, int D, int BK>
-void stats_typed(const Geometry& geo, const void* q, const void* k, const fsa_index& idx, float2* st,
-                 hipStream_t stream) {
+void stats_typed(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const fsa_index& idx,
+                 void* ws, hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
-  hipLaunchKernelGGL((k_stats<T, D, BK>), dim3(persistent_grid(k_stats<T, D, BK>, kAttnThreads, geo.max_work)), dim3(kAttnThreads), 0, stream,
-                     static_cast<const T*>(q), static_cast<const T*>(k), p.counts, p.offsets, p.qidx, p.work, p.nwork,
-                     p.queue, st, (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
+  float2* st = static_cast<float2*>(ws);
+  float2* st_local = reinterpret_cast<float2*>(static_cast<char*>(ws) + geo.stats_local_off);
+  if (geo.max_work > 0)
+    hipLaunchKernelGGL((k_stats<T, D, BK>), dim3(persistent_grid(k_stats<T, D, BK>, kAttnThreads, geo.max_work)),
+                       dim3(kAttnThreads), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k), p.counts,
+                       p.offsets, p.qidx, p.work, p.nwork, p.queue, st, (size_t)geo.dump_row, geo.H, geo.g, geo.NB,
+                       geo.chunk_tokens, sl2);
+  if (!geo.local) return;
+  int groups = 0;
+  const unsigned grid = local_grid(geo, &groups);
+  hipLaunchKernelGGL((k_stats_local<T, D, BK>), dim3(grid), dim3(kAttnThreads), 0, stream, static_cast<const T*>(q),
+                     static_cast<const T*>(k), cu, p.gboff, geo.num_seqs, p.loc, st_local, geo.N, geo.H, geo.g,
+                     geo.NB, groups, sl2);
 }
 
 template <typename T, int D, int BK, typename PT>
-void main_typed(const Geometry& geo, const void* q, const void* k, const void* v, const fsa_index& idx,
-                const float* lse, void* partial, hipStream_t stream) {
+void main_typed(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v,
+                const fsa_index& idx, const float* lse, void* partial, hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
-  hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3(persistent_grid(k_main<T, D, BK, PT>, kAttnThreads, geo.max_work)), dim3(kAttnThreads), 0, stream,
-                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), p.counts,
-                     p.offsets, p.qidx, p.work, p.nwork, p.queue + kQueueInts, lse, static_cast<PT*>(partial), (size_t)geo.dump_row, geo.H,
-                     geo.g, geo.NB, geo.chunk_tokens, sl2);
+  PT* const dump = static_cast<PT*>(partial) + geo.dump_row * geo.d;
+  if (geo.max_work > 0)
+    hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3(persistent_grid(k_main<T, D, BK, PT>, kAttnThreads, geo.max_work)),
+                       dim3(kAttnThreads), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), p.counts, p.offsets, p.qidx, p.work, p.nwork, p.queue + kQueueInts,
+                       lse, static_cast<PT*>(partial), (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens,
+                       sl2);
+  if (!geo.local) return;
+  int groups = 0;
+  const unsigned grid = local_grid(geo, &groups);
+  PT* const local_part = reinterpret_cast<PT*>(static_cast<char*>(partial) + geo.partial_local_off);
+  hipLaunchKernelGGL((k_main_local<T, D, BK, PT>), dim3(grid), dim3(kAttnThreads), 0, stream,
+                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), cu, p.gboff,
+                     geo.num_seqs, p.loc, lse, local_part, dump, geo.N, geo.H, geo.g, geo.NB, groups, sl2);
 }
 
 template <typename T, typename PT>
-void reduce_typed(const Geometry& geo, const fsa_index& idx, const void* partial, void* out, hipStream_t stream) {
+void reduce_typed(const Geometry& geo, const fsa_index& idx, const void* partial, void* out, bool local,
+                  hipStream_t stream) {
   const int nvec = geo.g * geo.d / 8;
   const int tpi = nvec < kReduceThreads ? nvec : kReduceThreads;
   const int ipb = kReduceThreads / tpi;
   const int64_t items = (int64_t)geo.N * geo.H;
   const unsigned blocks = (unsigned)((items + ipb - 1) / ipb);
-  hipLaunchKernelGGL((k_reduce<T, PT>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot,
-                     static_cast<const PT*>(partial), static_cast<T*>(out), geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+  const PT* const part = static_cast<const PT*>(partial);
+  if (local) {
+    const auto p = index_ptrs(geo, idx);
+    const PT* const local_part =
+        reinterpret_cast<const PT*>(static_cast<const char*>(partial) + geo.partial_local_off);
+    hipLaunchKernelGGL((k_reduce<T, PT, true>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot, part, p.loc,
+                       local_part, static_cast<T*>(out), geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+  } else {
+    hipLaunchKernelGGL((k_reduce<T, PT, false>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot, part,
+                       nullptr, nullptr, static_cast<T*>(out), geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+  }
 }
 
 template <typename T, int BK>
-void stats_d(const Geometry& geo, const void* q, const void* k, const fsa_index& idx, float2* st,
+void stats_d(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const fsa_index& idx, void* ws,
              hipStream_t s) {
   switch (geo.d) {
-    case 64: stats_typed<T, 64, BK>(geo, q, k, idx, st, s); break;
-    case 128: stats_typed<T, 128, BK>(geo, q, k, idx, st, s); break;
+    case 64: stats_typed<T, 64, BK>(geo, cu, q, k, idx, ws, s); break;
+    case 128: stats_typed<T, 128, BK>(geo, cu, q, k, idx, ws, s); break;
     default:
-      if constexpr (BK == 64) stats_typed<T, 256, BK>(geo, q, k, idx, st, s);
+      if constexpr (BK == 64) stats_typed<T, 256, BK>(geo, cu, q, k, idx, ws, s);
       break;
   }
 }
 
 template <typename T, int BK, typename PT>
-void main_d(const Geometry& geo, const void* q, const void* k, const void* v, const fsa_index& idx,
+void main_d(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v, const fsa_index& idx,
             const float* lse, void* partial, hipStream_t s) {
   switch (geo.d) {
-    case 64: main_typed<T, 64, BK, PT>(geo, q, k, v, idx, lse, partial, s); break;
-    case 128: main_typed<T, 128, BK, PT>(geo, q, k, v, idx, lse, partial, s); break;
+    case 64: main_typed<T, 64, BK, PT>(geo, cu, q, k, v, idx, lse, partial, s); break;
+    case 128: main_typed<T, 128, BK, PT>(geo, cu, q, k, v, idx, lse, partial, s); break;
     default:
-      if constexpr (BK == 64) main_typed<T, 256, BK, PT>(geo, q, k, v, idx, lse, partial, s);
+      if constexpr (BK == 64) main_typed<T, 256, BK, PT>(geo, cu, q, k, v, idx, lse, partial, s);
       break;
   }
 }
 
 template <typename T, typename PT>
-void main_bk(const Geometry& geo, const void* q, const void* k, const void* v, const fsa_index& idx,
-             const float* lse, void* partial, hipStream_t s) {
-  if (geo.BK == 64) main_d<T, 64, PT>(geo, q, k, v, idx, lse, partial, s);
-  else main_d<T, 128, PT>(geo, q, k, v, idx, lse, partial, s);
+void main_bk(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v,
+             const fsa_index& idx, const float* lse, void* partial, hipStream_t s) {
+  if (geo.BK == 64) main_d<T, 64, PT>(geo, cu, q, k, v, idx, lse, partial, s);
+  else main_d<T, 128, PT>(geo, cu, q, k, v, idx, lse, partial, s);
 }
 
 }  // namespace
 
-hipError_t launch_stats(const Geometry& geo, const void* q, const void* k, const fsa_index& idx, float* row_max,
-                        float* lse, void* ws, hipStream_t stream) {
+hipError_t launch_stats(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k,
+                        const fsa_index& idx, float* row_max, float* lse, void* ws, hipStream_t stream) {
   if (geo.N == 0) return hipSuccess;
-  float2* st = static_cast<float2*>(ws);
-  if (geo.max_work > 0) {
-    if (geo.dtype == FSA_DTYPE_BF16) {
-      if (geo.BK == 64) stats_d<__bf16, 64>(geo, q, k, idx, st, stream);
-      else stats_d<__bf16, 128>(geo, q, k, idx, st, stream);
-    } else {
-      if (geo.BK == 64) stats_d<_Float16, 64>(geo, q, k, idx, st, stream);
-      else stats_d<_Float16, 128>(geo, q, k, idx, st, stream);
-    }
+  if (geo.dtype == FSA_DTYPE_BF16) {
+    if (geo.BK == 64) stats_d<__bf16, 64>(geo, cu_dev, q, k, idx, ws, stream);
+    else stats_d<__bf16, 128>(geo, cu_dev, q, k, idx, ws, stream);
+  } else {
+    if (geo.BK == 64) stats_d<_Float16, 64>(geo, cu_dev, q, k, idx, ws, stream);
+    else stats_d<_Float16, 128>(geo, cu_dev, q, k, idx, ws, stream);
   }
+  const auto p = index_ptrs(geo, idx);
   const int64_t n = (int64_t)geo.N * geo.HQ;
-  hipLaunchKernelGGL(k_stats_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, idx.slot, st, row_max,
-                     lse, geo.N, geo.H, geo.g, geo.T);
+  hipLaunchKernelGGL(k_stats_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, idx.slot,
+                     static_cast<const float2*>(ws), p.loc,
+                     reinterpret_cast<const float2*>(static_cast<const char*>(ws) + geo.stats_local_off), row_max, lse,
+                     geo.N, geo.H, geo.g, geo.T);
   return hipGetLastError();
 }
 
-hipError_t launch_main(const Geometry& geo, const void* q, const void* k, const void* v, const fsa_index& idx,
-                       const float* lse, void* partial, hipStream_t stream) {
-  if (geo.N == 0 || geo.max_work == 0) return hipSuccess;
+hipError_t launch_main(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
+                       const fsa_index& idx, const float* lse, void* partial, hipStream_t stream) {
+  if (geo.N == 0) return hipSuccess;
   const bool p32 = geo.partial_dtype == FSA_PARTIAL_FP32;
   if (geo.dtype == FSA_DTYPE_BF16) {
-    if (p32) main_bk<__bf16, float>(geo, q, k, v, idx, lse, partial, stream);
-    else main_bk<__bf16, __bf16>(geo, q, k, v, idx, lse, partial, stream);
+    if (p32) main_bk<__bf16, float>(geo, cu_dev, q, k, v, idx, lse, partial, stream);
+    else main_bk<__bf16, __bf16>(geo, cu_dev, q, k, v, idx, lse, partial, stream);
   } else {
-    if (p32) main_bk<_Float16, float>(geo, q, k, v, idx, lse, partial, stream);
-    else main_bk<_Float16, _Float16>(geo, q, k, v, idx, lse, partial, stream);
+    if (p32) main_bk<_Float16, float>(geo, cu_dev, q, k, v, idx, lse, partial, stream);
+    else main_bk<_Float16, _Float16>(geo, cu_dev, q, k, v, idx, lse, partial, stream);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_reduce(const Geometry& geo, const fsa_index& idx, const void* partial, void* out,
+hipError_t launch_reduce(const Geometry& geo, const fsa_index& idx, const void* partial, void* out, bool local,
                          hipStream_t stream) {
   if (geo.N == 0) return hipSuccess;
   const bool p32 = geo.partial_dtype == FSA_PARTIAL_FP32;
   if (geo.dtype == FSA_DTYPE_BF16) {
-    if (p32) reduce_typed<__bf16, float>(geo, idx, partial, out, stream);
-    else reduce_typed<__bf16, __bf16>(geo, idx, partial, out, stream);
+    if (p32) reduce_typed<__bf16, float>(geo, idx, partial, out, local, stream);
+    else reduce_typed<__bf16, __bf16>(geo, idx, partial, out, local, stream);
   } else {
-    if (p32) reduce_typed<_Float16, float>(geo, idx, partial, out, stream);
-    else reduce_typed<_Float16, _Float16>(geo, idx, partial, out, stream);
+    if (p32) reduce_typed<_Float16, float>(geo, idx, partial, out, local, stream);
+    else reduce_typed<_Float16, _Float16>(geo, idx, partial, out, local, stream);
   }
   return hipGetLastError();
 }

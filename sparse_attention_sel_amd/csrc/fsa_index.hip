@@ -15,18 +15,27 @@
 //
 // Integer atomics only count (their result does not depend on order); ranks
 // come from per-step bit masks, so the output is bit-exact and deterministic.
+#include <algorithm>
+
 #include "fsa_internal.h"
 
 namespace fsa {
 namespace {
 
 // ---- seq_table ------------------------------------------------------------
+// Every workgroup clears its share of the work-queue counters and of the
+// per-segment local counts (which k_hist accumulates); workgroup 0 also
+// builds the per-sequence block offsets.
 __global__ __launch_bounds__(kBuildThreads) void k_seq_table(const int32_t* __restrict__ cu, int num_seqs,
                                                              int BK, int32_t* __restrict__ gboff,
-                                                             int32_t* __restrict__ queue) {
+                                                             int32_t* __restrict__ queue,
+                                                             int32_t* __restrict__ nloc, int M) {
   __shared__ int buf[kBuildThreads];
   const int tid = threadIdx.x;
-  for (int i = tid; i < kQueueKinds * kQueueInts; i += kBuildThreads) queue[i] = 0;
+  for (int i = blockIdx.x * kBuildThreads + tid; i < kQueueKinds * kQueueInts; i += gridDim.x * kBuildThreads)
+    queue[i] = 0;
+  for (int i = blockIdx.x * kBuildThreads + tid; i < M; i += gridDim.x * kBuildThreads) nloc[i] = 0;
+  if (blockIdx.x != 0) return;
   int carry = 0;
   for (int base = 0; base < num_seqs; base += kBuildThreads) {
     const int s = base + tid;
@@ -65,28 +74,36 @@ __device__ __forceinline__ TileWindow tile_window(const int32_t* __restrict__ cu
 }
 
 // ---- hist -------------------------------------------------------------------
-// grid (ntiles, H); dynamic LDS: win_max ints of histogram, then a staging
-// buffer of kHistStage ints for the Sel rows of kHistStage / T tokens at a time
-// (the first-occurrence check reads earlier entries of the row from LDS).
+// grid (ntiles, H); dynamic LDS: win_max ints of histogram, win_max ints of
+// local counts, then a staging buffer of kHistStage ints for the Sel rows of
+// kHistStage / T tokens at a time (the first-occurrence check reads earlier
+// entries of the row from LDS) and kHistStage local words.
+// Besides the tile histogram it writes each token's local word and adds, for
+// every block e >= 1, the number of local entries (tokens of blocks e and e + 1
+// selecting e) to nloc; those are the first entries of the block's query list.
 constexpr int kHistStage = 4096;
 
 __global__ __launch_bounds__(kBuildThreads) void k_hist(const int32_t* __restrict__ sel,
                                                         const int32_t* __restrict__ cu,
                                                         const int32_t* __restrict__ gboff, int num_seqs, int N,
                                                         int T, int BK, int TT, int ntiles, int NB, int win_max,
-                                                        int32_t* __restrict__ tile_hist) {
+                                                        int32_t* __restrict__ tile_hist, int32_t* __restrict__ loc,
+                                                        int32_t* __restrict__ nloc, int use_local) {
   extern __shared__ int lds[];
   int* hist = lds;
-  int* rows = lds + win_max;
+  int* lhist = lds + win_max;
+  int* rows = lds + 2 * win_max;
+  unsigned* lword = reinterpret_cast<unsigned*>(lds + 2 * win_max + kHistStage);
   const int tile = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const TileWindow w = tile_window(cu, gboff, num_seqs, N, TT, BK, tile);
-  for (int i = tid; i < w.win; i += kBuildThreads) hist[i] = 0;
+  for (int i = tid; i < w.win; i += kBuildThreads) hist[i] = lhist[i] = 0;
   const int chunk = max(1, kHistStage / T);  // tokens per staging round
   for (int c0 = w.t_lo; c0 < w.t_hi; c0 += chunk) {
     const int nt = min(chunk, w.t_hi - c0);
     const int32_t* src = sel + ((size_t)h * N + c0) * T;
-    __syncthreads();  // previous round's reads done (and the histogram zeroed)
+    __syncthreads();  // previous round's reads done (and the histograms zeroed)
     for (int i = tid; i < nt * T; i += kBuildThreads) rows[i] = src[i];
+    for (int i = tid; i < nt; i += kBuildThreads) lword[i] = 0u;
     __syncthreads();
     for (int i = tid; i < nt * T; i += kBuildThreads) {
       const int tl = i / T, j = i - tl * T;
@@ -95,16 +112,27 @@ __global__ __launch_bounds__(kBuildThreads) void k_hist(const int32_t* __restric
       const int e = row[j];
       if (e < 0) continue;
       const int s = seq_of_token(cu, num_seqs, t);
-      if (e > (t - cu[s]) / BK) continue;
+      const int own = (t - cu[s]) / BK;
+      if (e > own) continue;
       bool dup = false;
       for (int jj = 0; jj < j; ++jj) dup |= (row[jj] == e);
       if (dup) continue;
       atomicAdd(&hist[gboff[s] + e - w.gb_lo], 1);
+      const int kind = use_local ? local_kind(e, own) : -1;
+      if (kind >= 0) {
+        atomicOr(&lword[tl], (unsigned)(j + 1) << (9 * kind));
+        if (kind < 2 && e > 0) atomicAdd(&lhist[gboff[s] + e - w.gb_lo], 1);
+      }
     }
+    __syncthreads();
+    for (int i = tid; i < nt; i += kBuildThreads) loc[(size_t)h * N + c0 + i] = (int32_t)lword[i];
   }
   __syncthreads();
   int32_t* out = tile_hist + ((size_t)h * ntiles + tile) * NB + w.gb_lo;
-  for (int i = tid; i < w.win; i += kBuildThreads) out[i] = hist[i];
+  for (int i = tid; i < w.win; i += kBuildThreads) {
+    out[i] = hist[i];
+    if (lhist[i] != 0) atomicAdd(&nloc[(size_t)h * NB + w.gb_lo + i], lhist[i]);
+  }
 }
 
 // ---- tile_scan --------------------------------------------------------------
@@ -157,10 +185,13 @@ __global__ __launch_bounds__(kBuildThreads) void k_tile_scan(int32_t* __restrict
   if (active && seg == 0) counts[idx] = total;
 }
 
-// ---- offsets + work list ------------------------------------------------------
+// ---- offsets + work-list bases ------------------------------------------------
 // One workgroup.  Exclusive scan of counts (-> offsets) and of the number of
-// query chunks per segment (-> work-item positions), both in one 64-bit scan:
-// high word = pair count, low word = chunk count (neither total reaches 2^32).
+// query chunks per segment (-> the segment's first work item, cb_full), both
+// in one 64-bit scan: high word = pair count, low word = chunk count (neither
+// total reaches 2^32).  A second scan gives the forward list's bases (cb_fwd):
+// its chunks of a segment start after the segment's local entries.  The items
+// themselves are derived from these bases by the work-order kernels.
 __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t x) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -173,59 +204,84 @@ __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t x) {
 
 constexpr int kScanItems = 4;
 
-__global__ __launch_bounds__(kScanThreads) void k_offsets(const int32_t* __restrict__ counts, int M,
-                                                          int CT, const int32_t* __restrict__ cu,
+// Local entries at the head of segment f with `count` entries: all of them for
+// the first block of a sequence (every query's first block), else the count
+// k_hist gathered (queries of the block and of the next one); none when the
+// problem does not use the local path.
+__device__ __forceinline__ int segment_local(int f, int count, const int32_t* __restrict__ nloc,
+                                             const int32_t* __restrict__ cu, const int32_t* __restrict__ gboff,
+                                             int num_seqs, int NB, int BK, int use_local) {
+  if (count == 0 || !use_local) return 0;
+  const int gb = f % NB;
+  const int s = seq_of_block(gboff, num_seqs, gb);
+  return gb == gboff[s] ? count : min(count, nloc[f]);
+}
+
+__global__ __launch_bounds__(kScanThreads) void k_offsets(const int32_t* __restrict__ counts,
+                                                          const int32_t* __restrict__ nloc, int M, int CT,
+                                                          const int32_t* __restrict__ cu,
                                                           const int32_t* __restrict__ gboff, int num_seqs,
                                                           int NB, int BK, int32_t* __restrict__ offsets,
-                                                          int4* __restrict__ work, int32_t* __restrict__ nwork,
-                                                          int32_t* __restrict__ buckets, int nbuckets) {
-  __shared__ int64_t wave_tot[kScanThreads / 64];
+                                                          int32_t* __restrict__ cb_full,
+                                                          int32_t* __restrict__ cb_fwd, int32_t* __restrict__ nwork,
+                                                          int32_t* __restrict__ buckets, int nbuckets, int use_local) {
+  __shared__ int64_t wave_tot[2][kScanThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int b = tid; b < nbuckets; b += kScanThreads) buckets[b] = 0;
-  int64_t carry = 0;
+  for (int b = tid; b < 2 * nbuckets; b += kScanThreads) buckets[b] = 0;
+  int64_t carry = 0, carry_f = 0;
   for (int base = 0; base < M; base += kScanThreads * kScanItems) {
-    int c[kScanItems];
-    int64_t local = 0;
+    int c[kScanItems], cf[kScanItems];
+    int64_t local = 0, local_f = 0;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
       const int f = base + tid * kScanItems + i;
       c[i] = f < M ? counts[f] : 0;
+      cf[i] = c[i] - segment_local(f, c[i], nloc, cu, gboff, num_seqs, NB, BK, use_local);
       local += ((int64_t)c[i] << 32) + (c[i] + CT - 1) / CT;
+      local_f += (cf[i] + CT - 1) / CT;
     }
     const int64_t incl = wave_inclusive_scan(local);
-    if (lane == 63) wave_tot[wave] = incl;
+    const int64_t incl_f = wave_inclusive_scan(local_f);
+    if (lane == 63) {
+      wave_tot[0][wave] = incl;
+      wave_tot[1][wave] = incl_f;
+    }
     __syncthreads();
-    int64_t before = 0, total = 0;
+    int64_t before = 0, total = 0, before_f = 0, total_f = 0;
     for (int w = 0; w < kScanThreads / 64; ++w) {
-      const int64_t t = wave_tot[w];
-      if (w < wave) before += t;
+      const int64_t t = wave_tot[0][w], tf = wave_tot[1][w];
+      if (w < wave) {
+        before += t;
+        before_f += tf;
+      }
       total += t;
+      total_f += tf;
     }
     int64_t run = carry + before + incl - local;
+    int64_t run_f = carry_f + before_f + incl_f - local_f;
 #pragma unroll
     for (int i = 0; i < kScanItems; ++i) {
       const int f = base + tid * kScanItems + i;
       if (f < M) {
         offsets[f] = (int32_t)(run >> 32);
-        const int nch = (c[i] + CT - 1) / CT;
-        if (nch > 0) {
-          const int gb = f % NB;
-          const int s = seq_of_block(gboff, num_seqs, gb);
-          const int bs = cu[s] + (gb - gboff[s]) * BK;
-          const int se = cu[s + 1];
-          int4* wp = work + (uint32_t)run;
-          for (int ch = 0; ch < nch; ++ch) wp[ch] = make_int4(f, ch * CT, bs, se);
-        }
+        cb_full[f] = (int32_t)(uint32_t)run;
+        cb_fwd[f] = (int32_t)run_f;
         run += ((int64_t)c[i] << 32) + (c[i] + CT - 1) / CT;
+        run_f += (cf[i] + CT - 1) / CT;
       }
     }
     carry += total;
+    carry_f += total_f;
     __syncthreads();
   }
   if (tid == 0) {
     offsets[M] = (int32_t)(carry >> 32);
+    cb_full[M] = (int32_t)(uint32_t)carry;
+    cb_fwd[M] = (int32_t)carry_f;
     nwork[0] = (int32_t)(uint32_t)carry;
     nwork[1] = (int32_t)(carry >> 32);
+    nwork[2] = (int32_t)carry_f;
+    nwork[3] = 0;
   }
 }
 
@@ -312,14 +368,51 @@ __device__ __forceinline__ int work_key(const int4& it, const int32_t* __restric
   return (it.x / NB) * nbh + (qidx[offsets[it.x] + it.y] >> shift);
 }
 
-__global__ __launch_bounds__(kBuildThreads) void k_work_count(const int4* __restrict__ work,
-                                                              const int32_t* __restrict__ nwork,
-                                                              const int32_t* __restrict__ qidx,
-                                                              const int32_t* __restrict__ offsets, int NB, int shift,
-                                                              int nbh, int32_t* __restrict__ buckets) {
-  const int w = blockIdx.x * kBuildThreads + threadIdx.x;
-  if (w >= nwork[0]) return;
-  atomicAdd(&buckets[work_key(work[w], qidx, offsets, NB, shift, nbh)], 1);
+// Item w of the two lists: the full list's items come first (nwork[0] of them,
+// buckets [0, nbuckets)), then the forward list's (nwork[2], buckets
+// [nbuckets, 2 nbuckets)), so one scan of both bucket arrays places the
+// forward list right after the full one.  An item's segment is the last f with
+// cb[f] <= its index in the list (binary search); its chunk starts at
+// (index - cb[f]) * CT queries, after the local entries in the forward list.
+struct ListArgs {
+  const int32_t* counts;
+  const int32_t* nloc;
+  const int32_t* cb_full;
+  const int32_t* cb_fwd;
+  const int32_t* nwork;
+  const int32_t* cu;
+  const int32_t* gboff;
+  int num_seqs, M, NB, BK, CT, nbuckets, use_local;
+};
+
+__device__ __forceinline__ bool list_item(const ListArgs& a, int w, int4* it, int* bucket0) {
+  const int nfull = a.nwork[0];
+  const bool fwd = w >= nfull;
+  if (fwd) w -= nfull;
+  if (w >= (fwd ? a.nwork[2] : nfull)) return false;
+  const int32_t* cb = fwd ? a.cb_fwd : a.cb_full;
+  int lo = 0, hi = a.M;  // last f in [lo, hi) with cb[f] <= w
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cb[mid] <= w) lo = mid; else hi = mid;
+  }
+  const int f = lo;
+  const int gb = f % a.NB;
+  const int s = seq_of_block(a.gboff, a.num_seqs, gb);
+  const int first =
+      fwd ? segment_local(f, a.counts[f], a.nloc, a.cu, a.gboff, a.num_seqs, a.NB, a.BK, a.use_local) : 0;
+  *it = make_int4(f, first + (w - cb[f]) * a.CT, a.cu[s] + (gb - a.gboff[s]) * a.BK, a.cu[s + 1]);
+  *bucket0 = fwd ? a.nbuckets : 0;
+  return true;
+}
+
+__global__ __launch_bounds__(kBuildThreads) void k_work_count(ListArgs a, const int32_t* __restrict__ qidx,
+                                                              const int32_t* __restrict__ offsets, int shift, int nbh,
+                                                              int32_t* __restrict__ buckets) {
+  int4 it;
+  int b0;
+  if (!list_item(a, blockIdx.x * kBuildThreads + threadIdx.x, &it, &b0)) return;
+  atomicAdd(&buckets[b0 + work_key(it, qidx, offsets, a.NB, shift, nbh)], 1);
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_bucket_scan(int32_t* __restrict__ buckets, int nbuckets) {
@@ -355,16 +448,14 @@ __global__ __launch_bounds__(kScanThreads) void k_bucket_scan(int32_t* __restric
   }
 }
 
-__global__ __launch_bounds__(kBuildThreads) void k_work_place(const int4* __restrict__ work,
-                                                              const int32_t* __restrict__ nwork,
-                                                              const int32_t* __restrict__ qidx,
-                                                              const int32_t* __restrict__ offsets, int NB, int shift,
-                                                              int nbh, int32_t* __restrict__ buckets,
+__global__ __launch_bounds__(kBuildThreads) void k_work_place(ListArgs a, const int32_t* __restrict__ qidx,
+                                                              const int32_t* __restrict__ offsets, int shift, int nbh,
+                                                              int32_t* __restrict__ buckets,
                                                               int4* __restrict__ work_out) {
-  const int w = blockIdx.x * kBuildThreads + threadIdx.x;
-  if (w >= nwork[0]) return;
-  const int4 it = work[w];
-  work_out[atomicAdd(&buckets[work_key(it, qidx, offsets, NB, shift, nbh)], 1)] = it;
+  int4 it;
+  int b0;
+  if (!list_item(a, blockIdx.x * kBuildThreads + threadIdx.x, &it, &b0)) return;
+  work_out[atomicAdd(&buckets[b0 + work_key(it, qidx, offsets, a.NB, shift, nbh)], 1)] = it;
 }
 
 }  // namespace
@@ -374,26 +465,34 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
   char* aux = static_cast<char*>(idx.aux);
   int32_t* gboff = reinterpret_cast<int32_t*>(aux + geo.aux_seq_gboff);
   int32_t* nwork = reinterpret_cast<int32_t*>(aux + geo.aux_nwork);
-  int4* work = reinterpret_cast<int4*>(aux + geo.aux_work);
+  int32_t* loc = reinterpret_cast<int32_t*>(aux + geo.aux_loc);
+  int32_t* nloc = reinterpret_cast<int32_t*>(aux + geo.aux_nloc);
   int4* work_sorted = reinterpret_cast<int4*>(aux + geo.aux_work_sorted);
-  int32_t* tile_hist = static_cast<int32_t*>(ws);
-  int32_t* buckets = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + geo.build_ws_buckets);
+  char* wsb = static_cast<char*>(ws);
+  int32_t* tile_hist = reinterpret_cast<int32_t*>(wsb);
+  int32_t* buckets = reinterpret_cast<int32_t*>(wsb + geo.build_ws_buckets);
+  int32_t* cb_full = reinterpret_cast<int32_t*>(wsb + geo.build_ws_cb);
   const int M = geo.H * geo.NB;
+  int32_t* cb_fwd = cb_full + (M + 1);
+  const int nbk = geo.N > 0 ? geo.sort_buckets : 0;
+  const int NB1 = geo.NB > 0 ? geo.NB : 1;
 
-  hipLaunchKernelGGL(k_seq_table, dim3(1), dim3(kBuildThreads), 0, stream, cu_dev, geo.num_seqs, geo.BK, gboff,
-                     reinterpret_cast<int32_t*>(aux + geo.aux_queue));
+  const unsigned zero_wg = (unsigned)std::min<int64_t>(64, (int64_t)M / (4 * kBuildThreads) + 1);
+  hipLaunchKernelGGL(k_seq_table, dim3(zero_wg), dim3(kBuildThreads), 0, stream, cu_dev, geo.num_seqs, geo.BK, gboff,
+                     reinterpret_cast<int32_t*>(aux + geo.aux_queue), nloc, M);
   if (geo.N > 0) {
     hipLaunchKernelGGL(k_hist, dim3(geo.ntiles, geo.H), dim3(kBuildThreads),
-                       (geo.win_max + kHistStage) * sizeof(int), stream, sel, cu_dev, gboff, geo.num_seqs, geo.N, geo.T,
-                       geo.BK, geo.tile_tokens, geo.ntiles, geo.NB, geo.win_max, tile_hist);
+                       (2 * geo.win_max + 2 * kHistStage) * sizeof(int), stream, sel, cu_dev, gboff, geo.num_seqs,
+                       geo.N, geo.T, geo.BK, geo.tile_tokens, geo.ntiles, geo.NB, geo.win_max, tile_hist, loc, nloc,
+                       (int)geo.local);
     constexpr int cols = kBuildThreads / kScanSegs;
     hipLaunchKernelGGL(k_tile_scan, dim3((M + cols - 1) / cols), dim3(kBuildThreads), 0, stream,
                        tile_hist, cu_dev, gboff, geo.num_seqs, geo.H, geo.NB, geo.BK, geo.tile_tokens, geo.ntiles,
                        idx.counts);
   }
-  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(kScanThreads), 0, stream, idx.counts, M, geo.chunk_tokens, cu_dev,
-                     gboff, geo.num_seqs, geo.NB > 0 ? geo.NB : 1, geo.BK, idx.offsets, work, nwork, buckets,
-                     geo.N > 0 ? geo.sort_buckets : 0);
+  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(kScanThreads), 0, stream, idx.counts, nloc, M, geo.chunk_tokens, cu_dev,
+                     gboff, geo.num_seqs, NB1, geo.BK, idx.offsets, cb_full, cb_fwd, nwork, buckets, nbk,
+                     (int)geo.local);
   if (geo.N > 0) {
     int Tp = 1;
     while (Tp < geo.T) Tp <<= 1;
@@ -402,13 +501,15 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
     hipLaunchKernelGGL(k_scatter, dim3(geo.ntiles, geo.H), dim3(kBuildThreads), lds, stream, sel, cu_dev, gboff,
                        geo.num_seqs, geo.N, geo.T, Tp, tps, geo.BK, geo.tile_tokens, geo.ntiles, geo.NB, geo.win_max,
                        tile_hist, idx.offsets, idx.qidx, idx.slot);
-    const unsigned wg = (unsigned)((geo.max_work + kBuildThreads - 1) / kBuildThreads);
-    if (wg > 0) {
-      hipLaunchKernelGGL(k_work_count, dim3(wg), dim3(kBuildThreads), 0, stream, work, nwork, idx.qidx, idx.offsets,
-                         geo.NB, geo.sort_shift, geo.sort_buckets_per_head, buckets);
-      hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(kScanThreads), 0, stream, buckets, geo.sort_buckets);
-      hipLaunchKernelGGL(k_work_place, dim3(wg), dim3(kBuildThreads), 0, stream, work, nwork, idx.qidx, idx.offsets,
-                         geo.NB, geo.sort_shift, geo.sort_buckets_per_head, buckets, work_sorted);
+    if (geo.max_work > 0) {
+      const ListArgs la{idx.counts, nloc, cb_full, cb_fwd, nwork, cu_dev, gboff, geo.num_seqs, M, NB1, geo.BK,
+                        geo.chunk_tokens, nbk, (int)geo.local};
+      const unsigned wg = (unsigned)((2 * geo.max_work + kBuildThreads - 1) / kBuildThreads);
+      hipLaunchKernelGGL(k_work_count, dim3(wg), dim3(kBuildThreads), 0, stream, la, idx.qidx, idx.offsets,
+                         geo.sort_shift, geo.sort_buckets_per_head, buckets);
+      hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(kScanThreads), 0, stream, buckets, 2 * nbk);
+      hipLaunchKernelGGL(k_work_place, dim3(wg), dim3(kBuildThreads), 0, stream, la, idx.qidx, idx.offsets,
+                         geo.sort_shift, geo.sort_buckets_per_head, buckets, work_sorted);
     }
   }
   return hipGetLastError();

@@ -41,6 +41,9 @@ struct Geometry {
   int32_t ntiles;        // index tiles
   int32_t win_max;       // largest block window of any tile
   int32_t chunk_tokens;  // query tokens per work item
+  bool local;            // local entries are computed per query block (B_K = 64, g >= 2: there the
+                         // block's rows fill the local kernels' tiles; elsewhere the block-outer
+                         // kernels take every entry, the local words stay zero)
   int32_t dtype;
   int32_t partial_dtype;
   float scale;           // softmax scale (natural units)
@@ -50,18 +53,24 @@ struct Geometry {
                          // stores of rows past a chunk's end (never read)
   // aux blob layout (byte offsets)
   size_t aux_seq_gboff;  // int32 [B+1] exclusive prefix of per-sequence block counts
-  size_t aux_nwork;      // int32 [4]: number of work items, P, spare
+  size_t aux_nwork;      // int32 [4]: items of the full work list, P, items of the forward list, spare
   size_t aux_queue;      // int32 [kQueueKinds][kQueueInts]: work-queue counters
-  size_t aux_work;       // int4 [max_work]: (segment, first token, block start, seq end)
-  size_t aux_work_sorted;// int4 [max_work]: the same items ordered by (KV head, first query token)
+  size_t aux_loc;        // int32 [H][N]: local word of each (KV head, token), see local_entry()
+  size_t aux_nloc;       // int32 [H * NB]: local entries at the head of each segment (blocks >= 1)
+  size_t aux_work_sorted;// int4 [2 * max_work]: work items (segment, first query of the chunk, block
+                         // start, seq end) of the full and the forward list, each ordered by
+                         // (KV head, first query token); the forward list from index nwork[0] on
   int32_t sort_shift;    // work-order bucket = query token >> sort_shift
   int32_t sort_buckets_per_head;
   int32_t sort_buckets;
   size_t aux_bytes;
   size_t build_ws_bytes;
   size_t build_ws_buckets;  // byte offset of the work-order bucket counters in the build workspace
+  size_t build_ws_cb;       // byte offset of the work-list bases cb_full, cb_fwd (int32 [H * NB + 1] each)
   size_t stats_ws_bytes;
+  size_t stats_local_off;   // byte offset of the local (max, sum) pairs [N][H * g] in the stats workspace
   size_t partial_ws_bytes;
+  size_t partial_local_off; // byte offset of the local partial rows [H][N][g][d] in the partial workspace
   // backward workspace: delta [N, HQ] fp32 | dQ partial rows (as partial_ws) |
   // dK / dV slots: fp32 [kv_slots][2][BK][d], slot = offsets[f] / CT + f + chunk
   bool bwd_ok;           // a backward kernel is compiled for (d, BK)
@@ -77,11 +86,13 @@ int32_t compute_geometry(const fsa_problem* prob, Geometry* geo);
 // ---------------------------------------------------------------------------
 hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const int32_t* sel,
                               const fsa_index& idx, void* ws, hipStream_t stream);
-hipError_t launch_stats(const Geometry& geo, const void* q, const void* k, const fsa_index& idx,
-                        float* row_max, float* lse, void* ws, hipStream_t stream);
-hipError_t launch_main(const Geometry& geo, const void* q, const void* k, const void* v,
+hipError_t launch_stats(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k,
+                        const fsa_index& idx, float* row_max, float* lse, void* ws, hipStream_t stream);
+hipError_t launch_main(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
                        const fsa_index& idx, const float* lse, void* partial, hipStream_t stream);
-hipError_t launch_reduce(const Geometry& geo, const fsa_index& idx, const void* partial, void* out,
+// local: the forward's reduction (local partial rows plus the other slots);
+// otherwise every slot is summed (the backward's dQ).
+hipError_t launch_reduce(const Geometry& geo, const fsa_index& idx, const void* partial, void* out, bool local,
                          hipStream_t stream);
 hipError_t launch_bwd(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
                       const void* out, const void* dout, const float* lse, const fsa_index& idx, void* dq, void* dk,
@@ -135,6 +146,27 @@ __device__ __forceinline__ int seq_of_token(const int32_t* __restrict__ cu, int 
 __device__ __forceinline__ int seq_of_block(const int32_t* __restrict__ gboff, int num_seqs, int gb) {
   return seq_of_token(gboff, num_seqs, gb);
 }
+
+// Local entries.  NSA keeps a query's first block and its own and previous
+// blocks in every selection, so the selected entries of those blocks ("local"
+// entries) belong to every query of a query block.  The forward computes them
+// per query block, where the block's queries are contiguous and share the
+// three key blocks, and writes one partial row (and one (max, sum) pair) per
+// query instead of three; the block-outer kernels take the other entries.
+// The local word of a (KV head, token) packs, for each kind k (0: own block,
+// 1: previous block, 2: block 0 of the sequence when it is neither), 1 + the
+// Sel index of the token's valid entry of that block in bits [9k, 9k + 9), or
+// 0 when the token does not select it (Sel rows have at most 256 entries).
+__device__ __forceinline__ int local_kind(int e, int own) {
+  return e == own ? 0 : e == own - 1 ? 1 : e == 0 ? 2 : -1;
+}
+__device__ __forceinline__ bool local_has(uint32_t word, int kind) { return ((word >> (9 * kind)) & 511u) != 0u; }
+__device__ __forceinline__ bool local_entry(uint32_t word, int j) {
+  const uint32_t x = (uint32_t)j + 1u;
+  return (word & 511u) == x || ((word >> 9) & 511u) == x || ((word >> 18) & 511u) == x;
+}
+// Key block of local kind k for query block e (kinds 0 .. min(e, 2)).
+__device__ __forceinline__ int local_block(int kind, int e) { return kind == 0 ? e : kind == 1 ? e - 1 : 0; }
 
 // One work item of the attention kernels: KV head, number of query tokens,
 // first pair (position in qidx), block start token and keys in the block.

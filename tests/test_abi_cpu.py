@@ -86,13 +86,17 @@ def test_sizes_closed_form(name):
     assert s.max_pairs == pmax
     assert s.counts_bytes == 4 * H * sum(nb) and s.offsets_bytes == 4 * (H * sum(nb) + 1)
     assert s.slot_bytes == 4 * H * N * T and s.qidx_bytes == 4 * pmax
-    assert s.partial_ws_bytes >= pmax * sp.gqa_group * sp.head_dim * 4
-    assert s.stats_ws_bytes >= pmax * sp.gqa_group * 8
-    # backward: delta [N, h_q] fp32 + dQ partial rows + fp32 dK/dV slots of [2][B_K][d]
-    if B == 64 and sp.head_dim in (64, 128):
-        CT = -(-1024 // sp.gqa_group)
+    # partial rows of every pair (+ 32 dump rows) and one local row per (KV head, token, group head)
+    g, d = sp.gqa_group, sp.head_dim
+    rows = pmax * g + 32
+    local_rows = H * N * g
+    assert s.partial_ws_bytes >= (rows + local_rows) * d * 4
+    assert s.stats_ws_bytes >= (rows + local_rows) * 8
+    # backward: delta [N, h_q] fp32 + dQ partial rows (no local rows) + fp32 dK/dV slots of [2][B_K][d]
+    if B == 64 and d in (64, 128):
+        CT = -(-1024 // g)
         slots = pmax // CT + H * sum(nb) + 2
-        assert s.bwd_ws_bytes >= 4 * N * H * sp.gqa_group + s.partial_ws_bytes + slots * 2 * B * sp.head_dim * 4
+        assert s.bwd_ws_bytes >= 4 * N * H * g + rows * d * 4 + slots * 2 * B * d * 4
     else:
         assert s.bwd_ws_bytes == 0
 

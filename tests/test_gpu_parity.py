@@ -211,21 +211,37 @@ def test_repeated_calls_on_one_index():
 
 
 def test_partial_rows_sum_to_output():
-    # fp32 partials: summing each query's partial rows (slot order) gives the
-    # output before its final rounding.
+    # fp32 partials: each query's local row (its own, previous and first
+    # block, computed per query block) plus the partial rows of its other
+    # selecting entries, summed in slot order, give the output before its
+    # final rounding.  Locality is derived here from Sel itself.
     w = workload("n8k_h4_g2_d128_t16_bf16")
     res = run_gpu(w, "fp32", keep_partial=True)
     idx = res["index"]
-    g, d, H = w.gqa_group, w.head_dim, w.num_kv_heads
+    g, d, H, B = w.gqa_group, w.head_dim, w.num_kv_heads, w.block_size
     P = res["pairs"]
-    part = res["partial"].view(torch.float32)[: P * g * d].view(P, g, d)
+    part = res["partial"].view(torch.float32)
+    dev = part.device
+    rows = idx.sizes["max_pairs"] * g + 32
+    local_off = (rows * d * 4 + 255) // 256 * 256 // 4
     slot = idx.slot.long()  # [H, N, T]
     N = slot.shape[1]
-    acc = torch.zeros((N, H, g, d), dtype=torch.float32, device=part.device)
+    local = part[local_off: local_off + H * N * g * d].view(H, N, g, d).permute(1, 0, 2, 3)
+    pairs = part[: P * g * d].view(P, g, d)
+    sel = torch.from_numpy(w.sel).to(dev).long()
+    tok = torch.arange(N, device=dev)
+    cu = torch.from_numpy(np.asarray(w.cu_seqlens, dtype=np.int64)).to(dev)
+    seq = torch.searchsorted(cu, tok, right=True) - 1
+    own = ((tok - cu[seq]) // B).view(1, N, 1)
+    # the library takes this path for B_K = 64 and g >= 2 (this workload)
+    assert B == 64 and g >= 2
+    is_local = (slot >= 0) & ((sel == own) | (sel == own - 1) | (sel == 0))
+    has_local = is_local.any(dim=2).permute(1, 0).view(N, H, 1, 1)
+    acc = torch.where(has_local, local, torch.zeros((), device=dev))
     for j in range(slot.shape[2]):
-        s = slot[:, :, j].permute(1, 0)  # [N, H]
-        ok = (s >= 0).unsqueeze(-1).unsqueeze(-1)
-        acc += torch.where(ok, part[s.clamp(min=0)], torch.zeros((), device=part.device))
+        s_ = slot[:, :, j].permute(1, 0)  # [N, H]
+        ok = ((s_ >= 0) & ~is_local[:, :, j].permute(1, 0)).unsqueeze(-1).unsqueeze(-1)
+        acc += torch.where(ok, pairs[s_.clamp(min=0)], torch.zeros((), device=dev))
     out = res["out_dev"].float().view(N, H, g, d)
     ulp = torch.clamp(out.abs(), min=2.0**-126)
     half_ulp = torch.pow(2.0, torch.floor(torch.log2(ulp)) - 8)
