@@ -191,8 +191,17 @@ struct BwdTile {
   }
 };
 
+// Waves per SIMD: two up to d = 128.  At d = 256 the item's K / V fragments
+// and the dK / dV accumulators need more than 256 registers per lane, so one
+// wave per SIMD takes the whole register file (accumulators in AGPRs); the
+// LDS tiles (~110 KB) allow one workgroup per CU anyway.
+template <int D>
+constexpr int bwd_waves_per_eu() {
+  return D == 256 ? 1 : 2;
+}
+
 template <typename T, int D, typename PT>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_bwd_main(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>()))) void k_bwd_main(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
@@ -472,6 +481,7 @@ hipError_t bwd_d(const Geometry& geo, const int32_t* cu_dev, const void* q, cons
                  const void* out, const void* dout, const float* lse, const fsa_index& idx, void* dq, void* dk,
                  void* dv, void* ws, hipStream_t s) {
   if (geo.d == 64) return bwd_typed<T, 64, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
+  if (geo.d == 256) return bwd_typed<T, 256, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
   return bwd_typed<T, 128, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
 }
 

@@ -15,7 +15,7 @@ import torch
 
 import oracle.fsa_oracle as O
 from gpu_helpers import custom_workload, log, run_gpu_bwd, sample_tokens
-from sparse_attention_sel_amd.inputs import cu_seqlens_of, make_dout, make_workload
+from sparse_attention_sel_amd.inputs import cu_seqlens_of, make_dout, make_sel, make_workload
 from test_gpu_parity import adversarial_sel
 
 pytestmark = pytest.mark.gpu
@@ -76,6 +76,8 @@ CASES = [
     ((1000,), 2, 1, 128, 64, 8, "bf16"),
     ((64, 1, 65), 1, 2, 64, 64, 1, "fp16"),
     ((700, 300), 2, 5, 128, 64, 12, "bf16"),
+    ((640, 384), 2, 8, 256, 64, 6, "bf16"),
+    ((200, 57), 1, 3, 256, 64, 4, "fp16"),
 ]
 
 
@@ -90,6 +92,19 @@ def test_backward_adversarial_selection(case):
     do = dout_for(w, 960 + case)
     log(f"[run] bwd adversarial case {case} {CASES[case]}")
     check_all(run_gpu_bwd(w, do, "fp32"), oracle_grads(w, do), dtype)
+
+
+@pytest.mark.parametrize("partial", ["fp32", "input"])
+def test_backward_d256_hot_selection_all_tokens(partial):
+    # the large-head shape (two packed sequences, g = 8, d = 256, hot-block
+    # selection) at a size the oracle covers on every token; sequences this
+    # short reach a 30% hot share with hot sets of 20% of the blocks
+    seqlens, H, g, d, B, T = (2048, 1024), 2, 8, 256, 64, 16
+    sel, _ = make_sel("init_local_hot", seqlens, H, B, T, seed=5150, hot_fraction=0.2, hot_share=0.3)
+    w = custom_workload(seqlens, H, g, d, B, T, "bf16", sel, seed=5160)
+    do = dout_for(w, 5170)
+    log(f"[run] bwd d=256 hot selection partial={partial}")
+    check_all(run_gpu_bwd(w, do, partial), oracle_grads(w, do), w.dtype)
 
 
 def test_backward_full_selection_matches_torch_autograd():
@@ -152,5 +167,27 @@ def test_backward_64k_sampled_dq_and_dv_column_sums():
         tol = 2.0**-8 * np.abs(dvh).sum(axis=0) + 1e-3
         log(f"    dV column sums head {h}: max|diff|={float(np.max(np.abs(got - want))):.3e} "
             f"(tol {float(tol.min()):.3e}..{float(tol.max()):.3e})")
+        assert np.all(np.abs(got - want) <= tol)
+    assert np.all(np.isfinite(res["dk"])) and np.all(np.isfinite(res["dv"]))
+
+
+def test_backward_large_head_shape_sampled_dq_and_dv_column_sums():
+    # two packed 32K sequences, h_K = 8, g = 8, d = 256 with 16-bit partials
+    w = workload("b2_n32k_h8_g8_d256_t16_bf16")
+    do = dout_for(w, 14)
+    log("[run] bwd 2x32K g=8 d=256 (16-bit partials)")
+    res = run_gpu_bwd(w, do, "input")
+    toks = sample_tokens(w.cu_seqlens, w.block_size, n_random=24, seed=4)
+    log(f"    dq on {toks.size} sampled tokens")
+    dq_ref, _, _ = oracle_grads(w, do, toks)
+    check_all({"dq": res["dq"][toks]}, (dq_ref[toks], None, None), w.dtype, what=("dq",))
+    H, g = w.num_kv_heads, w.gqa_group
+    dof = do.float().numpy()
+    for h in range(H):
+        want = dof[:, h * g : (h + 1) * g, :].astype(np.float64).sum(axis=(0, 1))
+        dvh = res["dv"][:, h, :].astype(np.float64)
+        got = dvh.sum(axis=0)
+        tol = 2.0**-8 * np.abs(dvh).sum(axis=0) + 1e-3
+        log(f"    dV column sums head {h}: max|diff|={float(np.max(np.abs(got - want))):.3e}")
         assert np.all(np.abs(got - want) <= tol)
     assert np.all(np.isfinite(res["dk"])) and np.all(np.isfinite(res["dv"]))
