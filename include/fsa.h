@@ -228,8 +228,9 @@ int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, 
  *   dq                  device [N, h_K*g, d]; dk, dv device [N, h_K, d]; input
  *                       dtype, 16-byte aligned, fully written;
  *   ws                  device scratch of at least bwd_ws_bytes, 256-byte aligned.
- * Compiled for B_K = 64 and d in {64, 128, 256}; other shapes return
- * FSA_ERR_UNSUPPORTED (and fsa_get_sizes reports bwd_ws_bytes = 0).
+ * Compiled for every shape the forward supports (B_K = 64 with d in
+ * {64, 128, 256}, B_K = 128 with d in {64, 128}); a shape without a backward
+ * would return FSA_ERR_UNSUPPORTED with bwd_ws_bytes = 0.
  */
 int32_t fsa_selected_attn_bwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
                               const void* out, const void* dout, const float* lse, const fsa_index* idx,

@@ -147,7 +147,7 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   geo->partial_ws_bytes = round_up(geo->partial_local_off + local_rows * (size_t)geo->d * s_p, 256);
   // Backward: the chunk slot offsets[f] / CT + f + c (c < ceil(count_f / CT))
   // is injective and below max_pairs / CT + M + 2.
-  geo->bwd_ok = BK == 64;  // d = 64, 128, 256
+  geo->bwd_ok = BK == 64 || geo->d <= 128;  // B_K = 128 with d = 256 is not compiled
   geo->kv_slots = geo->max_pairs / geo->chunk_tokens + H * NB + 2;
   geo->bwd_dq_off = round_up((size_t)N * H * g * 4, 256);
   geo->bwd_kv_off = round_up(geo->bwd_dq_off + geo->partial_local_off, 256);  // dQ rows: no local region

@@ -9,11 +9,12 @@
 //                    fragments of its dQ d tiles in registers for the whole
 //                    item; the item's query rows stream through in 32-row
 //                    tiles staged row-major in LDS.  Wave w owns keys
-//                    16w .. 16w+15: it forms S = Q K^T and dP = dO V^T for its
+//                    16w .. 16w+15 (4 waves for 64-key blocks, 8 for
+//                    128-key blocks): it forms S = Q K^T and dP = dO V^T for its
 //                    keys, P = exp(S - lse), dS = P (dP - D), and accumulates
 //                    dV^T += dO^T P and dK^T += Q^T dS in registers over the
 //                    chunk, reading dO^T and Q^T with LDS transpose reads.
-//                    dS of all 64 keys meets in LDS and dQ^T = K^T dS^T
+//                    dS of all the keys meets in LDS and dQ^T = K^T dS^T
 //                    (split over d across the waves) is staged in LDS and
 //                    written as whole rows to the compact partial rows of
 //                    the forward.  At the end of the
@@ -41,9 +42,12 @@ namespace fsa {
 namespace {
 
 constexpr float kBwdLog2e = 1.4426950408889634f;
-constexpr int kBwdThreads = 256;  // 4 waves x 16 keys = the 64-key block
-constexpr int kBwdWaves = kBwdThreads / 64;
-constexpr int kBwdBK = 64;
+// One wave per 16 keys of the block: 4 waves (256 threads) for B_K = 64,
+// 8 waves (512 threads) for B_K = 128.
+template <int BK>
+constexpr int bwd_threads() {
+  return BK * 4;
+}
 constexpr int kBwdRows = 32;  // query rows per tile: two 16-row MFMA blocks
 constexpr int kBwdRowTable = kRowsPerItem + kBwdRows;
 
@@ -106,11 +110,14 @@ __device__ __forceinline__ uint32_t bbits(T x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x);
 }
 
-// LDS pitches (elements).  K: [64][D + 8]; Q, dO tiles: [32][D + 8]; dS:
-// [32][64 + 8].
+// LDS pitches (elements).  K: [B_K][D + 8]; Q, dO tiles: [32][D + 8]; dS:
+// [32][B_K + 8].
 template <int D>
 constexpr int b_kld() { return D + 8; }
-constexpr int kSLd = kBwdBK + 8;
+template <int BK>
+constexpr int s_ld() {
+  return BK + 8;
+}
 
 // ---- D = rowsum(dO * O) -------------------------------------------------------
 // D / 8 lanes per row, 16-byte loads, a butterfly over those lanes.
@@ -141,12 +148,12 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ out, co
 // consumes a loaded value before put(), so the loads stay in flight while
 // the previous tile computes; the row mask and the base-2 scaling of lse are
 // applied in put().
-template <typename T, int D>
+template <typename T, int D, int NT>
 struct BwdTile {
   using V8 = typename Vec8<T>::type;
-  static constexpr int PER = kBwdRows * D / 8;               // vectors of one tensor's tile
-  static constexpr int NV = 2 * PER / kBwdThreads;           // Q and dO tiles over the threads
-  static_assert(2 * PER % kBwdThreads == 0 && PER % kBwdThreads == 0, "whole vectors, one tensor per vector slot");
+  static constexpr int PER = kBwdRows * D / 8;  // vectors of one tensor's tile
+  static constexpr int NV = 2 * PER / NT;       // Q and dO tiles over the NT threads
+  static_assert(2 * PER % NT == 0, "whole vectors per thread");
   V8 x[NV];
   bool ok[NV];  // the vector's row is a row of the chunk
   float lraw, draw;
@@ -157,7 +164,7 @@ struct BwdTile {
                                        const int* __restrict__ rtok, int tile, int h, int g, int HQ) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int vi = threadIdx.x + i * kBwdThreads;
+      const int vi = threadIdx.x + i * NT;
       const int tensor = vi / PER, e = vi % PER;
       const int row = e / (D / 8), c = e % (D / 8);
       const int r = tile * kBwdRows + row;
@@ -179,7 +186,7 @@ struct BwdTile {
                                       float* __restrict__ tab_d) const {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      const int vi = threadIdx.x + i * kBwdThreads;
+      const int vi = threadIdx.x + i * NT;
       const int tensor = vi / PER, e = vi % PER;
       const int row = e / (D / 8), c = e % (D / 8);
       *reinterpret_cast<V8*>((tensor == 0 ? Qs : Ds) + row * b_kld<D>() + c * 8) = ok[i] ? x[i] : V8{};
@@ -200,8 +207,8 @@ constexpr int bwd_waves_per_eu() {
   return D == 256 ? 1 : 2;
 }
 
-template <typename T, int D, typename PT>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>()))) void k_bwd_main(
+template <typename T, int D, int BK, typename PT>
+__global__ __launch_bounds__(bwd_threads<BK>()) __attribute__((amdgpu_waves_per_eu(bwd_waves_per_eu<D>()))) void k_bwd_main(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dout,
     const float* __restrict__ lse, const float* __restrict__ delta, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
@@ -209,17 +216,26 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd
     float* __restrict__ kv_part, int H, int g, int NB, int CT, float scale, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   using V4 = typename Vec4<T>::type;
+  constexpr int NT = bwd_threads<BK>();
+  constexpr int W = NT / 64;           // waves, 16 keys each
   constexpr int KS = D / 32;           // 32-wide contraction steps over d
   constexpr int MT = D / 16;           // 16-wide d tiles
-  constexpr int MW = MT / kBwdWaves;   // d tiles of dQ per wave
+  // dQ^T work of a tile: 2 row blocks x MT d tiles over the W waves.  With
+  // W <= MT a wave takes MT / W d tiles of both row blocks; with W = 2 MT
+  // (B_K = 128, d = 64) one d tile of one row block.
+  constexpr int RBW = W > MT ? 1 : 2;  // row blocks per wave
+  constexpr int MW = W > MT ? 1 : MT / W;  // d tiles per wave
+  constexpr int KB = BK / 32;          // 32-key contraction steps of dQ^T
+  constexpr int SLD = s_ld<BK>();
   constexpr int C8 = D / 8;
-  constexpr int KV = kBwdBK * C8 / kBwdThreads;  // K vectors staged per thread
-  constexpr int RT = (kBwdRowTable + kBwdThreads - 1) / kBwdThreads;
-  static_assert(MT % kBwdWaves == 0 && kBwdBK * C8 % kBwdThreads == 0, "whole tiles");
-  __shared__ __attribute__((aligned(16))) T Ks[kBwdBK * b_kld<D>()];
+  constexpr int KV = BK * C8 / NT;     // K vectors staged per thread
+  constexpr int RT = (kBwdRowTable + NT - 1) / NT;
+  static_assert(W <= MT ? MT % W == 0 : W == 2 * MT, "dQ tiles split evenly over the waves");
+  static_assert(BK * C8 % NT == 0, "whole K vectors per thread");
+  __shared__ __attribute__((aligned(16))) T Ks[BK * b_kld<D>()];
   __shared__ __attribute__((aligned(16))) T Qs[kBwdRows * b_kld<D>()];
   __shared__ __attribute__((aligned(16))) T Ds[kBwdRows * b_kld<D>()];
-  __shared__ __attribute__((aligned(16))) T Ss[kBwdRows * kSLd];
+  __shared__ __attribute__((aligned(16))) T Ss[kBwdRows * SLD];
   constexpr int QOLD = D + 16 / (int)sizeof(PT);  // dQ stage pitch (elements): rows 16 bytes apart in banks
   __shared__ __attribute__((aligned(16))) PT Qo[kBwdRows * QOLD];
   __shared__ __attribute__((aligned(16))) int rtok[kBwdRowTable];
@@ -232,14 +248,18 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kl = lane & 15, u = lane >> 4;
   const int key = wave * 16 + kl;  // this lane's key within the block (S, dP, dK, dV)
+  // d tile of this wave's m-th dQ^T tile, and its row block when RBW = 1
+  auto mt_of = [&](int m) { return W > MT ? wave % MT : wave + W * m; };
+  const int rb_own = W > MT ? wave / MT : 0;
   // Writes the staged dQ rows of tile `tl` of the current item as whole rows
   // (consecutive threads, consecutive 16-byte pieces; non-temporal).
   auto flush_dq = [&](int tl, int pair0, int nrows) {
     constexpr int CPR = D * (int)sizeof(PT) / 16;  // 16-byte pieces per row
     constexpr int EPC = 16 / (int)sizeof(PT);      // elements per piece
 #pragma unroll
-    for (int j = 0; j < kBwdRows * CPR / kBwdThreads; ++j) {
-      const int pc = threadIdx.x + j * kBwdThreads;
+    for (int j = 0; j < (kBwdRows * CPR + NT - 1) / NT; ++j) {
+      const int pc = threadIdx.x + j * NT;
+      if (kBwdRows * CPR % NT != 0 && pc >= kBwdRows * CPR) break;
       const int row = pc / CPR, col = pc % CPR;
       const int r = tl * kBwdRows + row;
       if (r < nrows)
@@ -252,7 +272,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd
   while (ch.cur >= 0) {
     const int wi = ch.cur;
     const int4 wraw = work[wi];
-    const Item it = read_item(work, counts, offsets, wi, NB, CT, kBwdBK);
+    const Item it = read_item(work, counts, offsets, wi, NB, CT, BK);
     const int nrows = it.ntok * g, ntile = (nrows + kBwdRows - 1) / kBwdRows;
     // Item operands that stay in registers for all of its tiles: the B
     // fragments of this lane's key for S = Q K^T and dP = dO V^T (16-byte
@@ -268,24 +288,24 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd
     V8 kst[KV];
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const int vi = threadIdx.x + i * kBwdThreads;
+      const int vi = threadIdx.x + i * NT;
       kst[i] = bld8(k + ((size_t)(it.bs + min(vi / C8, it.nkeys - 1)) * H + it.h) * D + (vi % C8) * 8);
     }
     int tk[RT];
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      const int r = threadIdx.x + i * kBwdThreads;
+      const int r = threadIdx.x + i * NT;
       tk[i] = qidx[it.pair0 + min(r / g, it.ntok - 1)];
     }
     __syncthreads();  // every wave is done with the previous item's K and row table
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const int vi = threadIdx.x + i * kBwdThreads;
+      const int vi = threadIdx.x + i * NT;
       *reinterpret_cast<V8*>(Ks + (vi / C8) * b_kld<D>() + (vi % C8) * 8) = kst[i];
     }
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      const int r = threadIdx.x + i * kBwdThreads;
+      const int r = threadIdx.x + i * NT;
       if (r < kBwdRowTable) rtok[r] = r < nrows ? tk[i] : -1;
     }
     ch.publish(s_items);
@@ -293,15 +313,15 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd
     const int after = ch.after(s_items);
     // K^T fragments of dQ^T = K^T dS^T: lane (kl, u) of d tile mt holds
     // K[32 ks + 8u + e][16 mt + kl], e < 8.
-    V8 kt[MW][2];
+    V8 kt[MW][KB];
 #pragma unroll
     for (int m = 0; m < MW; ++m)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < KB; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kt[m][ks][e] = Ks[(32 * ks + 8 * u + e) * b_kld<D>() + 16 * (wave + kBwdWaves * m) + kl];
+        for (int e = 0; e < 8; ++e) kt[m][ks][e] = Ks[(32 * ks + 8 * u + e) * b_kld<D>() + 16 * mt_of(m) + kl];
 
-    BwdTile<T, D> tl;
+    BwdTile<T, D, NT> tl;
     tl.load(q, dout, lse, delta, rtok, 0, it.h, g, HQ);
     f32x4 dk[MT], dv[MT];
 #pragma unroll
@@ -354,20 +374,21 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) Ss[(16 * rb + 4 * u + r) * kSLd + key] = ds4[rb][r];
-      __syncthreads();  // dS of all 64 keys in LDS
+        for (int r = 0; r < 4; ++r) Ss[(16 * rb + 4 * u + r) * SLD + key] = ds4[rb][r];
+      __syncthreads();  // dS of all the block's keys in LDS
 
       // dQ^T = K^T dS^T for the d tiles of this wave, staged in LDS; lane:
       // row 16 rb + kl, d = 16mt + 4u + r.
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rbi = 0; rbi < RBW; ++rbi)
 #pragma unroll
         for (int m = 0; m < MW; ++m) {
+          const int rb = RBW == 1 ? rb_own : rbi;
           f32x4 acc = {};
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            acc = mfma_k32(kt[m][ks], bld8(Ss + (16 * rb + kl) * kSLd + 32 * ks + 8 * u), acc);
-          PT* const o = Qo + (16 * rb + kl) * QOLD + 16 * (wave + kBwdWaves * m) + 4 * u;
+          for (int ks = 0; ks < KB; ++ks)
+            acc = mfma_k32(kt[m][ks], bld8(Ss + (16 * rb + kl) * SLD + 32 * ks + 8 * u), acc);
+          PT* const o = Qo + (16 * rb + kl) * QOLD + 16 * mt_of(m) + 4 * u;
           if constexpr (sizeof(PT) == 4) {
             *reinterpret_cast<f32x4*>(o) = acc * scale;
           } else {
@@ -379,13 +400,13 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd
     __syncthreads();  // the last tile's dQ is staged
     flush_dq(ntile - 1, it.pair0, nrows);
 
-    // The block's dK (scaled) / dV partial of this chunk: slot [2][64][D] fp32.
+    // The block's dK (scaled) / dV partial of this chunk: slot [2][B_K][D] fp32.
     const int64_t slot = (int64_t)(offsets[wraw.x] / CT) + wraw.x + wraw.y / CT;
-    float* const kvp = kv_part + slot * 2 * kBwdBK * D + (size_t)key * D + 4 * u;
+    float* const kvp = kv_part + slot * 2 * BK * D + (size_t)key * D + 4 * u;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       *reinterpret_cast<f32x4*>(kvp + 16 * mt) = dk[mt] * scale;
-      *reinterpret_cast<f32x4*>(kvp + kBwdBK * D + 16 * mt) = dv[mt];
+      *reinterpret_cast<f32x4*>(kvp + BK * D + 16 * mt) = dv[mt];
     }
     ch.advance(after);
   }
@@ -395,7 +416,7 @@ __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(bwd
 // ---- dK, dV = ordered sum of the block's chunk slots --------------------------
 // One thread per (segment f, key, 4 columns); keys past the sequence end are
 // skipped, keys of blocks nobody selects get zero.
-template <typename T, int D>
+template <typename T, int D, int BK>
 __global__ __launch_bounds__(256) void k_bwd_kv_reduce(const int32_t* __restrict__ counts,
                                                        const int32_t* __restrict__ offsets,
                                                        const int32_t* __restrict__ gboff,
@@ -405,13 +426,13 @@ __global__ __launch_bounds__(256) void k_bwd_kv_reduce(const int32_t* __restrict
   typedef T T4 __attribute__((ext_vector_type(4)));
   constexpr int C4 = D / 4;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)H * NB * kBwdBK * C4) return;
+  if (idx >= (int64_t)H * NB * BK * C4) return;
   const int c4 = (int)(idx % C4);
-  const int key = (int)((idx / C4) % kBwdBK);
-  const int f = (int)(idx / ((int64_t)C4 * kBwdBK));
+  const int key = (int)((idx / C4) % BK);
+  const int f = (int)(idx / ((int64_t)C4 * BK));
   const int h = f / NB, gb = f - h * NB;
   const int s = seq_of_block(gboff, num_seqs, gb);
-  const int token = cu[s] + (gb - gboff[s]) * kBwdBK + key;
+  const int token = cu[s] + (gb - gboff[s]) * BK + key;
   if (token >= cu[s + 1]) return;
   const int nch = (counts[f] + CT - 1) / CT;
   const int64_t slot0 = (int64_t)(offsets[f] / CT) + f;
@@ -423,9 +444,9 @@ __global__ __launch_bounds__(256) void k_bwd_kv_reduce(const int32_t* __restrict
     f32x4 xk[U], xv[U];
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const float* p = kv_part + (slot0 + min(c + j, nch - 1)) * 2 * kBwdBK * D + (size_t)key * D + 4 * c4;
+      const float* p = kv_part + (slot0 + min(c + j, nch - 1)) * 2 * BK * D + (size_t)key * D + 4 * c4;
       xk[j] = *reinterpret_cast<const f32x4*>(p);
-      xv[j] = *reinterpret_cast<const f32x4*>(p + kBwdBK * D);
+      xv[j] = *reinterpret_cast<const f32x4*>(p + BK * D);
     }
 #pragma unroll
     for (int j = 0; j < U; ++j)
@@ -439,7 +460,7 @@ __global__ __launch_bounds__(256) void k_bwd_kv_reduce(const int32_t* __restrict
   *reinterpret_cast<T4*>(dv + o) = __builtin_convertvector(sv, T4);
 }
 
-template <typename T, int D, typename PT>
+template <typename T, int D, int BK, typename PT>
 hipError_t bwd_typed(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
                      const void* out, const void* dout, const float* lse, const fsa_index& idx, void* dq, void* dk,
                      void* dv, void* ws, hipStream_t stream) {
@@ -459,8 +480,9 @@ hipError_t bwd_typed(const Geometry& geo, const int32_t* cu_dev, const void* q, 
                      static_cast<const T*>(out), static_cast<const T*>(dout), delta, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_bwd_main<T, D, PT>),
-                     dim3(persistent_grid(k_bwd_main<T, D, PT>, kBwdThreads, geo.max_work)), dim3(kBwdThreads), 0,
+  constexpr int NT = bwd_threads<BK>();
+  hipLaunchKernelGGL((k_bwd_main<T, D, BK, PT>), dim3(persistent_grid(k_bwd_main<T, D, BK, PT>, NT, geo.max_work)),
+                     dim3(NT), 0,
                      stream, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                      static_cast<const T*>(dout), lse, delta, idx.counts, idx.offsets, idx.qidx, work, nwork, queue, dq_part,
                      kv_part, geo.H, geo.g, geo.NB, geo.chunk_tokens, geo.scale, geo.scale * kBwdLog2e);
@@ -468,9 +490,9 @@ hipError_t bwd_typed(const Geometry& geo, const int32_t* cu_dev, const void* q, 
   if (e != hipSuccess) return e;
   e = launch_reduce(geo, idx, dq_part, dq, false, stream);
   if (e != hipSuccess) return e;
-  const int64_t kthreads = (int64_t)geo.H * geo.NB * kBwdBK * (D / 4);
+  const int64_t kthreads = (int64_t)geo.H * geo.NB * BK * (D / 4);
   if (kthreads > 0)
-    hipLaunchKernelGGL((k_bwd_kv_reduce<T, D>), dim3((unsigned)((kthreads + 255) / 256)), dim3(256), 0, stream,
+    hipLaunchKernelGGL((k_bwd_kv_reduce<T, D, BK>), dim3((unsigned)((kthreads + 255) / 256)), dim3(256), 0, stream,
                        idx.counts, idx.offsets, gboff, cu_dev, geo.num_seqs, kv_part, static_cast<T*>(dk),
                        static_cast<T*>(dv), geo.H, geo.NB, geo.chunk_tokens);
   return hipGetLastError();
@@ -480,9 +502,13 @@ template <typename T, typename PT>
 hipError_t bwd_d(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
                  const void* out, const void* dout, const float* lse, const fsa_index& idx, void* dq, void* dk,
                  void* dv, void* ws, hipStream_t s) {
-  if (geo.d == 64) return bwd_typed<T, 64, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
-  if (geo.d == 256) return bwd_typed<T, 256, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
-  return bwd_typed<T, 128, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
+  if (geo.BK == 128) {  // d <= 128 (checked by the caller)
+    if (geo.d == 64) return bwd_typed<T, 64, 128, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
+    return bwd_typed<T, 128, 128, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
+  }
+  if (geo.d == 64) return bwd_typed<T, 64, 64, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
+  if (geo.d == 256) return bwd_typed<T, 256, 64, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
+  return bwd_typed<T, 128, 64, PT>(geo, cu_dev, q, k, v, out, dout, lse, idx, dq, dk, dv, ws, s);
 }
 
 }  // namespace

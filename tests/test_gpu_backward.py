@@ -78,6 +78,8 @@ CASES = [
     ((700, 300), 2, 5, 128, 64, 12, "bf16"),
     ((640, 384), 2, 8, 256, 64, 6, "bf16"),
     ((200, 57), 1, 3, 256, 64, 4, "fp16"),
+    ((700, 300), 2, 4, 128, 128, 6, "bf16"),
+    ((257, 130, 1), 1, 3, 64, 128, 4, "fp16"),
 ]
 
 
@@ -104,6 +106,17 @@ def test_backward_d256_hot_selection_all_tokens(partial):
     w = custom_workload(seqlens, H, g, d, B, T, "bf16", sel, seed=5160)
     do = dout_for(w, 5170)
     log(f"[run] bwd d=256 hot selection partial={partial}")
+    check_all(run_gpu_bwd(w, do, partial), oracle_grads(w, do), w.dtype)
+
+
+@pytest.mark.parametrize("partial", ["fp32", "input"])
+def test_backward_b128_zipf_all_tokens(partial):
+    # 128-key blocks (eight waves per block in the backward), 8 selected blocks
+    seqlens, H, g, d, B, T = (4096,), 2, 4, 128, 128, 8
+    sel, _ = make_sel("init_local_zipf", seqlens, H, B, T, seed=3350)
+    w = custom_workload(seqlens, H, g, d, B, T, "bf16", sel, seed=3360)
+    do = dout_for(w, 3370)
+    log(f"[run] bwd B_K=128 partial={partial}")
     check_all(run_gpu_bwd(w, do, partial), oracle_grads(w, do), w.dtype)
 
 
