@@ -7,7 +7,7 @@ Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--partial input|fp32] [--no-cpu-baseline] [--no-variants]
-                    [--no-query-outer] [--no-backward] [--no-selection]
+                    [--no-query-outer] [--no-backward] [--no-selection] [--no-onepass]
                     [--cold-reps R]
 
 The query-outer forward (fsa_nsa_selected_attn_fwd, the vanilla NSA loop
@@ -63,6 +63,8 @@ def parse():
                     help="skip timing the query-outer (vanilla NSA order) forward")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--no-selection", action="store_true", help="skip timing block selection")
+    ap.add_argument("--no-onepass", action="store_true",
+                    help="skip timing the one-pass forward (statistics fused into main and reduction)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="extra steps timed after a 1 GiB cache-evicting fill each (0: skip)")
@@ -215,7 +217,8 @@ def cpu_baseline(w, target_s):
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
-def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, selection=False, cold_reps=0):
+def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, selection=False, cold_reps=0,
+            onepass=False):
     import torch
 
     import sparse_attention_sel_amd as fsa
@@ -303,6 +306,35 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
             b.record(stream)
         torch.cuda.synchronize()
         qo_ms = sum(a.elapsed_time(b) for a, b in qev) / len(qev)
+    # the one-pass forward (fsa_selected_attn_fwd_onepass: the statistics fused
+    # into the main kernel and the reduction) on the same inputs: index build
+    # plus the fused call per step, timed like the step above
+    op = None
+    if onepass:
+        o_lse, o_rm, o_out = torch.empty_like(lse), torch.empty_like(row_max), torch.empty_like(out)
+
+        def ostep(ev):
+            ev[0].record(stream)
+            fsa.build_index(prob, sel, index, ws.build, stream)
+            ev[1].record(stream)
+            fsa.selected_attn_fwd_onepass(prob, q, k, v, index, o_rm, o_lse, o_out, ws.stats, ws.partial, stream)
+            ev[2].record(stream)
+
+        for _ in range(max(2, warmup)):
+            ostep([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+        oev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for ev in oev:
+            ostep(ev)
+        torch.cuda.synchronize()
+        owall = time.perf_counter() - t1
+        op = {
+            "ms_per_step": owall * 1e3 / steps,
+            "index_ms": sum(ev[0].elapsed_time(ev[1]) for ev in oev) / steps,
+            "fused_ms": sum(ev[1].elapsed_time(ev[2]) for ev in oev) / steps,
+        }
+        del o_lse, o_rm, o_out
     # the backward (fsa_selected_attn_bwd) from this forward's O and lse, for
     # a seeded output gradient, timed the same way
     bwd_ms = None
@@ -352,6 +384,7 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
         "selection_ms": sel_ms,
         "selection_bytes": sel_bytes,
         "query_outer_ms": qo_ms,
+        "onepass": op,
         "backward_ms": bwd_ms,
         "stage_ms": stage,
         "pairs": index.num_pairs(),
@@ -395,9 +428,10 @@ def measured_peaks(dtype):
     return out
 
 
-def measure(w, partial, steps, warmup, query_outer=False, backward=False, selection=False, cold_reps=0):
+def measure(w, partial, steps, warmup, query_outer=False, backward=False, selection=False, cold_reps=0,
+            onepass=False):
     P_host, P_loc, keys = work_counts(w.sel, w.cu_seqlens, w.block_size)
-    r = run_gpu(w, partial, steps, warmup, query_outer, backward, selection, cold_reps)
+    r = run_gpu(w, partial, steps, warmup, query_outer, backward, selection, cold_reps, onepass)
     assert r["pairs"] == P_host, (r["pairs"], P_host)
     f_alg = 4.0 * w.gqa_group * w.head_dim * keys
     f_main = 4.0 * w.gqa_group * w.block_size * w.head_dim * P_host
@@ -436,7 +470,7 @@ def main():
         log(f"cpu baseline done: {cpu['value']:.4g} TFLOP/s on {cpu['cores']} cores")
     log("gpu run")
     r = measure(w, args.partial, args.steps, args.warmup, not args.no_query_outer, not args.no_backward,
-                not args.no_selection, cold_reps=args.cold_reps)
+                not args.no_selection, cold_reps=args.cold_reps, onepass=not args.no_onepass)
     peaks = measured_peaks(w.dtype)
     log(f"gpu run done: {r['ms_per_step']:.3f} ms/step")
     ms = r["ms_per_step"]
@@ -519,6 +553,15 @@ def main():
             "tflops_alg": round(f_bwd / (r["backward_ms"] * 1e-3) / 1e12, 2),
             "ratio_to_forward": round(r["backward_ms"] / ms, 3),
         }
+    if r["onepass"] is not None:
+        # not the pages' three-kernel split: a measured alternative, same outputs
+        opm = r["onepass"]["ms_per_step"]
+        line["onepass"] = {
+            "ms_per_step": round(opm, 4),
+            "tflops": round(r["f_alg"] / (opm * 1e-3) / 1e12, 2),
+            "fused_ms": round(r["onepass"]["fused_ms"], 4),
+            "speedup_vs_three_pass": round(ms / opm, 3),
+        }
     if r["query_outer_ms"] is not None:
         line["query_outer"] = {
             "ms": round(r["query_outer_ms"], 4),
@@ -531,12 +574,14 @@ def main():
         for name in VARIANTS:
             log(f"variant {name}")
             wv = make_workload(name)
-            rv = measure(wv, args.partial, max(3, args.steps // 2), 2, not args.no_query_outer, not args.no_backward)
+            rv = measure(wv, args.partial, max(3, args.steps // 2), 2, not args.no_query_outer, not args.no_backward,
+                         onepass=not args.no_onepass)
             stv = rv["stage_ms"]
             var[name] = {
                 "ms_per_step": round(rv["ms_per_step"], 4),
                 "backward_ms": None if rv["backward_ms"] is None else round(rv["backward_ms"], 4),
                 "query_outer_ms": None if rv["query_outer_ms"] is None else round(rv["query_outer_ms"], 4),
+                "onepass_ms": None if rv["onepass"] is None else round(rv["onepass"]["ms_per_step"], 4),
                 "tflops": round(rv["f_alg"] / (rv["ms_per_step"] * 1e-3) / 1e12, 2),
                 "stages_ms": {k_: round(v_, 4) for k_, v_ in stv.items()},
                 "main_mfma_frac": round(rv["f_alg"] / (stv["main"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[wv.dtype], 4),

@@ -32,6 +32,9 @@
  *   fsa_softmax_stats      per-query row max and log-sum-exp.
  *   fsa_selected_attn_fwd  main kernel (partials) + reduction -> O.
  *                          (= fsa_selected_attn_main then _reduce.)
+ *   fsa_selected_attn_fwd_onepass  statistics fused into the main kernel
+ *                          and the reduction: row max, lse and O in two
+ *                          passes (replaces the two calls above).
  *   fsa_selected_attn_bwd  dQ, dK, dV for an output gradient dO, from the
  *                          same index, O and lse.
  *   fsa_nsa_selected_attn_fwd  the same forward in the query-outer order of
@@ -191,6 +194,29 @@ int32_t fsa_softmax_stats(const fsa_problem* prob, const void* q, const void* k,
 int32_t fsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
                               const fsa_index* idx, const float* lse, void* out, void* partial_ws,
                               size_t partial_ws_bytes, void* stream);
+
+/*
+ * One-pass forward: the statistics and the output of fsa_softmax_stats
+ * followed by fsa_selected_attn_fwd, in two kernel passes instead of three.
+ * The pages run a separate online-softmax kernel first because thread blocks
+ * that each see one KV block cannot know a query's running max (paper notes,
+ * Key design 4).  Here each (block, query) pair instead keeps its own
+ * softmax: the main kernel writes the block's softmax average of V,
+ *   o_b = sum_k exp(s_k - m_b) v_k / l_b  over the block's visible keys,
+ * and the pair's (m_b, l_b); the reduction merges the pairs of a query in
+ * slot order (the statistics kernel's merge, so row_max and lse are the
+ * values fsa_softmax_stats returns) and sums l_b exp(m_b - m) / l * o_b.
+ * The same outputs within rounding: o_b is rounded to the partial dtype
+ * before its weight is applied instead of after.
+ *   q, k, v, out  device, 16-byte aligned; row_max, lse: device fp32
+ *                 [N, h_K*g], written.
+ *   stats_ws      device scratch of at least stats_ws_bytes (16-byte aligned).
+ *   partial_ws    device scratch of at least partial_ws_bytes (16-byte aligned).
+ */
+int32_t fsa_selected_attn_fwd_onepass(const fsa_problem* prob, const void* q, const void* k, const void* v,
+                                      const fsa_index* idx, float* row_max, float* lse, void* out,
+                                      void* stats_ws, size_t stats_ws_bytes, void* partial_ws,
+                                      size_t partial_ws_bytes, void* stream);
 
 /*
  * Main (token-selection) kernel alone (paper notes, Key designs 1-3): one

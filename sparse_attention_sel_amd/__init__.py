@@ -35,6 +35,7 @@ __all__ = [
     "build_index",
     "softmax_stats",
     "selected_attn_fwd",
+    "selected_attn_fwd_onepass",
     "selected_attn_main",
     "selected_attn_reduce",
     "nsa_selected_attn_fwd",
@@ -137,6 +138,8 @@ def load_library():
     lib.fsa_softmax_stats.argtypes = [P, vp, vp, I, vp, vp, vp, sz, vp]
     lib.fsa_selected_attn_fwd.restype = i32
     lib.fsa_selected_attn_fwd.argtypes = [P, vp, vp, vp, I, vp, vp, vp, sz, vp]
+    lib.fsa_selected_attn_fwd_onepass.restype = i32
+    lib.fsa_selected_attn_fwd_onepass.argtypes = [P, vp, vp, vp, I, vp, vp, vp, vp, sz, vp, sz, vp]
     lib.fsa_selected_attn_main.restype = i32
     lib.fsa_selected_attn_main.argtypes = [P, vp, vp, vp, I, vp, vp, sz, vp]
     lib.fsa_selected_attn_reduce.restype = i32
@@ -330,6 +333,26 @@ def selected_attn_fwd(prob, q, k, v, index: Index, lse, out, partial_ws, stream=
     _check(load_library().fsa_selected_attn_fwd(prob.c(), *args, _stream(stream)), "fsa_selected_attn_fwd")
 
 
+def selected_attn_fwd_onepass(prob, q, k, v, index: Index, row_max, lse, out, stats_ws, partial_ws, stream=None):
+    """fsa_selected_attn_fwd_onepass: row max, lse [N, h_q] and out [N, h_q, d]
+    with the statistics fused into the main kernel and the reduction."""
+    qs, ks = _qkv_shapes(prob)
+    st = (prob.total_tokens, prob.num_q_heads)
+    args = (
+        _ptr(q, "q", prob.dtype, qs),
+        _ptr(k, "k", prob.dtype, ks),
+        _ptr(v, "v", prob.dtype, ks),
+        index.c(),
+        _ptr(row_max, "row_max", torch.float32, st),
+        _ptr(lse, "lse", torch.float32, st),
+        _ptr(out, "out", prob.dtype, qs),
+        *_ws(stats_ws, "stats workspace", index.sizes["stats_ws_bytes"]),
+        *_ws(partial_ws, "partial workspace", index.sizes["partial_ws_bytes"]),
+    )
+    _check(load_library().fsa_selected_attn_fwd_onepass(prob.c(), *args, _stream(stream)),
+           "fsa_selected_attn_fwd_onepass")
+
+
 def selected_attn_main(prob, q, k, v, index: Index, lse, partial_ws, stream=None):
     """fsa_selected_attn_main: the token-selection kernel alone (partials)."""
     qs, ks = _qkv_shapes(prob)
@@ -434,9 +457,10 @@ def nsa_selected_attn_fwd(prob: Problem, q, k, v, sel, lse, out, stream=None):
     _check(load_library().fsa_nsa_selected_attn_fwd(prob.c(), *args, _stream(stream)), "fsa_nsa_selected_attn_fwd")
 
 
-def selected_attention(prob: Problem, q, k, v, sel, stream=None):
+def selected_attention(prob: Problem, q, k, v, sel, stream=None, onepass: bool = False):
     """Whole forward: index, statistics and output, with torch-allocated
-    buffers.  Returns (out, lse, row_max, index)."""
+    buffers (onepass: the statistics fused into the main kernel and the
+    reduction).  Returns (out, lse, row_max, index)."""
     dev = q.device
     if prob.cu_dev is None or prob.cu_dev.device != dev:
         raise ValueError("Problem must be created with device= the tensors' device")
@@ -447,6 +471,9 @@ def selected_attention(prob: Problem, q, k, v, sel, stream=None):
     row_max = torch.empty((n, hq), dtype=torch.float32, device=dev)
     out = torch.empty((n, hq, prob.head_dim), dtype=prob.dtype, device=dev)
     build_index(prob, sel, index, ws.build, stream)
-    softmax_stats(prob, q, k, index, row_max, lse, ws.stats, stream)
-    selected_attn_fwd(prob, q, k, v, index, lse, out, ws.partial, stream)
+    if onepass:
+        selected_attn_fwd_onepass(prob, q, k, v, index, row_max, lse, out, ws.stats, ws.partial, stream)
+    else:
+        softmax_stats(prob, q, k, index, row_max, lse, ws.stats, stream)
+        selected_attn_fwd(prob, q, k, v, index, lse, out, ws.partial, stream)
     return out, lse, row_max, index

@@ -287,7 +287,7 @@ int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const voi
   st = check_main_args(geo, q, k, v, idx, lse, partial_ws, partial_ws_bytes);
   if (st != FSA_OK) return st;
   return hip_status(
-      launch_main(geo, prob->cu_seqlens_dev, q, k, v, *idx, lse, partial_ws, static_cast<hipStream_t>(stream)));
+      launch_main(geo, prob->cu_seqlens_dev, q, k, v, *idx, lse, nullptr, partial_ws, static_cast<hipStream_t>(stream)));
 }
 
 int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, const void* partial_ws,
@@ -297,7 +297,8 @@ int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, 
   if (st != FSA_OK) return st;
   st = check_reduce_args(geo, idx, partial_ws, partial_ws_bytes, out);
   if (st != FSA_OK) return st;
-  return hip_status(launch_reduce(geo, *idx, partial_ws, out, true, static_cast<hipStream_t>(stream)));
+  return hip_status(
+      launch_reduce(geo, *idx, partial_ws, out, true, nullptr, nullptr, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int32_t fsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
@@ -311,9 +312,30 @@ int32_t fsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void
   st = check_reduce_args(geo, idx, partial_ws, partial_ws_bytes, out);
   if (st != FSA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  st = hip_status(launch_main(geo, prob->cu_seqlens_dev, q, k, v, *idx, lse, partial_ws, s));
+  st = hip_status(launch_main(geo, prob->cu_seqlens_dev, q, k, v, *idx, lse, nullptr, partial_ws, s));
   if (st != FSA_OK) return st;
-  return hip_status(launch_reduce(geo, *idx, partial_ws, out, true, s));
+  return hip_status(launch_reduce(geo, *idx, partial_ws, out, true, nullptr, nullptr, nullptr, s));
+}
+
+int32_t fsa_selected_attn_fwd_onepass(const fsa_problem* prob, const void* q, const void* k, const void* v,
+                                      const fsa_index* idx, float* row_max, float* lse, void* out, void* stats_ws,
+                                      size_t stats_ws_bytes, void* partial_ws, size_t partial_ws_bytes,
+                                      void* stream) {
+  Geometry geo;
+  int32_t st = prepare(prob, &geo);
+  if (st != FSA_OK) return st;
+  if (!data(row_max, geo) || !data(lse, geo) || stats_ws == nullptr) return FSA_ERR_NULL;
+  // lse is an output here; the main-kernel checks only need a non-null pointer
+  st = check_main_args(geo, q, k, v, idx, lse, partial_ws, partial_ws_bytes);
+  if (st != FSA_OK) return st;
+  st = check_reduce_args(geo, idx, partial_ws, partial_ws_bytes, out);
+  if (st != FSA_OK) return st;
+  if (!aligned(row_max, 4) || !aligned(stats_ws, 16)) return FSA_ERR_ALIGN;
+  if (stats_ws_bytes < geo.stats_ws_bytes) return FSA_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(launch_main(geo, prob->cu_seqlens_dev, q, k, v, *idx, nullptr, stats_ws, partial_ws, s));
+  if (st != FSA_OK) return st;
+  return hip_status(launch_reduce(geo, *idx, partial_ws, out, true, stats_ws, row_max, lse, s));
 }
 
 int32_t fsa_selected_attn_bwd(const fsa_problem* prob, const void* q, const void* k, const void* v,

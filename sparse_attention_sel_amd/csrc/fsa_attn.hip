@@ -472,12 +472,58 @@ __device__ __forceinline__ void probs(const f32x16* s, float c, float l2, int hl
     }
 }
 
-template <typename T, int D, int BK, typename PT>
+// probs() with the row's own statistics (the one-pass forward): the max m of
+// the visible scaled scores and l = sum exp(s - m), computed exactly as
+// row_stats() computes them (same terms, same order), so the pair matches the
+// statistics kernel's bit for bit.  The probabilities handed to the PV MFMA
+// are exp(s - max(m, mprev)), the running max mprev of earlier blocks
+// (-inf: none), as exp(s - m) * exp(m - max(m, mprev)).
+template <typename T, int BK, bool MASKED>
+__device__ __forceinline__ float2 probs_stats(const f32x16* s, float c, int hl, int lim, float mprev,
+                                              typename Vec8<T>::type* pb) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int kt = 0; kt < BK / 32; ++kt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+      if (!MASKED || key <= lim) m = fmaxf(m, s[kt][r]);
+    }
+  m = xhalf_max(m) * c;
+  const float mx = fmaxf(m, mprev);
+  const float scale = m == mx ? 1.f : __builtin_amdgcn_exp2f(m - mx);
+  float l = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < BK / 32; ++kt)
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      f32x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * u + e;
+        const int key = kt * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -m));
+        const float pv = (!MASKED || key <= lim) ? p : 0.f;
+        l += pv;
+        x[e] = pv * scale;
+      }
+      pb[2 * kt + u] = __builtin_convertvector(x, typename Vec8<T>::type);
+    }
+  return make_float2(m, xhalf_sum(l));
+}
+
+// FUSED (the one-pass forward): instead of reading lse, each row takes the
+// (max, sum) of its scores over this block, P = exp(s - max), and the
+// partial row is divided by the sum, so it holds the block's own softmax
+// average of V; the (max, sum) pair goes to `st` as the statistics kernel
+// would write it, and the reduction weighs the partial rows by it.
+template <typename T, int D, int BK, typename PT, bool FUSED>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
     const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
-    PT* __restrict__ partial, size_t dump_row, int H, int g, int NB, int CT, float scale_log2) {
+    float2* __restrict__ st, PT* __restrict__ partial, size_t dump_row, int H, int g, int NB, int CT,
+    float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
   static_assert(32 * Stage<PT, D>::P * sizeof(PT) <= 32 * tile_ld<D>() * sizeof(T), "stage fits the Q tile");
@@ -515,7 +561,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     float lnext = 0.f;
     if (wave < ntile) {
       load_q_tile<T, D>(q, ridx, wave, lane, qv);
-      lnext = lse[ridx[wave * 32 + lr]];
+      if constexpr (!FUSED) lnext = lse[ridx[wave * 32 + lr]];
     }
     if (ch.nxt >= 0) pre.load(k, v, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
     for (int tl = wave; tl < ntile; tl += kWaves) {
@@ -523,18 +569,33 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
       const float l2 = lnext * kLog2e;
       if (tl + kWaves < ntile) {
         load_q_tile<T, D>(q, ridx, tl + kWaves, lane, qv);
-        lnext = lse[ridx[(tl + kWaves) * 32 + lr]];
+        if constexpr (!FUSED) lnext = lse[ridx[(tl + kWaves) * 32 + lr]];
       }
       f32x16 s[KT];
       qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
-      const int tok = rtok[tl * 32 + lr];
+      const int row = tl * 32 + lr;
+      const int tok = rtok[row];
+      const bool unmasked = tile_unmasked<BK>(tok, it.bs);
+      const int lim = tok < 0 ? -1 : tok - it.bs;
+      float inv = 1.f;
       V8 pb[KK];
-      if (tile_unmasked<BK>(tok, it.bs)) probs<T, BK, false>(s, scale_log2, l2, hl, 0, pb);
-      else probs<T, BK, true>(s, scale_log2, l2, hl, tok < 0 ? -1 : tok - it.bs, pb);
+      if constexpr (FUSED) {
+        const float2 ml = unmasked ? probs_stats<T, BK, false>(s, scale_log2, hl, 0, -INFINITY, pb)
+                                   : probs_stats<T, BK, true>(s, scale_log2, hl, lim, -INFINITY, pb);
+        inv = ml.y > 0.f ? 1.f / ml.y : 0.f;
+        st[tok >= 0 ? (size_t)it.pair0 * g + row : dump_row + lr] = ml;
+      } else {
+        if (unmasked) probs<T, BK, false>(s, scale_log2, l2, hl, 0, pb);
+        else probs<T, BK, true>(s, scale_log2, l2, hl, lim, pb);
+      }
       f32x16 o[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
       pv_tile<T, D, BK>(Vt, pb, lr, hl, o);
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[mt] *= inv;
+      }
       store_tile<PT, D>(stage, o, lane, min(32, nrows - tl * 32),
                         partial + ((size_t)it.pair0 * g + (size_t)tl * 32) * D, dump);
     }
@@ -713,11 +774,16 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   if (busy && hl == 0 && tok >= 0) st_local[qrow] = make_float2(M, L);
 }
 
-template <typename T, int D, int BK, typename PT>
+// FUSED: the rows' (max, sum) run over the local blocks as in k_stats_local
+// (the same merge, so the pair written to st_local is the one it writes) and
+// the accumulator is rescaled when the max grows; the partial row is divided
+// by the final sum.
+template <typename T, int D, int BK, typename PT, bool FUSED>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main_local(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc, const float* __restrict__ lse,
-    PT* __restrict__ local_part, PT* __restrict__ dump, int N, int H, int g, int NB, int groups, float scale_log2) {
+    float2* __restrict__ st_local, PT* __restrict__ local_part, PT* __restrict__ dump, int N, int H, int g, int NB,
+    int groups, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
@@ -741,7 +807,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   const int qrow = local_qrow(it, row, g, HQ);
   const int tok = row < it.rows ? qrow / HQ : -1;
   const unsigned word = tok >= 0 ? (unsigned)loc[(size_t)it.h * N + tok] : 0u;
-  const float l2 = tok >= 0 ? lse[qrow] * kLog2e : 0.f;
+  const float l2 = !FUSED && tok >= 0 ? lse[qrow] * kLog2e : 0.f;
+  float M = -INFINITY, L = 0.f;
   f32x16 o[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16{};
@@ -757,9 +824,30 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
     const int lim = local_lim<BK>(tok, word, kind, kbs);
     V8 pb[KK];
-    if (__all(lim == BK - 1)) probs<T, BK, false>(s, scale_log2, l2, hl, 0, pb);
-    else probs<T, BK, true>(s, scale_log2, l2, hl, lim, pb);
+    if constexpr (FUSED) {
+      // rows that do not select this block (lim < 0) get no probabilities
+      // and keep their statistics
+      const float2 ml = __all(lim == BK - 1) ? probs_stats<T, BK, false>(s, scale_log2, hl, 0, M, pb)
+                                             : probs_stats<T, BK, true>(s, scale_log2, hl, lim, M, pb);
+      if (lim >= 0) {
+        const float mn = fmaxf(M, ml.x);
+        const float alpha = __builtin_amdgcn_exp2f(M - mn);  // 0 while M is -inf
+        L = L * alpha + ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
+        M = mn;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+      }
+    } else {
+      if (__all(lim == BK - 1)) probs<T, BK, false>(s, scale_log2, l2, hl, 0, pb);
+      else probs<T, BK, true>(s, scale_log2, l2, hl, lim, pb);
+    }
     pv_tile<T, D, BK>(Vt, pb, lr, hl, o);
+  }
+  if constexpr (FUSED) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[mt] *= inv;
+    if (busy && hl == 0 && tok >= 0) st_local[qrow] = make_float2(M, L);
   }
   if (busy)
     store_tile<PT, D>(reinterpret_cast<PT*>(qt), o, lane, min(32, it.rows - wave * 32),
@@ -803,11 +891,17 @@ struct Part8<_Float16> {
 // partial row group and skips the local slots; the backward's dQ reduction
 // sums every slot.  Slots are taken 8 at a time; the 8 partial loads are
 // issued together (row 0 stands in for empty slots) and summed in slot order.
-template <typename T, typename PT, bool LOCAL>
+// FUSED (the one-pass forward): the partial rows are per-block softmax
+// averages o_b with (max, sum) pairs (m_b, l_b); O = sum_b l_b 2^(m_b - m) o_b
+// / l with the row's merged (m, l), also written out as row max and lse.
+template <typename T, typename PT, bool LOCAL, bool FUSED>
 __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __restrict__ slot,
                                                            const PT* __restrict__ partial,
                                                            const int32_t* __restrict__ loc,
                                                            const PT* __restrict__ local_part, T* __restrict__ out,
+                                                           const float2* __restrict__ st,
+                                                           const float2* __restrict__ st_local,
+                                                           float* __restrict__ row_max, float* __restrict__ lse,
                                                            int N, int H, int g, int D, int Tn, int TPI) {
   const int ipb = kReduceThreads / TPI;
   const int local = threadIdx.x / TPI;
@@ -822,22 +916,70 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __rest
   T* dst = out + ((size_t)t * H + h) * GD;
   for (int vec = sub; vec < nvec; vec += TPI) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (LOCAL && word != 0u) {
-      const auto x = Part8<PT>::load(local_part + ((size_t)h * N + t) * GD + vec * 8);
+    if constexpr (FUSED) {
+      // One pass in slot order: the row's running max M and sum L (base 2,
+      // scaled scores) merge each pair as k_stats_combine does, and the
+      // accumulator, kept relative to M, is rescaled when M grows; O = acc / L.
+      const int j = vec * 8 / D;  // query head of the vector within the group
+      const size_t r = ((size_t)t * H + h) * g + j;
+      float M = -INFINITY, L = 0.f;
+      if (LOCAL && word != 0u) {
+        const float2 v = st_local[r];
+        const auto x = Part8<PT>::load(local_part + ((size_t)h * N + t) * GD + vec * 8);
+        M = v.x;
+        L = v.y;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = Part8<PT>::at(x, i);
-    }
-    for (int j0 = 0; j0 < Tn; j0 += 8) {
-      int sv[8];
-      typename Part8<PT>::type x[8];
+        for (int i = 0; i < 8; ++i) acc[i] = Part8<PT>::at(x, i) * v.y;
+      }
+      for (int j0 = 0; j0 < Tn; j0 += 8) {
+        int sv[8];
+        float2 v[8];
+        typename Part8<PT>::type x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sv[u] = j0 + u < Tn && !(LOCAL && local_entry(word, j0 + u)) ? sl[j0 + u] : -1;
+        for (int u = 0; u < 8; ++u) sv[u] = j0 + u < Tn && !(LOCAL && local_entry(word, j0 + u)) ? sl[j0 + u] : -1;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = Part8<PT>::load(partial + (size_t)max(sv[u], 0) * GD + vec * 8);
+        for (int u = 0; u < 8; ++u) {
+          v[u] = st[(size_t)max(sv[u], 0) * g + j];
+          x[u] = Part8<PT>::load(partial + (size_t)max(sv[u], 0) * GD + vec * 8);
+        }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < 8; ++u) {
+          if (sv[u] >= 0) {
+            const float mn = fmaxf(M, v[u].x);
+            const float a = __builtin_amdgcn_exp2f(M - mn);  // 0 while M is -inf
+            const float b = v[u].y * __builtin_amdgcn_exp2f(v[u].x - mn);
+            L = L * a + b;
+            M = mn;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += sv[u] >= 0 ? Part8<PT>::at(x[u], i) : 0.f;
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(Part8<PT>::at(x[u], i), b, acc[i] * a);
+          }
+        }
+      }
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= inv;
+      if (vec * 8 % D == 0) {
+        row_max[r] = L > 0.f ? M * kLn2 : -INFINITY;
+        lse[r] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+      }
+    } else {
+      if (LOCAL && word != 0u) {
+        const auto x = Part8<PT>::load(local_part + ((size_t)h * N + t) * GD + vec * 8);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = Part8<PT>::at(x, i);
+      }
+      for (int j0 = 0; j0 < Tn; j0 += 8) {
+        int sv[8];
+        typename Part8<PT>::type x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sv[u] = j0 + u < Tn && !(LOCAL && local_entry(word, j0 + u)) ? sl[j0 + u] : -1;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = Part8<PT>::load(partial + (size_t)max(sv[u], 0) * GD + vec * 8);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += sv[u] >= 0 ? Part8<PT>::at(x[u], i) : 0.f;
+      }
     }
     typename Vec8<T>::type o;
 #pragma unroll
@@ -897,45 +1039,73 @@ void stats_typed(const Geometry& geo, const int32_t* cu, const void* q, const vo
                      geo.NB, groups, sl2);
 }
 
-template <typename T, int D, int BK, typename PT>
-void main_typed(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v,
-                const fsa_index& idx, const float* lse, void* partial, hipStream_t stream) {
+// Main kernels.  With `st` (a statistics workspace) the one-pass variant:
+// no lse is read, and the per-block (max, sum) pairs go to `st` and its local
+// region.
+template <typename T, int D, int BK, typename PT, bool FUSED>
+void main_launch(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v,
+                 const fsa_index& idx, const float* lse, void* st_ws, void* partial, hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
   PT* const dump = static_cast<PT*>(partial) + geo.dump_row * geo.d;
+  float2* const st = static_cast<float2*>(st_ws);
+  float2* const st_local = FUSED ? reinterpret_cast<float2*>(static_cast<char*>(st_ws) + geo.stats_local_off) : nullptr;
   if (geo.max_work > 0)
-    hipLaunchKernelGGL((k_main<T, D, BK, PT>), dim3(persistent_grid(k_main<T, D, BK, PT>, kAttnThreads, geo.max_work)),
+    hipLaunchKernelGGL((k_main<T, D, BK, PT, FUSED>),
+                       dim3(persistent_grid(k_main<T, D, BK, PT, FUSED>, kAttnThreads, geo.max_work)),
                        dim3(kAttnThreads), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
                        static_cast<const T*>(v), p.counts, p.offsets, p.qidx, p.work, p.nwork, p.queue + kQueueInts,
-                       lse, static_cast<PT*>(partial), (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens,
-                       sl2);
+                       lse, st, static_cast<PT*>(partial), (size_t)geo.dump_row, geo.H, geo.g, geo.NB,
+                       geo.chunk_tokens, sl2);
   if (!geo.local) return;
   int groups = 0;
   const unsigned grid = local_grid(geo, &groups);
   PT* const local_part = reinterpret_cast<PT*>(static_cast<char*>(partial) + geo.partial_local_off);
-  hipLaunchKernelGGL((k_main_local<T, D, BK, PT>), dim3(grid), dim3(kAttnThreads), 0, stream,
+  hipLaunchKernelGGL((k_main_local<T, D, BK, PT, FUSED>), dim3(grid), dim3(kAttnThreads), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), cu, p.gboff,
-                     geo.num_seqs, p.loc, lse, local_part, dump, geo.N, geo.H, geo.g, geo.NB, groups, sl2);
+                     geo.num_seqs, p.loc, lse, st_local, local_part, dump, geo.N, geo.H, geo.g, geo.NB, groups, sl2);
 }
 
+template <typename T, int D, int BK, typename PT>
+void main_typed(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v,
+                const fsa_index& idx, const float* lse, void* st_ws, void* partial, hipStream_t stream) {
+  if (st_ws != nullptr) main_launch<T, D, BK, PT, true>(geo, cu, q, k, v, idx, lse, st_ws, partial, stream);
+  else main_launch<T, D, BK, PT, false>(geo, cu, q, k, v, idx, lse, nullptr, partial, stream);
+}
+
+// Reduction.  With `st_ws` the one-pass variant, which also writes row_max
+// and lse.
 template <typename T, typename PT>
 void reduce_typed(const Geometry& geo, const fsa_index& idx, const void* partial, void* out, bool local,
-                  hipStream_t stream) {
+                  const void* st_ws, float* row_max, float* lse, hipStream_t stream) {
   const int nvec = geo.g * geo.d / 8;
   const int tpi = nvec < kReduceThreads ? nvec : kReduceThreads;
   const int ipb = kReduceThreads / tpi;
   const int64_t items = (int64_t)geo.N * geo.H;
   const unsigned blocks = (unsigned)((items + ipb - 1) / ipb);
   const PT* const part = static_cast<const PT*>(partial);
-  if (local) {
-    const auto p = index_ptrs(geo, idx);
-    const PT* const local_part =
-        reinterpret_cast<const PT*>(static_cast<const char*>(partial) + geo.partial_local_off);
-    hipLaunchKernelGGL((k_reduce<T, PT, true>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot, part, p.loc,
-                       local_part, static_cast<T*>(out), geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+  const auto p = index_ptrs(geo, idx);
+  const PT* const local_part =
+      reinterpret_cast<const PT*>(static_cast<const char*>(partial) + geo.partial_local_off);
+  const float2* const st = static_cast<const float2*>(st_ws);
+  const float2* const st_local =
+      st_ws ? reinterpret_cast<const float2*>(static_cast<const char*>(st_ws) + geo.stats_local_off) : nullptr;
+  T* const o = static_cast<T*>(out);
+  if (st_ws != nullptr) {
+    if (local)
+      hipLaunchKernelGGL((k_reduce<T, PT, true, true>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot, part,
+                         p.loc, local_part, o, st, st_local, row_max, lse, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+    else
+      hipLaunchKernelGGL((k_reduce<T, PT, false, true>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot,
+                         part, nullptr, nullptr, o, st, nullptr, row_max, lse, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+  } else if (local) {
+    hipLaunchKernelGGL((k_reduce<T, PT, true, false>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot, part,
+                       p.loc, local_part, o, nullptr, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d, geo.T,
+                       tpi);
   } else {
-    hipLaunchKernelGGL((k_reduce<T, PT, false>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot, part,
-                       nullptr, nullptr, static_cast<T*>(out), geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+    hipLaunchKernelGGL((k_reduce<T, PT, false, false>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot,
+                       part, nullptr, nullptr, o, nullptr, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d,
+                       geo.T, tpi);
   }
 }
 
@@ -953,21 +1123,21 @@ void stats_d(const Geometry& geo, const int32_t* cu, const void* q, const void* 
 
 template <typename T, int BK, typename PT>
 void main_d(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v, const fsa_index& idx,
-            const float* lse, void* partial, hipStream_t s) {
+            const float* lse, void* st_ws, void* partial, hipStream_t s) {
   switch (geo.d) {
-    case 64: main_typed<T, 64, BK, PT>(geo, cu, q, k, v, idx, lse, partial, s); break;
-    case 128: main_typed<T, 128, BK, PT>(geo, cu, q, k, v, idx, lse, partial, s); break;
+    case 64: main_typed<T, 64, BK, PT>(geo, cu, q, k, v, idx, lse, st_ws, partial, s); break;
+    case 128: main_typed<T, 128, BK, PT>(geo, cu, q, k, v, idx, lse, st_ws, partial, s); break;
     default:
-      if constexpr (BK == 64) main_typed<T, 256, BK, PT>(geo, cu, q, k, v, idx, lse, partial, s);
+      if constexpr (BK == 64) main_typed<T, 256, BK, PT>(geo, cu, q, k, v, idx, lse, st_ws, partial, s);
       break;
   }
 }
 
 template <typename T, typename PT>
 void main_bk(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v,
-             const fsa_index& idx, const float* lse, void* partial, hipStream_t s) {
-  if (geo.BK == 64) main_d<T, 64, PT>(geo, cu, q, k, v, idx, lse, partial, s);
-  else main_d<T, 128, PT>(geo, cu, q, k, v, idx, lse, partial, s);
+             const fsa_index& idx, const float* lse, void* st_ws, void* partial, hipStream_t s) {
+  if (geo.BK == 64) main_d<T, 64, PT>(geo, cu, q, k, v, idx, lse, st_ws, partial, s);
+  else main_d<T, 128, PT>(geo, cu, q, k, v, idx, lse, st_ws, partial, s);
 }
 
 }  // namespace
@@ -992,29 +1162,29 @@ hipError_t launch_stats(const Geometry& geo, const int32_t* cu_dev, const void* 
 }
 
 hipError_t launch_main(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
-                       const fsa_index& idx, const float* lse, void* partial, hipStream_t stream) {
+                       const fsa_index& idx, const float* lse, void* st_ws, void* partial, hipStream_t stream) {
   if (geo.N == 0) return hipSuccess;
   const bool p32 = geo.partial_dtype == FSA_PARTIAL_FP32;
   if (geo.dtype == FSA_DTYPE_BF16) {
-    if (p32) main_bk<__bf16, float>(geo, cu_dev, q, k, v, idx, lse, partial, stream);
-    else main_bk<__bf16, __bf16>(geo, cu_dev, q, k, v, idx, lse, partial, stream);
+    if (p32) main_bk<__bf16, float>(geo, cu_dev, q, k, v, idx, lse, st_ws, partial, stream);
+    else main_bk<__bf16, __bf16>(geo, cu_dev, q, k, v, idx, lse, st_ws, partial, stream);
   } else {
-    if (p32) main_bk<_Float16, float>(geo, cu_dev, q, k, v, idx, lse, partial, stream);
-    else main_bk<_Float16, _Float16>(geo, cu_dev, q, k, v, idx, lse, partial, stream);
+    if (p32) main_bk<_Float16, float>(geo, cu_dev, q, k, v, idx, lse, st_ws, partial, stream);
+    else main_bk<_Float16, _Float16>(geo, cu_dev, q, k, v, idx, lse, st_ws, partial, stream);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_reduce(const Geometry& geo, const fsa_index& idx, const void* partial, void* out, bool local,
-                         hipStream_t stream) {
+                         const void* st_ws, float* row_max, float* lse, hipStream_t stream) {
   if (geo.N == 0) return hipSuccess;
   const bool p32 = geo.partial_dtype == FSA_PARTIAL_FP32;
   if (geo.dtype == FSA_DTYPE_BF16) {
-    if (p32) reduce_typed<__bf16, float>(geo, idx, partial, out, local, stream);
-    else reduce_typed<__bf16, __bf16>(geo, idx, partial, out, local, stream);
+    if (p32) reduce_typed<__bf16, float>(geo, idx, partial, out, local, st_ws, row_max, lse, stream);
+    else reduce_typed<__bf16, __bf16>(geo, idx, partial, out, local, st_ws, row_max, lse, stream);
   } else {
-    if (p32) reduce_typed<_Float16, float>(geo, idx, partial, out, local, stream);
-    else reduce_typed<_Float16, _Float16>(geo, idx, partial, out, local, stream);
+    if (p32) reduce_typed<_Float16, float>(geo, idx, partial, out, local, st_ws, row_max, lse, stream);
+    else reduce_typed<_Float16, _Float16>(geo, idx, partial, out, local, st_ws, row_max, lse, stream);
   }
   return hipGetLastError();
 }

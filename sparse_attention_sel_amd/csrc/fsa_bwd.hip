@@ -488,7 +488,7 @@ hipError_t bwd_typed(const Geometry& geo, const int32_t* cu_dev, const void* q, 
                      kv_part, geo.H, geo.g, geo.NB, geo.chunk_tokens, geo.scale, geo.scale * kBwdLog2e);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_reduce(geo, idx, dq_part, dq, false, stream);
+  e = launch_reduce(geo, idx, dq_part, dq, false, nullptr, nullptr, nullptr, stream);
   if (e != hipSuccess) return e;
   const int64_t kthreads = (int64_t)geo.H * geo.NB * BK * (D / 4);
   if (kthreads > 0)

@@ -88,12 +88,17 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
                               const fsa_index& idx, void* ws, hipStream_t stream);
 hipError_t launch_stats(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k,
                         const fsa_index& idx, float* row_max, float* lse, void* ws, hipStream_t stream);
+// st_ws == nullptr: the main kernels of the three-pass forward (P = exp(s -
+// lse) from the given lse).  Otherwise the one-pass variant: per-block
+// softmax averages, their (max, sum) pairs written to st_ws (laid out as the
+// statistics workspace); lse is not read.
 hipError_t launch_main(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
-                       const fsa_index& idx, const float* lse, void* partial, hipStream_t stream);
+                       const fsa_index& idx, const float* lse, void* st_ws, void* partial, hipStream_t stream);
 // local: the forward's reduction (local partial rows plus the other slots);
-// otherwise every slot is summed (the backward's dQ).
+// otherwise every slot is summed (the backward's dQ).  With st_ws (one-pass
+// forward) the rows are weighted by their pairs and row_max / lse written.
 hipError_t launch_reduce(const Geometry& geo, const fsa_index& idx, const void* partial, void* out, bool local,
-                         hipStream_t stream);
+                         const void* st_ws, float* row_max, float* lse, hipStream_t stream);
 hipError_t launch_bwd(const Geometry& geo, const int32_t* cu_dev, const void* q, const void* k, const void* v,
                       const void* out, const void* dout, const float* lse, const fsa_index& idx, void* dq, void* dk,
                       void* dv, void* ws, hipStream_t stream);

@@ -27,8 +27,10 @@ def problem_for(w: Workload, partial: str = "fp32", device="cuda") -> fsa.Proble
     )
 
 
-def run_gpu(w: Workload, partial: str = "fp32", keep_partial: bool = False):
-    """Whole forward on cuda:0.  Returns a dict of host numpy arrays."""
+def run_gpu(w: Workload, partial: str = "fp32", keep_partial: bool = False, onepass: bool = False):
+    """Whole forward on cuda:0 (onepass: fsa_selected_attn_fwd_onepass in
+    place of the statistics and forward calls).  Returns a dict of host numpy
+    arrays."""
     prob = problem_for(w, partial)
     dev = torch.device("cuda:0")
     q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
@@ -40,8 +42,11 @@ def run_gpu(w: Workload, partial: str = "fp32", keep_partial: bool = False):
     row_max = torch.full((n, hq), float("nan"), dtype=torch.float32, device=dev)
     out = torch.full((n, hq, prob.head_dim), float("nan"), dtype=prob.dtype, device=dev)
     fsa.build_index(prob, sel, index, ws.build)
-    fsa.softmax_stats(prob, q, k, index, row_max, lse, ws.stats)
-    fsa.selected_attn_fwd(prob, q, k, v, index, lse, out, ws.partial)
+    if onepass:
+        fsa.selected_attn_fwd_onepass(prob, q, k, v, index, row_max, lse, out, ws.stats, ws.partial)
+    else:
+        fsa.softmax_stats(prob, q, k, index, row_max, lse, ws.stats)
+        fsa.selected_attn_fwd(prob, q, k, v, index, lse, out, ws.partial)
     torch.cuda.synchronize()
     P = index.num_pairs()
     res = {

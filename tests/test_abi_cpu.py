@@ -171,6 +171,14 @@ def test_entry_points_reject_before_launch():
     assert lib.fsa_selected_attn_fwd(P, f, f, f, I, f, None, f, pw, None) == NULL
     assert lib.fsa_selected_attn_fwd(P, f, f, f, I, f, f + 4, f, pw, None) == ALIGN
     assert lib.fsa_selected_attn_fwd(P, f, f, f, I, f, f, f, pw - 1, None) == WS
+    sw = s.stats_ws_bytes
+    assert lib.fsa_selected_attn_fwd_onepass(P, f, f, f, I, None, f, f, f, sw, f, pw, None) == NULL
+    assert lib.fsa_selected_attn_fwd_onepass(P, f, f, f, I, f, f, f, None, sw, f, pw, None) == NULL
+    assert lib.fsa_selected_attn_fwd_onepass(P, f, f, f, I, f, f, f, f, sw, None, pw, None) == NULL
+    assert lib.fsa_selected_attn_fwd_onepass(P, f, f, f, I, f + 2, f, f, f, sw, f, pw, None) == ALIGN
+    assert lib.fsa_selected_attn_fwd_onepass(P, f, f, f, I, f, f, f, f + 8, sw, f, pw, None) == ALIGN
+    assert lib.fsa_selected_attn_fwd_onepass(P, f, f, f, I, f, f, f, f, sw - 1, f, pw, None) == WS
+    assert lib.fsa_selected_attn_fwd_onepass(P, f, f, f, I, f, f, f, f, sw, f, pw - 1, None) == WS
     assert lib.fsa_selected_attn_main(P, f, f, f, I, None, f, pw, None) == NULL
     assert lib.fsa_selected_attn_main(P, f, f, f, I, f, f, pw - 256, None) == WS
     assert lib.fsa_selected_attn_reduce(P, I, f, pw, None, None) == NULL
@@ -237,6 +245,8 @@ def test_empty_problem_accepts_null_data_pointers():
     assert lib.fsa_selected_attn_main(P, None, None, None, I, None, f, s.partial_ws_bytes, None) == OK
     assert lib.fsa_selected_attn_reduce(P, I, f, s.partial_ws_bytes, None, None) == OK
     assert lib.fsa_selected_attn_fwd(P, None, None, None, I, None, None, f, s.partial_ws_bytes, None) == OK
+    assert lib.fsa_selected_attn_fwd_onepass(P, None, None, None, I, None, None, None, f, s.stats_ws_bytes, f,
+                                             s.partial_ws_bytes, None) == OK
     assert lib.fsa_selected_attn_bwd(P, None, None, None, None, None, None, I, None, None, None, f, s.bwd_ws_bytes,
                                      None) == OK
     assert lib.fsa_nsa_selected_attn_fwd(P, None, None, None, None, None, None, None) == OK

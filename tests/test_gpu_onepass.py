@@ -1,0 +1,76 @@
+"""GPU parity of the one-pass forward (fsa_selected_attn_fwd_onepass, through
+the C ABI): statistics fused into the main kernel and the reduction.
+
+Same bar as the three-pass path: O within max-abs 2e-2 (bf16) / 5e-3 (fp16)
+and lse, row max within 1e-3 of the float64 oracle, on every token of the
+small shapes and on sampled tokens of the large ones.  The merged (max, sum)
+of a row is computed exactly as the statistics kernels compute it, so lse and
+row max must equal those of fsa_softmax_stats bit for bit.
+"""
+
+import numpy as np
+import pytest
+
+from gpu_helpers import custom_workload, log, run_gpu, sample_tokens
+from sparse_attention_sel_amd.inputs import cu_seqlens_of
+from test_gpu_parity import CASES, adversarial_sel, check_attention, check_index, oracle_index, workload
+
+import oracle.fsa_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("partial", ["fp32", "input"])
+@pytest.mark.parametrize("name", ["n1k_h1_g1_d64_t4_bf16", "n8k_h4_g2_d128_t16_bf16"])
+def test_onepass_all_tokens(name, partial):
+    w = workload(name)
+    log(f"[run] one-pass {name} partial={partial}")
+    res = run_gpu(w, partial, onepass=True)
+    check_index(res, oracle_index(name))
+    check_attention(res, w)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_onepass_adversarial_selection(case):
+    seqlens, H, g, d, B, T, dtype = CASES[case]
+    rng = np.random.default_rng(700 + case)
+    cu = cu_seqlens_of(seqlens)
+    sel = adversarial_sel(rng, H, cu, B, T)
+    sel[:, ::37, :] = -1  # some rows select nothing
+    w = custom_workload(seqlens, H, g, d, B, T, dtype, sel, seed=900 + case)
+    log(f"[run] one-pass adversarial case {case} {CASES[case]}")
+    res = run_gpu(w, "input", onepass=True)
+    check_index(res, O.build_index(w.sel, w.cu_seqlens, B))
+    check_attention(res, w)
+
+
+@pytest.mark.parametrize(
+    "name,partial",
+    [
+        ("n64k_h4_g4_d128_t16_bf16", "input"),
+        ("n64k_h4_g1_d128_t16_fp16", "fp32"),
+        ("b2_n32k_h8_g8_d256_t16_bf16", "input"),
+        ("n64k_h4_g4_d128_b128_t8_bf16", "input"),
+    ],
+)
+def test_onepass_large_sampled_and_stats_bitwise(name, partial):
+    w = workload(name)
+    log(f"[run] one-pass {name} partial={partial}")
+    one = run_gpu(w, partial, onepass=True)
+    toks = sample_tokens(w.cu_seqlens, w.block_size, n_random=48, seed=2)
+    log(f"    attention on {toks.size} sampled tokens")
+    check_attention(one, w, toks)
+    log("    three-pass statistics for comparison")
+    three = run_gpu(w, partial)
+    for key in ("lse", "row_max"):
+        assert np.array_equal(one[key], three[key]), key
+    d = float(np.max(np.abs(one["out"] - three["out"])))
+    log(f"    max|O one-pass - O three-pass| = {d:.3e}")
+
+
+def test_onepass_deterministic_bitwise():
+    w = workload("n8k_h4_g2_d128_t16_bf16")
+    a = run_gpu(w, "input", onepass=True)
+    b = run_gpu(w, "input", onepass=True)
+    for key in ("out", "lse", "row_max"):
+        assert np.array_equal(a[key], b[key], equal_nan=True), key
