@@ -74,3 +74,39 @@ def test_onepass_deterministic_bitwise():
     b = run_gpu(w, "input", onepass=True)
     for key in ("out", "lse", "row_max"):
         assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+def test_onepass_repeated_and_interleaved_on_one_index():
+    # the one-pass call claims work items through the same index counters as
+    # the three-pass calls: alternating them on one index gives every call
+    # the result of a fresh index
+    import torch
+
+    import sparse_attention_sel_amd as fsa
+
+    w = workload("n8k_h4_g2_d128_t16_bf16")
+    ref1 = run_gpu(w, "input", onepass=True)
+    ref3 = run_gpu(w, "input")
+    dev = torch.device("cuda:0")
+    prob = fsa.Problem(w.cu_seqlens, w.num_kv_heads, w.gqa_group, w.head_dim, w.block_size, w.topk,
+                       dtype=torch.bfloat16, partial_dtype="input", softmax_scale=w.scale, device=dev)
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    index = fsa.allocate_index(prob, dev)
+    ws = fsa.Workspaces(prob, dev, index.sizes)
+    fsa.build_index(prob, torch.from_numpy(w.sel).to(dev), index, ws.build)
+    n, hq = prob.total_tokens, prob.num_q_heads
+    for rnd, onepass in enumerate((True, False, True, False)):
+        log(f"    call {rnd} onepass={onepass}")
+        lse = torch.full((n, hq), float("nan"), dtype=torch.float32, device=dev)
+        row_max = torch.full_like(lse, float("nan"))
+        out = torch.full((n, hq, prob.head_dim), float("nan"), dtype=prob.dtype, device=dev)
+        if onepass:
+            fsa.selected_attn_fwd_onepass(prob, q, k, v, index, row_max, lse, out, ws.stats, ws.partial)
+        else:
+            fsa.softmax_stats(prob, q, k, index, row_max, lse, ws.stats)
+            fsa.selected_attn_fwd(prob, q, k, v, index, lse, out, ws.partial)
+        torch.cuda.synchronize()
+        ref = ref1 if onepass else ref3
+        assert np.array_equal(out.float().cpu().numpy(), ref["out"])
+        assert np.array_equal(lse.cpu().numpy(), ref["lse"])
+        assert np.array_equal(row_max.cpu().numpy(), ref["row_max"])

@@ -268,6 +268,7 @@ def test_empty_problem_through_every_entry_point():
     fsa.build_index(prob, sel, index, ws.build)
     fsa.softmax_stats(prob, q, k, index, row_max, lse, ws.stats)
     fsa.selected_attn_fwd(prob, q, k, v, index, lse, out, ws.partial)
+    fsa.selected_attn_fwd_onepass(prob, q, k, v, index, row_max, lse, out, ws.stats, ws.partial)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     fsa.selected_attn_bwd(prob, q, k, v, out, q, lse, index, dq, dk, dv, ws.bwd)
     fsa.nsa_selected_attn_fwd(prob, q, k, v, sel, lse, out)
