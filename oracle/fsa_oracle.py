@@ -35,7 +35,11 @@ exclusive prefix of counts (the compact output offsets O_i), qidx = the query
 tokens of each segment in ascending order (I_i) and slot[h, t, j] = position of
 entry (h, t, j) in qidx, or -1 for entries that select nothing.
 
-Readings of points the pages leave open are listed in the design doc.
+Where the pages are silent this module takes the plainest reading: a Sel row
+is a set (a repeated block counts once, at its first position), negative
+entries and entries past the token's own block select nothing, key k is
+visible to token t iff k <= t, query head h*g + j belongs to KV head h, and
+lse is in natural-log units with the softmax scale applied.
 """
 
 from __future__ import annotations
