@@ -17,7 +17,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests run only where a GPU is present; on a CPU host they are skipped
-    # (the round driver selects them explicitly with -m gpu on the GPU machine).
+    # (select them with -m gpu on a machine with an MI355X).
     try:
         import torch
 
