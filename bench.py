@@ -394,9 +394,12 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
 
 def measured_peaks(dtype):
     """What this GPU reaches on plain work: a 1 GiB device copy (bytes read +
-    written per second) and an 8192^3 GEMM in the workload's dtype through
-    torch (hipBLASLt), each the median of 10 timed runs."""
+    written per second), an 8192^3 GEMM in the workload's dtype through torch
+    (hipBLASLt) and the library's MFMA loop (independent 32x32x16 MFMAs, eight
+    four-wave workgroups per CU), each the median of 10 timed runs."""
     import torch
+
+    import sparse_attention_sel_amd as fsa
 
     dev = torch.device("cuda:0")
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -419,12 +422,18 @@ def measured_peaks(dtype):
 
     t_copy = timed(lambda: dst.copy_(src))
     t_gemm = timed(lambda: torch.matmul(a, b))
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    mfma_dtype = torch.bfloat16 if dtype == "bf16" else torch.float16
+    wgs, iters = 8 * torch.cuda.get_device_properties(dev).multi_processor_count, 2000
+    loop_flops = fsa.mfma_loop(mfma_dtype, wgs, iters, sink)
+    t_loop = timed(lambda: fsa.mfma_loop(mfma_dtype, wgs, iters, sink))
     out = {
         "copy_gbs": round(2 * src.numel() * 4 / t_copy / 1e9, 1),
         "gemm_tflops": round(2.0 * n ** 3 / t_gemm / 1e12, 1),
         "gemm_dtype": dtype,
+        "mfma_loop_tflops": round(loop_flops / t_loop / 1e12, 1),
     }
-    del src, dst, a, b
+    del src, dst, a, b, sink
     return out
 
 
@@ -527,6 +536,7 @@ def main():
             "hbm_gbs": round(r["bytes"]["main"] / (st["main"] * 1e-3) / 1e9, 1),
             "hbm_frac_of_measured_copy": round(r["bytes"]["main"] / (st["main"] * 1e-3) / 1e9 / peaks["copy_gbs"], 4),
             "mfma_frac_of_measured_gemm": round(main_tflops / peaks["gemm_tflops"], 4),
+            "mfma_frac_of_measured_loop": round(main_tflops / peaks["mfma_loop_tflops"], 4),
         },
         "measured_peaks": peaks,
         "step_ms_median": round(r["step_ms_median"], 4),

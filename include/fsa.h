@@ -299,6 +299,19 @@ int32_t fsa_select_blocks(const fsa_problem* prob, const float* scores, int64_t 
 int32_t fsa_nsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
                                   const int32_t* sel, float* lse, void* out, void* stream);
 
+/*
+ * Measurement: `workgroups` workgroups of four waves each run `iters`
+ * rounds of eight independent v_mfma_f32_32x32x16 (bf16 or fp16, per
+ * fsa_dtype) instructions per wave, for timing the sustained matrix-core
+ * rate, 2 * 32 * 32 * 16 * 8 * iters * 4 * workgroups flops per call.  For
+ * benchmarks that report kernels against a measured peak next to the nominal
+ * one; computes nothing else.
+ *   sink  device fp32 [256], never written for these inputs (keeps the loop).
+ * Returns FSA_ERR_NULL / _SHAPE / _DTYPE before the launch, FSA_ERR_HIP if
+ * it fails.
+ */
+int32_t fsa_mfma_loop(int32_t dtype, int32_t workgroups, int32_t iters, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

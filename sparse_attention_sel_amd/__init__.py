@@ -39,6 +39,7 @@ __all__ = [
     "selected_attn_main",
     "selected_attn_reduce",
     "nsa_selected_attn_fwd",
+    "mfma_loop",
     "selected_attn_bwd",
     "selected_attention_backward",
     "select_blocks",
@@ -148,6 +149,8 @@ def load_library():
     lib.fsa_selected_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, I, vp, vp, vp, vp, sz, vp]
     lib.fsa_select_blocks.restype = i32
     lib.fsa_select_blocks.argtypes = [P, vp, ctypes.c_int64, i32, i32, vp, vp]
+    lib.fsa_mfma_loop.restype = i32
+    lib.fsa_mfma_loop.argtypes = [i32, i32, i32, vp, vp]
     lib.fsa_nsa_selected_attn_fwd.restype = i32
     lib.fsa_nsa_selected_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     if lib.fsa_abi_version() != ABI_VERSION:
@@ -440,6 +443,16 @@ def select_blocks(prob: Problem, scores, init_blocks: int, local_blocks: int, se
     o = _ptr(sel, "sel", torch.int32, (prob.num_kv_heads, prob.total_tokens, prob.topk))
     _check(load_library().fsa_select_blocks(prob.c(), p, S, int(init_blocks), int(local_blocks), o, _stream(stream)),
            "fsa_select_blocks")
+
+
+def mfma_loop(dtype, workgroups: int, iters: int, sink, stream=None) -> float:
+    """fsa_mfma_loop: launch the matrix-core throughput loop; returns the
+    flops it executes.  sink: fp32 device tensor of at least 256 elements."""
+    if sink.dtype != torch.float32 or sink.numel() < 256 or not sink.is_cuda:
+        raise ValueError("sink must be a float32 device tensor of at least 256 elements")
+    _check(load_library().fsa_mfma_loop(DTYPE_CODES[dtype], int(workgroups), int(iters), sink.data_ptr(),
+                                        _stream(stream)), "fsa_mfma_loop")
+    return 2.0 * 32 * 32 * 16 * 8 * iters * 4 * workgroups
 
 
 def nsa_selected_attn_fwd(prob: Problem, q, k, v, sel, lse, out, stream=None):

@@ -194,6 +194,11 @@ def test_entry_points_reject_before_launch():
     assert lib.fsa_selected_attn_bwd(P, f, f, f, f, f + 8, f, I, f, f, f, f, bw, None) == ALIGN
     assert lib.fsa_selected_attn_bwd(P, f, f, f, f, f, f, I, f, f, f, f + 16, bw, None) == ALIGN
     assert lib.fsa_selected_attn_bwd(P, f, f, f, f, f, f, I, f, f, f, f, bw - 1, None) == WS
+    # measurement loop
+    assert lib.fsa_mfma_loop(0, 8, 10, None, None) == NULL
+    assert lib.fsa_mfma_loop(0, 0, 10, f, None) == SHAPE
+    assert lib.fsa_mfma_loop(0, 8, 0, f, None) == SHAPE
+    assert lib.fsa_mfma_loop(5, 8, 10, f, None) == DTYPE
     # block selection
     assert lib.fsa_select_blocks(P, None, 16, 1, 2, f, None) == NULL
     assert lib.fsa_select_blocks(P, f, 16, 1, 2, None, None) == NULL
