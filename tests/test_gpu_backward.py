@@ -80,6 +80,7 @@ CASES = [
     ((200, 57), 1, 3, 256, 64, 4, "fp16"),
     ((700, 300), 2, 4, 128, 128, 6, "bf16"),
     ((257, 130, 1), 1, 3, 64, 128, 4, "fp16"),
+    ((900, 500), 2, 2, 64, 64, 40, "bf16"),
 ]
 
 

@@ -119,6 +119,8 @@ CASES = [
     ((1000,), 2, 1, 128, 128, 8, "bf16"),
     ((200, 333), 3, 5, 256, 64, 7, "bf16"),
     ((64, 1, 65), 1, 2, 64, 64, 1, "fp16"),
+    ((3000, 1100), 2, 4, 128, 64, 48, "bf16"),  # long rows: most blocks, duplicates, out-of-range
+    ((700,), 1, 2, 64, 64, 256, "fp16"),  # the largest T: one token per scatter step
 ]
 
 
