@@ -13,6 +13,16 @@
 //              compact buffer at the segment's offset.
 //   k_reduce   reduction kernel (Key design 3): each (token, KV head) sums its
 //              partial rows in slot order; no atomics.
+//   k_stats_local, k_main_local
+//              the same for the entries of a query's own, previous and first
+//              blocks, computed per query block (one partial row per query).
+//
+// One-pass variant (FUSED, fsa_selected_attn_fwd_onepass): k_main and
+// k_main_local take each row's max and sum over the block's visible keys
+// from the score tile they already hold (probs_stats: the statistics kernel's
+// terms in its order), write the block's softmax average of V and the
+// (max, sum) pair, and k_reduce merges the pairs in slot order into row max
+// and lse while it sums the weighted partial rows; no statistics pass runs.
 //
 // Work items come from the index builder: (segment f, first query of the
 // chunk, block start token, sequence end).  Rows of a chunk are
