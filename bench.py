@@ -32,6 +32,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import math
 import os
 import sys
@@ -114,21 +115,31 @@ def measured_traffic(workload):
     """HBM bytes per launch of the main kernel from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE record of this workload, or None when there is no
     record or the kernel sources changed since it was taken."""
-    import hashlib
-
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(root, "sparse_attention_sel_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    if rec.get("source_sha256") != h.hexdigest():
+    if rec.get("source_sha256") != kernel_source_hash(root):
         return None
     return rec
+
+
+def kernel_source_hash(root):
+    """SHA-256 of the forward kernels' sources with comments and blank lines
+    removed, so that the traffic record follows changes of the code only."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(root, "sparse_attention_sel_amd", "csrc", name)) as f:
+            text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        for line in text.splitlines():
+            line = re.sub(r"//.*", "", line).strip()
+            if line:
+                h.update(line.encode() + b"\n")
+    return h.hexdigest()
 
 
 def kernel_bytes(w, P, P_loc, s_in, s_p):
