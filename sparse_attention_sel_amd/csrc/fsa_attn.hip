@@ -166,13 +166,13 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // clamped indices so that they are unconditional: keys past a partial last
 // block are only ever seen by rows that take the causal mask (their values
 // get weight zero), rows past the chunk are marked with token -1.
-template <typename T, int D, int BK, bool WITH_V>
+template <typename T, int D, int BK, bool WITH_V, int NT>
 struct ItemStage {
   using V8 = typename Vec8<T>::type;
-  static constexpr int KV = BK * D / 8 / kAttnThreads;                          // K vectors per thread
-  static constexpr int VP = WITH_V ? (BK / 2) * (D / 8) / kAttnThreads : 1;    // V key pairs per thread
-  static constexpr int RT = (kRowTable + kAttnThreads - 1) / kAttnThreads;     // table rows per thread
-  static_assert(BK * D / 8 % kAttnThreads == 0 && (BK / 2) * (D / 8) % kAttnThreads == 0, "whole vectors");
+  static constexpr int KV = BK * D / 8 / NT;                        // K vectors per thread
+  static constexpr int VP = WITH_V ? (BK / 2) * (D / 8) / NT : 1;   // V key pairs per thread
+  static constexpr int RT = (kRowTable + NT - 1) / NT;              // table rows per thread
+  static_assert(BK * D / 8 % NT == 0 && (BK / 2) * (D / 8) % NT == 0, "whole vectors");
   Item it;
   V8 k[KV];
   V8 va[VP], vb[VP];
@@ -185,7 +185,7 @@ struct ItemStage {
     constexpr int C8 = D / 8;
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const int vi = threadIdx.x + i * kAttnThreads;
+      const int vi = threadIdx.x + i * NT;
       const int key = min(vi / C8, it.nkeys - 1), c = vi % C8;
       k[i] = load8(kg + ((size_t)(it.bs + key) * H + it.h) * D + c * 8);
     }
@@ -193,7 +193,7 @@ struct ItemStage {
       constexpr int KP = BK / 2;
 #pragma unroll
       for (int i = 0; i < VP; ++i) {
-        const int vi = threadIdx.x + i * kAttnThreads;
+        const int vi = threadIdx.x + i * NT;
         const int c = vi / KP, key = 2 * (vi % KP);
         va[i] = load8(vg + ((size_t)(it.bs + min(key, it.nkeys - 1)) * H + it.h) * D + c * 8);
         vb[i] = load8(vg + ((size_t)(it.bs + min(key + 1, it.nkeys - 1)) * H + it.h) * D + c * 8);
@@ -203,7 +203,7 @@ struct ItemStage {
     // commit), so the loads stay in flight while the current item computes.
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      const int r = threadIdx.x + i * kAttnThreads;
+      const int r = threadIdx.x + i * NT;
       tok[i] = qidx[it.pair0 + min(r / g, it.ntok - 1)];
     }
   }
@@ -213,14 +213,14 @@ struct ItemStage {
     constexpr int C8 = D / 8;
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const int vi = threadIdx.x + i * kAttnThreads;
+      const int vi = threadIdx.x + i * NT;
       *reinterpret_cast<V8*>(Ks + (vi / C8) * k_ld<D>() + (vi % C8) * 8) = k[i];
     }
     if constexpr (WITH_V) {
       constexpr int KP = BK / 2;
 #pragma unroll
       for (int i = 0; i < VP; ++i) {
-        const int vi = threadIdx.x + i * kAttnThreads;
+        const int vi = threadIdx.x + i * NT;
         const int c = vi / KP, key = 2 * (vi % KP);
         const int pos = vt_pos(key);
 #pragma unroll
@@ -233,7 +233,7 @@ struct ItemStage {
     const int nrows = it.ntok * g;
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      const int r = threadIdx.x + i * kAttnThreads;
+      const int r = threadIdx.x + i * NT;
       if (r < kRowTable) {
         const bool ok = r < nrows;
         ridx[r] = (ok ? tok[i] : 0) * HQ + it.h * g + (ok ? r % g : 0);
@@ -247,6 +247,18 @@ struct ItemStage {
 // the tile state fits, one (<= 512) for the wide head dim / long blocks.
 template <int D, int BK>
 constexpr int attn_waves_per_eu() { return (D >= 256 || (D >= 128 && BK >= 128)) ? 1 : 2; }
+
+// Threads of the statistics kernel's workgroups (one wave per 32-row tile in
+// flight).  At 128-key blocks and d = 128 its tile state fits 256 registers
+// but K and the Q tiles fill 113 KB of LDS, one workgroup per CU: eight waves
+// then keep two per SIMD (0.56 against 0.67 ms with four at 64K tokens).  The
+// main kernel's tile state at that shape needs more than 256 registers (an
+// eight-wave variant taking the scores 64 keys at a time spilled and ran no
+// faster), so it keeps four waves at one per SIMD.
+template <int D, int BK>
+constexpr int stats_threads() { return D == 128 && BK == 128 ? 2 * kAttnThreads : kAttnThreads; }
+template <int D, int BK>
+constexpr int stats_waves_per_eu() { return D == 128 && BK == 128 ? 2 : attn_waves_per_eu<D, BK>(); }
 
 // Every key of the block is visible to every row of the tile: the block lies
 // entirely before each row's token (rows of a chunk are in token order, so
@@ -285,15 +297,16 @@ __device__ __forceinline__ float2 row_stats(const f32x16* s, int hl, int lim, fl
 
 // ---- statistics -------------------------------------------------------------
 template <typename T, int D, int BK>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_stats(
+__global__ __launch_bounds__((stats_threads<D, BK>())) __attribute__((amdgpu_waves_per_eu(stats_waves_per_eu<D, BK>()))) void k_stats(
     const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
     const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, float2* __restrict__ st, size_t dump_row, int H,
     int g, int NB, int CT, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32;
+  constexpr int NT = stats_threads<D, BK>(), NW = NT / 64;
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
-  __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
+  __shared__ __attribute__((aligned(16))) T Qt[NW * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
   __shared__ int s_items[2];
   ItemChain ch(queue, nwork[2], s_items);  // the forward list
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
   T* const qt = Qt + wave * 32 * tile_ld<D>();
-  ItemStage<T, D, BK, false> pre;
+  ItemStage<T, D, BK, false, NT> pre;
   pre.load(k, nullptr, qidx, wl, counts, offsets, ch.cur, H, g, NB, CT);
   while (ch.cur >= 0) {
     __syncthreads();  // the previous item's LDS reads are done
@@ -324,9 +337,9 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     V8 qv[KS];
     if (wave < ntile) load_q_tile<T, D>(q, ridx, wave, lane, qv);
     if (ch.nxt >= 0) pre.load(k, nullptr, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
-    for (int tl = wave; tl < ntile; tl += kWaves) {
+    for (int tl = wave; tl < ntile; tl += NW) {
       put_q_tile<T, D>(qt, lane, qv);
-      if (tl + kWaves < ntile) load_q_tile<T, D>(q, ridx, tl + kWaves, lane, qv);
+      if (tl + NW < ntile) load_q_tile<T, D>(q, ridx, tl + NW, lane, qv);
       f32x16 s[KT];
       qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
       const int row = tl * 32 + lr;
@@ -536,10 +549,11 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
+  constexpr int NT = kAttnThreads, NW = kWaves;
   static_assert(32 * Stage<PT, D>::P * sizeof(PT) <= 32 * tile_ld<D>() * sizeof(T), "stage fits the Q tile");
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
   __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
-  __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
+  __shared__ __attribute__((aligned(16))) T Qt[NW * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
   __shared__ int s_items[2];
   ItemChain ch(queue, nwork[2], s_items);  // the forward list
@@ -554,7 +568,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   T* const qt = Qt + wave * 32 * tile_ld<D>();
   PT* const stage = reinterpret_cast<PT*>(qt);
   PT* const dump = partial + dump_row * D;
-  ItemStage<T, D, BK, true> pre;
+  ItemStage<T, D, BK, true, NT> pre;
   pre.load(k, v, qidx, wl, counts, offsets, ch.cur, H, g, NB, CT);
   while (ch.cur >= 0) {
     __syncthreads();  // the previous item's LDS reads are done
@@ -574,12 +588,12 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
       if constexpr (!FUSED) lnext = lse[ridx[wave * 32 + lr]];
     }
     if (ch.nxt >= 0) pre.load(k, v, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
-    for (int tl = wave; tl < ntile; tl += kWaves) {
+    for (int tl = wave; tl < ntile; tl += NW) {
       put_q_tile<T, D>(qt, lane, qv);
       const float l2 = lnext * kLog2e;
-      if (tl + kWaves < ntile) {
-        load_q_tile<T, D>(q, ridx, tl + kWaves, lane, qv);
-        if constexpr (!FUSED) lnext = lse[ridx[(tl + kWaves) * 32 + lr]];
+      if (tl + NW < ntile) {
+        load_q_tile<T, D>(q, ridx, tl + NW, lane, qv);
+        if constexpr (!FUSED) lnext = lse[ridx[(tl + NW) * 32 + lr]];
       }
       f32x16 s[KT];
       qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
@@ -1037,8 +1051,9 @@ void stats_typed(const Geometry& geo, const int32_t* cu, const void* q, const vo
   float2* st = static_cast<float2*>(ws);
   float2* st_local = reinterpret_cast<float2*>(static_cast<char*>(ws) + geo.stats_local_off);
   if (geo.max_work > 0)
-    hipLaunchKernelGGL((k_stats<T, D, BK>), dim3(persistent_grid(k_stats<T, D, BK>, kAttnThreads, geo.max_work)),
-                       dim3(kAttnThreads), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k), p.counts,
+    hipLaunchKernelGGL((k_stats<T, D, BK>),
+                       dim3(persistent_grid(k_stats<T, D, BK>, stats_threads<D, BK>(), geo.max_work)),
+                       dim3(stats_threads<D, BK>()), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k), p.counts,
                        p.offsets, p.qidx, p.work, p.nwork, p.queue, st, (size_t)geo.dump_row, geo.H, geo.g, geo.NB,
                        geo.chunk_tokens, sl2);
   if (!geo.local) return;
