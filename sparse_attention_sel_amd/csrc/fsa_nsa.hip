@@ -162,6 +162,39 @@ __device__ __forceinline__ void nsa_stage_vt(const T* __restrict__ v, int bs, in
   }
 }
 
+// The 32 keys [k0, k0 + 32) of a V block as register pairs (the lane's share
+// of the transposed staging of one 32-key step), and their LDS writes.
+template <typename T, int D>
+struct NsaVHalf {
+  using V8 = typename Vec8<T>::type;
+  static constexpr int VI = 16 * (D / 8) / 64;  // key pairs x 8-column chunks per lane
+  V8 va[VI], vb[VI];
+  __device__ __forceinline__ void load(const T* __restrict__ v, int bs, int k0, int nkeys, int H, int h, int lane) {
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int vi = lane + 64 * i;
+      const int c = vi / 16, key = k0 + 2 * (vi - c * 16);
+      va[i] = nsa_ld8(v + ((size_t)(bs + min(key, nkeys - 1)) * H + h) * D + c * 8);
+      vb[i] = nsa_ld8(v + ((size_t)(bs + min(key + 1, nkeys - 1)) * H + h) * D + c * 8);
+    }
+  }
+  template <int LDH>
+  __device__ __forceinline__ void put(T* __restrict__ Vt, int lane) const {
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const int vi = lane + 64 * i;
+      const int c = vi / 16, key = 2 * (vi - c * 16);
+      const int pos = nsa_vt_pos(key);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint32_t*>(Vt + (c * 8 + e) * LDH + pos) = nsa_bits(va[i][e]) | (nsa_bits(vb[i][e]) << 16);
+    }
+  }
+};
+
+template <int D, int BK>
+constexpr bool nsa_halves() { return D <= 128 && BK == 64; }
+
 template <typename T, int D, int BK>
 __global__ __launch_bounds__(kNsaWaves * 64) void k_nsa(const T* __restrict__ q, const T* __restrict__ k,
                                                         const T* __restrict__ v, const int32_t* __restrict__ sel,
@@ -174,7 +207,13 @@ __global__ __launch_bounds__(kNsaWaves * 64) void k_nsa(const T* __restrict__ q,
   constexpr int KT = BK / 16;  // 16-key tiles of a block
   constexpr int MT = D / 16;   // 16-column tiles of O^T
   constexpr int KK = BK / 32;  // 32-key contraction steps of O^T
-  constexpr int LD = nsa_vt_ld<BK>();
+  // With HALVES (64-key blocks, d <= 128) the block's V goes through the
+  // wave's LDS 32 keys at a time: both halves are loaded at the block start,
+  // the first staged before S, the second (held in registers) after the
+  // first half's PV (15.2 -> 14.3 ms at 64K tokens; forcing three waves per
+  // SIMD with the smaller LDS tile gained nothing more).
+  constexpr bool HALVES = nsa_halves<D, BK>();
+  constexpr int LD = HALVES ? 32 + 8 : nsa_vt_ld<BK>();
   __shared__ __attribute__((aligned(16))) T Vt_all[kNsaWaves * D * LD];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -221,10 +260,16 @@ __global__ __launch_bounds__(kNsaWaves * 64) void k_nsa(const T* __restrict__ q,
     cb.bs = c0 + srow[j] * BK;
     const int nkeys = min(BK, c1 - cb.bs);
     const int lim = t - cb.bs;  // block-local key visible iff key <= lim
+    NsaVHalf<T, D> vh;
     if constexpr (D >= 256) {
       cb.load_k(k, nkeys, H, h, lane);
       cb.load_v(v, nkeys, H, h, lane);
       cb.put_vt(Vt, lane);
+    } else if constexpr (HALVES) {
+      NsaVHalf<T, D> v0;
+      v0.load(v, cb.bs, 0, nkeys, H, h, lane);
+      vh.load(v, cb.bs, 32, nkeys, H, h, lane);
+      v0.template put<LD>(Vt, lane);
     } else {
       nsa_stage_vt<T, D, BK>(v, cb.bs, nkeys, H, h, lane, Vt);
     }
@@ -277,12 +322,26 @@ __global__ __launch_bounds__(kNsaWaves * 64) void k_nsa(const T* __restrict__ q,
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // O^T = alpha O^T + V^T P^T: lane supplies Vt[mt*16 + lr][kk*32 + 8*hu + e].
+    if constexpr (HALVES) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4 acc = o[mt] * alpha;
+      for (int mt = 0; mt < MT; ++mt) o[mt] = mfma16(nsa_ld8(Vt + (mt * 16 + lr) * LD + hu * 8), pb[0], o[mt] * alpha);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      vh.template put<LD>(Vt, lane);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) acc = mfma16(nsa_ld8(Vt + (mt * 16 + lr) * LD + kk * 32 + hu * 8), pb[kk], acc);
-      o[mt] = acc;
+      for (int mt = 0; mt < MT; ++mt) o[mt] = mfma16(nsa_ld8(Vt + (mt * 16 + lr) * LD + hu * 8), pb[1], o[mt]);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 acc = o[mt] * alpha;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) acc = mfma16(nsa_ld8(Vt + (mt * 16 + lr) * LD + kk * 32 + hu * 8), pb[kk], acc);
+        o[mt] = acc;
+      }
     }
     // the next block's staging writes come after these reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
