@@ -606,6 +606,7 @@ def main():
                 "tflops": round(rv["f_alg"] / (rv["ms_per_step"] * 1e-3) / 1e12, 2),
                 "stages_ms": {k_: round(v_, 4) for k_, v_ in stv.items()},
                 "main_mfma_frac": round(rv["f_alg"] / (stv["main"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[wv.dtype], 4),
+                "n_valid": rv["n_valid"],
             }
             del wv
         line["variants"] = var
