@@ -110,3 +110,25 @@ def test_onepass_repeated_and_interleaved_on_one_index():
         assert np.array_equal(out.float().cpu().numpy(), ref["out"])
         assert np.array_equal(lse.cpu().numpy(), ref["lse"])
         assert np.array_equal(row_max.cpu().numpy(), ref["row_max"])
+
+
+def test_backward_from_onepass_forward():
+    # training flow: the one-pass forward's O and lse feed the backward
+    import torch
+
+    import sparse_attention_sel_amd as fsa
+    from sparse_attention_sel_amd.inputs import make_dout
+    from test_gpu_backward import check_all, oracle_grads
+
+    w = workload("n8k_h4_g2_d128_t16_bf16")
+    dev = torch.device("cuda:0")
+    prob = fsa.Problem(w.cu_seqlens, w.num_kv_heads, w.gqa_group, w.head_dim, w.block_size, w.topk,
+                       dtype=torch.bfloat16, partial_dtype="input", softmax_scale=w.scale, device=dev)
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    out, lse, _, index = fsa.selected_attention(prob, q, k, v, torch.from_numpy(w.sel).to(dev), onepass=True)
+    do_cpu = make_dout(prob.total_tokens, prob.num_q_heads, prob.head_dim, w.dtype, 21)
+    dq, dk, dv = fsa.selected_attention_backward(prob, q, k, v, out, do_cpu.to(dev), lse, index)
+    torch.cuda.synchronize()
+    log("[run] backward from the one-pass forward")
+    res = {"dq": dq.float().cpu().numpy(), "dk": dk.float().cpu().numpy(), "dv": dv.float().cpu().numpy()}
+    check_all(res, oracle_grads(w, do_cpu), w.dtype)
