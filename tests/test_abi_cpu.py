@@ -258,3 +258,19 @@ def test_empty_problem_accepts_null_data_pointers():
     assert lib.fsa_select_blocks(P, None, 1, 1, 2, None, None) == OK
     # workspaces stay required
     assert lib.fsa_selected_attn_main(P, None, None, None, I, None, None, s.partial_ws_bytes, None) == NULL
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    # the ABI is C: the header compiles as strict C99 and a C program links
+    # against every declared entry point of libfsa.so (no GPU call is made)
+    src = tmp_path / "use_fsa.c"
+    names = declared_functions()
+    body = "\n".join(f"  (void)&{n};" for n in names)
+    src.write_text('#include "fsa.h"\nint main(void) {\n  fsa_problem p; fsa_sizes s; fsa_index i;\n'
+                   '  (void)p; (void)s; (void)i;\n' + body + '\n  return 0;\n}\n')
+    exe = tmp_path / "use_fsa"
+    lib = fsa.library_path()
+    cmd = ["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", f"-I{os.path.dirname(HEADER)}", str(src),
+           f"-L{os.path.dirname(lib)}", "-l:" + os.path.basename(lib), "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
