@@ -81,6 +81,7 @@ CASES = [
     ((700, 300), 2, 4, 128, 128, 6, "bf16"),
     ((257, 130, 1), 1, 3, 64, 128, 4, "fp16"),
     ((900, 500), 2, 2, 64, 64, 40, "bf16"),
+    ((300, 100), 1, 16, 256, 64, 6, "bf16"),
 ]
 
 

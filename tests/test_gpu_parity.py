@@ -121,6 +121,7 @@ CASES = [
     ((64, 1, 65), 1, 2, 64, 64, 1, "fp16"),
     ((3000, 1100), 2, 4, 128, 64, 48, "bf16"),  # long rows: most blocks, duplicates, out-of-range
     ((700,), 1, 2, 64, 64, 256, "fp16"),  # the largest T: one token per scatter step
+    ((300, 100), 1, 16, 256, 64, 6, "bf16"),  # g * d = 4096: two output vectors per reduction thread
 ]
 
 
