@@ -122,6 +122,8 @@ CASES = [
     ((3000, 1100), 2, 4, 128, 64, 48, "bf16"),  # long rows: most blocks, duplicates, out-of-range
     ((700,), 1, 2, 64, 64, 256, "fp16"),  # the largest T: one token per scatter step
     ((300, 100), 1, 16, 256, 64, 6, "bf16"),  # g * d = 4096: two output vectors per reduction thread
+    ((257,), 2, 3, 256, 64, 5, "fp16"),
+    ((600, 200), 1, 2, 64, 128, 4, "fp16"),
 ]
 
 
