@@ -317,6 +317,35 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
             b.record(stream)
         torch.cuda.synchronize()
         qo_ms = sum(a.elapsed_time(b) for a, b in qev) / len(qev)
+    # the same step captured once in a HIP graph and replayed (the library
+    # allocates nothing and clears its counters with kernels, so the calls
+    # capture as they are): what launch overhead costs at this size
+    graph_ms = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fsa.build_index(prob, sel, index, ws.build)
+            fsa.softmax_stats(prob, q, k, index, row_max, lse, ws.stats)
+            fsa.selected_attn_main(prob, q, k, v, index, lse, ws.partial)
+            fsa.selected_attn_reduce(prob, index, ws.partial, out)
+        graph.replay()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record(stream)
+        for _ in range(steps):
+            graph.replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = ga.elapsed_time(gb) / steps
+        del graph
+    except RuntimeError as e:  # capture unsupported in this runtime: report none
+        log(f"graph capture skipped: {e}")
     # the one-pass forward (fsa_selected_attn_fwd_onepass: the statistics fused
     # into the main kernel and the reduction) on the same inputs: index build
     # plus the fused call per step, timed like the step above
@@ -395,6 +424,7 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
         "selection_ms": sel_ms,
         "selection_bytes": sel_bytes,
         "query_outer_ms": qo_ms,
+        "graph_ms_per_step": graph_ms,
         "onepass": op,
         "backward_ms": bwd_ms,
         "stage_ms": stage,
@@ -574,6 +604,8 @@ def main():
             "tflops_alg": round(f_bwd / (r["backward_ms"] * 1e-3) / 1e12, 2),
             "ratio_to_forward": round(r["backward_ms"] / ms, 3),
         }
+    if r["graph_ms_per_step"] is not None:
+        line["graph_replay_ms_per_step"] = round(r["graph_ms_per_step"], 4)
     if r["onepass"] is not None:
         # not the pages' three-kernel split: a measured alternative, same outputs
         opm = r["onepass"]["ms_per_step"]
