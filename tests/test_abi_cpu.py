@@ -274,3 +274,13 @@ def test_header_is_plain_c_and_links(tmp_path):
            f"-L{os.path.dirname(lib)}", "-l:" + os.path.basename(lib), "-o", str(exe)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no CPU or PyTorch fallback: without libfsa.so every call raises
+    monkeypatch.setattr(fsa, "_LIB", None)
+    monkeypatch.setattr(fsa, "library_path", lambda: str(tmp_path / "absent" / "libfsa.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        fsa.load_library()
+    with pytest.raises(RuntimeError):
+        fsa.get_sizes(prob())
