@@ -198,13 +198,14 @@ def selected_attention_backward(
     dout,
     scale: Optional[float] = None,
     tokens: Optional[Iterable[int]] = None,
+    with_sq: bool = False,
 ):
     """Gradients of ``selected_attention`` for an output gradient ``dout``, in
     float64, one (token, KV head) at a time.
 
-    ``tokens`` restricts the loop to those query tokens: dq is then exact for
-    them (a row's dQ depends on that row only) and zero elsewhere, while dk
-    and dv hold only their contributions.
+    ``tokens`` restricts the loop to those query tokens: dq then holds their
+    rows only (in the given order; a row's dQ depends on that row alone), while
+    dk and dv, full size, hold only those tokens' contributions.
 
     The pages give the forward only and state that the module trains (README,
     Usage: ``loss.backward()``; Evaluation: the unit tests compare forward and
@@ -219,7 +220,15 @@ def selected_attention_backward(
     dK and dV summed over every (t, h) whose key set holds the key.  Rows with
     an empty key set contribute nothing.
 
-    Returns (dq [N, h_q, d], dk [N, h_K, d], dv [N, h_K, d]) in float64.
+    Returns (dq [n, h_q, d] for the n evaluated tokens, dk [N, h_K, d],
+    dv [N, h_K, d]) in float64.
+
+    ``with_sq`` also returns, for bounding the rounding error of an
+    implementation that rounds each term's operands, the sum of the squares of
+    the terms every gradient element adds up: dq_sq over the keys k of
+    (scale dS[:, k] K[k])^2, dk_sq over the rows of (scale dS Q)^2 and dv_sq over
+    the rows of (P dO)^2 (same shapes as dq, dk, dv).  These are not part of
+    the gradient.
     """
     q = np.asarray(q)
     k = np.asarray(k)
@@ -232,11 +241,13 @@ def selected_attention_backward(
     g = HQ // H
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    dq = np.zeros((N, HQ, D), dtype=np.float64)
+    toks = list(range(N)) if tokens is None else [int(x) for x in tokens]
+    dq = np.zeros((len(toks), HQ, D), dtype=np.float64)
     dk = np.zeros((N, H, D), dtype=np.float64)
     dv = np.zeros((N, H, v.shape[2]), dtype=np.float64)
-    toks = range(N) if tokens is None else [int(x) for x in tokens]
-    for t in toks:
+    if with_sq:
+        dq_sq, dk_sq, dv_sq = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
+    for i, t in enumerate(toks):
         s = int(np.searchsorted(cu, t, side="right") - 1)
         c0, c1 = int(cu[s]), int(cu[s + 1])
         for h in range(H):
@@ -255,9 +266,15 @@ def selected_attention_backward(
             dp = doh @ vh.T
             delta = (doh * o).sum(axis=1)
             ds = p * (dp - delta[:, None])
-            dq[t, h * g : (h + 1) * g, :] = scale * (ds @ kh)
+            dq[i, h * g : (h + 1) * g, :] = scale * (ds @ kh)
             dk[keys, h, :] += scale * (ds.T @ qh)
             dv[keys, h, :] += p.T @ doh
+            if with_sq:
+                dq_sq[i, h * g : (h + 1) * g, :] = scale**2 * ((ds**2) @ (kh**2))
+                dk_sq[keys, h, :] += scale**2 * ((ds**2).T @ (qh**2))
+                dv_sq[keys, h, :] += (p**2).T @ (doh**2)
+    if with_sq:
+        return dq, dk, dv, dq_sq, dk_sq, dv_sq
     return dq, dk, dv
 
 

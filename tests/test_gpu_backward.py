@@ -2,9 +2,12 @@
 against the float64 oracle's gradient: the GPU runs its own forward (index,
 statistics, output) and then the backward from that O and lse.
 
-Small shapes compare dQ, dK, dV element by element on every token; the 64K
-shape compares dQ on sampled tokens (a row's dQ depends on that row only) and
-checks dK / dV through the dV column-sum identity and bitwise determinism.
+Small shapes compare dQ, dK, dV element by element on every token.  The
+full-size shapes (through the oracle service, the oracle run in CPU worker
+processes started before the first GPU call) compare dQ on every token and
+dK / dV element by element on the keys of whole blocks: block 0 (every token
+selects it), the last block and the hottest and some random blocks; the dV
+column-sum identity covers every key.
 """
 
 import functools
@@ -14,7 +17,8 @@ import pytest
 import torch
 
 import oracle.fsa_oracle as O
-from gpu_helpers import custom_workload, log, run_gpu_bwd, sample_tokens
+from gpu_helpers import ResultFiles, custom_workload, log, run_gpu_bwd
+from oracle_service import decode_out
 from sparse_attention_sel_amd.inputs import cu_seqlens_of, make_dout, make_sel, make_workload
 from test_gpu_parity import adversarial_sel
 
@@ -160,49 +164,79 @@ def test_backward_deterministic_bitwise():
         assert np.array_equal(a[key], b[key]), key
 
 
-def test_backward_64k_sampled_dq_and_dv_column_sums():
-    w = workload("n64k_h4_g4_d128_t16_bf16")
-    do = dout_for(w, 13)
-    log("[run] bwd 64K g=4 (16-bit partials)")
-    res = run_gpu_bwd(w, do, "input")
-    toks = sample_tokens(w.cu_seqlens, w.block_size, n_random=48, seed=3)
-    log(f"    dq on {toks.size} sampled tokens")
-    dq_ref, _, _ = oracle_grads(w, do, toks)
-    check_all({"dq": res["dq"][toks]}, (dq_ref[toks], None, None), w.dtype, what=("dq",))
+def hot_key_blocks(w, n_hot=3, n_random=2, seed=0):
+    """(sequence, local block) pairs whose keys get an elementwise dK / dV
+    check: every sequence's block 0 (selected by every token: the longest
+    accumulation), its last block, the n_hot blocks selected most often in any
+    KV head, and n_random seeded others."""
+    idx = O.build_index(w.sel, w.cu_seqlens, w.block_size)
+    H = w.num_kv_heads
+    NB = idx["num_blocks"]
+    cnt = idx["counts"].reshape(H, NB).max(axis=0)
+    B = w.block_size
+    gboff = np.concatenate([[0], np.cumsum([-(-L // B) for L in w.seqlens])])
+    rng = np.random.default_rng(seed)
+    out = set()
+    for s_, L in enumerate(w.seqlens):
+        nb = -(-L // B)
+        if nb == 0:
+            continue
+        out.update({(s_, 0), (s_, nb - 1)})
+        c = cnt[gboff[s_] : gboff[s_] + nb].copy()
+        c[0] = -1
+        out.update((s_, int(e)) for e in np.argsort(-c, kind="stable")[:n_hot])
+        out.update((s_, int(e)) for e in rng.integers(0, nb, size=n_random))
+    return sorted(out)
+
+
+def check_large_backward(svc, w, seed, partial="input"):
+    svc.prepare(w.name)
+    do = dout_for(w, seed)
+    log(f"[run] bwd {w.name} (partials: {partial})")
+    res = run_gpu_bwd(w, do, partial, float_out=False)
+    blocks = hot_key_blocks(w)
+    with ResultFiles() as f:
+        r = svc.backward(w.name, seed, f.save("dq", res["dq_bits"]), f.save("dk", res["dk_bits"]),
+                         f.save("dv", res["dv_bits"]), blocks)
+    log(f"    dQ on all {r['tokens']} tokens: max|err|={r['dq_err']:.3e} err/tol={r['dq_ratio']:.3f} at {r['dq_at']}")
+    for nm in ("dk", "dv"):
+        log(f"    {nm} on {r['keys']} keys of blocks {blocks}: max|err|={r[nm + '_err']:.3e} "
+            f"max|ref|={r[nm + '_max_ref']:.3e} err/tol={r[nm + '_ratio']:.3f} at {r[nm + '_at']}")
+    log(f"    (oracle {r['oracle_s']:.1f} s on {r['workers']} processes)")
+    assert r["dq_nonfinite"] == 0 and r["dk_nonfinite"] == 0 and r["dv_nonfinite"] == 0
+    assert r["dq_ratio"] <= 1.0, f"dQ exceeds tolerance at {r['dq_at']}"
+    assert r["dk_ratio"] <= 1.0, f"dK exceeds tolerance at {r['dk_at']}"
+    assert r["dv_ratio"] <= 1.0, f"dV exceeds tolerance at {r['dv_at']}"
+    return res, do
+
+
+def check_dv_column_sums(w, res, do):
     # every softmax row sums to one: sum over keys of dV[:, h] = sum of dO over
-    # the rows of head h (every row attends to its own block here)
+    # the rows of head h (every row attends to its own block here), on all keys
     H, g = w.num_kv_heads, w.gqa_group
-    dof = do.float().numpy().astype(np.float64)
+    dof = do.float().numpy()
+    dv = res["dv_bits"]
     for h in range(H):
-        want = dof[:, h * g : (h + 1) * g, :].sum(axis=(0, 1))
-        dvh = res["dv"][:, h, :].astype(np.float64)
+        want = dof[:, h * g : (h + 1) * g, :].astype(np.float64).sum(axis=(0, 1))
+        dvh = decode_out(dv[:, h, :], w.dtype)
         got = dvh.sum(axis=0)
         # each 16-bit dV element is off by at most half an ulp (2^-9 relative):
         # the column sum by at most 2^-9 sum|dV|; 2^-8 leaves room for fp32 order
         tol = 2.0**-8 * np.abs(dvh).sum(axis=0) + 1e-3
-        log(f"    dV column sums head {h}: max|diff|={float(np.max(np.abs(got - want))):.3e} "
-            f"(tol {float(tol.min()):.3e}..{float(tol.max()):.3e})")
-        assert np.all(np.abs(got - want) <= tol)
-    assert np.all(np.isfinite(res["dk"])) and np.all(np.isfinite(res["dv"]))
-
-
-def test_backward_large_head_shape_sampled_dq_and_dv_column_sums():
-    # two packed 32K sequences, h_K = 8, g = 8, d = 256 with 16-bit partials
-    w = workload("b2_n32k_h8_g8_d256_t16_bf16")
-    do = dout_for(w, 14)
-    log("[run] bwd 2x32K g=8 d=256 (16-bit partials)")
-    res = run_gpu_bwd(w, do, "input")
-    toks = sample_tokens(w.cu_seqlens, w.block_size, n_random=24, seed=4)
-    log(f"    dq on {toks.size} sampled tokens")
-    dq_ref, _, _ = oracle_grads(w, do, toks)
-    check_all({"dq": res["dq"][toks]}, (dq_ref[toks], None, None), w.dtype, what=("dq",))
-    H, g = w.num_kv_heads, w.gqa_group
-    dof = do.float().numpy()
-    for h in range(H):
-        want = dof[:, h * g : (h + 1) * g, :].astype(np.float64).sum(axis=(0, 1))
-        dvh = res["dv"][:, h, :].astype(np.float64)
-        got = dvh.sum(axis=0)
-        tol = 2.0**-8 * np.abs(dvh).sum(axis=0) + 1e-3
         log(f"    dV column sums head {h}: max|diff|={float(np.max(np.abs(got - want))):.3e}")
         assert np.all(np.abs(got - want) <= tol)
-    assert np.all(np.isfinite(res["dk"])) and np.all(np.isfinite(res["dv"]))
+
+
+@pytest.mark.timeout(900)
+def test_backward_64k_all_dq_hot_block_dk_dv(oracle_service):
+    w = workload("n64k_h4_g4_d128_t16_bf16")
+    res, do = check_large_backward(oracle_service, w, 13)
+    check_dv_column_sums(w, res, do)
+
+
+@pytest.mark.timeout(900)
+def test_backward_large_head_shape_all_dq_hot_block_dk_dv(oracle_service):
+    # two packed 32K sequences, h_K = 8, g = 8, d = 256 with 16-bit partials
+    w = workload("b2_n32k_h8_g8_d256_t16_bf16")
+    res, do = check_large_backward(oracle_service, w, 14)
+    check_dv_column_sums(w, res, do)

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle.fsa_oracle as O
-from gpu_helpers import TOL_LSE, TOL_O, custom_workload, log, run_gpu, run_gpu_nsa, sample_tokens
+from gpu_helpers import TOL_LSE, TOL_O, check_full_forward, custom_workload, log, run_gpu, run_gpu_nsa
 from sparse_attention_sel_amd.inputs import cu_seqlens_of, make_workload
 from test_gpu_parity import CASES, adversarial_sel
 
@@ -45,14 +45,13 @@ def test_nsa_all_tokens(name):
     check(run_gpu_nsa(w), w)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", ["n64k_h4_g4_d128_t16_bf16", "n64k_h4_g1_d128_t16_fp16", "b2_n32k_h8_g8_d256_t16_bf16"])
-def test_nsa_large_sampled(name):
+def test_nsa_large_all_tokens(name, oracle_service):
+    oracle_service.prepare(name)
     w = workload(name)
     log(f"[run] nsa {name}")
-    res = run_gpu_nsa(w)
-    toks = sample_tokens(w.cu_seqlens, w.block_size, n_random=64, seed=2)
-    log(f"    attention on {toks.size} sampled tokens")
-    check(res, w, toks)
+    check_full_forward(oracle_service, w, run_gpu_nsa(w), with_row_max=False)
 
 
 @pytest.mark.parametrize("case", range(len(CASES)))

@@ -132,3 +132,52 @@ def test_shuffled_rows_bitwise():
     b = O.selected_attention_backward(q, k, v, shuffle_rows(sel, 7), cu, B, do)
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_sums_of_squared_terms_match_autograd():
+    # with_sq: the sums of squares of the terms each gradient element adds
+    # up, pinned to torch autograd through the dense block-masked softmax:
+    # a row's loss L_r = O_r . dO_r has dL_r/dK_k = scale dS_rk Q_r and
+    # dL_r/dV_k = P_rk dO_r (one term per row), and dL/dS_tk times scale K_k
+    # is the key-k term of dQ_t
+    q, k, v, sel, cu, B, do = small_problem(12, seqlens=(11, 14), H=2, g=2, d=4, B=4, T=3)
+    scale = 1.0 / math.sqrt(4)
+    res = O.selected_attention_backward(q, k, v, sel, cu, B, do, scale, with_sq=True)
+    dq, dk, dv, dq_sq, dk_sq, dv_sq = res
+    base = O.selected_attention_backward(q, k, v, sel, cu, B, do, scale)
+    for a, b in zip(base, (dq, dk, dv)):
+        assert np.array_equal(a, b)  # the gradients themselves are unchanged
+    qt, kt, vt = (torch.tensor(x, dtype=torch.float64) for x in (q, k, v))
+    dot = torch.from_numpy(do)
+
+    def row_losses(kk, vv):
+        return (dense_masked_torch(qt, kk, vv, sel, cu, B, scale) * dot).sum(-1).reshape(-1)
+
+    jk, jv = torch.autograd.functional.jacobian(row_losses, (kt, vt))  # [rows, N, H, D] each
+    np.testing.assert_allclose((jk**2).sum(0).numpy(), dk_sq, atol=1e-12, rtol=1e-10)
+    np.testing.assert_allclose((jv**2).sum(0).numpy(), dv_sq, atol=1e-12, rtol=1e-10)
+    # dQ terms: gradient of L with respect to each head's score matrix
+    N, HQ, D = q.shape
+    H = k.shape[1]
+    g = HQ // H
+    seq = np.searchsorted(cu, np.arange(N), side="right") - 1
+    want = np.zeros_like(dq_sq)
+    for h in range(H):
+        M = np.zeros((N, N), dtype=bool)
+        for t in range(N):
+            c0, c1 = int(cu[seq[t]]), int(cu[seq[t] + 1])
+            for e in sel[h, t]:
+                if e >= 0:
+                    M[t, c0 + e * B : min(c0 + (e + 1) * B, c1)] = True
+        M &= np.tril(np.ones((N, N), dtype=bool))
+        Mt = torch.from_numpy(M)
+        rows = Mt.any(dim=1, keepdim=True)
+        for j in range(g):
+            S = (scale * (qt[:, h * g + j, :] @ kt[:, h, :].T)).requires_grad_(True)
+            Sm = S.masked_fill(~Mt, float("-inf"))
+            P = torch.softmax(torch.where(rows, Sm, torch.zeros_like(Sm)), dim=1)
+            P = torch.where(Mt, P, torch.zeros_like(P))
+            ((P @ vt[:, h, :]) * dot[:, h * g + j, :]).sum().backward()
+            G = S.grad.numpy()  # dL/dS [N, N]
+            want[:, h * g + j, :] = (G**2) @ ((scale * k[:, h, :]) ** 2)
+    np.testing.assert_allclose(want, dq_sq, atol=1e-12, rtol=1e-10)

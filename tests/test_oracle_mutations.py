@@ -66,7 +66,7 @@ def fast_pins():
 # overwrite instead of accumulate
 BWD_MUTATIONS = [
     ("ds = p * (dp - delta[:, None])", "ds = p * dp"),
-    ("dq[t, h * g : (h + 1) * g, :] = scale * (ds @ kh)", "dq[t, h * g : (h + 1) * g, :] = ds @ kh"),
+    ("dq[i, h * g : (h + 1) * g, :] = scale * (ds @ kh)", "dq[i, h * g : (h + 1) * g, :] = ds @ kh"),
     ("dk[keys, h, :] += scale * (ds.T @ qh)", "dk[keys, h, :] += scale * (ds.T @ doh)"),
     ("dk[keys, h, :] += scale * (ds.T @ qh)", "dk[keys, h, :] = scale * (ds.T @ qh)"),
     ("dv[keys, h, :] += p.T @ doh", "dv[keys, h, :] += ds.T @ doh"),
