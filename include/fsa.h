@@ -29,6 +29,8 @@
  * Calls, in order (each enqueues kernels on `stream`, never synchronises):
  *   fsa_get_sizes          host only: byte sizes of every buffer below.
  *   fsa_build_index        Sel -> index tensors I_i / N_valid / O_i.
+ *                          (fsa_build_index_noalloc: the same without a
+ *                          workspace, for callers that cannot allocate.)
  *   fsa_softmax_stats      per-query row max and log-sum-exp.
  *   fsa_selected_attn_fwd  main kernel (partials) + reduction -> O.
  *                          (= fsa_selected_attn_main then _reduce.)
@@ -44,8 +46,9 @@
  *
  * Ownership.  The caller allocates and owns every buffer (device memory
  * unless marked host).  The library allocates nothing, keeps no pointer
- * after a call returns, holds no mutable global state and may be called from
- * several host threads.  Buffers must stay alive until the stream has
+ * after a call returns, holds no mutable global state (except the per-device
+ * address of fsa_build_index_noalloc's static scratch, looked up once) and
+ * may be called from several host threads.  Buffers must stay alive until the stream has
  * executed the enqueued work.  The `fsa_index` buffers and its `aux` blob
  * belong together: build them once, reuse them for the stats and forward
  * calls of the same problem and Sel.  The compute calls (stats, forward,
@@ -85,8 +88,13 @@ typedef enum {
   FSA_ERR_UNSUPPORTED = 4, /* valid shape, but no compiled kernel for it */
   FSA_ERR_WORKSPACE = 5,   /* a workspace is smaller than fsa_get_sizes asks */
   FSA_ERR_HIP = 6,         /* a HIP launch failed */
-  FSA_ERR_ALIGN = 7        /* a pointer is not aligned as documented */
+  FSA_ERR_ALIGN = 7,       /* a pointer is not aligned as documented */
+  FSA_ERR_SCRATCH = 8      /* fsa_build_index_noalloc: the problem needs more build
+                              scratch than FSA_NOALLOC_BUILD_SCRATCH_BYTES */
 } fsa_status;
+
+/* Build scratch held per GPU by fsa_build_index_noalloc (16 MiB). */
+#define FSA_NOALLOC_BUILD_SCRATCH_BYTES (16u << 20)
 
 typedef enum { FSA_DTYPE_BF16 = 0, FSA_DTYPE_FP16 = 1 } fsa_dtype;
 
@@ -170,6 +178,22 @@ int32_t fsa_get_sizes(const fsa_problem* prob, fsa_sizes* out);
  */
 int32_t fsa_build_index(const fsa_problem* prob, const int32_t* sel, const fsa_index* idx,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fsa_build_index without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, outputs and errors as
+ * fsa_build_index; the build scratch lives instead in a static device array
+ * of FSA_NOALLOC_BUILD_SCRATCH_BYTES that each GPU the library runs on holds
+ * until the process ends (its device address is looked up once per device).
+ * Nothing is allocated.  Problems whose build_ws_bytes (fsa_get_sizes)
+ * exceed that size return FSA_ERR_SCRATCH before anything is enqueued (about
+ * 4 MiB at 64K tokens and 4 KV heads, 8 MiB at 2 x 32K tokens and 8 KV heads).
+ * The scratch needs no clearing (every call writes what it reads), but all
+ * calls on one GPU share it: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ */
+int32_t fsa_build_index_noalloc(const fsa_problem* prob, const int32_t* sel, const fsa_index* idx, void* stream);
 
 /*
  * Online-softmax statistics (paper notes, Key design 4; README, Method

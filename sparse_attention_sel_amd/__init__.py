@@ -33,6 +33,7 @@ __all__ = [
     "get_sizes",
     "allocate_index",
     "build_index",
+    "build_index_noalloc",
     "softmax_stats",
     "selected_attn_fwd",
     "selected_attn_fwd_onepass",
@@ -135,6 +136,8 @@ def load_library():
     lib.fsa_get_sizes.argtypes = [P, S]
     lib.fsa_build_index.restype = i32
     lib.fsa_build_index.argtypes = [P, vp, I, vp, sz, vp]
+    lib.fsa_build_index_noalloc.restype = i32
+    lib.fsa_build_index_noalloc.argtypes = [P, vp, I, vp]
     lib.fsa_softmax_stats.restype = i32
     lib.fsa_softmax_stats.argtypes = [P, vp, vp, I, vp, vp, vp, sz, vp]
     lib.fsa_selected_attn_fwd.restype = i32
@@ -297,6 +300,17 @@ def build_index(prob: Problem, sel: torch.Tensor, index: Index, ws: torch.Tensor
     p = _ptr(sel, "sel", torch.int32, (prob.num_kv_heads, prob.total_tokens, prob.topk))
     w, wb = _ws(ws, "build workspace", index.sizes["build_ws_bytes"])
     _check(load_library().fsa_build_index(prob.c(), p, index.c(), w, wb, _stream(stream)), "fsa_build_index")
+
+
+# Build scratch that fsa_build_index_noalloc holds per GPU (FSA_NOALLOC_BUILD_SCRATCH_BYTES).
+NOALLOC_BUILD_SCRATCH_BYTES = 16 << 20
+
+
+def build_index_noalloc(prob: Problem, sel: torch.Tensor, index: Index, stream=None):
+    """fsa_build_index_noalloc: fsa_build_index without a workspace (the
+    library's static per-GPU scratch); allocates nothing."""
+    p = _ptr(sel, "sel", torch.int32, (prob.num_kv_heads, prob.total_tokens, prob.topk))
+    _check(load_library().fsa_build_index_noalloc(prob.c(), p, index.c(), _stream(stream)), "fsa_build_index_noalloc")
 
 
 def _qkv_shapes(prob: Problem):

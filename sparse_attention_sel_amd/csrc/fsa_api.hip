@@ -4,12 +4,39 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "fsa_internal.h"
 
+// Build scratch of fsa_build_index_noalloc: one copy per GPU, held from the
+// library's first use on that GPU until the process ends.  Host code never
+// passes this name to a kernel: on the host it is a stand-in, not the device
+// address, which hipGetSymbolAddress returns per device (scratch_of_device).
+static __device__ __align__(256) unsigned char scratch[FSA_NOALLOC_BUILD_SCRATCH_BYTES];
+
 namespace fsa {
 namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t scratch_of_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FSA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FSA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return FSA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FSA_OK;
+}
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -223,6 +250,9 @@ const char* fsa_status_string(int32_t status) {
     case FSA_ERR_WORKSPACE: return "workspace smaller than fsa_get_sizes requires";
     case FSA_ERR_HIP: return "HIP kernel launch failed";
     case FSA_ERR_ALIGN: return "pointer misaligned";
+    case FSA_ERR_SCRATCH:
+      return "the index build needs more scratch than fsa_build_index_noalloc holds "
+             "(FSA_NOALLOC_BUILD_SCRATCH_BYTES); use fsa_build_index with a workspace";
     default: return "unknown status";
   }
 }
@@ -260,6 +290,21 @@ int32_t fsa_build_index(const fsa_problem* prob, const int32_t* sel, const fsa_i
   if (st != FSA_OK) return st;
   if (!aligned(sel, 4) || !aligned(ws, 256)) return FSA_ERR_ALIGN;
   if (ws_bytes < geo.build_ws_bytes) return FSA_ERR_WORKSPACE;
+  return hip_status(launch_build_index(geo, prob->cu_seqlens_dev, sel, *idx, ws, static_cast<hipStream_t>(stream)));
+}
+
+int32_t fsa_build_index_noalloc(const fsa_problem* prob, const int32_t* sel, const fsa_index* idx, void* stream) {
+  Geometry geo;
+  int32_t st = prepare(prob, &geo);
+  if (st != FSA_OK) return st;
+  if (!data(sel, geo)) return FSA_ERR_NULL;
+  st = check_index(geo, idx);
+  if (st != FSA_OK) return st;
+  if (!aligned(sel, 4)) return FSA_ERR_ALIGN;
+  if (geo.build_ws_bytes > (size_t)FSA_NOALLOC_BUILD_SCRATCH_BYTES) return FSA_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = scratch_of_device(&ws);
+  if (st != FSA_OK) return st;
   return hip_status(launch_build_index(geo, prob->cu_seqlens_dev, sel, *idx, ws, static_cast<hipStream_t>(stream)));
 }
 

@@ -17,7 +17,7 @@ from sparse_attention_sel_amd.inputs import WORKLOADS, cu_seqlens_of
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fsa.h")
 
-OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIGN = range(8)
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIGN, SCRATCH = range(9)
 FAKE = 1 << 40  # 256-byte aligned fake device address, never dereferenced
 
 
@@ -48,9 +48,11 @@ def test_library_is_gfx950():
 def test_version_and_status_strings():
     lib = fsa.load_library()
     assert lib.fsa_abi_version() == fsa.ABI_VERSION == 2
-    for s in range(8):
-        assert len(fsa.status_string(s)) > 0
+    for s in range(9):
+        assert len(fsa.status_string(s)) > 0 and fsa.status_string(s) != "unknown status"
     assert fsa.status_string(99) == "unknown status"
+    m = re.search(r"#define FSA_NOALLOC_BUILD_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == fsa.NOALLOC_BUILD_SCRATCH_BYTES
 
 
 def prob(cu=(0, 1000), H=2, g=2, d=128, B=64, T=16, dtype=0, partial=0, scale=0.0, num_seqs=None, dev=True):
@@ -158,6 +160,21 @@ def test_entry_points_reject_before_launch():
     assert lib.fsa_build_index(P, FAKE, I, FAKE, s.build_ws_bytes - 1, None) == WS
     assert lib.fsa_build_index(ctypes.byref(prob(dev=False)), FAKE, I, FAKE, s.build_ws_bytes, None) == NULL
     assert lib.fsa_build_index(ctypes.byref(prob(g=0)), FAKE, I, FAKE, s.build_ws_bytes, None) == SHAPE
+    # build_index_noalloc: the same checks, no workspace argument, and problems
+    # whose build scratch exceeds the static array are refused
+    assert lib.fsa_build_index_noalloc(None, FAKE, I, None) == NULL
+    assert lib.fsa_build_index_noalloc(P, None, I, None) == NULL
+    assert lib.fsa_build_index_noalloc(P, FAKE, ctypes.byref(null_idx), None) == NULL
+    assert lib.fsa_build_index_noalloc(P, FAKE, ctypes.byref(bad_aux), None) == ALIGN
+    assert lib.fsa_build_index_noalloc(P, FAKE + 2, I, None) == ALIGN
+    assert lib.fsa_build_index_noalloc(ctypes.byref(prob(dev=False)), FAKE, I, None) == NULL
+    assert lib.fsa_build_index_noalloc(ctypes.byref(prob(g=0)), FAKE, I, None) == SHAPE
+    big = prob(cu=(0, 65536), H=16, T=16)
+    st_big, s_big = sizes(big)
+    assert st_big == OK and s_big.build_ws_bytes > fsa.NOALLOC_BUILD_SCRATCH_BYTES
+    assert lib.fsa_build_index_noalloc(ctypes.byref(big), FAKE, I, None) == SCRATCH
+    fits = prob(cu=(0, 32768, 65536), H=8, g=8, d=256)  # the largest workload's shape
+    assert sizes(fits)[1].build_ws_bytes <= fsa.NOALLOC_BUILD_SCRATCH_BYTES
     # softmax_stats
     f = FAKE
     assert lib.fsa_softmax_stats(P, None, f, I, f, f, f, s.stats_ws_bytes, None) == NULL
