@@ -7,8 +7,15 @@ Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--partial input|fp32] [--no-cpu-baseline] [--no-variants]
-                    [--no-query-outer] [--no-backward] [--no-selection] [--no-onepass]
-                    [--cold-reps R]
+                    [--no-query-outer] [--no-backward] [--no-selection]
+                    [--onepass] [--graph] [--cold-reps R]
+
+With the default workload (the 64K-token, 4 KV-head, g = 4 latency shape) the
+line also carries every other workload of the benchmark set under `variants`:
+the 1K and 8K shapes, the 64K fp16 g = 1 shape, the two packed 32K-token
+sequences with d = 256 and g = 8, the 64K bf16 shape at g = 2 and g = 1, and
+the 64K shape with 128-key blocks, each with its stage times, TFLOP/s and the
+main stage's fractions of the MFMA and HBM peaks.
 
 The query-outer forward (fsa_nsa_selected_attn_fwd, the vanilla NSA loop
 order) is timed on the same inputs and reported beside the step, with the
@@ -44,7 +51,15 @@ METRIC = "selected-attn fwd latency (ms) + TFLOP/s at 64K tokens, g=1/2/4; % MFM
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}  # dense MFMA
 DEFAULT_WORKLOAD = "n64k_h4_g4_d128_t16_bf16"
-VARIANTS = ["n64k_h4_g2_d128_t16_bf16", "n64k_h4_g1_d128_t16_bf16", "n64k_h4_g4_d128_b128_t8_bf16"]
+VARIANTS = [
+    "n1k_h1_g1_d64_t4_bf16",
+    "n8k_h4_g2_d128_t16_bf16",
+    "n64k_h4_g1_d128_t16_fp16",
+    "b2_n32k_h8_g8_d256_t16_bf16",
+    "n64k_h4_g2_d128_t16_bf16",
+    "n64k_h4_g1_d128_t16_bf16",
+    "n64k_h4_g4_d128_b128_t8_bf16",
+]
 
 
 def log(msg):
@@ -64,8 +79,9 @@ def parse():
                     help="skip timing the query-outer (vanilla NSA order) forward")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--no-selection", action="store_true", help="skip timing block selection")
-    ap.add_argument("--no-onepass", action="store_true",
-                    help="skip timing the one-pass forward (statistics fused into main and reduction)")
+    ap.add_argument("--onepass", action="store_true",
+                    help="also time the one-pass forward (statistics fused into main and reduction)")
+    ap.add_argument("--graph", action="store_true", help="also time the step captured in a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target wall time of the CPU baseline")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="extra steps timed after a 1 GiB cache-evicting fill each (0: skip)")
@@ -178,13 +194,46 @@ def _oracle_shard(tokens):
     return len(tokens)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cgroup_cpus():
+    """CPU quota of this process's cgroup (cgroup v2 cpu.max), or None."""
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        return None if quota == "max" else round(int(quota) / int(period), 2)
+    except (OSError, ValueError):
+        return None
+
+
 def cpu_baseline(w, target_s):
+    """The float64 oracle on a bounded sample of the workload's query tokens,
+    in worker processes (one per core of this process's CPU share: the
+    affinity set, at most 16, the share of a one-GPU machine), each with one BLAS
+    thread; plus the index oracle (a stable sort over every entry) on the
+    whole workload in this process.  Runs before the GPU is touched (the pool
+    forks)."""
     import multiprocessing as mp
+
+    import oracle
 
     q, k, v = (x.float().numpy() for x in (w.q, w.k, w.v))
     _G.update(q=q, k=k, v=v, sel=w.sel, cu=w.cu_seqlens, B=w.block_size, scale=w.scale)
     n = int(w.cu_seqlens[-1])
-    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    affinity = len(os.sched_getaffinity(0))
+    cores = max(1, min(16, affinity))
+    t0 = time.perf_counter()
+    oracle.build_index(w.sel, w.cu_seqlens, w.block_size)
+    index_s = time.perf_counter() - t0
     rng = np.random.default_rng(12345)
     # calibrate on one core
     probe = np.sort(rng.choice(n, size=min(32, n), replace=False))
@@ -221,15 +270,24 @@ def cpu_baseline(w, target_s):
         "kind": "oracle",
         "sample": f"{m} of {n} query tokens (all KV heads), uniform without replacement, seed 12345; "
                   f"{wall:.1f} s wall on {cores} worker processes, 1 BLAS thread each",
-        "wall_s": wall,
+        "wall_s": round(wall, 3),
+        "cpu_model": cpu_model(),
+        "affinity_cpus": affinity,
+        "cgroup_cpus": cgroup_cpus(),
+        "index_oracle_s": round(index_s, 3),
+        "index_oracle_sample": f"all {n} tokens, one process (numpy stable sort)",
     }
 
 
 # ---------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------
+class _Skip(Exception):
+    pass
+
+
 def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, selection=False, cold_reps=0,
-            onepass=False):
+            onepass=False, graph=False):
     import torch
 
     import sparse_attention_sel_amd as fsa
@@ -322,6 +380,8 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
     # capture as they are): what launch overhead costs at this size
     graph_ms = None
     try:
+        if not graph:
+            raise _Skip()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -344,6 +404,8 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
         torch.cuda.synchronize()
         graph_ms = ga.elapsed_time(gb) / steps
         del graph
+    except _Skip:
+        pass
     except RuntimeError as e:  # capture unsupported in this runtime: report none
         log(f"graph capture skipped: {e}")
     # the one-pass forward (fsa_selected_attn_fwd_onepass: the statistics fused
@@ -429,6 +491,7 @@ def run_gpu(w, partial, steps, warmup, query_outer=False, backward=False, select
         "backward_ms": bwd_ms,
         "stage_ms": stage,
         "pairs": index.num_pairs(),
+        "partial_ws_bytes": int(index.sizes["partial_ws_bytes"]),
         "n_valid": {"min": int(counts.min()), "median": float(np.median(counts)), "max": int(counts.max())},
     }
 
@@ -479,16 +542,34 @@ def measured_peaks(dtype):
 
 
 def measure(w, partial, steps, warmup, query_outer=False, backward=False, selection=False, cold_reps=0,
-            onepass=False):
+            onepass=False, graph=False):
     P_host, P_loc, keys = work_counts(w.sel, w.cu_seqlens, w.block_size)
-    r = run_gpu(w, partial, steps, warmup, query_outer, backward, selection, cold_reps, onepass)
+    r = run_gpu(w, partial, steps, warmup, query_outer, backward, selection, cold_reps, onepass, graph)
     assert r["pairs"] == P_host, (r["pairs"], P_host)
     f_alg = 4.0 * w.gqa_group * w.head_dim * keys
     f_main = 4.0 * w.gqa_group * w.block_size * w.head_dim * P_host
     s_in, s_p = 2, (2 if partial == "input" else 4)
     byts = kernel_bytes(w, P_host, P_loc, s_in, s_p)
-    r.update(f_alg=f_alg, f_main=f_main, bytes=byts, local_pairs=P_loc)
+    N, HQ = int(w.cu_seqlens[-1]), w.num_kv_heads * w.gqa_group
+    # partial rows the main stage writes: one per non-local (block, query) pair
+    # and head, plus one local row per (token, query head) where the local path runs
+    rows_written = (P_host - P_loc) * w.gqa_group + (N * HQ if P_loc else 0)
+    r.update(f_alg=f_alg, f_main=f_main, bytes=byts, local_pairs=P_loc,
+             partial_bytes_written=rows_written * w.head_dim * s_p)
     return r
+
+
+def stage_fractions(r, w):
+    """Main stage against the MFMA (algorithmic FLOPs) and HBM (algorithmic
+    bytes) peaks, and the reduction against HBM."""
+    st = r["stage_ms"]
+    main_tf = r["f_alg"] / (st["main"] * 1e-3) / 1e12
+    return {
+        "main_tflops_alg": round(main_tf, 2),
+        "main_mfma_frac": round(main_tf / PEAK_MFMA_TFLOPS[w.dtype], 4),
+        "main_hbm_frac": round(r["bytes"]["main"] / (st["main"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "reduce_hbm_frac": round(r["bytes"]["reduce"] / (st["reduce"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
 
 
 def main():
@@ -520,7 +601,7 @@ def main():
         log(f"cpu baseline done: {cpu['value']:.4g} TFLOP/s on {cpu['cores']} cores")
     log("gpu run")
     r = measure(w, args.partial, args.steps, args.warmup, not args.no_query_outer, not args.no_backward,
-                not args.no_selection, cold_reps=args.cold_reps, onepass=not args.no_onepass)
+                not args.no_selection, cold_reps=args.cold_reps, onepass=args.onepass, graph=args.graph)
     peaks = measured_peaks(w.dtype)
     log(f"gpu run done: {r['ms_per_step']:.3f} ms/step")
     ms = r["ms_per_step"]
@@ -558,6 +639,11 @@ def main():
             "partial_dtype": w.dtype if args.partial == "input" else "fp32",
             "pairs": r["pairs"],
             "local_pairs": r["local_pairs"],
+            "seed": w.meta.get("seed"),
+        },
+        "partial_buffer": {
+            "bytes_written": int(r["partial_bytes_written"]),
+            "workspace_bytes": r["partial_ws_bytes"],
         },
         "roofline": {
             "bound": "hbm",
@@ -621,24 +707,28 @@ def main():
             "fsa_speedup": round(r["query_outer_ms"] / ms, 3),
         }
     if cpu is not None:
-        line["cpu_baseline"] = {k_: v_ for k_, v_ in cpu.items() if k_ != "wall_s"}
+        line["cpu_baseline"] = cpu
     if not args.no_variants and args.workload == DEFAULT_WORKLOAD:
         var = {}
         for name in VARIANTS:
             log(f"variant {name}")
             wv = make_workload(name)
             rv = measure(wv, args.partial, max(3, args.steps // 2), 2, not args.no_query_outer, not args.no_backward,
-                         onepass=not args.no_onepass)
+                         onepass=args.onepass)
             stv = rv["stage_ms"]
             var[name] = {
                 "ms_per_step": round(rv["ms_per_step"], 4),
+                "tflops": round(rv["f_alg"] / (rv["ms_per_step"] * 1e-3) / 1e12, 2),
+                "dtype": wv.dtype,
+                "stages_ms": {k_: round(v_, 4) for k_, v_ in stv.items()},
+                **stage_fractions(rv, wv),
                 "backward_ms": None if rv["backward_ms"] is None else round(rv["backward_ms"], 4),
                 "query_outer_ms": None if rv["query_outer_ms"] is None else round(rv["query_outer_ms"], 4),
                 "onepass_ms": None if rv["onepass"] is None else round(rv["onepass"]["ms_per_step"], 4),
-                "tflops": round(rv["f_alg"] / (rv["ms_per_step"] * 1e-3) / 1e12, 2),
-                "stages_ms": {k_: round(v_, 4) for k_, v_ in stv.items()},
-                "main_mfma_frac": round(rv["f_alg"] / (stv["main"] * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS[wv.dtype], 4),
+                "pairs": rv["pairs"],
+                "partial_bytes_written": int(rv["partial_bytes_written"]),
                 "n_valid": rv["n_valid"],
+                "seed": wv.meta.get("seed"),
             }
             del wv
         line["variants"] = var

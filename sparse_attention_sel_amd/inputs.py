@@ -373,6 +373,7 @@ def make_workload(name: str, seed: Optional[int] = None, with_qkv: bool = True) 
     cu = cu_seqlens_of(spec.seqlens)
     n = int(cu[-1])
     sel, meta = make_sel(spec.sel_kind, spec.seqlens, spec.num_kv_heads, spec.block_size, spec.topk, s * 10 + 3)
+    meta = dict(meta, seed=s)  # Q, K, V from seed s (make_qkv), Sel from seed 10 s + 3
     if with_qkv:
         q, k, v = make_qkv(n, spec.num_kv_heads, spec.gqa_group, spec.head_dim, spec.dtype, s)
     else:

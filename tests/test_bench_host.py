@@ -1,6 +1,7 @@
 """Host-side logic of bench.py (no GPU): the traffic record's source key and
 the algorithmic byte counts it divides by."""
 
+import json
 import os
 import shutil
 
@@ -43,3 +44,45 @@ def test_kernel_bytes_counts_each_compulsory_access_once():
     main = q + 2 * N * H * d * 2 + N * H * g * 4 + (P - P_loc) * 4 + (P - P_loc) * g * d * 2 + N * H * g * d * 2 + 4 * H * N
     assert b["main"] == main
     assert b["reduce"] == (P - P_loc) * g * d * 2 + N * H * g * d * 2 + H * N * T * 4 + 4 * H * N + q
+
+
+def test_profile_summary_on_rocprof_csv(tmp_path):
+    # the summariser reads rocprofv3's CSV (mangled names of the library's
+    # template kernels) and scales FETCH_SIZE / WRITE_SIZE by a copy's bytes
+    import csv
+
+    from sparse_attention_sel_amd import profile_summary as ps
+
+    mangled = "_ZN3fsa12_GLOBAL__N_16k_mainIDF16bLi128ELi64EDF16bLb0EEEvPKT_S4_S4_PKiS6_S6_Pf"
+    assert ps.demangle(mangled) == "fsa::(anonymous namespace)::k_main<__bf16, 128, 64, __bf16, false>"
+    assert ps.pretty(mangled) == "`k_main<bf16, d=128, B_K=64, partial=bf16>`"
+    assert ps.pretty("_ZN3fsa12_GLOBAL__N_18k_reduceIDF16_fLb1ELb1EEEvPKi") == \
+        "`k_reduce<fp16, partial=fp32, local, one-pass>`"
+    assert ps.pretty("fsa::(anonymous namespace)::k_hist(int const*)") == "`k_hist`"
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+    def pmc(d, counter, rows):
+        os.makedirs(d)
+        with open(os.path.join(d, "x_counter_collection.csv"), "w", newline="") as f:
+            w = csv.writer(f)
+            w.writerow(hdr)
+            for i, (k, v) in enumerate(rows):
+                w.writerow([i, k, counter, v, 0, 1000])
+
+    pmc(tmp_path / "f", "FETCH_SIZE", [(mangled, 100.0), (mangled, 300.0)])
+    pmc(tmp_path / "w", "WRITE_SIZE", [(mangled, 400.0), (mangled, 400.0)])
+    pmc(tmp_path / "cf", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 524288.0)])
+    pmc(tmp_path / "cw", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", 1048576.0)])
+    os.makedirs(tmp_path / "t")
+    with open(tmp_path / "t" / "x_kernel_stats.csv", "w") as f:
+        f.write('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n')
+        f.write(f'"{mangled}",2,2000,1000,100,900,1100,1\n')
+    out, js = tmp_path / "t.md", tmp_path / "t.json"
+    ps.main(["traffic", "--fetch", str(tmp_path / "f"), "--write", str(tmp_path / "w"), "--copy-fetch",
+             str(tmp_path / "cf"), "--copy-write", str(tmp_path / "cw"), "--trace", str(tmp_path / "t"),
+             "--workload", "W", "--command", "c", "--out", str(out), "--json", str(js), "--source-sha256", "h"])
+    rec = json.load(open(js))
+    # copy: 1 GiB read as 524288 KiB of FETCH_SIZE -> x2; average fetch 200 KiB
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    assert rec["fetch_bytes"] == 200 * 1024 * 2 and rec["write_bytes"] == 400 * 1024
+    assert "k_main<bf16, d=128, B_K=64, partial=bf16>" in open(out).read()
