@@ -51,11 +51,11 @@
  * may be called from several host threads.  Buffers must stay alive until the stream has
  * executed the enqueued work.  The `fsa_index` buffers and its `aux` blob
  * belong together: build them once, reuse them for the stats and forward
- * calls of the same problem and Sel.  The compute calls (stats, forward,
- * backward) claim their work items through counters in the `aux` blob, which
- * fsa_build_index clears and every such call leaves cleared when it ends: the
- * calls that take one index must run one after another (as on one stream),
- * never overlapping in time.
+ * calls of the same problem and Sel.  After fsa_build_index the index is only
+ * read: the compute calls (stats, forward, backward) keep their work-queue
+ * counters in their own workspace, so calls that share one index may run
+ * concurrently (other streams, other threads) as long as each uses its own
+ * workspace; calls that share a workspace must not overlap.
  *
  * Errors.  Every call returns FSA_OK (0) or a nonzero fsa_status.  Argument
  * checks run before anything is enqueued: on any status other than
@@ -247,7 +247,14 @@ int32_t fsa_selected_attn_fwd_onepass(const fsa_problem* prob, const void* q, co
  * workgroup per (KV head, KV block, query chunk) stages the block's K and V
  * once, streams the block's query list, and writes the pre-scaled partial
  * rows exp(scale*q.k - lse) @ v contiguously to partial_ws rows
- * [offsets[f] * g, offsets[f+1] * g) (row = pair * g + j, d columns).
+ * [offsets[f] * g, offsets[f+1] * g) (row = pair * g + j, d columns, in the
+ * partial dtype).  For B_K = 64 and g >= 2 the entries of a query's own,
+ * previous and first block (its local entries) are computed per query block
+ * instead: their sum is written to the rows of one of them (the own-block
+ * entry, else the previous-block one, else the first-block one) and the
+ * other local entries' rows are left unwritten.  partial_ws is otherwise
+ * private to the library (it also holds the main kernel's work-queue
+ * counters after the rows); fsa_selected_attn_reduce reads it as written.
  */
 int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const void* k, const void* v,
                                const fsa_index* idx, const float* lse, void* partial_ws,
@@ -255,8 +262,10 @@ int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const voi
 
 /*
  * Reduction kernel alone (paper notes, Key design 3): out[t, h*g + r, :] =
- * sum, over the Sel entries j of row (h, t) in ascending j order whose slot
- * is valid, of partial row slot[h, t, j] * g + r; no atomics.
+ * the sum, over the valid Sel entries j of row (h, t) in ascending j order,
+ * of partial row slot[h, t, j] * g + r (the local entries counted once,
+ * through the rows that hold their sum; see fsa_selected_attn_main); no
+ * atomics.
  */
 int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, const void* partial_ws,
                                  size_t partial_ws_bytes, void* out, void* stream);

@@ -143,8 +143,6 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   off = round_up(off + (size_t)(B + 1) * 4, 256);
   geo->aux_nwork = off;
   off = round_up(off + 16, 256);
-  geo->aux_queue = off;
-  off = round_up(off + (size_t)kQueueKinds * kQueueInts * 4, 256);
   geo->aux_loc = off;
   off = round_up(off + (size_t)std::max<int64_t>(H * N, 1) * 4, 256);
   geo->aux_nloc = off;
@@ -164,22 +162,26 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   geo->build_ws_buckets = round_up((size_t)std::max<int64_t>(H * geo->ntiles * NB, 1) * 4, 256);
   geo->build_ws_cb = round_up(geo->build_ws_buckets + 2 * (size_t)std::max(geo->sort_buckets, 1) * 4, 256);
   geo->build_ws_bytes = round_up(geo->build_ws_cb + 2 * (size_t)(H * NB + 1) * 4, 256);
+  // One partial row per (selecting entry, query head): rows pair * g + j, the
+  // compact output of the pages' index O_i, plus 32 dump rows; no other region
+  // (a query's local row uses the rows of its designated local entry).
   geo->dump_row = std::max<int64_t>(geo->max_pairs, 1) * g;
   const size_t rows = (size_t)geo->dump_row + 32;
-  const size_t local_rows = (size_t)std::max<int64_t>(H * N * g, 1);
   const size_t s_p = geo->partial_dtype == FSA_PARTIAL_FP32 ? 4 : 2;
-  geo->stats_local_off = round_up(rows * 8, 256);
-  geo->stats_ws_bytes = round_up(geo->stats_local_off + local_rows * 8, 256);
-  geo->partial_local_off = round_up(rows * (size_t)geo->d * s_p, 256);
-  geo->partial_ws_bytes = round_up(geo->partial_local_off + local_rows * (size_t)geo->d * s_p, 256);
+  const size_t queue_bytes = (size_t)kQueueInts * 4;
+  geo->stats_queue_off = round_up(rows * 8, 256);
+  geo->stats_ws_bytes = round_up(geo->stats_queue_off + queue_bytes, 256);
+  geo->partial_rows_bytes = round_up(rows * (size_t)geo->d * s_p, 256);
+  geo->partial_queue_off = geo->partial_rows_bytes;
+  geo->partial_ws_bytes = round_up(geo->partial_queue_off + queue_bytes, 256);
   // Backward: the chunk slot offsets[f] / CT + f + c (c < ceil(count_f / CT))
   // is injective and below max_pairs / CT + M + 2.
   geo->bwd_ok = BK == 64 || geo->d <= 128;  // B_K = 128 with d = 256 is not compiled
   geo->kv_slots = geo->max_pairs / geo->chunk_tokens + H * NB + 2;
   geo->bwd_dq_off = round_up((size_t)N * H * g * 4, 256);
-  geo->bwd_kv_off = round_up(geo->bwd_dq_off + geo->partial_local_off, 256);  // dQ rows: no local region
-  geo->bwd_ws_bytes =
-      geo->bwd_ok ? round_up(geo->bwd_kv_off + (size_t)geo->kv_slots * 2 * BK * geo->d * 4, 256) : 0;
+  geo->bwd_kv_off = round_up(geo->bwd_dq_off + geo->partial_rows_bytes, 256);
+  geo->bwd_queue_off = round_up(geo->bwd_kv_off + (size_t)geo->kv_slots * 2 * BK * geo->d * 4, 256);
+  geo->bwd_ws_bytes = geo->bwd_ok ? round_up(geo->bwd_queue_off + queue_bytes, 256) : 0;
   return FSA_OK;
 }
 

@@ -311,10 +311,7 @@ __global__ __launch_bounds__((stats_threads<D, BK>())) __attribute__((amdgpu_wav
   __shared__ int s_items[2];
   ItemChain ch(queue, nwork[2], s_items);  // the forward list
   const int4* const wl = work + nwork[0];
-  if (ch.cur < 0) {
-    ch.finish();
-    return;
-  }
+  if (ch.cur < 0) return;
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
@@ -352,18 +349,17 @@ __global__ __launch_bounds__((stats_threads<D, BK>())) __attribute__((amdgpu_wav
     }
     ch.advance(after);
   }
-  ch.finish();
 }
 
 // One thread per (token, query head): merge the token's local (max, sum) pair
-// and the per-block pairs of its other selecting entries, in slot order, into
-// the row max and lse (stored in natural-log units).  Slots are read 8 at a
-// time and the pairs loaded unconditionally (row 0 stands in for empty and
-// local slots) so that the loads are independent.
+// (at the row of its designated local entry) and the per-block pairs of its
+// other selecting entries, in slot order, into the row max and lse (stored in
+// natural-log units).  Slots are read 8 at a time and the pairs loaded
+// unconditionally (row 0 stands in for empty and local slots) so that the
+// loads are independent.
 __global__ __launch_bounds__(256) void k_stats_combine(const int32_t* __restrict__ slot,
                                                        const float2* __restrict__ st,
                                                        const int32_t* __restrict__ loc,
-                                                       const float2* __restrict__ st_local,
                                                        float* __restrict__ row_max, float* __restrict__ lse, int N,
                                                        int H, int g, int T) {
   const int HQ = H * g;
@@ -375,7 +371,7 @@ __global__ __launch_bounds__(256) void k_stats_combine(const int32_t* __restrict
   const unsigned word = (unsigned)loc[(size_t)h * N + t];
   float M = -INFINITY, L = 0.f;
   if (word != 0u) {
-    const float2 v = st_local[idx];
+    const float2 v = st[(size_t)sl[local_designated(word)] * g + j];
     M = v.x;
     L = v.y;
   }
@@ -474,6 +470,45 @@ __device__ __forceinline__ void store_tile(PT* __restrict__ stage, const f32x16*
   }
 }
 
+// store_tile with a destination row per tile row: lane l < 32 holds in `drow`
+// the partial row (of `partial`, pitch D) of tile row l, or -1 to send it to
+// the matching dump row.  Each row is still written as whole 16-byte pieces.
+template <typename PT, int D>
+__device__ __forceinline__ void store_tile_rows(PT* __restrict__ stage, const f32x16* o, int lane, int64_t drow,
+                                                PT* __restrict__ partial, PT* __restrict__ dump) {
+  constexpr int CW = Stage<PT, D>::CW, P = Stage<PT, D>::P;
+  constexpr int EPL = 16 / (int)sizeof(PT);
+  constexpr int LPR = CW / EPL;
+  constexpr int RPI = 64 / LPR;
+  const int lr = lane & 31, hl = lane >> 5;
+  const int dlo = (int)(uint32_t)(uint64_t)drow, dhi = (int)(uint32_t)((uint64_t)drow >> 32);
+#pragma unroll
+  for (int c = 0; c < D / CW; ++c) {
+#pragma unroll
+    for (int m = 0; m < CW / 32; ++m)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x16& acc = o[(CW / 32) * c + m];
+        stage_write4<PT>(stage + lr * P + m * 32 + 8 * q4 + 4 * hl,
+                         f32x4{acc[4 * q4], acc[4 * q4 + 1], acc[4 * q4 + 2], acc[4 * q4 + 3]});
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = i * RPI + lane / LPR, col = (lane % LPR) * EPL;
+      const int64_t r = (int64_t)(((uint64_t)(uint32_t)__shfl(dhi, row, 64) << 32) | (uint32_t)__shfl(dlo, row, 64));
+      const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * P + col);
+      PT* dst = r >= 0 ? partial + (size_t)r * D : dump + (size_t)row * D;
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst + c * CW + col));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // P = exp2(s * c - lse2) as the 16-bit B operand of O^T = V^T P^T: element e
 // of pb[2*kt + u] is register r = 8*u + e of key tile kt.
 template <typename T, int BK, bool MASKED>
@@ -558,10 +593,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   __shared__ int s_items[2];
   ItemChain ch(queue, nwork[2], s_items);  // the forward list
   const int4* const wl = work + nwork[0];
-  if (ch.cur < 0) {
-    ch.finish();
-    return;
-  }
+  if (ch.cur < 0) return;
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
@@ -625,7 +657,6 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     }
     ch.advance(after);
   }
-  ch.finish();
 }
 
 // ---- local entries, per query block ---------------------------------------------
@@ -639,8 +670,10 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
 // local word), the own block causally.  Statistics: the rows' (max, sum) over
 // those blocks, merged, go to one (max, sum) pair per row.  Main: the rows'
 // exp(s - lse) V over those blocks, summed in registers, go to one partial row
-// per row.  Both land at row (h N + token) g + j of a local region, so the
-// combine and the reduction read one local row instead of up to three.
+// per row.  Both land at the rows of the token's designated local entry
+// (its own-block entry, else previous, else first; k_main skips local entries,
+// so those rows are free), so the combine and the reduction read one local
+// row instead of up to three.
 constexpr int kLocalTiles = kWaves;
 constexpr int kLocalRows = 32 * kLocalTiles;
 
@@ -748,15 +781,29 @@ __device__ __forceinline__ int local_lim(int tok, unsigned word, int kind, int k
   return kind == 0 ? tok - kbs : BK - 1;
 }
 
+// Row (slot * g + j) of a local item's row r where its token's local row
+// goes: the partial / statistics row of the token's designated local entry;
+// -1 for rows past the item and tokens without local entries.
+__device__ __forceinline__ int64_t local_dst(const LocalItem& it, int r, int tok, unsigned word,
+                                             const int32_t* __restrict__ slot, int N, int T, int g) {
+  if (tok < 0 || word == 0u) return -1;
+  const int p = slot[((size_t)it.h * N + tok) * T + local_designated(word)];
+  return (int64_t)p * g + (it.row0 + r) % g;
+}
+
+// queue: the statistics kernel's work-queue counters, cleared by workgroup 0
+// (this kernel runs first in the statistics call).
 template <typename T, int D, int BK>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_stats_local(
     const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc, float2* __restrict__ st_local,
-    int N, int H, int g, int NB, int groups, float scale_log2) {
+    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc,
+    const int32_t* __restrict__ slot, float2* __restrict__ st, int32_t* __restrict__ queue, int N, int H, int g,
+    int Tn, int NB, int groups, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32;
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
   __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
+  if (blockIdx.x == 0) clear_queue(queue);
   const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups);
   if (it.rows == 0) return;
   const int HQ = H * g;
@@ -795,24 +842,28 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
       M = mn;
     }
   }
-  if (busy && hl == 0 && tok >= 0) st_local[qrow] = make_float2(M, L);
+  const int64_t dst = local_dst(it, row, tok, word, slot, N, Tn, g);
+  if (busy && hl == 0 && dst >= 0) st[dst] = make_float2(M, L);
 }
 
 // FUSED: the rows' (max, sum) run over the local blocks as in k_stats_local
-// (the same merge, so the pair written to st_local is the one it writes) and
-// the accumulator is rescaled when the max grows; the partial row is divided
-// by the final sum.
+// (the same merge, so the pair written to st is the one it writes) and the
+// accumulator is rescaled when the max grows; the partial row is divided by
+// the final sum.  queue: the main kernel's work-queue counters, cleared by
+// workgroup 0 (this kernel runs first in the forward call).
 template <typename T, int D, int BK, typename PT, bool FUSED>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main_local(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc, const float* __restrict__ lse,
-    float2* __restrict__ st_local, PT* __restrict__ local_part, PT* __restrict__ dump, int N, int H, int g, int NB,
+    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc,
+    const int32_t* __restrict__ slot, const float* __restrict__ lse, float2* __restrict__ st,
+    PT* __restrict__ partial, PT* __restrict__ dump, int32_t* __restrict__ queue, int N, int H, int g, int Tn, int NB,
     int groups, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
   __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
   __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
+  if (blockIdx.x == 0) clear_queue(queue);
   const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups);
   if (it.rows == 0) return;
   const int HQ = H * g;
@@ -867,15 +918,14 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     }
     pv_tile<T, D, BK>(Vt, pb, lr, hl, o);
   }
+  const int64_t dst = local_dst(it, row, tok, word, slot, N, Tn, g);
   if constexpr (FUSED) {
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[mt] *= inv;
-    if (busy && hl == 0 && tok >= 0) st_local[qrow] = make_float2(M, L);
+    if (busy && hl == 0 && dst >= 0) st[dst] = make_float2(M, L);
   }
-  if (busy)
-    store_tile<PT, D>(reinterpret_cast<PT*>(qt), o, lane, min(32, it.rows - wave * 32),
-                      local_part + ((size_t)(it.h * N + it.bs) * g + it.row0 + wave * 32) * D, dump);
+  if (busy) store_tile_rows<PT, D>(reinterpret_cast<PT*>(qt), o, lane, dst, partial, dump);
 }
 
 // ---- reduce -----------------------------------------------------------------
@@ -921,10 +971,8 @@ struct Part8<_Float16> {
 template <typename T, typename PT, bool LOCAL, bool FUSED>
 __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __restrict__ slot,
                                                            const PT* __restrict__ partial,
-                                                           const int32_t* __restrict__ loc,
-                                                           const PT* __restrict__ local_part, T* __restrict__ out,
+                                                           const int32_t* __restrict__ loc, T* __restrict__ out,
                                                            const float2* __restrict__ st,
-                                                           const float2* __restrict__ st_local,
                                                            float* __restrict__ row_max, float* __restrict__ lse,
                                                            int N, int H, int g, int D, int Tn, int TPI) {
   const int ipb = kReduceThreads / TPI;
@@ -937,6 +985,11 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __rest
   const int GD = g * D, nvec = GD / 8;
   const int32_t* sl = slot + ((size_t)h * N + t) * Tn;
   const unsigned word = LOCAL ? (unsigned)loc[(size_t)h * N + t] : 0u;
+  // The local row group is at the rows of the designated local entry, whose
+  // slot is taken from the first batch of slot loads (the position is below 8
+  // unless Sel puts its local blocks late), so its load issues together with
+  // that batch's partial loads.
+  const int des = LOCAL && word != 0u ? local_designated(word) : 0;
   T* dst = out + ((size_t)t * H + h) * GD;
   for (int vec = sub; vec < nvec; vec += TPI) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -947,24 +1000,30 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __rest
       const int j = vec * 8 / D;  // query head of the vector within the group
       const size_t r = ((size_t)t * H + h) * g + j;
       float M = -INFINITY, L = 0.f;
-      if (LOCAL && word != 0u) {
-        const float2 v = st_local[r];
-        const auto x = Part8<PT>::load(local_part + ((size_t)h * N + t) * GD + vec * 8);
-        M = v.x;
-        L = v.y;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = Part8<PT>::at(x, i) * v.y;
-      }
       for (int j0 = 0; j0 < Tn; j0 += 8) {
-        int sv[8];
+        int raw[8], sv[8];
         float2 v[8];
         typename Part8<PT>::type x[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sv[u] = j0 + u < Tn && !(LOCAL && local_entry(word, j0 + u)) ? sl[j0 + u] : -1;
+        for (int u = 0; u < 8; ++u) raw[u] = j0 + u < Tn ? sl[j0 + u] : -1;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sv[u] = LOCAL && local_entry(word, j0 + u) ? -1 : raw[u];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           v[u] = st[(size_t)max(sv[u], 0) * g + j];
           x[u] = Part8<PT>::load(partial + (size_t)max(sv[u], 0) * GD + vec * 8);
+        }
+        if (LOCAL && j0 == 0 && word != 0u) {
+          int lrow = 0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) lrow = des == u ? raw[u] : lrow;
+          if (des >= 8) lrow = sl[des];
+          const float2 vl = st[(size_t)lrow * g + j];
+          const auto xl = Part8<PT>::load(partial + (size_t)lrow * GD + vec * 8);
+          M = vl.x;
+          L = vl.y;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = Part8<PT>::at(xl, i) * vl.y;
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -987,18 +1046,24 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __rest
         lse[r] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
       }
     } else {
-      if (LOCAL && word != 0u) {
-        const auto x = Part8<PT>::load(local_part + ((size_t)h * N + t) * GD + vec * 8);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = Part8<PT>::at(x, i);
-      }
       for (int j0 = 0; j0 < Tn; j0 += 8) {
-        int sv[8];
+        int raw[8], sv[8];
         typename Part8<PT>::type x[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) sv[u] = j0 + u < Tn && !(LOCAL && local_entry(word, j0 + u)) ? sl[j0 + u] : -1;
+        for (int u = 0; u < 8; ++u) raw[u] = j0 + u < Tn ? sl[j0 + u] : -1;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sv[u] = LOCAL && local_entry(word, j0 + u) ? -1 : raw[u];
 #pragma unroll
         for (int u = 0; u < 8; ++u) x[u] = Part8<PT>::load(partial + (size_t)max(sv[u], 0) * GD + vec * 8);
+        if (LOCAL && j0 == 0 && word != 0u) {
+          int lrow = 0;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) lrow = des == u ? raw[u] : lrow;
+          if (des >= 8) lrow = sl[des];
+          const auto xl = Part8<PT>::load(partial + (size_t)lrow * GD + vec * 8);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = Part8<PT>::at(xl, i);
+        }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
@@ -1020,22 +1085,24 @@ struct Ptrs {
   const int32_t* qidx;
   const int4* work;
   const int32_t* nwork;
-  int32_t* queue;
   const int32_t* gboff;
   const int32_t* loc;
 };
 
 inline Ptrs<int> index_ptrs(const Geometry& geo, const fsa_index& idx) {
-  char* aux = static_cast<char*>(idx.aux);
+  const char* aux = static_cast<const char*>(idx.aux);
   return Ptrs<int>{idx.counts,
                    idx.offsets,
                    idx.qidx,
                    reinterpret_cast<const int4*>(aux + geo.aux_work_sorted),
                    reinterpret_cast<const int32_t*>(aux + geo.aux_nwork),
-                   reinterpret_cast<int32_t*>(aux + geo.aux_queue),
                    reinterpret_cast<const int32_t*>(aux + geo.aux_seq_gboff),
                    reinterpret_cast<const int32_t*>(aux + geo.aux_loc)};
 }
+
+// Zeroes a persistent kernel's queue counters where no local kernel runs
+// before it (the local kernels clear them otherwise).
+__global__ __launch_bounds__(256) void k_clear_queue(int32_t* __restrict__ queue) { clear_queue(queue); }
 
 // Workgroups of the local kernels, one per item (KV head, global block, row group).
 inline unsigned local_grid(const Geometry& geo, int* groups) {
@@ -1049,46 +1116,53 @@ void stats_typed(const Geometry& geo, const int32_t* cu, const void* q, const vo
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
   float2* st = static_cast<float2*>(ws);
-  float2* st_local = reinterpret_cast<float2*>(static_cast<char*>(ws) + geo.stats_local_off);
+  int32_t* const queue = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + geo.stats_queue_off);
+  // the local kernel (or the clear kernel) runs first: it zeroes the queue counters
+  if (geo.local) {
+    int groups = 0;
+    const unsigned grid = local_grid(geo, &groups);
+    hipLaunchKernelGGL((k_stats_local<T, D, BK>), dim3(grid), dim3(kAttnThreads), 0, stream,
+                       static_cast<const T*>(q), static_cast<const T*>(k), cu, p.gboff, geo.num_seqs, p.loc, idx.slot,
+                       st, queue, geo.N, geo.H, geo.g, geo.T, geo.NB, groups, sl2);
+  } else {
+    hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(256), 0, stream, queue);
+  }
   if (geo.max_work > 0)
     hipLaunchKernelGGL((k_stats<T, D, BK>),
                        dim3(persistent_grid(k_stats<T, D, BK>, stats_threads<D, BK>(), geo.max_work)),
                        dim3(stats_threads<D, BK>()), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k), p.counts,
-                       p.offsets, p.qidx, p.work, p.nwork, p.queue, st, (size_t)geo.dump_row, geo.H, geo.g, geo.NB,
+                       p.offsets, p.qidx, p.work, p.nwork, queue, st, (size_t)geo.dump_row, geo.H, geo.g, geo.NB,
                        geo.chunk_tokens, sl2);
-  if (!geo.local) return;
-  int groups = 0;
-  const unsigned grid = local_grid(geo, &groups);
-  hipLaunchKernelGGL((k_stats_local<T, D, BK>), dim3(grid), dim3(kAttnThreads), 0, stream, static_cast<const T*>(q),
-                     static_cast<const T*>(k), cu, p.gboff, geo.num_seqs, p.loc, st_local, geo.N, geo.H, geo.g,
-                     geo.NB, groups, sl2);
 }
 
 // Main kernels.  With `st` (a statistics workspace) the one-pass variant:
-// no lse is read, and the per-block (max, sum) pairs go to `st` and its local
-// region.
+// no lse is read, and the per-block (max, sum) pairs go to `st`.
 template <typename T, int D, int BK, typename PT, bool FUSED>
 void main_launch(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v,
                  const fsa_index& idx, const float* lse, void* st_ws, void* partial, hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
   const float sl2 = geo.scale * kLog2e;
-  PT* const dump = static_cast<PT*>(partial) + geo.dump_row * geo.d;
+  PT* const part = static_cast<PT*>(partial);
+  PT* const dump = part + geo.dump_row * geo.d;
   float2* const st = static_cast<float2*>(st_ws);
-  float2* const st_local = FUSED ? reinterpret_cast<float2*>(static_cast<char*>(st_ws) + geo.stats_local_off) : nullptr;
+  int32_t* const queue = reinterpret_cast<int32_t*>(static_cast<char*>(partial) + geo.partial_queue_off);
+  // the local kernel (or the clear kernel) runs first: it zeroes the queue counters
+  if (geo.local) {
+    int groups = 0;
+    const unsigned grid = local_grid(geo, &groups);
+    hipLaunchKernelGGL((k_main_local<T, D, BK, PT, FUSED>), dim3(grid), dim3(kAttnThreads), 0, stream,
+                       static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), cu, p.gboff,
+                       geo.num_seqs, p.loc, idx.slot, lse, st, part, dump, queue, geo.N, geo.H, geo.g, geo.T,
+                       geo.NB, groups, sl2);
+  } else {
+    hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(256), 0, stream, queue);
+  }
   if (geo.max_work > 0)
     hipLaunchKernelGGL((k_main<T, D, BK, PT, FUSED>),
                        dim3(persistent_grid(k_main<T, D, BK, PT, FUSED>, kAttnThreads, geo.max_work)),
                        dim3(kAttnThreads), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
-                       static_cast<const T*>(v), p.counts, p.offsets, p.qidx, p.work, p.nwork, p.queue + kQueueInts,
-                       lse, st, static_cast<PT*>(partial), (size_t)geo.dump_row, geo.H, geo.g, geo.NB,
-                       geo.chunk_tokens, sl2);
-  if (!geo.local) return;
-  int groups = 0;
-  const unsigned grid = local_grid(geo, &groups);
-  PT* const local_part = reinterpret_cast<PT*>(static_cast<char*>(partial) + geo.partial_local_off);
-  hipLaunchKernelGGL((k_main_local<T, D, BK, PT, FUSED>), dim3(grid), dim3(kAttnThreads), 0, stream,
-                     static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), cu, p.gboff,
-                     geo.num_seqs, p.loc, lse, st_local, local_part, dump, geo.N, geo.H, geo.g, geo.NB, groups, sl2);
+                       static_cast<const T*>(v), p.counts, p.offsets, p.qidx, p.work, p.nwork, queue, lse, st, part,
+                       (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
 }
 
 template <typename T, int D, int BK, typename PT>
@@ -1110,27 +1184,21 @@ void reduce_typed(const Geometry& geo, const fsa_index& idx, const void* partial
   const unsigned blocks = (unsigned)((items + ipb - 1) / ipb);
   const PT* const part = static_cast<const PT*>(partial);
   const auto p = index_ptrs(geo, idx);
-  const PT* const local_part =
-      reinterpret_cast<const PT*>(static_cast<const char*>(partial) + geo.partial_local_off);
   const float2* const st = static_cast<const float2*>(st_ws);
-  const float2* const st_local =
-      st_ws ? reinterpret_cast<const float2*>(static_cast<const char*>(st_ws) + geo.stats_local_off) : nullptr;
   T* const o = static_cast<T*>(out);
   if (st_ws != nullptr) {
     if (local)
       hipLaunchKernelGGL((k_reduce<T, PT, true, true>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot, part,
-                         p.loc, local_part, o, st, st_local, row_max, lse, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+                         p.loc, o, st, row_max, lse, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
     else
       hipLaunchKernelGGL((k_reduce<T, PT, false, true>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot,
-                         part, nullptr, nullptr, o, st, nullptr, row_max, lse, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+                         part, nullptr, o, st, row_max, lse, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
   } else if (local) {
     hipLaunchKernelGGL((k_reduce<T, PT, true, false>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot, part,
-                       p.loc, local_part, o, nullptr, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d, geo.T,
-                       tpi);
+                       p.loc, o, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
   } else {
     hipLaunchKernelGGL((k_reduce<T, PT, false, false>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot,
-                       part, nullptr, nullptr, o, nullptr, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d,
-                       geo.T, tpi);
+                       part, nullptr, o, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
   }
 }
 
@@ -1180,9 +1248,7 @@ hipError_t launch_stats(const Geometry& geo, const int32_t* cu_dev, const void* 
   const auto p = index_ptrs(geo, idx);
   const int64_t n = (int64_t)geo.N * geo.HQ;
   hipLaunchKernelGGL(k_stats_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, idx.slot,
-                     static_cast<const float2*>(ws), p.loc,
-                     reinterpret_cast<const float2*>(static_cast<const char*>(ws) + geo.stats_local_off), row_max, lse,
-                     geo.N, geo.H, geo.g, geo.T);
+                     static_cast<const float2*>(ws), p.loc, row_max, lse, geo.N, geo.H, geo.g, geo.T);
   return hipGetLastError();
 }
 

@@ -121,10 +121,13 @@ constexpr int s_ld() {
 
 // ---- D = rowsum(dO * O) -------------------------------------------------------
 // D / 8 lanes per row, 16-byte loads, a butterfly over those lanes.
+// Workgroup 0 also zeroes the queue counters of k_bwd_main, which runs next.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ out, const T* __restrict__ dout,
-                                                   float* __restrict__ delta, int64_t rows) {
+                                                   float* __restrict__ delta, int64_t rows,
+                                                   int32_t* __restrict__ queue) {
   constexpr int LPR = D / 8;  // lanes per row (8, 16 or 32)
+  if (blockIdx.x == 0) clear_queue(queue);
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = idx / LPR;
   const int c = (int)(idx % LPR);
@@ -410,7 +413,6 @@ __global__ __launch_bounds__(bwd_threads<BK>()) __attribute__((amdgpu_waves_per_
     }
     ch.advance(after);
   }
-  ch.finish();
 }
 
 // ---- dK, dV = ordered sum of the block's chunk slots --------------------------
@@ -472,12 +474,12 @@ hipError_t bwd_typed(const Geometry& geo, const int32_t* cu_dev, const void* q, 
   const int4* work = reinterpret_cast<const int4*>(aux + geo.aux_work_sorted);
   const int32_t* nwork = reinterpret_cast<const int32_t*>(aux + geo.aux_nwork);
   const int32_t* gboff = reinterpret_cast<const int32_t*>(aux + geo.aux_seq_gboff);
-  int32_t* queue = reinterpret_cast<int32_t*>(static_cast<char*>(idx.aux) + geo.aux_queue) + 2 * kQueueInts;
+  int32_t* queue = reinterpret_cast<int32_t*>(wsb + geo.bwd_queue_off);
 
   const int64_t rows = (int64_t)geo.N * geo.HQ;
   const int64_t dthreads = rows * (D / 8);
   hipLaunchKernelGGL((k_bwd_delta<T, D>), dim3((unsigned)((dthreads + 255) / 256)), dim3(256), 0, stream,
-                     static_cast<const T*>(out), static_cast<const T*>(dout), delta, rows);
+                     static_cast<const T*>(out), static_cast<const T*>(dout), delta, rows, queue);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   constexpr int NT = bwd_threads<BK>();

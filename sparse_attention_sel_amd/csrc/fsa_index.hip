@@ -23,17 +23,13 @@ namespace fsa {
 namespace {
 
 // ---- seq_table ------------------------------------------------------------
-// Every workgroup clears its share of the work-queue counters and of the
-// per-segment local counts (which k_hist accumulates); workgroup 0 also
-// builds the per-sequence block offsets.
+// Every workgroup clears its share of the per-segment local counts (which
+// k_hist accumulates); workgroup 0 also builds the per-sequence block offsets.
 __global__ __launch_bounds__(kBuildThreads) void k_seq_table(const int32_t* __restrict__ cu, int num_seqs,
                                                              int BK, int32_t* __restrict__ gboff,
-                                                             int32_t* __restrict__ queue,
                                                              int32_t* __restrict__ nloc, int M) {
   __shared__ int buf[kBuildThreads];
   const int tid = threadIdx.x;
-  for (int i = blockIdx.x * kBuildThreads + tid; i < kQueueKinds * kQueueInts; i += gridDim.x * kBuildThreads)
-    queue[i] = 0;
   for (int i = blockIdx.x * kBuildThreads + tid; i < M; i += gridDim.x * kBuildThreads) nloc[i] = 0;
   if (blockIdx.x != 0) return;
   int carry = 0;
@@ -479,7 +475,7 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
 
   const unsigned zero_wg = (unsigned)std::min<int64_t>(64, (int64_t)M / (4 * kBuildThreads) + 1);
   hipLaunchKernelGGL(k_seq_table, dim3(zero_wg), dim3(kBuildThreads), 0, stream, cu_dev, geo.num_seqs, geo.BK, gboff,
-                     reinterpret_cast<int32_t*>(aux + geo.aux_queue), nloc, M);
+                     nloc, M);
   if (geo.N > 0) {
     hipLaunchKernelGGL(k_hist, dim3(geo.ntiles, geo.H), dim3(kBuildThreads),
                        (2 * geo.win_max + 2 * kHistStage) * sizeof(int), stream, sel, cu_dev, gboff, geo.num_seqs,

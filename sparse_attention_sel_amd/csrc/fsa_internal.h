@@ -54,7 +54,6 @@ struct Geometry {
   // aux blob layout (byte offsets)
   size_t aux_seq_gboff;  // int32 [B+1] exclusive prefix of per-sequence block counts
   size_t aux_nwork;      // int32 [4]: items of the full work list, P, items of the forward list, spare
-  size_t aux_queue;      // int32 [kQueueKinds][kQueueInts]: work-queue counters
   size_t aux_loc;        // int32 [H][N]: local word of each (KV head, token), see local_entry()
   size_t aux_nloc;       // int32 [H * NB]: local entries at the head of each segment (blocks >= 1)
   size_t aux_work_sorted;// int4 [2 * max_work]: work items (segment, first query of the chunk, block
@@ -67,15 +66,21 @@ struct Geometry {
   size_t build_ws_bytes;
   size_t build_ws_buckets;  // byte offset of the work-order bucket counters in the build workspace
   size_t build_ws_cb;       // byte offset of the work-list bases cb_full, cb_fwd (int32 [H * NB + 1] each)
+  // Statistics workspace: (max, sum) float2 per partial row, then the work-queue
+  // counters of the statistics kernel.  Partial workspace: the partial rows
+  // (dump_row + 32 rows of d elements), then the counters of the main kernel.
+  // A query's local row (its own, previous and first block, computed per query
+  // block) sits at the rows of its designated local entry (local_designated).
   size_t stats_ws_bytes;
-  size_t stats_local_off;   // byte offset of the local (max, sum) pairs [N][H * g] in the stats workspace
+  size_t stats_queue_off;   // byte offset of the statistics kernel's queue counters
+  size_t partial_rows_bytes;
   size_t partial_ws_bytes;
-  size_t partial_local_off; // byte offset of the local partial rows [H][N][g][d] in the partial workspace
-  // backward workspace: delta [N, HQ] fp32 | dQ partial rows (as partial_ws) |
-  // dK / dV slots: fp32 [kv_slots][2][BK][d], slot = offsets[f] / CT + f + chunk
+  size_t partial_queue_off; // byte offset of the main kernel's queue counters
+  // backward workspace: delta [N, HQ] fp32 | dQ partial rows (partial_rows_bytes) |
+  // dK / dV slots: fp32 [kv_slots][2][BK][d], slot = offsets[f] / CT + f + chunk | queue counters
   bool bwd_ok;           // a backward kernel is compiled for (d, BK)
   int64_t kv_slots;
-  size_t bwd_dq_off, bwd_kv_off, bwd_ws_bytes;
+  size_t bwd_dq_off, bwd_kv_off, bwd_queue_off, bwd_ws_bytes;
 };
 
 int32_t compute_geometry(const fsa_problem* prob, Geometry* geo);
@@ -166,6 +171,15 @@ __device__ __forceinline__ int local_kind(int e, int own) {
   return e == own ? 0 : e == own - 1 ? 1 : e == 0 ? 2 : -1;
 }
 __device__ __forceinline__ bool local_has(uint32_t word, int kind) { return ((word >> (9 * kind)) & 511u) != 0u; }
+// The designated local entry of a (KV head, token) with local word `word` != 0:
+// its own-block entry, else its previous-block entry, else its first-block
+// entry (the Sel position).  Its partial row (slot * g + j) and statistics
+// row hold the token's local row: k_main does not write the partial rows of
+// local entries, so that row is free.
+__device__ __forceinline__ int local_designated(uint32_t word) {
+  const uint32_t f = (word & 511u) != 0u ? word : (word & (511u << 9)) != 0u ? word >> 9 : word >> 18;
+  return (int)(f & 511u) - 1;
+}
 __device__ __forceinline__ bool local_entry(uint32_t word, int j) {
   const uint32_t x = (uint32_t)j + 1u;
   return (word & 511u) == x || ((word >> 9) & 511u) == x || ((word >> 18) & 511u) == x;
@@ -202,13 +216,13 @@ __device__ __forceinline__ Item read_item(const int4* __restrict__ work, const i
 // the other queues in turn, so every workgroup stays busy while any item is
 // left (item sizes vary, and a static split left some XCDs a quarter more rows
 // than others).  Which workgroup takes an item changes no output.  The
-// counters live in the index's aux blob: the index builder clears them and the
-// last workgroup of each launch sets them back to zero, so launches that use
-// one index must not overlap.
+// counters live in the workspace of the call (statistics, forward or backward
+// workspace), cleared by the kernel that runs before the persistent one, so
+// the index is read-only after it is built and calls that use one index with
+// different workspaces may overlap.
 constexpr int kQueues = 8;
 constexpr int kQueueStride = 32;  // ints between counters: one 128-byte line each
-constexpr int kQueueInts = (kQueues + 1) * kQueueStride;
-constexpr int kQueueKinds = 3;    // 0: statistics, 1: main, 2: backward
+constexpr int kQueueInts = kQueues * kQueueStride;
 
 struct WorkQueue {
   int32_t* q;
@@ -232,15 +246,13 @@ struct WorkQueue {
     }
     return -1;
   }
-  // One thread per workgroup, after its last claim.
-  __device__ __forceinline__ void finish() {
-    __threadfence();
-    if (atomicAdd(q + kQueues * kQueueStride, 1) == (int)gridDim.x - 1) {
-      for (int i = 0; i < kQueues; ++i) atomicExch(q + i * kQueueStride, 0);
-      atomicExch(q + kQueues * kQueueStride, 0);
-    }
-  }
 };
+
+// Zeroes a launch's queue counters; run by one workgroup of the kernel that
+// precedes the persistent kernel on the same stream in the same call.
+__device__ __forceinline__ void clear_queue(int32_t* __restrict__ q) {
+  for (int i = threadIdx.x; i < kQueueInts; i += blockDim.x) q[i] = 0;
+}
 
 // The item chain of one persistent workgroup: every thread knows the current
 // item and the next one (whose staging loads run during the current item);
@@ -274,9 +286,6 @@ struct ItemChain {
   __device__ __forceinline__ void advance(int a) {
     cur = nxt;
     nxt = a;
-  }
-  __device__ __forceinline__ void finish() {
-    if (threadIdx.x == 0) wq.finish();
   }
 };
 

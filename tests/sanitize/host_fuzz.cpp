@@ -8,8 +8,8 @@
 //     overflow (UBSan traps signed overflow);
 //   * for valid problems the workspace layout is ordered, aligned and large
 //     enough for the rows the kernels address: partial rows (pair * g + j)
-//     and the dump rows below the local region, stats pairs likewise, the aux
-//     blob's regions in order;
+//     and the dump rows below the queue counters, stats pairs likewise, the
+//     aux blob's regions in order;
 //   * the work-list and slot arithmetic stays in bounds for the largest
 //     selection the problem allows: segment counts at their per-block bound
 //     (tokens from the block's start to its sequence's end) until max_pairs
@@ -47,11 +47,13 @@ void check_counts(const fsa::Geometry& geo, const std::vector<int32_t>& cu, std:
   CHECK(off <= geo.max_pairs);
   CHECK(items <= geo.max_work);
   CHECK(max_slot < geo.kv_slots);
-  // partial rows of the last pair and the dump rows fit below the local region
+  // partial rows of the last pair and the dump rows fit below the queue counters
   const size_t s_p = geo.partial_dtype == FSA_PARTIAL_FP32 ? 4 : 2;
-  CHECK(((size_t)off * geo.g + 32) * geo.d * s_p <= geo.partial_local_off);
-  CHECK(((size_t)geo.dump_row + 32) * geo.d * s_p <= geo.partial_local_off);
-  CHECK(((size_t)geo.dump_row + 32) * 8 <= geo.stats_local_off);
+  CHECK(((size_t)off * geo.g + 32) * geo.d * s_p <= geo.partial_queue_off);
+  CHECK(((size_t)geo.dump_row + 32) * geo.d * s_p <= geo.partial_queue_off);
+  CHECK(((size_t)geo.dump_row + 32) * 8 <= geo.stats_queue_off);
+  CHECK(geo.partial_queue_off + (size_t)fsa::kQueueInts * 4 <= geo.partial_ws_bytes);
+  CHECK(geo.stats_queue_off + (size_t)fsa::kQueueInts * 4 <= geo.stats_ws_bytes);
 }
 
 // Largest per-segment counts: block e of sequence s can be selected by the
@@ -126,13 +128,14 @@ int main(int argc, char** argv) {
     CHECK(sz.counts_bytes >= 4 && sz.qidx_bytes >= 4 && sz.slot_bytes >= 4);
     CHECK(sz.offsets_bytes == ((size_t)geo.H * geo.NB + 1) * 4);
     CHECK(sz.total_tokens == cu[B] && sz.num_blocks == geo.NB);
-    CHECK(geo.aux_seq_gboff < geo.aux_nwork && geo.aux_nwork < geo.aux_queue && geo.aux_queue < geo.aux_loc &&
-          geo.aux_loc < geo.aux_nloc && geo.aux_nloc < geo.aux_work_sorted && geo.aux_work_sorted < geo.aux_bytes);
-    CHECK(geo.aux_work_sorted % 256 == 0 && geo.partial_local_off % 256 == 0 && geo.stats_local_off % 256 == 0);
+    CHECK(geo.aux_seq_gboff < geo.aux_nwork && geo.aux_nwork < geo.aux_loc && geo.aux_loc < geo.aux_nloc &&
+          geo.aux_nloc < geo.aux_work_sorted && geo.aux_work_sorted < geo.aux_bytes);
+    CHECK(geo.aux_work_sorted % 256 == 0 && geo.partial_queue_off % 256 == 0 && geo.stats_queue_off % 256 == 0);
     CHECK((int64_t)geo.H * geo.ntiles * geo.NB <= fsa::kMaxTileHist || geo.N == 0);
     CHECK(geo.win_max >= 1 && geo.win_max <= fsa::kWinMax);
-    CHECK(geo.partial_ws_bytes >= geo.partial_local_off + (size_t)geo.H * geo.N * geo.g * geo.d * 2);
-    CHECK(!geo.bwd_ok || geo.bwd_ws_bytes >= geo.bwd_kv_off + (size_t)geo.kv_slots * 2 * geo.BK * geo.d * 4);
+    CHECK(!geo.bwd_ok || (geo.bwd_queue_off >= geo.bwd_kv_off + (size_t)geo.kv_slots * 2 * geo.BK * geo.d * 4 &&
+                          geo.bwd_ws_bytes >= geo.bwd_queue_off + (size_t)fsa::kQueueInts * 4));
+    CHECK(geo.bwd_kv_off >= geo.bwd_dq_off + geo.partial_rows_bytes);
     // work-list and slot bounds for the heaviest and for random selections
     if ((int64_t)geo.H * geo.NB <= (1 << 22)) {
       check_counts(geo, cu, heavy_counts(geo, cu, rng, false));

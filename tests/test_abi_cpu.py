@@ -88,16 +88,22 @@ def test_sizes_closed_form(name):
     assert s.max_pairs == pmax
     assert s.counts_bytes == 4 * H * sum(nb) and s.offsets_bytes == 4 * (H * sum(nb) + 1)
     assert s.slot_bytes == 4 * H * N * T and s.qidx_bytes == 4 * pmax
-    # partial rows of every pair (+ 32 dump rows) and one local row per (KV head, token, group head)
+    # one partial row per (pair, group head) + 32 dump rows, and the work-queue
+    # counters (8 of them, 128 bytes apart); no region beyond that (a query's
+    # local row sits at the rows of one of its local entries)
     g, d = sp.gqa_group, sp.head_dim
     rows = pmax * g + 32
-    local_rows = H * N * g
-    assert s.partial_ws_bytes >= (rows + local_rows) * d * 4
-    assert s.stats_ws_bytes >= (rows + local_rows) * 8
+    queue = 8 * 128
+
+    def r256(x):
+        return -(-x // 256) * 256
+
+    assert s.partial_ws_bytes == r256(r256(rows * d * 4) + queue)
+    assert s.stats_ws_bytes == r256(r256(rows * 8) + queue)
     # backward: delta [N, h_q] fp32 + dQ partial rows (no local rows) + fp32 dK/dV slots of [2][B_K][d]
     CT = -(-1024 // g)
     slots = pmax // CT + H * sum(nb) + 2
-    assert s.bwd_ws_bytes >= 4 * N * H * g + rows * d * 4 + slots * 2 * B * d * 4
+    assert s.bwd_ws_bytes >= 4 * N * H * g + rows * d * 4 + slots * 2 * B * d * 4 + queue
 
 
 def test_max_pairs_bounds_real_pairs():
