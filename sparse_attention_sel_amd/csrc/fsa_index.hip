@@ -1,7 +1,7 @@
 // Index precompute on gfx950: Sel[h_K, N, T] -> counts (N_valid), offsets
 // (compact output offsets O_i), qidx (query lists I_i) and slot (per-entry
 // position), as described in the FSA paper notes, Overall framework and Key
-// design 2.  A stable counting sort in four launches:
+// design 2.  A stable counting sort in seven launches:
 //
 //   seq_table  per-sequence global-block offsets (one workgroup)
 //   hist       per (KV head, token tile): LDS histogram of the selected blocks
@@ -10,7 +10,8 @@
 //   offsets    one workgroup: exclusive scan of counts -> offsets, and the
 //              work-item list (segment, query chunk) for the attention kernels
 //   scatter    per (KV head, token tile): walks its tokens in order and places
-//              each selecting entry at offsets + tile base + rank in the tile
+//              each selecting entry at offsets + tile base + rank in the tile;
+//              the entries that start a work item count it into its bucket
 //   work order bucket sort of the work list by (KV head, first query token)
 //
 // Integer atomics only count (their result does not depend on order); ranks
@@ -70,14 +71,84 @@ __device__ __forceinline__ TileWindow tile_window(const int32_t* __restrict__ cu
 }
 
 // ---- hist -------------------------------------------------------------------
-// grid (ntiles, H); dynamic LDS: win_max ints of histogram, win_max ints of
-// local counts, then a staging buffer of kHistStage ints for the Sel rows of
-// kHistStage / T tokens at a time (the first-occurrence check reads earlier
-// entries of the row from LDS) and kHistStage local words.
+// grid (ntiles, H).  The tile's tokens are taken in rounds of up to
+// kRoundTokens tokens (kHistStage Sel ints): the round's Sel rows and, per
+// token, its own block and the window slot of its sequence's first block are
+// staged in LDS (one parallel lookup per token); one thread per token then
+// turns its row into window slots (validity, first-occurrence dedupe) and
+// counts them into the LDS histogram over the tile's block window.
 // Besides the tile histogram it writes each token's local word and adds, for
 // every block e >= 1, the number of local entries (tokens of blocks e and e + 1
 // selecting e) to nloc; those are the first entries of the block's query list.
+// LDS (ints): hist[win_max], lhist[win_max], rows[kHistStage + kRoundTokens]
+// (padded stride), own, base and lword [kRoundTokens] each.
 constexpr int kHistStage = 4096;
+constexpr int kRoundTokens = 512;
+
+__device__ __forceinline__ int round_tokens(int T) { return max(1, min(kRoundTokens, kHistStage / T)); }
+
+// Staged Sel rows use an odd stride (T, or T + 1 for even T), so that the
+// threads of a wave reading one row each hit distinct LDS banks.
+__device__ __forceinline__ int row_stride(int T) { return T | 1; }
+
+// Copies the Sel rows of tokens c0 .. c0 + nt - 1 (contiguous, T ints each)
+// into rows at the padded stride.  i / T by a float reciprocal: exact here
+// (i < 4096, T <= 256, so the quotient's fraction is at least 0.5 / T away
+// from an integer, far beyond float rounding).
+__device__ __forceinline__ void stage_rows(const int32_t* __restrict__ src, int nt, int T, int* __restrict__ rows) {
+  const int RS = row_stride(T);
+  const float inv = 1.0f / (float)T;
+  for (int i = threadIdx.x; i < nt * T; i += blockDim.x) {
+    const int tl = (int)(((float)i + 0.5f) * inv);
+    rows[tl * RS + (i - tl * T)] = src[i];
+  }
+}
+
+// Own block and window slot of the first block of the sequence of tokens
+// t0 + i, i < nt (one thread per token).
+__device__ __forceinline__ void token_info(const int32_t* __restrict__ cu, const int32_t* __restrict__ gboff,
+                                           int num_seqs, int BK, int gb_lo, int t0, int nt, int* __restrict__ own,
+                                           int* __restrict__ base) {
+  for (int i = threadIdx.x; i < nt; i += blockDim.x) {
+    const int t = t0 + i;
+    const int s = seq_of_token(cu, num_seqs, t);
+    own[i] = (t - cu[s]) / BK;
+    base[i] = gboff[s] - gb_lo;
+  }
+}
+
+// Replaces each staged Sel entry of tokens tl < nt by the window slot of the
+// block it selects (base + e), or -1 when it selects nothing (negative, past
+// the own block, or a repeat of an earlier entry of its row).  One thread per
+// token row: up to 16 entries in registers; longer rows are visited from the
+// last entry to the first, so the earlier entries the repeat test reads are
+// still block indices.
+__device__ __forceinline__ void entry_slots(int* __restrict__ rows, const int* __restrict__ own,
+                                            const int* __restrict__ base, int nt, int T) {
+  for (int tl = threadIdx.x; tl < nt; tl += blockDim.x) {
+    int* row = rows + tl * row_stride(T);
+    const int ob = own[tl], bs = base[tl];
+    if (T <= 16) {
+      int e[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) e[j] = j < T ? row[j] : -1;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        bool dup = false;
+#pragma unroll
+        for (int jj = 0; jj < j; ++jj) dup |= e[jj] == e[j];
+        if (j < T) row[j] = e[j] >= 0 && e[j] <= ob && !dup ? bs + e[j] : -1;
+      }
+    } else {
+      for (int j = T - 1; j >= 0; --j) {
+        const int e = row[j];
+        bool dup = false;
+        for (int jj = 0; jj < j; ++jj) dup |= row[jj] == e;
+        row[j] = e >= 0 && e <= ob && !dup ? bs + e : -1;
+      }
+    }
+  }
+}
 
 __global__ __launch_bounds__(kBuildThreads) void k_hist(const int32_t* __restrict__ sel,
                                                         const int32_t* __restrict__ cu,
@@ -87,38 +158,40 @@ __global__ __launch_bounds__(kBuildThreads) void k_hist(const int32_t* __restric
                                                         int32_t* __restrict__ nloc, int use_local) {
   extern __shared__ int lds[];
   int* hist = lds;
-  int* lhist = lds + win_max;
-  int* rows = lds + 2 * win_max;
-  unsigned* lword = reinterpret_cast<unsigned*>(lds + 2 * win_max + kHistStage);
+  int* lhist = hist + win_max;
+  int* rows = lhist + win_max;
+  int* own = rows + kHistStage + kRoundTokens;
+  int* base = own + kRoundTokens;
+  unsigned* lword = reinterpret_cast<unsigned*>(base + kRoundTokens);
   const int tile = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const TileWindow w = tile_window(cu, gboff, num_seqs, N, TT, BK, tile);
   for (int i = tid; i < w.win; i += kBuildThreads) hist[i] = lhist[i] = 0;
-  const int chunk = max(1, kHistStage / T);  // tokens per staging round
+  const int chunk = round_tokens(T);
   for (int c0 = w.t_lo; c0 < w.t_hi; c0 += chunk) {
     const int nt = min(chunk, w.t_hi - c0);
     const int32_t* src = sel + ((size_t)h * N + c0) * T;
     __syncthreads();  // previous round's reads done (and the histograms zeroed)
-    for (int i = tid; i < nt * T; i += kBuildThreads) rows[i] = src[i];
-    for (int i = tid; i < nt; i += kBuildThreads) lword[i] = 0u;
+    stage_rows(src, nt, T, rows);
+    token_info(cu, gboff, num_seqs, BK, w.gb_lo, c0, nt, own, base);
     __syncthreads();
-    for (int i = tid; i < nt * T; i += kBuildThreads) {
-      const int tl = i / T, j = i - tl * T;
-      const int t = c0 + tl;
-      const int* row = rows + tl * T;
-      const int e = row[j];
-      if (e < 0) continue;
-      const int s = seq_of_token(cu, num_seqs, t);
-      const int own = (t - cu[s]) / BK;
-      if (e > own) continue;
-      bool dup = false;
-      for (int jj = 0; jj < j; ++jj) dup |= (row[jj] == e);
-      if (dup) continue;
-      atomicAdd(&hist[gboff[s] + e - w.gb_lo], 1);
-      const int kind = use_local ? local_kind(e, own) : -1;
-      if (kind >= 0) {
-        atomicOr(&lword[tl], (unsigned)(j + 1) << (9 * kind));
-        if (kind < 2 && e > 0) atomicAdd(&lhist[gboff[s] + e - w.gb_lo], 1);
+    entry_slots(rows, own, base, nt, T);
+    __syncthreads();
+    // one thread per token: histogram its selected blocks, build its local word
+    for (int tl = tid; tl < nt; tl += kBuildThreads) {
+      const int* row = rows + tl * row_stride(T);
+      const int ob = own[tl], bs = base[tl];
+      unsigned word = 0u;
+      for (int j = 0; j < T; ++j) {
+        const int wi = row[j];
+        if (wi < 0) continue;
+        atomicAdd(&hist[wi], 1);
+        const int kind = use_local ? local_kind(wi - bs, ob) : -1;
+        if (kind >= 0) {
+          word |= (unsigned)(j + 1) << (9 * kind);
+          if (kind < 2 && wi > bs) atomicAdd(&lhist[wi], 1);
+        }
       }
+      lword[tl] = word;
     }
     __syncthreads();
     for (int i = tid; i < nt; i += kBuildThreads) loc[(size_t)h * N + c0 + i] = (int32_t)lword[i];
@@ -282,71 +355,93 @@ __global__ __launch_bounds__(kScanThreads) void k_offsets(const int32_t* __restr
 }
 
 // ---- scatter ------------------------------------------------------------------
-// grid (ntiles, H).  LDS: cursor[win_max], mark[win_max], row buffer.
-// Each step takes TPS consecutive tokens of the tile, one lane per entry
-// (lane = token_in_step * Tp + j).  A block's lanes set bit token_in_step in
-// mark[block]; a lane's rank among the step's selectors of its block is the
-// number of lower bits, so ranks follow token order.  The highest selector
-// then advances the block's cursor.
-__global__ __launch_bounds__(kBuildThreads) void k_scatter(
+// grid (ntiles, H).  The tile's tokens in rounds as in k_hist (Sel rows turned
+// into window slots in LDS), each round in steps of TPS consecutive tokens,
+// one lane per entry (lane = token_in_step * Tp + j).  A block's lanes set bit
+// token_in_step in mark[block]; a lane's rank among the step's selectors of
+// its block is the number of lower bits, so ranks follow token order.  The
+// highest selector then advances the block's cursor.
+// Work items start at the chunk boundaries of each segment's query list (rank
+// a multiple of CT in the full list, CT past the local head in the forward
+// list), so the entry placed there counts its item into the work-order bucket
+// of its (KV head, token bucket) for k_work_place.
+// LDS (ints): cursor, two mark sets, lstart, segoff [win_max] each,
+// rows[kHistStage + kRoundTokens] (padded stride), own and base
+// [kRoundTokens] each.
+constexpr int kScatterThreads = 512;  // 32 tokens per step at T = 16
+
+__global__ __launch_bounds__(kScatterThreads) void k_scatter(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ cu, const int32_t* __restrict__ gboff,
     int num_seqs, int N, int T, int Tp, int TPS, int BK, int TT, int ntiles, int NB, int win_max,
-    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ offsets, int32_t* __restrict__ qidx,
-    int32_t* __restrict__ slot) {
+    const int32_t* __restrict__ tile_base, const int32_t* __restrict__ offsets, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ nloc, int use_local, int CT, int shift, int nbh, int nbuckets,
+    int32_t* __restrict__ buckets, int32_t* __restrict__ qidx, int32_t* __restrict__ slot) {
   extern __shared__ int lds[];
-  int* cursor = lds;
-  unsigned* mark = reinterpret_cast<unsigned*>(lds + win_max);
-  int* rowbuf = lds + 2 * win_max;
+  int* cursor = lds;  // next rank within the segment
+  unsigned* mark = reinterpret_cast<unsigned*>(cursor + win_max);  // two sets, by step parity
+  int* lstart = reinterpret_cast<int*>(mark + 2 * win_max);        // local entries at the segment's head
+  int* segoff = lstart + win_max;                                   // offsets[f]
+  int* rows = segoff + win_max;
+  int* own = rows + kHistStage + kRoundTokens;
+  int* base = own + kRoundTokens;
   const int tile = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const TileWindow w = tile_window(cu, gboff, num_seqs, N, TT, BK, tile);
   {
     const int32_t* tb = tile_base + ((size_t)h * ntiles + tile) * NB + w.gb_lo;
-    const int32_t* of = offsets + (size_t)h * NB + w.gb_lo;
-    for (int i = tid; i < w.win; i += kBuildThreads) {
-      cursor[i] = of[i] + tb[i];
-      mark[i] = 0u;
+    for (int i = tid; i < w.win; i += kScatterThreads) {
+      const int f = h * NB + w.gb_lo + i;
+      cursor[i] = tb[i];
+      mark[i] = mark[win_max + i] = 0u;
+      segoff[i] = offsets[f];
+      lstart[i] = segment_local(f, counts[f], nloc, cu, gboff, num_seqs, NB, BK, use_local);
     }
   }
-  __syncthreads();
+  const int RS = row_stride(T);
   const int my_tok = tid / Tp, my_j = tid - my_tok * Tp;
-  for (int t0 = w.t_lo; t0 < w.t_hi; t0 += TPS) {
-    const int t = t0 + my_tok;
-    const bool active = my_tok < TPS && my_j < T && t < w.t_hi;
-    int e = -1;
-    if (active) e = sel[((size_t)h * N + t) * T + my_j];
-    rowbuf[tid] = e;
+  const int chunk = max(TPS, round_tokens(T));
+  for (int c0 = w.t_lo; c0 < w.t_hi; c0 += chunk) {
+    const int nt = min(chunk, w.t_hi - c0);
+    __syncthreads();  // previous round's reads done (and the cursors initialised)
+    stage_rows(sel + ((size_t)h * N + c0) * T, nt, T, rows);
+    token_info(cu, gboff, num_seqs, BK, w.gb_lo, c0, nt, own, base);
     __syncthreads();
-    bool valid = false;
-    int wi = 0;
-    if (active && e >= 0) {
-      const int s = seq_of_token(cu, num_seqs, t);
-      if (e <= (t - cu[s]) / BK) {
-        bool dup = false;
-        for (int jj = 0; jj < my_j; ++jj) dup |= (rowbuf[my_tok * Tp + jj] == e);
-        if (!dup) {
-          valid = true;
-          wi = gboff[s] + e - w.gb_lo;
-          atomicOr(&mark[wi], 1u << my_tok);
+    entry_slots(rows, own, base, nt, T);
+    __syncthreads();
+    // Step k sets bits in mark set k % 2 (atomicOr), reads them after a
+    // barrier, and its highest selectors advance the cursors and clear their
+    // marks after the next barrier; step k + 1 uses the other set, and step
+    // k + 2 reaches this set only after step k + 1's first barrier, which all
+    // of step k's clears precede.
+    for (int s0 = 0, par = 0; s0 < nt; s0 += TPS, par ^= 1) {
+      unsigned* mk = mark + par * win_max;
+      const int tl = s0 + my_tok;
+      const bool active = my_tok < TPS && my_j < T && tl < nt;
+      const int wi = active ? rows[tl * RS + my_j] : -1;
+      const bool valid = wi >= 0;
+      if (valid) atomicOr(&mk[wi], 1u << my_tok);
+      __syncthreads();
+      unsigned m = 0;
+      if (active) {
+        int pos = -1;
+        if (valid) {
+          m = mk[wi];
+          const int r = cursor[wi] + __popc(m & ((1u << my_tok) - 1u));
+          const int t = c0 + tl;
+          pos = segoff[wi] + r;
+          qidx[pos] = t;
+          const int key = h * nbh + (t >> shift);
+          if (r % CT == 0) atomicAdd(&buckets[key], 1);
+          const int l0 = lstart[wi];
+          if (r >= l0 && (r - l0) % CT == 0) atomicAdd(&buckets[nbuckets + key], 1);
         }
+        slot[((size_t)h * N + c0 + tl) * T + my_j] = pos;
+      }
+      __syncthreads();
+      if (valid && (m >> my_tok) == 1u) {
+        cursor[wi] += __popc(m);
+        mk[wi] = 0u;
       }
     }
-    __syncthreads();
-    unsigned m = 0;
-    if (active) {
-      int pos = -1;
-      if (valid) {
-        m = mark[wi];
-        pos = cursor[wi] + __popc(m & ((1u << my_tok) - 1u));
-        qidx[pos] = t;
-      }
-      slot[((size_t)h * N + t) * T + my_j] = pos;
-    }
-    __syncthreads();
-    if (valid && (m >> my_tok) == 1u) {
-      cursor[wi] += __popc(m);
-      mark[wi] = 0u;
-    }
-    __syncthreads();
   }
 }
 
@@ -354,8 +449,9 @@ __global__ __launch_bounds__(kBuildThreads) void k_scatter(
 // Reorders the work list by (KV head, first query token of the chunk) with a
 // bucket sort (bucket = token >> shift), so that the items that run together
 // on one XCD gather a narrow window of query rows, which then stays in that
-// XCD's L2.  Three grid-wide steps: count items per bucket, exclusive scan of
-// the bucket counts (one workgroup), place items at their bucket's cursor.
+// XCD's L2.  Three steps: count items per bucket (in k_scatter, by the entry
+// that starts each item), exclusive scan of the bucket counts (one
+// workgroup), place items at their bucket's cursor.
 // Within a bucket the order depends on atomics; the order only affects
 // scheduling: every item writes its own partial rows and the reduction sums
 // in slot order, so all outputs are unchanged.
@@ -400,15 +496,6 @@ __device__ __forceinline__ bool list_item(const ListArgs& a, int w, int4* it, in
   *it = make_int4(f, first + (w - cb[f]) * a.CT, a.cu[s] + (gb - a.gboff[s]) * a.BK, a.cu[s + 1]);
   *bucket0 = fwd ? a.nbuckets : 0;
   return true;
-}
-
-__global__ __launch_bounds__(kBuildThreads) void k_work_count(ListArgs a, const int32_t* __restrict__ qidx,
-                                                              const int32_t* __restrict__ offsets, int shift, int nbh,
-                                                              int32_t* __restrict__ buckets) {
-  int4 it;
-  int b0;
-  if (!list_item(a, blockIdx.x * kBuildThreads + threadIdx.x, &it, &b0)) return;
-  atomicAdd(&buckets[b0 + work_key(it, qidx, offsets, a.NB, shift, nbh)], 1);
 }
 
 __global__ __launch_bounds__(kScanThreads) void k_bucket_scan(int32_t* __restrict__ buckets, int nbuckets) {
@@ -478,7 +565,8 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
                      nloc, M);
   if (geo.N > 0) {
     hipLaunchKernelGGL(k_hist, dim3(geo.ntiles, geo.H), dim3(kBuildThreads),
-                       (2 * geo.win_max + 2 * kHistStage) * sizeof(int), stream, sel, cu_dev, gboff, geo.num_seqs,
+                       (2 * geo.win_max + kHistStage + 4 * kRoundTokens) * sizeof(int), stream, sel, cu_dev, gboff,
+                       geo.num_seqs,
                        geo.N, geo.T, geo.BK, geo.tile_tokens, geo.ntiles, geo.NB, geo.win_max, tile_hist, loc, nloc,
                        (int)geo.local);
     constexpr int cols = kBuildThreads / kScanSegs;
@@ -492,17 +580,16 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
   if (geo.N > 0) {
     int Tp = 1;
     while (Tp < geo.T) Tp <<= 1;
-    const int tps = min(32, kBuildThreads / Tp);
-    const size_t lds = (size_t)(2 * geo.win_max + kBuildThreads) * sizeof(int);
-    hipLaunchKernelGGL(k_scatter, dim3(geo.ntiles, geo.H), dim3(kBuildThreads), lds, stream, sel, cu_dev, gboff,
+    const int tps = min(32, kScatterThreads / Tp);
+    const size_t lds = (size_t)(5 * geo.win_max + kHistStage + 3 * kRoundTokens) * sizeof(int);
+    hipLaunchKernelGGL(k_scatter, dim3(geo.ntiles, geo.H), dim3(kScatterThreads), lds, stream, sel, cu_dev, gboff,
                        geo.num_seqs, geo.N, geo.T, Tp, tps, geo.BK, geo.tile_tokens, geo.ntiles, geo.NB, geo.win_max,
-                       tile_hist, idx.offsets, idx.qidx, idx.slot);
+                       tile_hist, idx.offsets, idx.counts, nloc, (int)geo.local, geo.chunk_tokens, geo.sort_shift,
+                       geo.sort_buckets_per_head, nbk, buckets, idx.qidx, idx.slot);
     if (geo.max_work > 0) {
       const ListArgs la{idx.counts, nloc, cb_full, cb_fwd, nwork, cu_dev, gboff, geo.num_seqs, M, NB1, geo.BK,
                         geo.chunk_tokens, nbk, (int)geo.local};
       const unsigned wg = (unsigned)((2 * geo.max_work + kBuildThreads - 1) / kBuildThreads);
-      hipLaunchKernelGGL(k_work_count, dim3(wg), dim3(kBuildThreads), 0, stream, la, idx.qidx, idx.offsets,
-                         geo.sort_shift, geo.sort_buckets_per_head, buckets);
       hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(kScanThreads), 0, stream, buckets, 2 * nbk);
       hipLaunchKernelGGL(k_work_place, dim3(wg), dim3(kBuildThreads), 0, stream, la, idx.qidx, idx.offsets,
                          geo.sort_shift, geo.sort_buckets_per_head, buckets, work_sorted);

@@ -15,7 +15,7 @@ constexpr int kBuildThreads = 256;     // workgroup of the index kernels
 constexpr int kScanThreads = 1024;     // single-workgroup offsets scan
 constexpr int kMinTileTokens = 256;    // tokens per histogram tile (grows for long inputs)
 constexpr int64_t kMaxTileHist = int64_t(1) << 24;  // cap on h_K * tiles * NB entries
-constexpr int kWinMax = 7680;          // max global blocks one tile can touch (LDS)
+constexpr int kWinMax = 6912;          // max global blocks one tile can touch (LDS of k_scatter: 5 ints each)
 constexpr int kAttnThreads = 256;      // 4 waves per main / stats workgroup
 constexpr int kRowsPerItem = 1024;     // target query rows (tokens * g) per work item
 constexpr int kReduceThreads = 256;

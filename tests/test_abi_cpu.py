@@ -132,6 +132,7 @@ def test_max_pairs_bounds_real_pairs():
         (dict(scale=float("nan")), SHAPE), (dict(scale=float("inf")), SHAPE),
         (dict(cu=(0, 2**29), H=8, T=16), SHAPE),
         (dict(cu=(0, 600000)), UNSUP),
+        (dict(cu=(0, 6912 * 64 + 1)), UNSUP),  # a tile's block window beyond 6912 blocks
     ],
 )
 def test_sizes_rejects(kw, status):
@@ -140,7 +141,7 @@ def test_sizes_rejects(kw, status):
 
 def test_sizes_accepts_edge_shapes():
     for kw in (dict(cu=(0, 0)), dict(cu=(0, 0, 5, 5)), dict(T=256), dict(g=16, d=256), dict(B=128, d=64),
-               dict(scale=-1.0), dict(cu=(0, 1))):
+               dict(scale=-1.0), dict(cu=(0, 1)), dict(cu=(0, 6912 * 64))):
         assert sizes(prob(**kw))[0] == OK, kw
     assert sizes(prob(cu=(0, 0)))[1].max_pairs == 0
 
