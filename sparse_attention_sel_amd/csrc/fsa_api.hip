@@ -54,7 +54,6 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   if (p->block_size < 1 || p->topk < 1 || p->topk > 256) return FSA_ERR_SHAPE;
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256) return FSA_ERR_UNSUPPORTED;
   if (p->block_size != 64 && p->block_size != 128) return FSA_ERR_UNSUPPORTED;
-  if (p->block_size == 128 && p->head_dim == 256) return FSA_ERR_UNSUPPORTED;  // would spill registers
   float scale = p->softmax_scale;
   if (std::isnan(scale) || std::isinf(scale)) return FSA_ERR_SHAPE;
   if (!(scale > 0.f)) scale = 1.0f / std::sqrt((float)p->head_dim);
@@ -165,7 +164,9 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   // One partial row per (selecting entry, query head): rows pair * g + j, the
   // compact output of the pages' index O_i, plus 32 dump rows; no other region
   // (a query's local row uses the rows of its designated local entry).
-  geo->dump_row = std::max<int64_t>(geo->max_pairs, 1) * g;
+  geo->split_halves = BK == 128 && geo->d == 256;
+  geo->split_half_rows = std::max<int64_t>(geo->max_pairs, 1) * g;
+  geo->dump_row = (geo->split_halves ? 2 : 1) * geo->split_half_rows;
   const size_t rows = (size_t)geo->dump_row + 32;
   const size_t s_p = geo->partial_dtype == FSA_PARTIAL_FP32 ? 4 : 2;
   const size_t queue_bytes = (size_t)kQueueInts * 4;
@@ -176,7 +177,7 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
   geo->partial_ws_bytes = round_up(geo->partial_queue_off + queue_bytes, 256);
   // Backward: the chunk slot offsets[f] / CT + f + c (c < ceil(count_f / CT))
   // is injective and below max_pairs / CT + M + 2.
-  geo->bwd_ok = BK == 64 || geo->d <= 128;  // B_K = 128 with d = 256 is not compiled
+  geo->bwd_ok = !geo->split_halves;  // no backward kernel for B_K = 128 with d = 256
   geo->kv_slots = geo->max_pairs / geo->chunk_tokens + H * NB + 2;
   geo->bwd_dq_off = round_up((size_t)N * H * g * 4, 256);
   geo->bwd_kv_off = round_up(geo->bwd_dq_off + geo->partial_rows_bytes, 256);
@@ -371,6 +372,7 @@ int32_t fsa_selected_attn_fwd_onepass(const fsa_problem* prob, const void* q, co
   Geometry geo;
   int32_t st = prepare(prob, &geo);
   if (st != FSA_OK) return st;
+  if (geo.split_halves) return FSA_ERR_UNSUPPORTED;  // no one-pass kernels for B_K = 128 with d = 256
   if (!data(row_max, geo) || !data(lse, geo) || stats_ws == nullptr) return FSA_ERR_NULL;
   // lse is an output here; the main-kernel checks only need a non-null pointer
   st = check_main_args(geo, q, k, v, idx, lse, partial_ws, partial_ws_bytes);
@@ -423,6 +425,7 @@ int32_t fsa_nsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const 
   Geometry geo;
   const int32_t st = prepare(prob, &geo);
   if (st != FSA_OK) return st;
+  if (geo.BK == 128 && geo.d == 256) return FSA_ERR_UNSUPPORTED;  // V of four waves' blocks exceeds LDS
   if (!data(q, geo) || !data(k, geo) || !data(v, geo) || !data(sel, geo) || !data(lse, geo) || !data(out, geo))
     return FSA_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(sel, 4) ||

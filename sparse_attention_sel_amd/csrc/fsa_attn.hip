@@ -166,7 +166,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // clamped indices so that they are unconditional: keys past a partial last
 // block are only ever seen by rows that take the causal mask (their values
 // get weight zero), rows past the chunk are marked with token -1.
-template <typename T, int D, int BK, bool WITH_V, int NT>
+template <typename T, int D, int BK, bool WITH_V, int NT, bool SPLIT = false>
 struct ItemStage {
   using V8 = typename Vec8<T>::type;
   static constexpr int KV = BK * D / 8 / NT;                        // K vectors per thread
@@ -181,13 +181,13 @@ struct ItemStage {
   __device__ __forceinline__ void load(const T* __restrict__ kg, const T* __restrict__ vg, const int32_t* __restrict__ qidx,
                                        const int4* __restrict__ work, const int32_t* __restrict__ counts,
                                        const int32_t* __restrict__ offsets, int wi, int H, int g, int NB, int CT) {
-    it = read_item(work, counts, offsets, wi, NB, CT, BK);
+    it = SPLIT ? read_item_half(work, counts, offsets, wi, NB, CT) : read_item(work, counts, offsets, wi, NB, CT, BK);
     constexpr int C8 = D / 8;
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
       const int vi = threadIdx.x + i * NT;
-      const int key = min(vi / C8, it.nkeys - 1), c = vi % C8;
-      k[i] = load8(kg + ((size_t)(it.bs + key) * H + it.h) * D + c * 8);
+      const int key = min(vi / C8, it.nk - 1), c = vi % C8;
+      k[i] = load8(kg + ((size_t)(it.kb + key) * H + it.h) * D + c * 8);
     }
     if constexpr (WITH_V) {
       constexpr int KP = BK / 2;
@@ -195,8 +195,8 @@ struct ItemStage {
       for (int i = 0; i < VP; ++i) {
         const int vi = threadIdx.x + i * NT;
         const int c = vi / KP, key = 2 * (vi % KP);
-        va[i] = load8(vg + ((size_t)(it.bs + min(key, it.nkeys - 1)) * H + it.h) * D + c * 8);
-        vb[i] = load8(vg + ((size_t)(it.bs + min(key + 1, it.nkeys - 1)) * H + it.h) * D + c * 8);
+        va[i] = load8(vg + ((size_t)(it.kb + min(key, it.nk - 1)) * H + it.h) * D + c * 8);
+        vb[i] = load8(vg + ((size_t)(it.kb + min(key + 1, it.nk - 1)) * H + it.h) * D + c * 8);
       }
     }
     // Nothing here consumes the loaded values (the row bound is applied at
@@ -575,13 +575,17 @@ __device__ __forceinline__ float2 probs_stats(const f32x16* s, float c, int hl, 
 // partial row is divided by the sum, so it holds the block's own softmax
 // average of V; the (max, sum) pair goes to `st` as the statistics kernel
 // would write it, and the reduction weighs the partial rows by it.
-template <typename T, int D, int BK, typename PT, bool FUSED>
+// SPLIT (B_K = 128 with d = 256, instantiated with BK = 64): each work item
+// of 128-key blocks runs as two items, one per 64-key half, whose partial
+// rows lie half_rows apart; the reduction adds both.
+template <typename T, int D, int BK, typename PT, bool FUSED, bool SPLIT = false>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
     const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
-    float2* __restrict__ st, PT* __restrict__ partial, size_t dump_row, int H, int g, int NB, int CT,
-    float scale_log2) {
+    float2* __restrict__ st, PT* __restrict__ partial, size_t dump_row, size_t half_rows, int H, int g, int NB,
+    int CT, float scale_log2) {
+  static_assert(!(SPLIT && FUSED), "split items only in the three-pass forward");
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
   constexpr int NT = kAttnThreads, NW = kWaves;
@@ -591,7 +595,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   __shared__ __attribute__((aligned(16))) T Qt[NW * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
   __shared__ int s_items[2];
-  ItemChain ch(queue, nwork[2], s_items);  // the forward list
+  ItemChain ch(queue, SPLIT ? 2 * nwork[2] : nwork[2], s_items);  // the forward list
   const int4* const wl = work + nwork[0];
   if (ch.cur < 0) return;
   const int HQ = H * g;
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   T* const qt = Qt + wave * 32 * tile_ld<D>();
   PT* const stage = reinterpret_cast<PT*>(qt);
   PT* const dump = partial + dump_row * D;
-  ItemStage<T, D, BK, true, NT> pre;
+  ItemStage<T, D, BK, true, NT, SPLIT> pre;
   pre.load(k, v, qidx, wl, counts, offsets, ch.cur, H, g, NB, CT);
   while (ch.cur >= 0) {
     __syncthreads();  // the previous item's LDS reads are done
@@ -653,7 +657,8 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
         for (int mt = 0; mt < MT; ++mt) o[mt] *= inv;
       }
       store_tile<PT, D>(stage, o, lane, min(32, nrows - tl * 32),
-                        partial + ((size_t)it.pair0 * g + (size_t)tl * 32) * D, dump);
+                        partial + ((size_t)it.half * half_rows + (size_t)it.pair0 * g + (size_t)tl * 32) * D,
+                        dump);
     }
     ch.advance(after);
   }
@@ -968,13 +973,18 @@ struct Part8<_Float16> {
 // FUSED (the one-pass forward): the partial rows are per-block softmax
 // averages o_b with (max, sum) pairs (m_b, l_b); O = sum_b l_b 2^(m_b - m) o_b
 // / l with the row's merged (m, l), also written out as row max and lse.
-template <typename T, typename PT, bool LOCAL, bool FUSED>
+// SPLIT (B_K = 128 with d = 256): every slot has two partial rows, one per
+// key half, the second half_elems elements after the first; both are added,
+// the first half first.
+template <typename T, typename PT, bool LOCAL, bool FUSED, bool SPLIT = false>
 __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __restrict__ slot,
                                                            const PT* __restrict__ partial,
                                                            const int32_t* __restrict__ loc, T* __restrict__ out,
                                                            const float2* __restrict__ st,
                                                            float* __restrict__ row_max, float* __restrict__ lse,
-                                                           int N, int H, int g, int D, int Tn, int TPI) {
+                                                           int N, int H, int g, int D, int Tn, int TPI,
+                                                           size_t half_elems) {
+  static_assert(!SPLIT || (!LOCAL && !FUSED), "split rows only in the three-pass forward without local rows");
   const int ipb = kReduceThreads / TPI;
   const int local = threadIdx.x / TPI;
   if (local >= ipb) return;
@@ -1055,6 +1065,20 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __rest
         for (int u = 0; u < 8; ++u) sv[u] = LOCAL && local_entry(word, j0 + u) ? -1 : raw[u];
 #pragma unroll
         for (int u = 0; u < 8; ++u) x[u] = Part8<PT>::load(partial + (size_t)max(sv[u], 0) * GD + vec * 8);
+        if constexpr (SPLIT) {
+          typename Part8<PT>::type y[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            y[u] = Part8<PT>::load(partial + half_elems + (size_t)max(sv[u], 0) * GD + vec * 8);
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              acc[i] += sv[u] >= 0 ? Part8<PT>::at(x[u], i) : 0.f;
+              acc[i] += sv[u] >= 0 ? Part8<PT>::at(y[u], i) : 0.f;
+            }
+          continue;
+        }
         if (LOCAL && j0 == 0 && word != 0u) {
           int lrow = 0;
 #pragma unroll
@@ -1137,7 +1161,7 @@ void stats_typed(const Geometry& geo, const int32_t* cu, const void* q, const vo
 
 // Main kernels.  With `st` (a statistics workspace) the one-pass variant:
 // no lse is read, and the per-block (max, sum) pairs go to `st`.
-template <typename T, int D, int BK, typename PT, bool FUSED>
+template <typename T, int D, int BK, typename PT, bool FUSED, bool SPLIT = false>
 void main_launch(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v,
                  const fsa_index& idx, const float* lse, void* st_ws, void* partial, hipStream_t stream) {
   const auto p = index_ptrs(geo, idx);
@@ -1158,18 +1182,25 @@ void main_launch(const Geometry& geo, const int32_t* cu, const void* q, const vo
     hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(256), 0, stream, queue);
   }
   if (geo.max_work > 0)
-    hipLaunchKernelGGL((k_main<T, D, BK, PT, FUSED>),
-                       dim3(persistent_grid(k_main<T, D, BK, PT, FUSED>, kAttnThreads, geo.max_work)),
+    hipLaunchKernelGGL((k_main<T, D, BK, PT, FUSED, SPLIT>),
+                       dim3(persistent_grid(k_main<T, D, BK, PT, FUSED, SPLIT>, kAttnThreads,
+                                            (SPLIT ? 2 : 1) * geo.max_work)),
                        dim3(kAttnThreads), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
                        static_cast<const T*>(v), p.counts, p.offsets, p.qidx, p.work, p.nwork, queue, lse, st, part,
-                       (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
+                       (size_t)geo.dump_row, (size_t)geo.split_half_rows, geo.H, geo.g, geo.NB, geo.chunk_tokens,
+                       sl2);
 }
 
 template <typename T, int D, int BK, typename PT>
 void main_typed(const Geometry& geo, const int32_t* cu, const void* q, const void* k, const void* v,
                 const fsa_index& idx, const float* lse, void* st_ws, void* partial, hipStream_t stream) {
-  if (st_ws != nullptr) main_launch<T, D, BK, PT, true>(geo, cu, q, k, v, idx, lse, st_ws, partial, stream);
-  else main_launch<T, D, BK, PT, false>(geo, cu, q, k, v, idx, lse, nullptr, partial, stream);
+  if constexpr (D == 256 && BK == 128) {
+    // 128-key blocks at d = 256: two 64-key halves per item (three-pass forward only)
+    main_launch<T, 256, 64, PT, false, true>(geo, cu, q, k, v, idx, lse, nullptr, partial, stream);
+  } else {
+    if (st_ws != nullptr) main_launch<T, D, BK, PT, true>(geo, cu, q, k, v, idx, lse, st_ws, partial, stream);
+    else main_launch<T, D, BK, PT, false>(geo, cu, q, k, v, idx, lse, nullptr, partial, stream);
+  }
 }
 
 // Reduction.  With `st_ws` the one-pass variant, which also writes row_max
@@ -1189,16 +1220,22 @@ void reduce_typed(const Geometry& geo, const fsa_index& idx, const void* partial
   if (st_ws != nullptr) {
     if (local)
       hipLaunchKernelGGL((k_reduce<T, PT, true, true>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot, part,
-                         p.loc, o, st, row_max, lse, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+                         p.loc, o, st, row_max, lse, geo.N, geo.H, geo.g, geo.d, geo.T, tpi, (size_t)0);
     else
       hipLaunchKernelGGL((k_reduce<T, PT, false, true>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot,
-                         part, nullptr, o, st, row_max, lse, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+                         part, nullptr, o, st, row_max, lse, geo.N, geo.H, geo.g, geo.d, geo.T, tpi, (size_t)0);
+  } else if (local && geo.split_halves) {
+    // the forward at B_K = 128, d = 256: two rows per slot (no local rows at B_K = 128)
+    hipLaunchKernelGGL((k_reduce<T, PT, false, false, true>), dim3(blocks), dim3(kReduceThreads), 0, stream,
+                       idx.slot, part, nullptr, o, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d, geo.T, tpi,
+                       (size_t)geo.split_half_rows * geo.d);
   } else if (local) {
     hipLaunchKernelGGL((k_reduce<T, PT, true, false>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot, part,
-                       p.loc, o, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+                       p.loc, o, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d, geo.T, tpi, (size_t)0);
   } else {
     hipLaunchKernelGGL((k_reduce<T, PT, false, false>), dim3(blocks), dim3(kReduceThreads), 0, stream, idx.slot,
-                       part, nullptr, o, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d, geo.T, tpi);
+                       part, nullptr, o, nullptr, nullptr, nullptr, geo.N, geo.H, geo.g, geo.d, geo.T, tpi,
+                       (size_t)0);
   }
 }
 
@@ -1208,9 +1245,7 @@ void stats_d(const Geometry& geo, const int32_t* cu, const void* q, const void* 
   switch (geo.d) {
     case 64: stats_typed<T, 64, BK>(geo, cu, q, k, idx, ws, s); break;
     case 128: stats_typed<T, 128, BK>(geo, cu, q, k, idx, ws, s); break;
-    default:
-      if constexpr (BK == 64) stats_typed<T, 256, BK>(geo, cu, q, k, idx, ws, s);
-      break;
+    default: stats_typed<T, 256, BK>(geo, cu, q, k, idx, ws, s); break;
   }
 }
 
@@ -1220,9 +1255,7 @@ void main_d(const Geometry& geo, const int32_t* cu, const void* q, const void* k
   switch (geo.d) {
     case 64: main_typed<T, 64, BK, PT>(geo, cu, q, k, v, idx, lse, st_ws, partial, s); break;
     case 128: main_typed<T, 128, BK, PT>(geo, cu, q, k, v, idx, lse, st_ws, partial, s); break;
-    default:
-      if constexpr (BK == 64) main_typed<T, 256, BK, PT>(geo, cu, q, k, v, idx, lse, st_ws, partial, s);
-      break;
+    default: main_typed<T, 256, BK, PT>(geo, cu, q, k, v, idx, lse, st_ws, partial, s); break;
   }
 }
 

@@ -41,6 +41,10 @@ struct Geometry {
   int32_t ntiles;        // index tiles
   int32_t win_max;       // largest block window of any tile
   int32_t chunk_tokens;  // query tokens per work item
+  bool split_halves;     // B_K = 128 with d = 256: the main kernel takes each 128-key block as two 64-key
+                         // halves (K and V of a whole block do not fit in LDS next to the query tiles), each
+                         // with its own partial rows: half 1's rows follow half 0's (split_half_rows apart)
+  int64_t split_half_rows;
   bool local;            // local entries are computed per query block (B_K = 64, g >= 2: there the
                          // block's rows fill the local kernels' tiles; elsewhere the block-outer
                          // kernels take every entry, the local words stay zero)
@@ -191,6 +195,8 @@ __device__ __forceinline__ int local_block(int kind, int e) { return kind == 0 ?
 // first pair (position in qidx), block start token and keys in the block.
 struct Item {
   int h, ntok, pair0, bs, nkeys;
+  int kb, nk;  // first token and count (>= 1) of the key rows loaded: bs and nkeys unless the item has no keys
+  int half;    // key half of a 128-key block (split items), else 0
 };
 
 // Work item wi = (segment f, first query of the chunk within the segment,
@@ -204,6 +210,25 @@ __device__ __forceinline__ Item read_item(const int4* __restrict__ work, const i
   r.pair0 = offsets[it.x] + it.y;
   r.bs = it.z;
   r.nkeys = min(BK, it.w - it.z);
+  r.kb = r.bs;
+  r.nk = r.nkeys;
+  r.half = 0;
+  return r;
+}
+
+// Item wi2 of the split list: work item wi2 / 2 taken over the 64 keys of
+// half wi2 % 2 of its 128-key block.  A second half past the sequence end has
+// no keys: its rows see no key (every query of such a block lies before the
+// half), and its key loads use the block's first row.
+__device__ __forceinline__ Item read_item_half(const int4* __restrict__ work, const int32_t* __restrict__ counts,
+                                               const int32_t* __restrict__ offsets, int wi2, int NB, int CT) {
+  Item r = read_item(work, counts, offsets, wi2 >> 1, NB, CT, 128);
+  r.half = wi2 & 1;
+  const int4 it = work[wi2 >> 1];
+  r.bs = it.z + 64 * r.half;
+  r.nkeys = min(64, it.w - r.bs);
+  r.kb = r.nkeys > 0 ? r.bs : it.z;
+  r.nk = max(r.nkeys, 1);
   return r;
 }
 

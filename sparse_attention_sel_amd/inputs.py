@@ -67,6 +67,8 @@ WORKLOADS: Dict[str, WorkloadSpec] = {
     # same 1024 selected keys per token; the README's Performance section
     # benchmarks both (B_K, T) = (64, 16) and (128, 8))
     "n64k_h4_g4_d128_b128_t8_bf16": WorkloadSpec((65536,), 4, 4, 128, 128, 8, "bf16", "init_local_zipf", 3300),
+    # 128-key blocks at head dim 256 (8 selected blocks: the same 1024 keys per token)
+    "n32k_h4_g4_d256_b128_t8_bf16": WorkloadSpec((32768,), 4, 4, 256, 128, 8, "bf16", "init_local_zipf", 3400),
     # two short packed sequences: a quick case for the checking harness
     "b2_n1k_h2_g4_d64_t8_bf16": WorkloadSpec((640, 384), 2, 4, 64, 64, 8, "bf16", "init_local_zipf", 6000),
 }

@@ -92,7 +92,8 @@ def test_sizes_closed_form(name):
     # counters (8 of them, 128 bytes apart); no region beyond that (a query's
     # local row sits at the rows of one of its local entries)
     g, d = sp.gqa_group, sp.head_dim
-    rows = pmax * g + 32
+    halves = 2 if (B, d) == (128, 256) else 1  # two 64-key halves per 128-key block at d = 256
+    rows = halves * pmax * g + 32
     queue = 8 * 128
 
     def r256(x):
@@ -103,7 +104,10 @@ def test_sizes_closed_form(name):
     # backward: delta [N, h_q] fp32 + dQ partial rows (no local rows) + fp32 dK/dV slots of [2][B_K][d]
     CT = -(-1024 // g)
     slots = pmax // CT + H * sum(nb) + 2
-    assert s.bwd_ws_bytes >= 4 * N * H * g + rows * d * 4 + slots * 2 * B * d * 4 + queue
+    if halves == 1:
+        assert s.bwd_ws_bytes >= 4 * N * H * g + rows * d * 4 + slots * 2 * B * d * 4 + queue
+    else:
+        assert s.bwd_ws_bytes == 0  # no backward kernel for this shape
 
 
 def test_max_pairs_bounds_real_pairs():
@@ -125,7 +129,7 @@ def test_max_pairs_bounds_real_pairs():
     [
         (dict(g=0), SHAPE), (dict(g=17), SHAPE), (dict(H=0), SHAPE),
         (dict(d=48), UNSUP), (dict(d=100), SHAPE), (dict(d=512), SHAPE),
-        (dict(B=32), UNSUP), (dict(B=0), SHAPE), (dict(B=128, d=256), UNSUP),
+        (dict(B=32), UNSUP), (dict(B=0), SHAPE),
         (dict(T=0), SHAPE), (dict(T=257), SHAPE),
         (dict(dtype=2), DTYPE), (dict(partial=5), DTYPE),
         (dict(cu=(1, 100)), SHAPE), (dict(cu=(0, 100, 50)), SHAPE), (dict(num_seqs=0), SHAPE),
@@ -141,8 +145,12 @@ def test_sizes_rejects(kw, status):
 
 def test_sizes_accepts_edge_shapes():
     for kw in (dict(cu=(0, 0)), dict(cu=(0, 0, 5, 5)), dict(T=256), dict(g=16, d=256), dict(B=128, d=64),
-               dict(scale=-1.0), dict(cu=(0, 1)), dict(cu=(0, 6912 * 64))):
+               dict(scale=-1.0), dict(cu=(0, 1)), dict(cu=(0, 6912 * 64)), dict(B=128, d=256)):
         assert sizes(prob(**kw))[0] == OK, kw
+    # 128-key blocks at d = 256: forward only (two partial rows per pair, no backward)
+    st, s = sizes(prob(B=128, d=256, g=2))
+    st64, s64 = sizes(prob(B=64, d=256, g=2))
+    assert st == OK and s.bwd_ws_bytes == 0 and s.partial_ws_bytes >= 2 * s.max_pairs * 2 * 256 * 4
     assert sizes(prob(cu=(0, 0)))[1].max_pairs == 0
 
 

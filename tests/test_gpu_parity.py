@@ -29,6 +29,7 @@ LARGE = [
     ("n64k_h4_g2_d128_t16_bf16", "fp32"),
     ("n64k_h4_g1_d128_t16_bf16", "fp32"),
     ("n64k_h4_g4_d128_b128_t8_bf16", "input"),
+    ("n32k_h4_g4_d256_b128_t8_bf16", "input"),
 ]
 
 
@@ -144,6 +145,57 @@ def test_adversarial_selection(case, partial):
     res = run_gpu(w, partial)
     check_index(res, O.build_index(w.sel, w.cu_seqlens, B))
     check_attention(res, w)
+
+
+BLOCK128_D256 = [
+    # seqlens, H, g, T, dtype: last blocks of 44, 1, 64 and 65 tokens leave the
+    # second 64-key half of the block empty or one key long
+    ((300, 129, 64, 1000), 2, 3, 5, "fp16"),
+    ((4096, 700), 2, 4, 8, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BLOCK128_D256)))
+@pytest.mark.parametrize("partial", ["fp32", "input"])
+def test_block128_d256_all_tokens(case, partial):
+    # 128-key blocks at head dim 256: the main kernel runs each block as two
+    # 64-key halves with a partial row each; the reduction adds both
+    seqlens, H, g, T, dtype = BLOCK128_D256[case]
+    rng = np.random.default_rng(7100 + case)
+    from sparse_attention_sel_amd.inputs import cu_seqlens_of
+
+    cu = cu_seqlens_of(seqlens)
+    sel = adversarial_sel(rng, H, cu, 128, T)
+    sel[:, ::37, :] = -1
+    w = custom_workload(seqlens, H, g, 256, 128, T, dtype, sel, seed=7200 + case)
+    log(f"[run] B_K=128 d=256 case {case} partial={partial}")
+    res = run_gpu(w, partial)
+    check_index(res, O.build_index(w.sel, w.cu_seqlens, 128))
+    check_attention(res, w)
+
+
+def test_block128_d256_unsupported_paths():
+    # no query-outer, one-pass or backward kernels exist for this shape
+    import sparse_attention_sel_amd as fsa
+
+    w = custom_workload((300,), 1, 2, 256, 128, 3, "bf16", np.zeros((1, 300, 3), np.int32), seed=1)
+    dev = torch.device("cuda:0")
+    prob = fsa.Problem(w.cu_seqlens, 1, 2, 256, 128, 3, device=dev)
+    assert fsa.get_sizes(prob)["bwd_ws_bytes"] == 0
+    q, k, v = (x.to(dev) for x in (w.q, w.k, w.v))
+    sel = torch.zeros((1, 300, 3), dtype=torch.int32, device=dev)
+    lse = torch.empty((300, 2), dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    with pytest.raises(fsa.FsaError) as e:
+        fsa.nsa_selected_attn_fwd(prob, q, k, v, sel, lse, out)
+    assert e.value.status == 4
+    index = fsa.allocate_index(prob, dev)
+    ws = fsa.Workspaces(prob, dev, index.sizes)
+    fsa.build_index(prob, sel, index, ws.build)
+    with pytest.raises(fsa.FsaError) as e:
+        fsa.selected_attn_fwd_onepass(prob, q, k, v, index, torch.empty_like(lse), lse, out, ws.stats, ws.partial)
+    assert e.value.status == 4
+    torch.cuda.synchronize()
 
 
 def test_full_selection_equals_causal_attention():
