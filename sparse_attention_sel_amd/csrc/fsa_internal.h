@@ -234,13 +234,16 @@ __device__ __forceinline__ Item read_item_half(const int4* __restrict__ work, co
 
 // Persistent workgroups take their items from dynamic work queues.  The grid
 // is a multiple of 8 and workgroup i runs on XCD x = i % 8 (round-robin
-// dispatch).  Queue x covers the contiguous range [x * per, min((x + 1) * per,
-// total)) of the token-ordered work list, so the items in flight on one XCD
-// gather neighbouring query rows into that XCD's L2.  The workgroups of XCD x
-// claim the items of queue x in order with an atomic counter, then move on to
-// the other queues in turn, so every workgroup stays busy while any item is
-// left (item sizes vary, and a static split left some XCDs a quarter more rows
-// than others).  Which workgroup takes an item changes no output.  The
+// dispatch).  The token-ordered work list is dealt to the queues in stripes of
+// kStripe consecutive items (stripe s to queue s % 8), so each XCD works on
+// runs of neighbouring items (query rows that its L2 may already hold) while
+// all eight XCDs stay within one window of the list (one KV head and stretch
+// of tokens, whose Q rows the memory-side cache can hold; splitting the list
+// into eight contiguous ranges instead ran 1-3% slower).  The workgroups of
+// XCD x claim the items of queue x in order with an atomic counter, then move
+// on to the other queues in turn, so every workgroup stays busy while any item
+// is left (item sizes vary).  Which workgroup takes an item changes no
+// output.  The
 // counters live in the workspace of the call (statistics, forward or backward
 // workspace), cleared by the kernel that runs before the persistent one, so
 // the index is read-only after it is built and calls that use one index with
@@ -249,24 +252,26 @@ constexpr int kQueues = 8;
 constexpr int kQueueStride = 32;  // ints between counters: one 128-byte line each
 constexpr int kQueueInts = kQueues * kQueueStride;
 
+constexpr int kStripe = 64;
+
 struct WorkQueue {
   int32_t* q;
-  int per, total, x, tried;
+  int total, x, tried;
   __device__ __forceinline__ WorkQueue(int32_t* counters, int total_items) : q(counters), total(total_items) {
-    per = (total + kQueues - 1) / kQueues;
     x = blockIdx.x & (kQueues - 1);
     tried = 0;
   }
   // One thread per workgroup: the next item, or -1 once every queue is empty.
+  // Claim i of queue qq is item ((i / S) * kQueues + qq) * S + i % S, which
+  // increases with i, so the first claim past the end ends the queue (each
+  // workgroup overshoots a queue at most once: the counters stay far below
+  // 2^31 for any list the index can hold).
   __device__ __forceinline__ int claim() {
     while (tried < kQueues) {
       const int qq = (x + tried) & (kQueues - 1);
-      const int base = qq * per;
-      const int n = min(per, total - base);
-      if (n > 0) {
-        const int i = atomicAdd(q + qq * kQueueStride, 1);
-        if (i < n) return base + i;
-      }
+      const int i = atomicAdd(q + qq * kQueueStride, 1);
+      const int w = ((i / kStripe) * kQueues + qq) * kStripe + i % kStripe;
+      if (w < total) return w;
       ++tried;
     }
     return -1;
