@@ -127,6 +127,31 @@ __device__ __forceinline__ void qk_tile(const T* __restrict__ Ks, const T* __res
   }
 }
 
+// Gather of one 32-row Q tile straight into the B-operand layout of
+// S^T = K Q^T: lane (lr, hl) holds row lr, elements ks*16 + hl*8 .. +8 for
+// every ks (each load covers 32 bytes of each of the tile's 32 rows).
+template <typename T, int D>
+__device__ __forceinline__ void load_q_frag(const T* __restrict__ q, const int* __restrict__ ridx, int tile, int lr,
+                                            int hl, typename Vec8<T>::type* b) {
+  const T* row = q + (size_t)ridx[tile * 32 + lr] * D + hl * 8;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) b[ks] = load8(row + ks * 16);
+}
+
+// S^T tile from a gathered B operand (as qk_tile, without the LDS tile).
+template <typename T, int D, int BK>
+__device__ __forceinline__ void qk_frag(const T* __restrict__ Ks, const typename Vec8<T>::type* b, int lr, int hl,
+                                        f32x16* s) {
+  constexpr int KS = D / 16, KT = BK / 32;
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) s[kt] = f32x16{};
+  const T* kp = Ks + lr * k_ld<D>() + hl * 8;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) s[kt] = mfma32(load8(kp + kt * 32 * k_ld<D>() + ks * 16), b[ks], s[kt]);
+}
+
 // O^T += V^T P^T over one key block: o[mt] holds O^T rows (d) mt*32.. of the
 // lane's query row; pb are the 16-bit probabilities of probs().
 template <typename T, int D, int BK>
@@ -248,17 +273,26 @@ struct ItemStage {
 template <int D, int BK>
 constexpr int attn_waves_per_eu() { return (D >= 256 || (D >= 128 && BK >= 128)) ? 1 : 2; }
 
-// Threads of the statistics kernel's workgroups (one wave per 32-row tile in
-// flight).  At 128-key blocks and d = 128 its tile state fits 256 registers
-// but K and the Q tiles fill 113 KB of LDS, one workgroup per CU: eight waves
-// then keep two per SIMD (0.56 against 0.67 ms with four at 64K tokens).  The
-// main kernel's tile state at that shape needs more than 256 registers (an
-// eight-wave variant taking the scores 64 keys at a time spilled and ran no
-// faster), so it keeps four waves at one per SIMD.
+// The statistics kernel's shapes.  Small tiles (d * B_K below 128 * 128)
+// gather each Q tile with coalesced loads and pass it through an LDS tile to
+// the MFMA B operand, two waves per SIMD.  Wider tiles gather the B operand
+// straight into registers (32 bytes of each row per load): with no Q tiles in
+// LDS, two workgroups fit a CU, two waves per SIMD where one fit before, and
+// the next item's K is loaded at the item boundary instead of into registers
+// during the current item (the other workgroup covers that latency).  At
+// d = 256, B_K = 128 the scores take the registers, one wave per SIMD, and
+// the prefetch stays.  Measured on the statistics stage: d = 256 B_K = 64
+// 4.98 -> 4.51 ms, d = 256 B_K = 128 0.52 -> 0.42 ms, d = 128 B_K = 128
+// 0.47 -> 0.43 ms; the register gather at d = 128 B_K = 64 (occupancy
+// unchanged, four times the load instructions) ran 14% slower.
 template <int D, int BK>
-constexpr int stats_threads() { return D == 128 && BK == 128 ? 2 * kAttnThreads : kAttnThreads; }
+constexpr int stats_threads() { return kAttnThreads; }
 template <int D, int BK>
-constexpr int stats_waves_per_eu() { return D == 128 && BK == 128 ? 2 : attn_waves_per_eu<D, BK>(); }
+constexpr bool stats_gather_b() { return D * BK >= 128 * 128; }
+template <int D, int BK>
+constexpr int stats_waves_per_eu() { return D == 256 && BK == 128 ? 1 : 2; }
+template <int D, int BK>
+constexpr bool stats_prefetch() { return !stats_gather_b<D, BK>() || (D == 256 && BK == 128); }
 
 // Every key of the block is visible to every row of the tile: the block lies
 // entirely before each row's token (rows of a chunk are in token order, so
@@ -305,8 +339,9 @@ __global__ __launch_bounds__((stats_threads<D, BK>())) __attribute__((amdgpu_wav
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32;
   constexpr int NT = stats_threads<D, BK>(), NW = NT / 64;
+  constexpr bool FRAG = stats_gather_b<D, BK>(), PRE = stats_prefetch<D, BK>();
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
-  __shared__ __attribute__((aligned(16))) T Qt[NW * 32 * tile_ld<D>()];
+  __shared__ __attribute__((aligned(16))) T Qt[FRAG ? 8 : NW * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
   __shared__ int s_items[2];
   ItemChain ch(queue, nwork[2], s_items);  // the forward list
@@ -315,11 +350,12 @@ __global__ __launch_bounds__((stats_threads<D, BK>())) __attribute__((amdgpu_wav
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
-  T* const qt = Qt + wave * 32 * tile_ld<D>();
+  T* const qt = Qt + (FRAG ? 0 : wave * 32 * tile_ld<D>());
   ItemStage<T, D, BK, false, NT> pre;
-  pre.load(k, nullptr, qidx, wl, counts, offsets, ch.cur, H, g, NB, CT);
+  if constexpr (PRE) pre.load(k, nullptr, qidx, wl, counts, offsets, ch.cur, H, g, NB, CT);
   while (ch.cur >= 0) {
     __syncthreads();  // the previous item's LDS reads are done
+    if constexpr (!PRE) pre.load(k, nullptr, qidx, wl, counts, offsets, ch.cur, H, g, NB, CT);
     pre.commit(Ks, nullptr, ridx, rtok, g, HQ);
     ch.publish(s_items);
     const Item it = pre.it;
@@ -327,20 +363,7 @@ __global__ __launch_bounds__((stats_threads<D, BK>())) __attribute__((amdgpu_wav
     const int after = ch.after(s_items);
     const int nrows = it.ntok * g, ntile = (nrows + 31) / 32;
 
-    // Q pipeline: one register set plus the wave's LDS tile.  At each tile the
-    // registers (tile i, loaded during tile i - 1) go to LDS and are refilled
-    // with tile i + 1 while tile i computes from LDS.  The next item's staging
-    // loads are issued after the first Q tile's.  (A second register set, two
-    // gathers in flight per wave, ran no faster at d = 128 and 7% slower at
-    // d = 256: the gathers are bandwidth-bound, not latency-bound.)
-    V8 qv[KS];
-    if (wave < ntile) load_q_tile<T, D>(q, ridx, wave, lane, qv);
-    if (ch.nxt >= 0) pre.load(k, nullptr, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
-    for (int tl = wave; tl < ntile; tl += NW) {
-      put_q_tile<T, D>(qt, lane, qv);
-      if (tl + NW < ntile) load_q_tile<T, D>(q, ridx, tl + NW, lane, qv);
-      f32x16 s[KT];
-      qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
+    auto stats_of = [&](int tl, const f32x16* s) {
       const int row = tl * 32 + lr;
       const int tok = rtok[row];
       float2 ml;
@@ -348,6 +371,43 @@ __global__ __launch_bounds__((stats_threads<D, BK>())) __attribute__((amdgpu_wav
       else ml = row_stats<BK, true>(s, hl, tok < 0 ? -1 : tok - it.bs, scale_log2);
       // lanes l and l + 32 store the same pair; rows past the chunk go to the dump
       st[tok >= 0 ? (size_t)it.pair0 * g + row : dump_row + lr] = ml;
+    };
+    if constexpr (FRAG) {
+      // Q pipeline: two register sets, each a tile's B operand gathered
+      // straight from memory; tile i + 1 is in flight while tile i computes.
+      auto tile = [&](int tl, const V8* b) {
+        f32x16 s[KT];
+        qk_frag<T, D, BK>(Ks, b, lr, hl, s);
+        stats_of(tl, s);
+      };
+      V8 qa[KS], qb[KS];
+      if (wave < ntile) load_q_frag<T, D>(q, ridx, wave, lr, hl, qa);
+      if constexpr (PRE)
+        if (ch.nxt >= 0) pre.load(k, nullptr, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
+      for (int tl = wave; tl < ntile; tl += 2 * NW) {
+        if (tl + NW < ntile) load_q_frag<T, D>(q, ridx, tl + NW, lr, hl, qb);
+        tile(tl, qa);
+        if (tl + NW >= ntile) break;
+        if (tl + 2 * NW < ntile) load_q_frag<T, D>(q, ridx, tl + 2 * NW, lr, hl, qa);
+        tile(tl + NW, qb);
+      }
+    } else {
+      // Q pipeline: one register set of coalesced loads plus the wave's LDS
+      // tile.  At each tile the registers (tile i, loaded during tile i - 1)
+      // go to LDS and are refilled with tile i + 1 while tile i computes from
+      // LDS.  The next item's staging loads are issued after the first Q
+      // tile's.  (A second register set, two gathers in flight per wave, ran
+      // no faster at d = 128.)
+      V8 qv[KS];
+      if (wave < ntile) load_q_tile<T, D>(q, ridx, wave, lane, qv);
+      if (ch.nxt >= 0) pre.load(k, nullptr, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
+      for (int tl = wave; tl < ntile; tl += NW) {
+        put_q_tile<T, D>(qt, lane, qv);
+        if (tl + NW < ntile) load_q_tile<T, D>(q, ridx, tl + NW, lane, qv);
+        f32x16 s[KT];
+        qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
+        stats_of(tl, s);
+      }
     }
     ch.advance(after);
   }

@@ -98,8 +98,10 @@ def pretty(name: str) -> str:
     t = lambda x: _TYPES.get(x, x)  # noqa: E731
     for k in ("k_main_local", "k_main"):
         a = _template_args(name, k)
-        if a and len(a) == 5:
-            return f"`{k}<{t(a[0])}, d={a[1]}, B_K={a[2]}, partial={t(a[3])}{', one-pass' if a[4] == 'true' else ''}>`"
+        if a and len(a) in (5, 6):
+            split = ", two 64-key halves" if len(a) == 6 and a[5] == "true" else ""
+            return (f"`{k}<{t(a[0])}, d={a[1]}, B_K={a[2]}, partial={t(a[3])}"
+                    f"{', one-pass' if a[4] == 'true' else ''}{split}>`")
     for k in ("k_stats_local", "k_stats", "k_nsa", "k_bwd_kv_reduce"):
         a = _template_args(name, k)
         if a and len(a) == 3:
@@ -111,9 +113,10 @@ def pretty(name: str) -> str:
     if a and len(a) == 2:
         return f"`k_bwd_delta<{t(a[0])}, d={a[1]}>`"
     a = _template_args(name, "k_reduce")
-    if a and len(a) == 4:
+    if a and len(a) in (4, 5):
         kind = "local" if a[2] == "true" else "all slots"
-        return f"`k_reduce<{t(a[0])}, partial={t(a[1])}, {kind}{', one-pass' if a[3] == 'true' else ''}>`"
+        split = ", two 64-key halves" if len(a) == 5 and a[4] == "true" else ""
+        return f"`k_reduce<{t(a[0])}, partial={t(a[1])}, {kind}{', one-pass' if a[3] == 'true' else ''}{split}>`"
     a = _template_args(name, "k_select")
     if a and len(a) == 1:
         return f"`k_select<{'rows in registers' if a[0] == 'true' else 'rows from memory'}>`"

@@ -59,6 +59,13 @@ def test_profile_summary_on_rocprof_csv(tmp_path):
     assert ps.pretty("_ZN3fsa12_GLOBAL__N_18k_reduceIDF16_fLb1ELb1EEEvPKi") == \
         "`k_reduce<fp16, partial=fp32, local, one-pass>`"
     assert ps.pretty("fsa::(anonymous namespace)::k_hist(int const*)") == "`k_hist`"
+    # the current kernels carry a split-halves flag after the one-pass flag
+    assert ps.pretty("_ZN3fsa12_GLOBAL__N_16k_mainIDF16bLi128ELi64EDF16bLb0ELb0EEEvPKT_S4_S4_PKi") == \
+        "`k_main<bf16, d=128, B_K=64, partial=bf16>`"
+    assert ps.pretty("_ZN3fsa12_GLOBAL__N_16k_mainIDF16bLi256ELi64EDF16bLb0ELb1EEEvPKT_S4_S4_PKi") == \
+        "`k_main<bf16, d=256, B_K=64, partial=bf16, two 64-key halves>`"
+    assert ps.pretty("_ZN3fsa12_GLOBAL__N_18k_reduceIDF16bDF16bLb1ELb0ELb0EEEvPKi") == \
+        "`k_reduce<bf16, partial=bf16, local>`"
     hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
 
     def pmc(d, counter, rows):
