@@ -293,6 +293,8 @@ template <int D, int BK>
 constexpr int stats_waves_per_eu() { return D == 256 && BK == 128 ? 1 : 2; }
 template <int D, int BK>
 constexpr bool stats_prefetch() { return !stats_gather_b<D, BK>() || (D == 256 && BK == 128); }
+template <int D, int BK>
+constexpr int stats_local_waves_per_eu() { return stats_gather_b<D, BK>() ? 2 : attn_waves_per_eu<D, BK>(); }
 
 // Every key of the block is visible to every row of the tile: the block lies
 // entirely before each row's token (rows of a chunk are in token order, so
@@ -787,6 +789,16 @@ __device__ __forceinline__ void load_q_local(const T* __restrict__ q, const Loca
   }
 }
 
+// The wave's Q tile of a local item gathered straight into the B-operand
+// layout of S^T = K Q^T (as load_q_frag).
+template <typename T, int D>
+__device__ __forceinline__ void load_q_local_frag(const T* __restrict__ q, const LocalItem& it, int wave, int lr,
+                                                  int hl, int g, int HQ, typename Vec8<T>::type* b) {
+  const T* row = q + (size_t)local_qrow(it, wave * 32 + lr, g, HQ) * D + hl * 8;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) b[ks] = load8(row + ks * 16);
+}
+
 // One key block of head h in registers, then in LDS: K as [key][D + 8] and,
 // WITH_V, V transposed and key-permuted as in ItemStage.  Keys past nk repeat
 // the last key (only the own block can be short, and there the causal mask
@@ -861,15 +873,18 @@ __device__ __forceinline__ int64_t local_dst(const LocalItem& it, int r, int tok
 // queue: the statistics kernel's work-queue counters, cleared by workgroup 0
 // (this kernel runs first in the statistics call).
 template <typename T, int D, int BK>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_stats_local(
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(stats_local_waves_per_eu<D, BK>()))) void k_stats_local(
     const T* __restrict__ q, const T* __restrict__ k, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc,
     const int32_t* __restrict__ slot, float2* __restrict__ st, int32_t* __restrict__ queue, int N, int H, int g,
     int Tn, int NB, int groups, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32;
+  // wide tiles keep the Q tile as the B operand in registers (no LDS tile),
+  // as the statistics kernel does
+  constexpr bool FRAG = stats_gather_b<D, BK>();
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
-  __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
+  __shared__ __attribute__((aligned(16))) T Qt[FRAG ? 8 : kWaves * 32 * tile_ld<D>()];
   if (blockIdx.x == 0) clear_queue(queue);
   const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups);
   if (it.rows == 0) return;
@@ -877,14 +892,17 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
   const bool busy = wave * 32 < it.rows;
-  T* const qt = Qt + wave * 32 * tile_ld<D>();
+  T* const qt = Qt + (FRAG ? 0 : wave * 32 * tile_ld<D>());
   const int kinds = min(it.e, 2) + 1;
   // every load of the item's start goes out here: the own block's K, the Q
   // tile and the row's local word
   BlockStage<T, D, BK, false> pre;
   pre.load(k, nullptr, H, it.h, it.bs, it.ntok);
   V8 qv[KS];
-  if (busy) load_q_local<T, D>(q, it, wave, lane, g, HQ, qv);
+  if (busy) {
+    if constexpr (FRAG) load_q_local_frag<T, D>(q, it, wave, lr, hl, g, HQ, qv);
+    else load_q_local<T, D>(q, it, wave, lane, g, HQ, qv);
+  }
   const int row = wave * 32 + lr;
   const int qrow = local_qrow(it, row, g, HQ);
   const int tok = row < it.rows ? qrow / HQ : -1;
@@ -897,9 +915,13 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     __syncthreads();
     if (kind + 1 < kinds) pre.load(k, nullptr, H, it.h, it.seq_lo + local_block(kind + 1, it.e) * BK, BK);
     if (!busy) continue;
-    if (kind == 0) put_q_tile<T, D>(qt, lane, qv);
     f32x16 s[KT];
-    qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
+    if constexpr (FRAG) {
+      qk_frag<T, D, BK>(Ks, qv, lr, hl, s);
+    } else {
+      if (kind == 0) put_q_tile<T, D>(qt, lane, qv);
+      qk_tile<T, D, BK>(Ks, qt, lr, hl, s);
+    }
     const int lim = local_lim<BK>(tok, word, kind, kbs);
     const float2 ml = kind == 0 ? row_stats<BK, true>(s, hl, lim, scale_log2)
                                 : row_stats<BK, false>(s, hl, 0, scale_log2);
