@@ -164,6 +164,18 @@ __device__ __forceinline__ void pv_tile(const T* __restrict__ Vt, const typename
     for (int mt = 0; mt < MT; ++mt) o[mt] = mfma32(load8(Vt + (mt * 32 + lr) * vt_ld<BK>() + kk * 16 + hl * 8), pb[kk], o[mt]);
 }
 
+// pv_tile for the output tiles M0 .. M0 + NM (d = M0*32 .. (M0 + NM)*32).
+template <typename T, int D, int BK, int M0, int NM>
+__device__ __forceinline__ void pv_part(const T* __restrict__ Vt, const typename Vec8<T>::type* pb, int lr, int hl,
+                                        f32x16* o) {
+  constexpr int KK = BK / 16;
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+      o[m] = mfma32(load8(Vt + ((M0 + m) * 32 + lr) * vt_ld<BK>() + kk * 16 + hl * 8), pb[kk], o[m]);
+}
+
 // x combined with the same register of lane l ^ 32 by a commutative op:
 // v_permlane32_swap of x with itself hands each lane the values of lanes
 // l % 32 (first result) and l % 32 + 32 (second result).  The compiler treats
@@ -293,6 +305,9 @@ template <int D, int BK>
 constexpr int stats_waves_per_eu() { return D == 256 && BK == 128 ? 1 : 2; }
 template <int D, int BK>
 constexpr bool stats_prefetch() { return !stats_gather_b<D, BK>() || (D == 256 && BK == 128); }
+// The three-pass main kernel's d = 256 pipeline (see k_main).
+template <int D, bool FUSED>
+constexpr bool main_deep_q() { return D == 256 && !FUSED; }
 template <int D, int BK>
 constexpr int stats_local_waves_per_eu() { return stats_gather_b<D, BK>() ? 2 : attn_waves_per_eu<D, BK>(); }
 
@@ -497,19 +512,22 @@ __device__ __forceinline__ void stage_write4<_Float16>(_Float16* p, f32x4 x) {
   *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, __builtin_convertvector(x, v4));
 }
 
-// o[mt][r] holds O^T[d = mt*32 + 8*(r/4) + 4*hl + r%4][row = lane % 32].
-// Writes rows [0, rows) of the tile to dst (row-major, pitch D), the others
-// to the matching rows of dump.
-template <typename PT, int D>
+// o[mt][r] holds O^T[d = C0 + mt*32 + 8*(r/4) + 4*hl + r%4][row = lane % 32]
+// for the NC columns C0 .. C0 + NC of the tile.  Writes rows [0, rows) of the
+// tile to dst (row-major, pitch D), the others to the matching rows of dump.
+template <typename PT, int D, int NC = D, int C0 = 0>
 __device__ __forceinline__ void store_tile(PT* __restrict__ stage, const f32x16* o, int lane, int rows,
                                            PT* __restrict__ dst, PT* __restrict__ dump) {
-  constexpr int CW = Stage<PT, D>::CW, P = Stage<PT, D>::P;
+  constexpr int CW = Stage<PT, D>::CW < NC ? Stage<PT, D>::CW : NC, P = CW + 16 / (int)sizeof(PT);
   constexpr int EPL = 16 / (int)sizeof(PT);  // elements per 16-byte lane store
   constexpr int LPR = CW / EPL;              // lanes per staged row
   constexpr int RPI = 64 / LPR;              // rows per store instruction
+  static_assert(NC % CW == 0, "whole passes");
   const int lr = lane & 31, hl = lane >> 5;
+  dst += C0;
+  dump += C0;
 #pragma unroll
-  for (int c = 0; c < D / CW; ++c) {
+  for (int c = 0; c < NC / CW; ++c) {
 #pragma unroll
     for (int m = 0; m < CW / 32; ++m)
 #pragma unroll
@@ -678,6 +696,55 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     __syncthreads();
     const int after = ch.after(s_items);
     const int nrows = it.ntok * g, ntile = (nrows + 31) / 32;
+
+    if constexpr (main_deep_q<D, FUSED>()) {
+      // d = 256: Q tiles gathered straight into B-operand registers (two
+      // sets: tile i + 1 in flight while tile i computes; no LDS round trip)
+      // and O^T in two 128-column halves, each stored before the next
+      // accumulates.  The lse of a tile's rows comes with its Q rows.
+      auto ld = [&](int tl, V8* b, float& l) {
+        load_q_frag<T, D>(q, ridx, tl, lr, hl, b);
+        l = lse[ridx[tl * 32 + lr]];
+      };
+      auto tile = [&](int tl, const V8* b, float lrow) {
+        f32x16 s[KT];
+        qk_frag<T, D, BK>(Ks, b, lr, hl, s);
+        const int tok = rtok[tl * 32 + lr];
+        const int lim = tok < 0 ? -1 : tok - it.bs;
+        V8 pb[KK];
+        if (tile_unmasked<BK>(tok, it.bs)) probs<T, BK, false>(s, scale_log2, lrow * kLog2e, hl, 0, pb);
+        else probs<T, BK, true>(s, scale_log2, lrow * kLog2e, hl, lim, pb);
+        PT* const dst = partial + ((size_t)it.half * half_rows + (size_t)it.pair0 * g + (size_t)tl * 32) * D;
+        const int rows = min(32, nrows - tl * 32);
+        {
+          f32x16 o[MT / 2];
+#pragma unroll
+          for (int m = 0; m < MT / 2; ++m) o[m] = f32x16{};
+          pv_part<T, D, BK, 0, MT / 2>(Vt, pb, lr, hl, o);
+          store_tile<PT, D, D / 2, 0>(stage, o, lane, rows, dst, dump);
+        }
+        {
+          f32x16 o[MT / 2];
+#pragma unroll
+          for (int m = 0; m < MT / 2; ++m) o[m] = f32x16{};
+          pv_part<T, D, BK, MT / 2, MT / 2>(Vt, pb, lr, hl, o);
+          store_tile<PT, D, D / 2, D / 2>(stage, o, lane, rows, dst, dump);
+        }
+      };
+      V8 qa[KS], qb[KS];
+      float la = 0.f, lb = 0.f;
+      if (wave < ntile) ld(wave, qa, la);
+      if (ch.nxt >= 0) pre.load(k, v, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
+      for (int tl = wave; tl < ntile; tl += 2 * NW) {
+        if (tl + NW < ntile) ld(tl + NW, qb, lb);
+        tile(tl, qa, la);
+        if (tl + NW >= ntile) break;
+        if (tl + 2 * NW < ntile) ld(tl + 2 * NW, qa, la);
+        tile(tl + NW, qb, lb);
+      }
+      ch.advance(after);
+      continue;
+    }
 
     // Q pipeline: one register set plus the wave's LDS tile (as in k_stats);
     // the lse of tile i + 1 is loaded with its Q rows.
