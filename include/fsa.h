@@ -236,6 +236,7 @@ int32_t fsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void
  *                 [N, h_K*g], written.
  *   stats_ws      device scratch of at least stats_ws_bytes (16-byte aligned).
  *   partial_ws    device scratch of at least partial_ws_bytes (16-byte aligned).
+ * B_K = 128 with d = 256 returns FSA_ERR_UNSUPPORTED.
  */
 int32_t fsa_selected_attn_fwd_onepass(const fsa_problem* prob, const void* q, const void* k, const void* v,
                                       const fsa_index* idx, float* row_max, float* lse, void* out,
@@ -252,9 +253,12 @@ int32_t fsa_selected_attn_fwd_onepass(const fsa_problem* prob, const void* q, co
  * previous and first block (its local entries) are computed per query block
  * instead: their sum is written to the rows of one of them (the own-block
  * entry, else the previous-block one, else the first-block one) and the
- * other local entries' rows are left unwritten.  partial_ws is otherwise
- * private to the library (it also holds the main kernel's work-queue
- * counters after the rows); fsa_selected_attn_reduce reads it as written.
+ * other local entries' rows are left unwritten.  With B_K = 128 and d = 256
+ * each block runs as two 64-key halves: the first half's rows are as above,
+ * the second half's lie max_pairs * g rows further on, and the reduction adds
+ * both.  partial_ws is otherwise private to the library (it also holds the
+ * main kernel's work-queue counters after the rows);
+ * fsa_selected_attn_reduce reads it as written.
  */
 int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const void* k, const void* v,
                                const fsa_index* idx, const float* lse, void* partial_ws,
@@ -287,9 +291,9 @@ int32_t fsa_selected_attn_reduce(const fsa_problem* prob, const fsa_index* idx, 
  *   dq                  device [N, h_K*g, d]; dk, dv device [N, h_K, d]; input
  *                       dtype, 16-byte aligned, fully written;
  *   ws                  device scratch of at least bwd_ws_bytes, 256-byte aligned.
- * Compiled for every shape the forward supports (B_K = 64 with d in
- * {64, 128, 256}, B_K = 128 with d in {64, 128}); a shape without a backward
- * would return FSA_ERR_UNSUPPORTED with bwd_ws_bytes = 0.
+ * Compiled for every shape the forward supports except B_K = 128 with
+ * d = 256, which returns FSA_ERR_UNSUPPORTED (fsa_get_sizes reports
+ * bwd_ws_bytes = 0 for it).
  */
 int32_t fsa_selected_attn_bwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
                               const void* out, const void* dout, const float* lse, const fsa_index* idx,
@@ -326,8 +330,8 @@ int32_t fsa_select_blocks(const fsa_problem* prob, const float* scores, int64_t 
  *                 output row for a row with no valid Sel entry).
  *   q, k, v, out  device, 16-byte aligned;  sel  device int32 [h_K, N, T],
  *                 4-byte aligned;  lse  device, 4-byte aligned.
- * Returns FSA_ERR_NULL / _ALIGN / _SHAPE / _UNSUPPORTED before any launch,
- * FSA_ERR_HIP if the launch fails.
+ * Returns FSA_ERR_NULL / _ALIGN / _SHAPE / _UNSUPPORTED (also for B_K = 128
+ * with d = 256) before any launch, FSA_ERR_HIP if the launch fails.
  */
 int32_t fsa_nsa_selected_attn_fwd(const fsa_problem* prob, const void* q, const void* k, const void* v,
                                   const int32_t* sel, float* lse, void* out, void* stream);
