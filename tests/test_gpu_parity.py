@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle.fsa_oracle as O
-from gpu_helpers import TOL_LSE, TOL_O, check_full_forward, custom_workload, log, run_gpu
+from gpu_helpers import TOL_LSE, TOL_O, check_full_forward, custom_workload, log, run_gpu, sample_tokens
 from sparse_attention_sel_amd.inputs import WORKLOADS, make_workload
 
 pytestmark = pytest.mark.gpu
@@ -145,6 +145,60 @@ def test_adversarial_selection(case, partial):
     res = run_gpu(w, partial)
     check_index(res, O.build_index(w.sel, w.cu_seqlens, B))
     check_attention(res, w)
+
+
+def test_largest_block_window():
+    # One sequence of 6912 blocks of 64 tokens: the last token tiles can select
+    # any of the 6912 blocks, the largest window the index builder takes (one
+    # more block is FSA_ERR_UNSUPPORTED), which sizes k_scatter's LDS.  Rows keep
+    # their own block and block 0 and add one pick uniform over every earlier
+    # block and one recent block; every 41st row is padding only.  The index is
+    # compared bit for bit; outputs on sampled tokens, and lse / row max of
+    # every token against bounds that hold at any size.
+    nb, B, T = 6912, 64, 4
+    n = nb * B
+    rng = np.random.default_rng(8800)
+    own = np.arange(n, dtype=np.int64) // B
+    sel = np.empty((1, n, T), dtype=np.int32)
+    sel[0, :, 0] = own
+    sel[0, :, 1] = 0
+    sel[0, :, 2] = (rng.random(n) * (own + 1)).astype(np.int64)
+    sel[0, :, 3] = own - rng.geometric(0.2, size=n)  # -1 and below: padding
+    sel[:, ::41, :] = -1
+    w = custom_workload((n,), 1, 2, 64, B, T, "bf16", sel, seed=8801)
+    log(f"[run] largest block window: {n} tokens, {nb} blocks")
+    res = run_gpu(w, "input")
+    ref = O.build_index(w.sel, w.cu_seqlens, B)
+    log(f"    index: {ref['pairs']} pairs")
+    check_index(res, ref)
+    lse, m = res["lse"], res["row_max"]
+    empty = np.zeros(n, dtype=bool)
+    empty[::41] = True
+    assert np.all(np.isneginf(lse[empty])) and np.all(np.isneginf(m[empty]))
+    assert np.all(res["out"][empty] == 0)
+    # lse - row max = ln(sum exp(s - max)) lies in [0, ln(visible keys)]
+    nkeys = np.zeros(n, dtype=np.float64)
+    for t0 in range(0, n, 1 << 16):
+        toks = np.arange(t0, min(n, t0 + (1 << 16)))
+        rows = w.sel[0, toks]
+        e = np.where(_valid_rows(rows, toks, B), rows, -1)
+        ownb = (toks // B)[:, None]
+        full = ((e >= 0) & (e < ownb)).sum(axis=1) * B
+        nkeys[toks] = full + np.where((e == ownb).any(axis=1), toks % B + 1, 0)
+    fin = ~empty
+    d = lse[fin] - m[fin]
+    bound = np.log(nkeys[fin])[:, None]
+    assert np.all(d >= -1e-3) and np.all(d <= bound + 1e-3), "lse outside [row max, row max + ln(keys)]"
+    check_attention(res, w, sample_tokens(w.cu_seqlens, B, n_random=160, seed=8802))
+
+
+def _valid_rows(rows, toks, B):
+    # first occurrences of the entries 0 <= e <= own block of each row
+    own = (toks // B)[:, None]
+    ok = (rows >= 0) & (rows <= own)
+    for j in range(1, rows.shape[1]):
+        ok[:, j] &= ~np.any(rows[:, :j] == rows[:, j : j + 1], axis=1)
+    return ok
 
 
 BLOCK128_D256 = [
