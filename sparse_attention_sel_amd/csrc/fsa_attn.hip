@@ -817,13 +817,25 @@ struct LocalItem {
   int h, e, bs, ntok, seq_lo, seq_hi, row0, rows;
 };
 
-// Local item i = (KV head, global block, row group); rows = 0 when the group
-// lies past the block's rows.
+// Workgroup i runs on XCD i % 8.  The row groups of kLocalUnit consecutive
+// query blocks (one unit) go to one XCD, so the key blocks they share (their
+// own blocks, each other's previous blocks and the first block) are fetched
+// into that XCD's L2 once instead of by every XCD.
+constexpr int kLocalUnit = 4;
+
+// Local item of workgroup i = (KV head, global block, row group); rows = 0
+// when the group lies past the block's rows or past the last block.
 __device__ __forceinline__ LocalItem local_item(int i, const int32_t* __restrict__ cu,
                                                 const int32_t* __restrict__ gboff, int num_seqs, int NB, int BK, int g,
-                                                int groups) {
+                                                int groups, int nblocks) {
   LocalItem it;
-  const int grp = i % groups, f = i / groups;
+  const int per_unit = kLocalUnit * groups, k = i >> 3;
+  const int u = (k / per_unit) * 8 + (i & 7), w = k % per_unit;
+  const int f = u * kLocalUnit + w / groups, grp = w % groups;
+  if (f >= nblocks) {
+    it.rows = 0;
+    return it;
+  }
   it.h = f / NB;
   const int gb = f - it.h * NB;
   const int sq = seq_of_block(gboff, num_seqs, gb);
@@ -953,7 +965,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(st
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
   __shared__ __attribute__((aligned(16))) T Qt[FRAG ? 8 : kWaves * 32 * tile_ld<D>()];
   if (blockIdx.x == 0) clear_queue(queue);
-  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups);
+  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups, H * NB);
   if (it.rows == 0) return;
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1020,7 +1032,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
   __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
   if (blockIdx.x == 0) clear_queue(queue);
-  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups);
+  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups, H * NB);
   if (it.rows == 0) return;
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -1279,10 +1291,12 @@ inline Ptrs<int> index_ptrs(const Geometry& geo, const fsa_index& idx) {
 // before it (the local kernels clear them otherwise).
 __global__ __launch_bounds__(256) void k_clear_queue(int32_t* __restrict__ queue) { clear_queue(queue); }
 
-// Workgroups of the local kernels, one per item (KV head, global block, row group).
+// Workgroups of the local kernels, one per item (KV head, global block, row
+// group), in whole units per XCD (local_item); the surplus returns at once.
 inline unsigned local_grid(const Geometry& geo, int* groups) {
   *groups = (geo.BK * geo.g + kLocalRows - 1) / kLocalRows;
-  return (unsigned)((int64_t)geo.H * geo.NB * *groups);
+  const int64_t units = ((int64_t)geo.H * geo.NB + kLocalUnit - 1) / kLocalUnit;
+  return (unsigned)(((units + 7) / 8) * 8 * kLocalUnit * *groups);
 }
 
 template <typename T, int D, int BK>
