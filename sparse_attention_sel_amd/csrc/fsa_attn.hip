@@ -84,6 +84,14 @@ __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~15) + ((w >> 2) & 1) * 8 + (w >> 3) * 4 + (w & 3);
 }
 
+// The same for the 16-row tiles of v_mfma_f32_16x16x32: within each 32-key
+// group, lane group u (lanes 16u..16u+15) contributes keys {4u..4u+3,
+// 16+4u..16+4u+3} as MFMA elements e = 0..7, the keys its S^T tiles hold.
+__device__ __forceinline__ int vt_pos16(int key) {
+  const int w = key & 31;
+  return (key & ~31) + ((w >> 2) & 3) * 8 + (w >> 4) * 4 + (w & 3);
+}
+
 // Coalesced gather of the Q rows of one 32-row tile: vector v of lane l holds
 // tile elements (v*64 + l)*8 .. +8, i.e. row (v*64 + l)*8 / D, column
 // (v*64 + l)*8 % D.
@@ -164,18 +172,6 @@ __device__ __forceinline__ void pv_tile(const T* __restrict__ Vt, const typename
     for (int mt = 0; mt < MT; ++mt) o[mt] = mfma32(load8(Vt + (mt * 32 + lr) * vt_ld<BK>() + kk * 16 + hl * 8), pb[kk], o[mt]);
 }
 
-// pv_tile for the output tiles M0 .. M0 + NM (d = M0*32 .. (M0 + NM)*32).
-template <typename T, int D, int BK, int M0, int NM>
-__device__ __forceinline__ void pv_part(const T* __restrict__ Vt, const typename Vec8<T>::type* pb, int lr, int hl,
-                                        f32x16* o) {
-  constexpr int KK = BK / 16;
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-    for (int m = 0; m < NM; ++m)
-      o[m] = mfma32(load8(Vt + ((M0 + m) * 32 + lr) * vt_ld<BK>() + kk * 16 + hl * 8), pb[kk], o[m]);
-}
-
 // x combined with the same register of lane l ^ 32 by a commutative op:
 // v_permlane32_swap of x with itself hands each lane the values of lanes
 // l % 32 (first result) and l % 32 + 32 (second result).  The compiler treats
@@ -203,7 +199,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // clamped indices so that they are unconditional: keys past a partial last
 // block are only ever seen by rows that take the causal mask (their values
 // get weight zero), rows past the chunk are marked with token -1.
-template <typename T, int D, int BK, bool WITH_V, int NT, bool SPLIT = false>
+template <typename T, int D, int BK, bool WITH_V, int NT, bool SPLIT = false, bool VT16 = false>
 struct ItemStage {
   using V8 = typename Vec8<T>::type;
   static constexpr int KV = BK * D / 8 / NT;                        // K vectors per thread
@@ -259,7 +255,7 @@ struct ItemStage {
       for (int i = 0; i < VP; ++i) {
         const int vi = threadIdx.x + i * NT;
         const int c = vi / KP, key = 2 * (vi % KP);
-        const int pos = vt_pos(key);
+        const int pos = VT16 ? vt_pos16(key) : vt_pos(key);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t packed = (uint32_t)bits16(va[i][e]) | ((uint32_t)bits16(vb[i][e]) << 16);
@@ -305,9 +301,6 @@ template <int D, int BK>
 constexpr int stats_waves_per_eu() { return D == 256 && BK == 128 ? 1 : 2; }
 template <int D, int BK>
 constexpr bool stats_prefetch() { return !stats_gather_b<D, BK>() || (D == 256 && BK == 128); }
-// The three-pass main kernel's d = 256 pipeline (see k_main).
-template <int D, bool FUSED>
-constexpr bool main_deep_q() { return D == 256 && !FUSED; }
 template <int D, int BK>
 constexpr int stats_local_waves_per_eu() { return stats_gather_b<D, BK>() ? 2 : attn_waves_per_eu<D, BK>(); }
 
@@ -512,22 +505,19 @@ __device__ __forceinline__ void stage_write4<_Float16>(_Float16* p, f32x4 x) {
   *reinterpret_cast<u32x2*>(p) = __builtin_bit_cast(u32x2, __builtin_convertvector(x, v4));
 }
 
-// o[mt][r] holds O^T[d = C0 + mt*32 + 8*(r/4) + 4*hl + r%4][row = lane % 32]
-// for the NC columns C0 .. C0 + NC of the tile.  Writes rows [0, rows) of the
-// tile to dst (row-major, pitch D), the others to the matching rows of dump.
-template <typename PT, int D, int NC = D, int C0 = 0>
+// o[mt][r] holds O^T[d = mt*32 + 8*(r/4) + 4*hl + r%4][row = lane % 32].
+// Writes rows [0, rows) of the tile to dst (row-major, pitch D), the others
+// to the matching rows of dump.
+template <typename PT, int D>
 __device__ __forceinline__ void store_tile(PT* __restrict__ stage, const f32x16* o, int lane, int rows,
                                            PT* __restrict__ dst, PT* __restrict__ dump) {
-  constexpr int CW = Stage<PT, D>::CW < NC ? Stage<PT, D>::CW : NC, P = CW + 16 / (int)sizeof(PT);
+  constexpr int CW = Stage<PT, D>::CW, P = Stage<PT, D>::P;
   constexpr int EPL = 16 / (int)sizeof(PT);  // elements per 16-byte lane store
   constexpr int LPR = CW / EPL;              // lanes per staged row
   constexpr int RPI = 64 / LPR;              // rows per store instruction
-  static_assert(NC % CW == 0, "whole passes");
   const int lr = lane & 31, hl = lane >> 5;
-  dst += C0;
-  dump += C0;
 #pragma unroll
-  for (int c = 0; c < NC / CW; ++c) {
+  for (int c = 0; c < D / CW; ++c) {
 #pragma unroll
     for (int m = 0; m < CW / 32; ++m)
 #pragma unroll
@@ -656,18 +646,15 @@ __device__ __forceinline__ float2 probs_stats(const f32x16* s, float c, int hl, 
 // (max, sum) of its scores over this block, P = exp(s - max), and the
 // partial row is divided by the sum, so it holds the block's own softmax
 // average of V; the (max, sum) pair goes to `st` as the statistics kernel
-// would write it, and the reduction weighs the partial rows by it.
-// SPLIT (B_K = 128 with d = 256, instantiated with BK = 64): each work item
-// of 128-key blocks runs as two items, one per 64-key half, whose partial
-// rows lie half_rows apart; the reduction adds both.
-template <typename T, int D, int BK, typename PT, bool FUSED, bool SPLIT = false>
+// would write it, and the reduction weighs the partial rows by it.  The
+// three-pass forward at d = 256 with 64-key blocks runs k_main16 instead.
+template <typename T, int D, int BK, typename PT, bool FUSED>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
     const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
-    float2* __restrict__ st, PT* __restrict__ partial, size_t dump_row, size_t half_rows, int H, int g, int NB,
-    int CT, float scale_log2) {
-  static_assert(!(SPLIT && FUSED), "split items only in the three-pass forward");
+    float2* __restrict__ st, PT* __restrict__ partial, size_t dump_row, int H, int g, int NB, int CT,
+    float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
   constexpr int NT = kAttnThreads, NW = kWaves;
@@ -677,7 +664,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   __shared__ __attribute__((aligned(16))) T Qt[NW * 32 * tile_ld<D>()];
   __shared__ int ridx[kRowTable], rtok[kRowTable];
   __shared__ int s_items[2];
-  ItemChain ch(queue, SPLIT ? 2 * nwork[2] : nwork[2], s_items);  // the forward list
+  ItemChain ch(queue, nwork[2], s_items);  // the forward list
   const int4* const wl = work + nwork[0];
   if (ch.cur < 0) return;
   const int HQ = H * g;
@@ -686,7 +673,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   T* const qt = Qt + wave * 32 * tile_ld<D>();
   PT* const stage = reinterpret_cast<PT*>(qt);
   PT* const dump = partial + dump_row * D;
-  ItemStage<T, D, BK, true, NT, SPLIT> pre;
+  ItemStage<T, D, BK, true, NT> pre;
   pre.load(k, v, qidx, wl, counts, offsets, ch.cur, H, g, NB, CT);
   while (ch.cur >= 0) {
     __syncthreads();  // the previous item's LDS reads are done
@@ -696,55 +683,6 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     __syncthreads();
     const int after = ch.after(s_items);
     const int nrows = it.ntok * g, ntile = (nrows + 31) / 32;
-
-    if constexpr (main_deep_q<D, FUSED>()) {
-      // d = 256: Q tiles gathered straight into B-operand registers (two
-      // sets: tile i + 1 in flight while tile i computes; no LDS round trip)
-      // and O^T in two 128-column halves, each stored before the next
-      // accumulates.  The lse of a tile's rows comes with its Q rows.
-      auto ld = [&](int tl, V8* b, float& l) {
-        load_q_frag<T, D>(q, ridx, tl, lr, hl, b);
-        l = lse[ridx[tl * 32 + lr]];
-      };
-      auto tile = [&](int tl, const V8* b, float lrow) {
-        f32x16 s[KT];
-        qk_frag<T, D, BK>(Ks, b, lr, hl, s);
-        const int tok = rtok[tl * 32 + lr];
-        const int lim = tok < 0 ? -1 : tok - it.bs;
-        V8 pb[KK];
-        if (tile_unmasked<BK>(tok, it.bs)) probs<T, BK, false>(s, scale_log2, lrow * kLog2e, hl, 0, pb);
-        else probs<T, BK, true>(s, scale_log2, lrow * kLog2e, hl, lim, pb);
-        PT* const dst = partial + ((size_t)it.half * half_rows + (size_t)it.pair0 * g + (size_t)tl * 32) * D;
-        const int rows = min(32, nrows - tl * 32);
-        {
-          f32x16 o[MT / 2];
-#pragma unroll
-          for (int m = 0; m < MT / 2; ++m) o[m] = f32x16{};
-          pv_part<T, D, BK, 0, MT / 2>(Vt, pb, lr, hl, o);
-          store_tile<PT, D, D / 2, 0>(stage, o, lane, rows, dst, dump);
-        }
-        {
-          f32x16 o[MT / 2];
-#pragma unroll
-          for (int m = 0; m < MT / 2; ++m) o[m] = f32x16{};
-          pv_part<T, D, BK, MT / 2, MT / 2>(Vt, pb, lr, hl, o);
-          store_tile<PT, D, D / 2, D / 2>(stage, o, lane, rows, dst, dump);
-        }
-      };
-      V8 qa[KS], qb[KS];
-      float la = 0.f, lb = 0.f;
-      if (wave < ntile) ld(wave, qa, la);
-      if (ch.nxt >= 0) pre.load(k, v, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
-      for (int tl = wave; tl < ntile; tl += 2 * NW) {
-        if (tl + NW < ntile) ld(tl + NW, qb, lb);
-        tile(tl, qa, la);
-        if (tl + NW >= ntile) break;
-        if (tl + 2 * NW < ntile) ld(tl + 2 * NW, qa, la);
-        tile(tl + NW, qb, lb);
-      }
-      ch.advance(after);
-      continue;
-    }
 
     // Q pipeline: one register set plus the wave's LDS tile (as in k_stats);
     // the lse of tile i + 1 is loaded with its Q rows.
@@ -788,8 +726,160 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
         for (int mt = 0; mt < MT; ++mt) o[mt] *= inv;
       }
       store_tile<PT, D>(stage, o, lane, min(32, nrows - tl * 32),
-                        partial + ((size_t)it.half * half_rows + (size_t)it.pair0 * g + (size_t)tl * 32) * D,
+                        partial + ((size_t)it.pair0 * g + (size_t)tl * 32) * D,
                         dump);
+    }
+    ch.advance(after);
+  }
+}
+
+// ---- main kernel at d = 256: 16-row tiles ------------------------------------------
+// v_mfma_f32_16x16x32 (lane l: A row / B column l % 16, contraction elements
+// 8u .. 8u + 7 with u = l / 16; result column l % 16, rows 4u .. 4u + 3).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// P = exp2(s * c - l2) of the lane's query row as the B operands of
+// O^T = V^T P^T: s[kt][r] is key kt*16 + 4u + r; element e of pb[kk] is key
+// 32kk + 16 (e / 4) + 4u + e % 4, the order vt_pos16 gives V^T.
+template <typename T, bool MASKED>
+__device__ __forceinline__ void probs16(const f32x4* s, float c, float l2, int u, int lim,
+                                        typename Vec8<T>::type* pb) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    typename Vec8<T>::type x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int kt = 2 * kk + (e >> 2), r = e & 3;
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kt][r], c, -l2));
+      x[e] = (T)((!MASKED || kt * 16 + 4 * u + r <= lim) ? p : 0.f);
+    }
+    pb[kk] = x;
+  }
+}
+
+// o[m][r] = O^T[d = C0 + 16m + 4u + r][row = l % 16] for the NC columns
+// C0 .. C0 + NC of a 16-row tile: staged row-major in the wave's LDS stage,
+// then written as whole 16-byte pieces (rows [0, rows) to dst, pitch D; the
+// others to the matching rows of dump).
+template <typename PT, int D, int NC, int C0>
+__device__ __forceinline__ void store_tile16(PT* __restrict__ stage, const f32x4* o, int lane, int rows,
+                                             PT* __restrict__ dst, PT* __restrict__ dump) {
+  constexpr int P = NC + 16 / (int)sizeof(PT);  // stage pitch: rows 16 bytes apart in banks
+  constexpr int EPL = 16 / (int)sizeof(PT), LPR = NC / EPL, RPI = 64 / LPR;
+  const int lr = lane & 15, u = lane >> 4;
+#pragma unroll
+  for (int m = 0; m < NC / 16; ++m) stage_write4<PT>(stage + lr * P + m * 16 + 4 * u, o[m]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < 16 / RPI; ++i) {
+    const int row = i * RPI + lane / LPR, col = (lane % LPR) * EPL;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * P + col);
+    PT* base = row < rows ? dst : dump;
+    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(base + (size_t)row * D + C0 + col));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The three-pass main kernel at d = 256 and 64-key blocks (SPLIT: the halves
+// of 128-key blocks, as in k_main).  The 32-row tiles of k_main hold O^T in
+// 128 registers per lane, one wave per SIMD; with 16-row tiles a lane holds a
+// quarter of that per O half, so eight waves of a workgroup share the staged
+// K and V at two waves per SIMD.  Each wave walks 16-row tiles; the Q rows of
+// a tile are gathered straight into the B operand of S^T = K Q^T (64
+// contiguous bytes of each row per load), tile i + 1 in flight while tile i
+// computes; O^T is accumulated and stored in two 128-column halves.
+template <typename T, typename PT, bool SPLIT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_main16(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
+    const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
+    PT* __restrict__ partial, size_t dump_row, size_t half_rows, int H, int g, int NB, int CT, float scale_log2) {
+  using V8 = typename Vec8<T>::type;
+  constexpr int D = 256, BK = 64, NT = 512, NW = NT / 64;
+  constexpr int KS = D / 32;   // contraction steps of S^T
+  constexpr int KT = BK / 16;  // key tiles of S^T
+  constexpr int MH = D / 32;   // 16-column O^T tiles per half
+  constexpr int SP = D / 2 + 16 / (int)sizeof(PT);  // stage pitch of store_tile16
+  __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
+  __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
+  __shared__ __attribute__((aligned(16))) PT Stg[NW * 16 * SP];
+  __shared__ int ridx[kRowTable], rtok[kRowTable];
+  __shared__ int s_items[2];
+  ItemChain ch(queue, SPLIT ? 2 * nwork[2] : nwork[2], s_items);  // the forward list
+  const int4* const wl = work + nwork[0];
+  if (ch.cur < 0) return;
+  const int HQ = H * g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, u = lane >> 4;
+  PT* const stage = Stg + wave * 16 * SP;
+  PT* const dump = partial + dump_row * D;
+  ItemStage<T, D, BK, true, NT, SPLIT, true> pre;
+  pre.load(k, v, qidx, wl, counts, offsets, ch.cur, H, g, NB, CT);
+  while (ch.cur >= 0) {
+    __syncthreads();  // the previous item's LDS reads are done
+    pre.commit(Ks, Vt, ridx, rtok, g, HQ);
+    ch.publish(s_items);
+    const Item it = pre.it;
+    __syncthreads();
+    const int after = ch.after(s_items);
+    const int nrows = it.ntok * g, ntile = (nrows + 15) / 16;
+
+    auto ld = [&](int tl, V8* b, float& l) {
+      const int qr = ridx[tl * 16 + lr];
+      const T* row = q + (size_t)qr * D + 8 * u;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) b[ks] = load8(row + ks * 32);
+      l = lse[qr];
+    };
+    auto tile = [&](int tl, const V8* b, float lrow) {
+      f32x4 s[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) s[kt] = f32x4{};
+      const T* kp = Ks + lr * k_ld<D>() + 8 * u;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) s[kt] = mfma16(load8(kp + kt * 16 * k_ld<D>() + ks * 32), b[ks], s[kt]);
+      const int tok = rtok[tl * 16 + lr];
+      V8 pb[2];
+      if (tile_unmasked<BK>(tok, it.bs)) probs16<T, false>(s, scale_log2, lrow * kLog2e, u, 0, pb);
+      else probs16<T, true>(s, scale_log2, lrow * kLog2e, u, tok < 0 ? -1 : tok - it.bs, pb);
+      PT* const dst = partial + ((size_t)it.half * half_rows + (size_t)it.pair0 * g + (size_t)tl * 16) * D;
+      const int rows = min(16, nrows - tl * 16);
+      const T* vp = Vt + lr * vt_ld<BK>() + 8 * u;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 o[MH];
+#pragma unroll
+        for (int m = 0; m < MH; ++m) o[m] = f32x4{};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int m = 0; m < MH; ++m)
+            o[m] = mfma16(load8(vp + ((h * MH + m) * 16) * vt_ld<BK>() + kk * 32), pb[kk], o[m]);
+        if (h == 0) store_tile16<PT, D, D / 2, 0>(stage, o, lane, rows, dst, dump);
+        else store_tile16<PT, D, D / 2, D / 2>(stage, o, lane, rows, dst, dump);
+      }
+    };
+    V8 qa[KS], qb[KS];
+    float la = 0.f, lb = 0.f;
+    if (wave < ntile) ld(wave, qa, la);
+    if (ch.nxt >= 0) pre.load(k, v, qidx, wl, counts, offsets, ch.nxt, H, g, NB, CT);
+    for (int tl = wave; tl < ntile; tl += 2 * NW) {
+      if (tl + NW < ntile) ld(tl + NW, qb, lb);
+      tile(tl, qa, la);
+      if (tl + NW >= ntile) break;
+      if (tl + 2 * NW < ntile) ld(tl + 2 * NW, qa, la);
+      tile(tl + NW, qb, lb);
     }
     ch.advance(after);
   }
@@ -1346,14 +1436,22 @@ void main_launch(const Geometry& geo, const int32_t* cu, const void* q, const vo
   } else {
     hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(256), 0, stream, queue);
   }
-  if (geo.max_work > 0)
-    hipLaunchKernelGGL((k_main<T, D, BK, PT, FUSED, SPLIT>),
-                       dim3(persistent_grid(k_main<T, D, BK, PT, FUSED, SPLIT>, kAttnThreads,
-                                            (SPLIT ? 2 : 1) * geo.max_work)),
+  if (geo.max_work <= 0) return;
+  if constexpr (D == 256 && BK == 64 && !FUSED) {
+    // 16-row tiles, eight waves (see k_main16)
+    hipLaunchKernelGGL((k_main16<T, PT, SPLIT>),
+                       dim3(persistent_grid(k_main16<T, PT, SPLIT>, 512, (SPLIT ? 2 : 1) * geo.max_work)), dim3(512),
+                       0, stream, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
+                       p.counts, p.offsets, p.qidx, p.work, p.nwork, queue, lse, part, (size_t)geo.dump_row,
+                       (size_t)geo.split_half_rows, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
+  } else {
+    static_assert(!SPLIT, "split items only at d = 256");
+    hipLaunchKernelGGL((k_main<T, D, BK, PT, FUSED>),
+                       dim3(persistent_grid(k_main<T, D, BK, PT, FUSED>, kAttnThreads, geo.max_work)),
                        dim3(kAttnThreads), 0, stream, static_cast<const T*>(q), static_cast<const T*>(k),
                        static_cast<const T*>(v), p.counts, p.offsets, p.qidx, p.work, p.nwork, queue, lse, st, part,
-                       (size_t)geo.dump_row, (size_t)geo.split_half_rows, geo.H, geo.g, geo.NB, geo.chunk_tokens,
-                       sl2);
+                       (size_t)geo.dump_row, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
+  }
 }
 
 template <typename T, int D, int BK, typename PT>
