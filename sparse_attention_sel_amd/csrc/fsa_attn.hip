@@ -789,6 +789,34 @@ __device__ __forceinline__ void store_tile16(PT* __restrict__ stage, const f32x4
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// store_tile16 with a destination row per tile row: lane l < 16 holds in
+// `drow` the partial row (pitch D) of tile row l, or -1 to send it to the
+// matching dump row.
+template <typename PT, int D, int NC, int C0>
+__device__ __forceinline__ void store_tile16_rows(PT* __restrict__ stage, const f32x4* o, int lane, int64_t drow,
+                                                  PT* __restrict__ partial, PT* __restrict__ dump) {
+  constexpr int P = NC + 16 / (int)sizeof(PT);
+  constexpr int EPL = 16 / (int)sizeof(PT), LPR = NC / EPL, RPI = 64 / LPR;
+  const int lr = lane & 15, u = lane >> 4;
+  const int dlo = (int)(uint32_t)(uint64_t)drow, dhi = (int)(uint32_t)((uint64_t)drow >> 32);
+#pragma unroll
+  for (int m = 0; m < NC / 16; ++m) stage_write4<PT>(stage + lr * P + m * 16 + 4 * u, o[m]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int i = 0; i < 16 / RPI; ++i) {
+    const int row = i * RPI + lane / LPR, col = (lane % LPR) * EPL;
+    const int64_t r = (int64_t)(((uint64_t)(uint32_t)__shfl(dhi, row, 64) << 32) | (uint32_t)__shfl(dlo, row, 64));
+    const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * P + col);
+    PT* dst = r >= 0 ? partial + (size_t)r * D : dump + (size_t)row * D;
+    __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(dst + C0 + col));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // The three-pass main kernel at d = 256 and 64-key blocks (SPLIT: the halves
 // of 128-key blocks, as in k_main).  The 32-row tiles of k_main hold O^T in
 // 128 registers per lane, one wave per SIMD; with 16-row tiles a lane holds a
@@ -973,24 +1001,25 @@ __device__ __forceinline__ void load_q_local_frag(const T* __restrict__ q, const
 // the last key (only the own block can be short, and there the causal mask
 // hides them).  load() only issues the loads, so they stay in flight while the
 // previous block computes; commit() writes them to LDS.
-template <typename T, int D, int BK, bool WITH_V>
+template <typename T, int D, int BK, bool WITH_V, int NT = kAttnThreads, bool VT16 = false>
 struct BlockStage {
   using V8 = typename Vec8<T>::type;
-  static constexpr int C8 = D / 8, KV = BK * C8 / kAttnThreads, KP = BK / 2;
-  static constexpr int VP = WITH_V ? KP * C8 / kAttnThreads : 1;
+  static constexpr int C8 = D / 8, KV = BK * C8 / NT, KP = BK / 2;
+  static constexpr int VP = WITH_V ? KP * C8 / NT : 1;
+  static_assert(BK * C8 % NT == 0 && (!WITH_V || KP * C8 % NT == 0), "whole vectors");
   V8 kr[KV], va[VP], vb[VP];
 
   __device__ __forceinline__ void load(const T* __restrict__ kg, const T* __restrict__ vg, int H, int h, int kbs,
                                        int nk) {
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const int vi = threadIdx.x + i * kAttnThreads;
+      const int vi = threadIdx.x + i * NT;
       kr[i] = load8(kg + ((size_t)(kbs + min(vi / C8, nk - 1)) * H + h) * D + (vi % C8) * 8);
     }
     if constexpr (WITH_V) {
 #pragma unroll
       for (int i = 0; i < VP; ++i) {
-        const int vi = threadIdx.x + i * kAttnThreads;
+        const int vi = threadIdx.x + i * NT;
         const int c = vi / KP, key = 2 * (vi % KP);
         va[i] = load8(vg + ((size_t)(kbs + min(key, nk - 1)) * H + h) * D + c * 8);
         vb[i] = load8(vg + ((size_t)(kbs + min(key + 1, nk - 1)) * H + h) * D + c * 8);
@@ -1001,15 +1030,15 @@ struct BlockStage {
   __device__ __forceinline__ void commit(T* __restrict__ Ks, T* __restrict__ Vt) const {
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const int vi = threadIdx.x + i * kAttnThreads;
+      const int vi = threadIdx.x + i * NT;
       *reinterpret_cast<V8*>(Ks + (vi / C8) * k_ld<D>() + (vi % C8) * 8) = kr[i];
     }
     if constexpr (WITH_V) {
 #pragma unroll
       for (int i = 0; i < VP; ++i) {
-        const int vi = threadIdx.x + i * kAttnThreads;
+        const int vi = threadIdx.x + i * NT;
         const int c = vi / KP, key = 2 * (vi % KP);
-        const int pos = vt_pos(key);
+        const int pos = VT16 ? vt_pos16(key) : vt_pos(key);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t packed = (uint32_t)bits16(va[i][e]) | ((uint32_t)bits16(vb[i][e]) << 16);
@@ -1184,6 +1213,86 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     if (busy && hl == 0 && dst >= 0) st[dst] = make_float2(M, L);
   }
   if (busy) store_tile_rows<PT, D>(reinterpret_cast<PT*>(qt), o, lane, dst, partial, dump);
+}
+
+// The three-pass local main kernel at d = 256 (k_main_local's items, 128
+// rows each): eight waves with one 16-row tile each, so that a lane's O^T
+// over the whole head dimension takes 64 registers and two waves fit a SIMD
+// (k_main_local's 32-row tiles take 128, one wave per SIMD).  The layouts are
+// k_main16's; the accumulation over the local blocks and the designated-row
+// stores are k_main_local's.
+template <typename T, typename PT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_main_local16(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc,
+    const int32_t* __restrict__ slot, const float* __restrict__ lse, PT* __restrict__ partial,
+    PT* __restrict__ dump, int32_t* __restrict__ queue, int N, int H, int g, int Tn, int NB, int groups,
+    float scale_log2) {
+  using V8 = typename Vec8<T>::type;
+  constexpr int D = 256, BK = 64, NT = 512, NW = NT / 64;
+  constexpr int KS = D / 32, KT = BK / 16, MT = D / 16;
+  constexpr int SP = D / 2 + 16 / (int)sizeof(PT);
+  static_assert(NW * 16 == kLocalRows, "one 16-row tile per wave");
+  __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
+  __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
+  __shared__ __attribute__((aligned(16))) PT Stg[NW * 16 * SP];
+  if (blockIdx.x == 0) clear_queue(queue);
+  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups, H * NB);
+  if (it.rows == 0) return;
+  const int HQ = H * g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lr = lane & 15, u = lane >> 4;
+  const bool busy = wave * 16 < it.rows;
+  PT* const stage = Stg + wave * 16 * SP;
+  const int kinds = min(it.e, 2) + 1;
+  // every load of the item's start goes out here: the own block's K and V,
+  // the Q rows (the B operand of S^T = K Q^T), the row's local word and lse
+  BlockStage<T, D, BK, true, NT, true> pre;
+  pre.load(k, v, H, it.h, it.bs, it.ntok);
+  const int row = wave * 16 + lr;
+  const int qrow = local_qrow(it, row, g, HQ);
+  V8 qv[KS];
+  if (busy) {
+    const T* qp = q + (size_t)qrow * D + 8 * u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qv[ks] = load8(qp + ks * 32);
+  }
+  const int tok = row < it.rows ? qrow / HQ : -1;
+  const unsigned word = tok >= 0 ? (unsigned)loc[(size_t)it.h * N + tok] : 0u;
+  const float l2 = tok >= 0 ? lse[qrow] * kLog2e : 0.f;
+  f32x4 o[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) o[m] = f32x4{};
+  for (int kind = 0; kind < kinds; ++kind) {
+    const int kbs = it.seq_lo + local_block(kind, it.e) * BK;
+    __syncthreads();  // the previous block's K / V reads are done
+    pre.commit(Ks, Vt);
+    __syncthreads();
+    if (kind + 1 < kinds) pre.load(k, v, H, it.h, it.seq_lo + local_block(kind + 1, it.e) * BK, BK);
+    if (!busy) continue;
+    f32x4 s[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) s[kt] = f32x4{};
+    const T* kp = Ks + lr * k_ld<D>() + 8 * u;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) s[kt] = mfma16(load8(kp + kt * 16 * k_ld<D>() + ks * 32), qv[ks], s[kt]);
+    const int lim = local_lim<BK>(tok, word, kind, kbs);
+    V8 pb[2];
+    if (__all(lim == BK - 1)) probs16<T, false>(s, scale_log2, l2, u, 0, pb);
+    else probs16<T, true>(s, scale_log2, l2, u, lim, pb);
+    const T* vp = Vt + lr * vt_ld<BK>() + 8 * u;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) o[m] = mfma16(load8(vp + m * 16 * vt_ld<BK>() + kk * 32), pb[kk], o[m]);
+  }
+  const int64_t dst = local_dst(it, row, tok, word, slot, N, Tn, g);
+  if (busy) {
+    store_tile16_rows<PT, D, D / 2, 0>(stage, o, lane, dst, partial, dump);
+    store_tile16_rows<PT, D, D / 2, D / 2>(stage, o + MT / 2, lane, dst, partial, dump);
+  }
 }
 
 // ---- reduce -----------------------------------------------------------------
@@ -1426,15 +1535,22 @@ void main_launch(const Geometry& geo, const int32_t* cu, const void* q, const vo
   float2* const st = static_cast<float2*>(st_ws);
   int32_t* const queue = reinterpret_cast<int32_t*>(static_cast<char*>(partial) + geo.partial_queue_off);
   // the local kernel (or the clear kernel) runs first: it zeroes the queue counters
-  if (geo.local) {
+  if (!geo.local) {
+    hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(256), 0, stream, queue);
+  } else if constexpr (D == 256 && BK == 64 && !FUSED) {
+    // 16-row tiles, eight waves (see k_main_local16)
+    int groups = 0;
+    const unsigned grid = local_grid(geo, &groups);
+    hipLaunchKernelGGL((k_main_local16<T, PT>), dim3(grid), dim3(512), 0, stream, static_cast<const T*>(q),
+                       static_cast<const T*>(k), static_cast<const T*>(v), cu, p.gboff, geo.num_seqs, p.loc, idx.slot,
+                       lse, part, dump, queue, geo.N, geo.H, geo.g, geo.T, geo.NB, groups, sl2);
+  } else {
     int groups = 0;
     const unsigned grid = local_grid(geo, &groups);
     hipLaunchKernelGGL((k_main_local<T, D, BK, PT, FUSED>), dim3(grid), dim3(kAttnThreads), 0, stream,
                        static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), cu, p.gboff,
                        geo.num_seqs, p.loc, idx.slot, lse, st, part, dump, queue, geo.N, geo.H, geo.g, geo.T,
                        geo.NB, groups, sl2);
-  } else {
-    hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(256), 0, stream, queue);
   }
   if (geo.max_work <= 0) return;
   if constexpr (D == 256 && BK == 64 && !FUSED) {
