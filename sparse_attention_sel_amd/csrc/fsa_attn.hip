@@ -301,6 +301,10 @@ template <int D, int BK>
 constexpr int stats_waves_per_eu() { return D == 256 && BK == 128 ? 1 : 2; }
 template <int D, int BK>
 constexpr bool stats_prefetch() { return !stats_gather_b<D, BK>() || (D == 256 && BK == 128); }
+// Shapes whose three-pass main kernel is k_main16: those where k_main's
+// 32-row tiles need more than 256 registers (one wave per SIMD).
+template <int D, int BK, bool FUSED>
+constexpr bool main16() { return !FUSED && ((D == 256 && BK == 64) || (D == 128 && BK == 128)); }
 template <int D, int BK>
 constexpr int stats_local_waves_per_eu() { return stats_gather_b<D, BK>() ? 2 : attn_waves_per_eu<D, BK>(); }
 
@@ -733,7 +737,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
   }
 }
 
-// ---- main kernel at d = 256: 16-row tiles ------------------------------------------
+// ---- main kernel with 16-row tiles ------------------------------------------------
 // v_mfma_f32_16x16x32 (lane l: A row / B column l % 16, contraction elements
 // 8u .. 8u + 7 with u = l / 16; result column l % 16, rows 4u .. 4u + 3).
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -746,11 +750,11 @@ __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
 // P = exp2(s * c - l2) of the lane's query row as the B operands of
 // O^T = V^T P^T: s[kt][r] is key kt*16 + 4u + r; element e of pb[kk] is key
 // 32kk + 16 (e / 4) + 4u + e % 4, the order vt_pos16 gives V^T.
-template <typename T, bool MASKED>
+template <typename T, int BK, bool MASKED>
 __device__ __forceinline__ void probs16(const f32x4* s, float c, float l2, int u, int lim,
                                         typename Vec8<T>::type* pb) {
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < BK / 32; ++kk) {
     typename Vec8<T>::type x;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -817,24 +821,26 @@ __device__ __forceinline__ void store_tile16_rows(PT* __restrict__ stage, const 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The three-pass main kernel at d = 256 and 64-key blocks (SPLIT: the halves
-// of 128-key blocks, as in k_main).  The 32-row tiles of k_main hold O^T in
-// 128 registers per lane, one wave per SIMD; with 16-row tiles a lane holds a
-// quarter of that per O half, so eight waves of a workgroup share the staged
-// K and V at two waves per SIMD.  Each wave walks 16-row tiles; the Q rows of
+// The three-pass main kernel where k_main's 32-row tiles run one wave per
+// SIMD: d = 256 with 64-key blocks (SPLIT: the halves of 128-key blocks) and
+// d = 128 with 128-key blocks.  There a lane of k_main holds 128 registers of
+// O^T (d = 256) or 64 of scores plus 64 of O^T (B_K = 128); with 16-row tiles
+// it holds a quarter of the scores and of each O^T half, so eight waves of a
+// workgroup share the staged K and V at two waves per SIMD.  Each wave walks 16-row tiles; the Q rows of
 // a tile are gathered straight into the B operand of S^T = K Q^T (64
 // contiguous bytes of each row per load), tile i + 1 in flight while tile i
 // computes; O^T is accumulated and stored in two 128-column halves.
-template <typename T, typename PT, bool SPLIT>
+template <typename T, int D, int BK, typename PT, bool SPLIT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_main16(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
     const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
     PT* __restrict__ partial, size_t dump_row, size_t half_rows, int H, int g, int NB, int CT, float scale_log2) {
   using V8 = typename Vec8<T>::type;
-  constexpr int D = 256, BK = 64, NT = 512, NW = NT / 64;
+  constexpr int NT = 512, NW = NT / 64;
   constexpr int KS = D / 32;   // contraction steps of S^T
   constexpr int KT = BK / 16;  // key tiles of S^T
+  constexpr int KK = BK / 32;  // contraction steps of O^T
   constexpr int MH = D / 32;   // 16-column O^T tiles per half
   constexpr int SP = D / 2 + 16 / (int)sizeof(PT);  // stage pitch of store_tile16
   __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
@@ -878,9 +884,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) s[kt] = mfma16(load8(kp + kt * 16 * k_ld<D>() + ks * 32), b[ks], s[kt]);
       const int tok = rtok[tl * 16 + lr];
-      V8 pb[2];
-      if (tile_unmasked<BK>(tok, it.bs)) probs16<T, false>(s, scale_log2, lrow * kLog2e, u, 0, pb);
-      else probs16<T, true>(s, scale_log2, lrow * kLog2e, u, tok < 0 ? -1 : tok - it.bs, pb);
+      V8 pb[KK];
+      if (tile_unmasked<BK>(tok, it.bs)) probs16<T, BK, false>(s, scale_log2, lrow * kLog2e, u, 0, pb);
+      else probs16<T, BK, true>(s, scale_log2, lrow * kLog2e, u, tok < 0 ? -1 : tok - it.bs, pb);
       PT* const dst = partial + ((size_t)it.half * half_rows + (size_t)it.pair0 * g + (size_t)tl * 16) * D;
       const int rows = min(16, nrows - tl * 16);
       const T* vp = Vt + lr * vt_ld<BK>() + 8 * u;
@@ -890,7 +896,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
         for (int m = 0; m < MH; ++m) o[m] = f32x4{};
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
           for (int m = 0; m < MH; ++m)
             o[m] = mfma16(load8(vp + ((h * MH + m) * 16) * vt_ld<BK>() + kk * 32), pb[kk], o[m]);
@@ -1280,8 +1286,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int kt = 0; kt < KT; ++kt) s[kt] = mfma16(load8(kp + kt * 16 * k_ld<D>() + ks * 32), qv[ks], s[kt]);
     const int lim = local_lim<BK>(tok, word, kind, kbs);
     V8 pb[2];
-    if (__all(lim == BK - 1)) probs16<T, false>(s, scale_log2, l2, u, 0, pb);
-    else probs16<T, true>(s, scale_log2, l2, u, lim, pb);
+    if (__all(lim == BK - 1)) probs16<T, BK, false>(s, scale_log2, l2, u, 0, pb);
+    else probs16<T, BK, true>(s, scale_log2, l2, u, lim, pb);
     const T* vp = Vt + lr * vt_ld<BK>() + 8 * u;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -1553,10 +1559,11 @@ void main_launch(const Geometry& geo, const int32_t* cu, const void* q, const vo
                        geo.NB, groups, sl2);
   }
   if (geo.max_work <= 0) return;
-  if constexpr (D == 256 && BK == 64 && !FUSED) {
+  if constexpr (main16<D, BK, FUSED>()) {
     // 16-row tiles, eight waves (see k_main16)
-    hipLaunchKernelGGL((k_main16<T, PT, SPLIT>),
-                       dim3(persistent_grid(k_main16<T, PT, SPLIT>, 512, (SPLIT ? 2 : 1) * geo.max_work)), dim3(512),
+    hipLaunchKernelGGL((k_main16<T, D, BK, PT, SPLIT>),
+                       dim3(persistent_grid(k_main16<T, D, BK, PT, SPLIT>, 512, (SPLIT ? 2 : 1) * geo.max_work)),
+                       dim3(512),
                        0, stream, static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v),
                        p.counts, p.offsets, p.qidx, p.work, p.nwork, queue, lse, part, (size_t)geo.dump_row,
                        (size_t)geo.split_half_rows, geo.H, geo.g, geo.NB, geo.chunk_tokens, sl2);
