@@ -103,9 +103,9 @@ def pretty(name: str) -> str:
             return (f"`{k}<{t(a[0])}, d={a[1]}, B_K={a[2]}, partial={t(a[3])}"
                     f"{', one-pass' if a[4] == 'true' else ''}{split}>`")
     a = _template_args(name, "k_main16")
-    if a and len(a) == 3:
-        split = ", two 64-key halves" if a[2] == "true" else ""
-        return f"`k_main16<{t(a[0])}, d=256, B_K=64, partial={t(a[1])}{split}>`"
+    if a and len(a) == 5:
+        split = ", two 64-key halves" if a[4] == "true" else ""
+        return f"`k_main16<{t(a[0])}, d={a[1]}, B_K={a[2]}, partial={t(a[3])}{split}>`"
     a = _template_args(name, "k_main_local16")
     if a and len(a) == 2:
         return f"`k_main_local16<{t(a[0])}, d=256, B_K=64, partial={t(a[1])}>`"

@@ -66,8 +66,10 @@ def test_profile_summary_on_rocprof_csv(tmp_path):
         "`k_main<bf16, d=256, B_K=64, partial=bf16, two 64-key halves>`"
     assert ps.pretty("_ZN3fsa12_GLOBAL__N_18k_reduceIDF16bDF16bLb1ELb0ELb0EEEvPKi") == \
         "`k_reduce<bf16, partial=bf16, local>`"
-    assert ps.pretty("_ZN3fsa12_GLOBAL__N_18k_main16IDF16bDF16bLb1EEEvPKT_S4_S4_PKi") == \
+    assert ps.pretty("_ZN3fsa12_GLOBAL__N_18k_main16IDF16bLi256ELi64EDF16bLb1EEEvPKT_S4_S4_PKi") == \
         "`k_main16<bf16, d=256, B_K=64, partial=bf16, two 64-key halves>`"
+    assert ps.pretty("_ZN3fsa12_GLOBAL__N_18k_main16IDF16_Li128ELi128EfLb0EEEvPKT_S4_S4_PKi") == \
+        "`k_main16<fp16, d=128, B_K=128, partial=fp32>`"
     assert ps.pretty("_ZN3fsa12_GLOBAL__N_114k_main_local16IDF16_fEEvPKT_S4_S4_PKiS6_i") == \
         "`k_main_local16<fp16, d=256, B_K=64, partial=fp32>`"
     hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
