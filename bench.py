@@ -164,17 +164,19 @@ def kernel_bytes(w, P, P_loc, s_in, s_p):
     """Compulsory HBM bytes of each stage (each input read once, each output
     written once).  Block-outer kernels take the P - P_loc non-local pairs;
     the local entries of a (KV head, token) give one partial row group and one
-    (max, sum) pair per query head."""
+    (max, sum) pair per query head (P_loc = 0 where the local path does not
+    run: then the local rows, pairs and words drop out)."""
     N, H, g, d, T = int(w.cu_seqlens[-1]), w.num_kv_heads, w.gqa_group, w.head_dim, w.topk
     HQ = H * g
     Pn = P - P_loc
+    has_local = 1 if P_loc else 0
     q_bytes = N * HQ * d * s_in
     kv_bytes = 2 * N * H * d * s_in
-    loc = 4 * H * N
-    local_rows = N * HQ * d * s_p
+    loc = 4 * H * N * has_local
+    local_rows = N * HQ * d * s_p * has_local
     main = q_bytes + kv_bytes + N * HQ * 4 + Pn * 4 + Pn * g * d * s_p + local_rows + loc
     reduce = Pn * g * d * s_p + local_rows + H * N * T * 4 + loc + N * HQ * d * s_in
-    stats = (q_bytes + kv_bytes // 2 + Pn * 4 + 2 * Pn * g * 8 + 2 * N * HQ * 8 + H * N * T * 4 + loc
+    stats = (q_bytes + kv_bytes // 2 + Pn * 4 + 2 * Pn * g * 8 + 2 * N * HQ * 8 * has_local + H * N * T * 4 + loc
              + 2 * N * HQ * 4)
     index = 3 * H * N * T * 4 + P * 4 + loc
     return {"index": index, "stats": stats, "main": main, "reduce": reduce}
@@ -555,6 +557,8 @@ def measured_peaks(dtype):
 def measure(w, partial, steps, warmup, query_outer=False, backward=False, selection=False, cold_reps=0,
             onepass=False, graph=False):
     P_host, P_loc, keys = work_counts(w.sel, w.cu_seqlens, w.block_size)
+    if w.block_size != 64 or w.gqa_group < 2:
+        P_loc = 0  # the library computes local entries per query block only with B_K = 64 and g >= 2
     r = run_gpu(w, partial, steps, warmup, query_outer, backward, selection, cold_reps, onepass, graph)
     assert r["pairs"] == P_host, (r["pairs"], P_host)
     f_alg = 4.0 * w.gqa_group * w.head_dim * keys

@@ -44,6 +44,10 @@ def test_kernel_bytes_counts_each_compulsory_access_once():
     main = q + 2 * N * H * d * 2 + N * H * g * 4 + (P - P_loc) * 4 + (P - P_loc) * g * d * 2 + N * H * g * d * 2 + 4 * H * N
     assert b["main"] == main
     assert b["reduce"] == (P - P_loc) * g * d * 2 + N * H * g * d * 2 + H * N * T * 4 + 4 * H * N + q
+    # without the local path every entry is block-outer: no local rows, pairs or words
+    b0 = bench.kernel_bytes(W, P, 0, 2, 2)
+    assert b0["main"] == q + 2 * N * H * d * 2 + N * H * g * 4 + P * 4 + P * g * d * 2
+    assert b0["reduce"] == P * g * d * 2 + H * N * T * 4 + q
 
 
 def test_profile_summary_on_rocprof_csv(tmp_path):

@@ -127,6 +127,8 @@ CASES = [
     ((300, 100), 1, 16, 256, 64, 6, "bf16"),  # g * d = 4096: two output vectors per reduction thread
     ((257,), 2, 3, 256, 64, 5, "fp16"),
     ((600, 200), 1, 2, 64, 128, 4, "fp16"),
+    ((500, 77, 300), 2, 1, 128, 64, 6, "bf16"),  # g = 1 with 64-key blocks: every entry block-outer
+    ((300, 129), 1, 1, 256, 64, 4, "fp16"),
 ]
 
 
