@@ -567,8 +567,10 @@ def measure(w, partial, steps, warmup, query_outer=False, backward=False, select
     byts = kernel_bytes(w, P_host, P_loc, s_in, s_p)
     N, HQ = int(w.cu_seqlens[-1]), w.num_kv_heads * w.gqa_group
     # partial rows the main stage writes: one per non-local (block, query) pair
-    # and head, plus one local row per (token, query head) where the local path runs
-    rows_written = (P_host - P_loc) * w.gqa_group + (N * HQ if P_loc else 0)
+    # and head (two with 128-key blocks at d = 256, one per 64-key half), plus
+    # one local row per (token, query head) where the local path runs
+    halves = 2 if (w.block_size == 128 and w.head_dim == 256) else 1
+    rows_written = (P_host - P_loc) * w.gqa_group * halves + (N * HQ if P_loc else 0)
     r.update(f_alg=f_alg, f_main=f_main, bytes=byts, local_pairs=P_loc,
              partial_bytes_written=rows_written * w.head_dim * s_p)
     return r
