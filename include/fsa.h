@@ -258,7 +258,12 @@ int32_t fsa_selected_attn_fwd_onepass(const fsa_problem* prob, const void* q, co
  * the second half's lie max_pairs * g rows further on, and the reduction adds
  * both.  partial_ws is otherwise private to the library (it also holds the
  * main kernel's work-queue counters after the rows);
- * fsa_selected_attn_reduce reads it as written.
+ * fsa_selected_attn_reduce reads it as written.  With local entries at
+ * d <= 128 the per-query-block work and the block-outer work can run in one
+ * persistent launch or in two launches in a row; the library picks by the
+ * amount of per-query-block work, and the environment variable
+ * FSA_MAIN_MIXED (read at each call) forces one launch (1) or two (0).  The
+ * results are the same bits either way.
  */
 int32_t fsa_selected_attn_main(const fsa_problem* prob, const void* q, const void* k, const void* v,
                                const fsa_index* idx, const float* lse, void* partial_ws,

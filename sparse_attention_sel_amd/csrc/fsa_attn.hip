@@ -42,6 +42,7 @@
 // staged transposed (Vt[d][key]) with the keys of every 16-key group permuted
 // so that the 8 keys a lane contributes to one MFMA are adjacent in LDS.
 #include <algorithm>
+#include <cstdlib>
 
 #include "fsa_internal.h"
 
@@ -652,22 +653,38 @@ __device__ __forceinline__ float2 probs_stats(const f32x16* s, float c, int hl, 
 // average of V; the (max, sum) pair goes to `st` as the statistics kernel
 // would write it, and the reduction weighs the partial rows by it.  The
 // three-pass forward at d = 256 with 64-key blocks runs k_main16 instead.
+// The LDS of k_main (also that of k_main_mixed, whose local items use the
+// first three arrays as k_main_local does).
+template <typename T, int D, int BK>
+struct MainLds {
+  alignas(16) T Ks[BK * k_ld<D>()];
+  alignas(16) T Vt[D * vt_ld<BK>()];
+  alignas(16) T Qt[kWaves * 32 * tile_ld<D>()];
+  int ridx[kRowTable], rtok[kRowTable];
+  int s_items[2];
+  int s_local;  // k_main_mixed: the workgroup's current local item
+};
+
+// k_main's persistent loop over the block-outer items of the forward list.
 template <typename T, int D, int BK, typename PT, bool FUSED>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
-    const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
-    float2* __restrict__ st, PT* __restrict__ partial, size_t dump_row, int H, int g, int NB, int CT,
-    float scale_log2) {
+__device__ __forceinline__ void main_items(MainLds<T, D, BK>& sm, const T* __restrict__ q,
+                                           const T* __restrict__ k, const T* __restrict__ v,
+                                           const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+                                           const int32_t* __restrict__ qidx, const int4* __restrict__ work,
+                                           const int32_t* __restrict__ nwork, int32_t* __restrict__ queue,
+                                           const float* __restrict__ lse, float2* __restrict__ st,
+                                           PT* __restrict__ partial, size_t dump_row, int H, int g, int NB, int CT,
+                                           float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
   constexpr int NT = kAttnThreads, NW = kWaves;
   static_assert(32 * Stage<PT, D>::P * sizeof(PT) <= 32 * tile_ld<D>() * sizeof(T), "stage fits the Q tile");
-  __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
-  __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
-  __shared__ __attribute__((aligned(16))) T Qt[NW * 32 * tile_ld<D>()];
-  __shared__ int ridx[kRowTable], rtok[kRowTable];
-  __shared__ int s_items[2];
+  T* const Ks = sm.Ks;
+  T* const Vt = sm.Vt;
+  T* const Qt = sm.Qt;
+  int* const ridx = sm.ridx;
+  int* const rtok = sm.rtok;
+  int* const s_items = sm.s_items;
   ItemChain ch(queue, nwork[2], s_items);  // the forward list
   const int4* const wl = work + nwork[0];
   if (ch.cur < 0) return;
@@ -735,6 +752,18 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     }
     ch.advance(after);
   }
+}
+
+template <typename T, int D, int BK, typename PT, bool FUSED>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
+    const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
+    float2* __restrict__ st, PT* __restrict__ partial, size_t dump_row, int H, int g, int NB, int CT,
+    float scale_log2) {
+  __shared__ __attribute__((aligned(16))) MainLds<T, D, BK> sm;
+  main_items<T, D, BK, PT, FUSED>(sm, q, k, v, counts, offsets, qidx, work, nwork, queue, lse, st, partial, dump_row,
+                                  H, g, NB, CT, scale_log2);
 }
 
 // ---- main kernel with 16-row tiles ------------------------------------------------
@@ -1139,26 +1168,18 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(st
   if (busy && hl == 0 && dst >= 0) st[dst] = make_float2(M, L);
 }
 
-// FUSED: the rows' (max, sum) run over the local blocks as in k_stats_local
-// (the same merge, so the pair written to st is the one it writes) and the
-// accumulator is rescaled when the max grows; the partial row is divided by
-// the final sum.  queue: the main kernel's work-queue counters, cleared by
-// workgroup 0 (this kernel runs first in the forward call).
+// One local item of the main stage (rows > 0); Ks, Vt and Qt are the
+// workgroup's LDS arrays, whose earlier readers finish before its first
+// barrier.
 template <typename T, int D, int BK, typename PT, bool FUSED>
-__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main_local(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc,
-    const int32_t* __restrict__ slot, const float* __restrict__ lse, float2* __restrict__ st,
-    PT* __restrict__ partial, PT* __restrict__ dump, int32_t* __restrict__ queue, int N, int H, int g, int Tn, int NB,
-    int groups, float scale_log2) {
+__device__ __forceinline__ void local_main_item(const LocalItem& it, T* Ks, T* Vt, T* Qt, const T* __restrict__ q,
+                                                const T* __restrict__ k, const T* __restrict__ v,
+                                                const int32_t* __restrict__ loc, const int32_t* __restrict__ slot,
+                                                const float* __restrict__ lse, float2* __restrict__ st,
+                                                PT* __restrict__ partial, PT* __restrict__ dump, int N, int H, int g,
+                                                int Tn, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32, KK = BK / 16, MT = D / 32;
-  __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
-  __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
-  __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
-  if (blockIdx.x == 0) clear_queue(queue);
-  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups, H * NB);
-  if (it.rows == 0) return;
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 31, hl = lane >> 5;
@@ -1219,6 +1240,105 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     if (busy && hl == 0 && dst >= 0) st[dst] = make_float2(M, L);
   }
   if (busy) store_tile_rows<PT, D>(reinterpret_cast<PT*>(qt), o, lane, dst, partial, dump);
+}
+
+// FUSED: the rows' (max, sum) run over the local blocks as in k_stats_local
+// (the same merge, so the pair written to st is the one it writes) and the
+// accumulator is rescaled when the max grows; the partial row is divided by
+// the final sum.  queue: the main kernel's work-queue counters, cleared by
+// workgroup 0 (this kernel runs first in the forward call).
+template <typename T, int D, int BK, typename PT, bool FUSED>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main_local(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc,
+    const int32_t* __restrict__ slot, const float* __restrict__ lse, float2* __restrict__ st,
+    PT* __restrict__ partial, PT* __restrict__ dump, int32_t* __restrict__ queue, int N, int H, int g, int Tn, int NB,
+    int groups, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
+  __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
+  __shared__ __attribute__((aligned(16))) T Qt[kWaves * 32 * tile_ld<D>()];
+  if (blockIdx.x == 0) clear_queue(queue);
+  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups, H * NB);
+  if (it.rows == 0) return;
+  local_main_item<T, D, BK, PT, FUSED>(it, Ks, Vt, Qt, q, k, v, loc, slot, lse, st, partial, dump, N, H, g, Tn,
+                                       scale_log2);
+}
+
+// Counter of k_main_mixed's local items within each XCD queue's line (the
+// block-outer items count at offset 0).
+constexpr int kLocalCounter = kQueueStride / 2;
+
+// Thread 0: the next local item of a mixed launch, or -1 once none is left.
+// Claim c of XCD x is local item 8c + x, the order of the local kernels'
+// grid, so a unit's items stay on its XCD while that XCD has items left;
+// then the other XCDs' items are taken.
+__device__ __forceinline__ int claim_local(int32_t* __restrict__ queue, int per_xcd, int& tried) {
+  const int x = blockIdx.x & (kQueues - 1);
+  while (tried < kQueues) {
+    const int xx = (x + tried) & (kQueues - 1);
+    const int c = atomicAdd(queue + xx * kQueueStride + kLocalCounter, 1);
+    if (c < per_xcd) return 8 * c + xx;
+    ++tried;
+  }
+  return -1;
+}
+
+// A workgroup's loop over local items until none is left; thread 0 claims
+// the next item while the current one runs.
+template <typename T, int D, int BK, typename PT>
+__device__ __forceinline__ void local_items(MainLds<T, D, BK>& sm, int32_t* __restrict__ queue, int per_xcd,
+                                            const T* __restrict__ q, const T* __restrict__ k,
+                                            const T* __restrict__ v, const int32_t* __restrict__ cu,
+                                            const int32_t* __restrict__ gboff, int num_seqs,
+                                            const int32_t* __restrict__ loc, const int32_t* __restrict__ slot,
+                                            const float* __restrict__ lse, PT* __restrict__ partial,
+                                            PT* __restrict__ dump, int N, int H, int g, int Tn, int NB, int groups,
+                                            float scale_log2) {
+  int tried = 0;
+  if (threadIdx.x == 0) sm.s_local = claim_local(queue, per_xcd, tried);
+  __syncthreads();
+  int cur = __builtin_amdgcn_readfirstlane(sm.s_local);
+  while (cur >= 0) {
+    int nxt = -1;
+    if (threadIdx.x == 0) nxt = claim_local(queue, per_xcd, tried);
+    const LocalItem it = local_item(cur, cu, gboff, num_seqs, NB, BK, g, groups, H * NB);
+    if (it.rows > 0)
+      local_main_item<T, D, BK, PT, false>(it, sm.Ks, sm.Vt, sm.Qt, q, k, v, loc, slot, lse, nullptr, partial, dump,
+                                           N, H, g, Tn, scale_log2);
+    __syncthreads();  // every thread has read the current item
+    if (threadIdx.x == 0) sm.s_local = nxt;
+    __syncthreads();
+    cur = __builtin_amdgcn_readfirstlane(sm.s_local);
+  }
+}
+
+// The three-pass main stage at d = 64 and 128 with 64-key blocks as one
+// persistent launch over both kinds of items: k_main_local's and k_main's.
+// A local item walks up to three dependent blocks and is bound by latency; a
+// block-outer item is bound by its Q gather and partial-row traffic.  Run
+// side by side, the local items' latency hides under the block-outer items'
+// traffic instead of filling a launch of its own.  Workgroups with
+// (b >> 3) < local_first start on the local items, the others on the
+// block-outer items, and each goes on to the other kind when its first kind
+// runs out, so neither kind waits on the other.  The counters of both kinds
+// are cleared by the launch before this one.
+template <typename T, int D, int BK, typename PT>
+__global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main_mixed(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
+    const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
+    PT* __restrict__ partial, size_t dump_row, const int32_t* __restrict__ cu, const int32_t* __restrict__ gboff,
+    int num_seqs, const int32_t* __restrict__ loc, const int32_t* __restrict__ slot, int N, int H, int g, int Tn,
+    int NB, int CT, int groups, int local_per_xcd, int local_first, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) MainLds<T, D, BK> sm;
+  PT* const dump = partial + dump_row * D;
+  if ((int)(blockIdx.x >> 3) < local_first)
+    local_items<T, D, BK, PT>(sm, queue, local_per_xcd, q, k, v, cu, gboff, num_seqs, loc, slot, lse, partial, dump,
+                              N, H, g, Tn, NB, groups, scale_log2);
+  main_items<T, D, BK, PT, false>(sm, q, k, v, counts, offsets, qidx, work, nwork, queue, lse, nullptr, partial,
+                                  dump_row, H, g, NB, CT, scale_log2);
+  local_items<T, D, BK, PT>(sm, queue, local_per_xcd, q, k, v, cu, gboff, num_seqs, loc, slot, lse, partial, dump, N,
+                            H, g, Tn, NB, groups, scale_log2);
 }
 
 // The three-pass local main kernel at d = 256 (k_main_local's items, 128
@@ -1496,6 +1616,22 @@ inline Ptrs<int> index_ptrs(const Geometry& geo, const fsa_index& idx) {
 // before it (the local kernels clear them otherwise).
 __global__ __launch_bounds__(256) void k_clear_queue(int32_t* __restrict__ queue) { clear_queue(queue); }
 
+// One workgroup of k_main_mixed in kLocalFirstShare starts on the local items.
+// The mixed launch is taken where the local items fill at least
+// kMixedMinRounds rounds of its workgroups; with fewer, both kinds take about
+// one round each and the two launches in a row measured faster (at 8K tokens,
+// 4 KV heads, g = 2: 84 us against 97 us for the main stage).
+constexpr int kLocalFirstShare = 2;
+constexpr unsigned kMixedMinRounds = 4;
+
+// FSA_MAIN_MIXED=0 keeps the two launches, =1 takes the mixed launch wherever
+// both kinds of items exist; unset (or any other value): the rounds rule.
+// Both give the same bits: each item runs the same code either way.
+inline int mixed_main_override() {
+  const char* e = std::getenv("FSA_MAIN_MIXED");
+  return e != nullptr && (e[0] == '0' || e[0] == '1') && e[1] == 0 ? e[0] - '0' : -1;
+}
+
 // Workgroups of the local kernels, one per item (KV head, global block, row
 // group), in whole units per XCD (local_item); the surplus returns at once.
 inline unsigned local_grid(const Geometry& geo, int* groups) {
@@ -1540,6 +1676,25 @@ void main_launch(const Geometry& geo, const int32_t* cu, const void* q, const vo
   PT* const dump = part + geo.dump_row * geo.d;
   float2* const st = static_cast<float2*>(st_ws);
   int32_t* const queue = reinterpret_cast<int32_t*>(static_cast<char*>(partial) + geo.partial_queue_off);
+  if constexpr (!FUSED && BK == 64 && D <= 128) {
+    int groups = 0;
+    const unsigned lgrid = geo.local ? local_grid(geo, &groups) : 0;
+    const unsigned grid =
+        geo.local && geo.max_work > 0 ? persistent_grid(k_main_mixed<T, D, BK, PT>, kAttnThreads, geo.max_work + lgrid)
+                                      : 0;
+    const int ov = mixed_main_override();
+    if (grid > 0 && (ov == 1 || (ov != 0 && lgrid >= kMixedMinRounds * grid))) {
+      // both kinds of items in one persistent launch (see k_main_mixed); the
+      // clear kernel zeroes the counters of both
+      hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(256), 0, stream, queue);
+      hipLaunchKernelGGL((k_main_mixed<T, D, BK, PT>), dim3(grid), dim3(kAttnThreads), 0, stream,
+                         static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), p.counts,
+                         p.offsets, p.qidx, p.work, p.nwork, queue, lse, part, (size_t)geo.dump_row, cu, p.gboff,
+                         geo.num_seqs, p.loc, idx.slot, geo.N, geo.H, geo.g, geo.T, geo.NB, geo.chunk_tokens, groups,
+                         (int)(lgrid / 8), (int)(grid / 8 / kLocalFirstShare), sl2);
+      return;
+    }
+  }
   // the local kernel (or the clear kernel) runs first: it zeroes the queue counters
   if (!geo.local) {
     hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(256), 0, stream, queue);

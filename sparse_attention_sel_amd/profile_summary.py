@@ -106,6 +106,9 @@ def pretty(name: str) -> str:
     if a and len(a) == 5:
         split = ", two 64-key halves" if a[4] == "true" else ""
         return f"`k_main16<{t(a[0])}, d={a[1]}, B_K={a[2]}, partial={t(a[3])}{split}>`"
+    a = _template_args(name, "k_main_mixed")
+    if a and len(a) == 4:
+        return f"`k_main_mixed<{t(a[0])}, d={a[1]}, B_K={a[2]}, partial={t(a[3])}>`"
     a = _template_args(name, "k_main_local16")
     if a and len(a) == 2:
         return f"`k_main_local16<{t(a[0])}, d=256, B_K=64, partial={t(a[1])}>`"
@@ -246,9 +249,10 @@ def write_traffic(a):
     for k, n, fb, wb, fk, wk, avg, gbs in rows:
         lines.append(f"| {pretty(k)} | {n} | {fb / 1e9:.3f} | {wb / 1e9:.3f} | {fk:.0f} | {wk:.0f} | "
                      f"{avg / 1e3:.1f} | {gbs:.0f} | {100 * gbs / PEAK_HBM_GBS:.1f}% |")
-    # the three-pass forward's main stage: k_main / k_main16 and k_main_local / k_main_local16, not the
-    # one-pass variants
-    main = [r for r in rows if re.match(r"`k_main(_local)?(16)?<", pretty(r[0])) and "one-pass" not in pretty(r[0])]
+    # the three-pass forward's main stage: k_main_mixed, or k_main / k_main16 and k_main_local /
+    # k_main_local16, not the one-pass variants
+    main = [r for r in rows
+            if re.match(r"`k_main(_local|_mixed)?(16)?<", pretty(r[0])) and "one-pass" not in pretty(r[0])]
     if main:
         fb, wb = sum(r[2] for r in main), sum(r[3] for r in main)
         names = " + ".join(pretty(r[0]).strip("`") for r in main)

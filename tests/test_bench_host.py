@@ -76,6 +76,8 @@ def test_profile_summary_on_rocprof_csv(tmp_path):
         "`k_main16<fp16, d=128, B_K=128, partial=fp32>`"
     assert ps.pretty("_ZN3fsa12_GLOBAL__N_114k_main_local16IDF16_fEEvPKT_S4_S4_PKiS6_i") == \
         "`k_main_local16<fp16, d=256, B_K=64, partial=fp32>`"
+    assert ps.pretty("_ZN3fsa12_GLOBAL__N_112k_main_mixedIDF16bLi128ELi64EDF16bEEvPKT_S4_S4_PKi") == \
+        "`k_main_mixed<bf16, d=128, B_K=64, partial=bf16>`"
     hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
 
     def pmc(d, counter, rows):
@@ -103,3 +105,22 @@ def test_profile_summary_on_rocprof_csv(tmp_path):
     assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
     assert rec["fetch_bytes"] == 200 * 1024 * 2 and rec["write_bytes"] == 400 * 1024
     assert "k_main<bf16, d=128, B_K=64, partial=bf16>" in open(out).read()
+
+
+def test_main_stage_kernel_names(monkeypatch):
+    # the roofline's kernel label follows the library's choice of launches
+    class W:
+        num_kv_heads, head_dim, block_size = 4, 128, 64
+
+    big, small = W(), W()
+    big.cu_seqlens, big.gqa_group = np.array([0, 65536], dtype=np.int32), 4
+    small.cu_seqlens, small.gqa_group = np.array([0, 8192], dtype=np.int32), 2
+    monkeypatch.delenv("FSA_MAIN_MIXED", raising=False)
+    assert bench.main_stage_kernels(big) == "k_main_mixed"  # 8192 local items
+    assert bench.main_stage_kernels(small) == "k_main_local+k_main"  # 512
+    monkeypatch.setenv("FSA_MAIN_MIXED", "1")
+    assert bench.main_stage_kernels(small) == "k_main_mixed"
+    monkeypatch.setenv("FSA_MAIN_MIXED", "0")
+    assert bench.main_stage_kernels(big) == "k_main_local+k_main"
+    small.gqa_group = 1
+    assert bench.main_stage_kernels(small) == "k_main"

@@ -132,9 +132,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", range(len(CASES)))
-@pytest.mark.parametrize("partial", ["fp32", "input"])
-def test_adversarial_selection(case, partial):
+def adversarial_workload(case):
     seqlens, H, g, d, B, T, dtype = CASES[case]
     rng = np.random.default_rng(700 + case)
     from sparse_attention_sel_amd.inputs import cu_seqlens_of
@@ -142,11 +140,52 @@ def test_adversarial_selection(case, partial):
     cu = cu_seqlens_of(seqlens)
     sel = adversarial_sel(rng, H, cu, B, T)
     sel[:, ::37, :] = -1  # some rows select nothing
-    w = custom_workload(seqlens, H, g, d, B, T, dtype, sel, seed=900 + case)
+    return custom_workload(seqlens, H, g, d, B, T, dtype, sel, seed=900 + case)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+@pytest.mark.parametrize("partial", ["fp32", "input"])
+def test_adversarial_selection(case, partial):
+    w = adversarial_workload(case)
     log(f"[run] adversarial case {case} {CASES[case]} partial={partial}")
     res = run_gpu(w, partial)
-    check_index(res, O.build_index(w.sel, w.cu_seqlens, B))
+    check_index(res, O.build_index(w.sel, w.cu_seqlens, CASES[case][4]))
     check_attention(res, w)
+
+
+# the cases with per-query-block (local) entries at d <= 128
+MIXED_CASES = [i for i, c in enumerate(CASES) if c[4] == 64 and c[2] >= 2 and c[3] <= 128]
+
+
+def _same_bits(a, b):
+    for key in ("out_bits", "lse", "row_max"):
+        assert np.array_equal(a[key], b[key], equal_nan=True), key
+
+
+@pytest.mark.parametrize("case", MIXED_CASES)
+def test_mixed_main_launch(case, monkeypatch):
+    # The local and block-outer items of the forward in one persistent launch,
+    # forced (these sizes take two launches by default): the oracle's outputs
+    # on every token, and the bits of the two-launch path.
+    w = adversarial_workload(case)
+    log(f"[run] mixed main launch, adversarial case {case} {CASES[case]}")
+    monkeypatch.setenv("FSA_MAIN_MIXED", "1")
+    a = run_gpu(w, "input")
+    check_attention(a, w)
+    monkeypatch.setenv("FSA_MAIN_MIXED", "0")
+    _same_bits(a, run_gpu(w, "input"))
+
+
+@pytest.mark.parametrize("name", ["n8k_h4_g2_d128_t16_bf16", "n64k_h4_g4_d128_t16_bf16"])
+def test_mixed_and_split_main_launch_bitwise(name, monkeypatch):
+    # 8K tokens take two launches by default and 64K one: both ways agree bit
+    # for bit (each item runs the same code).
+    w = workload(name)
+    log(f"[run] mixed against split main launch: {name}")
+    monkeypatch.setenv("FSA_MAIN_MIXED", "1")
+    a = run_gpu(w, "input")
+    monkeypatch.setenv("FSA_MAIN_MIXED", "0")
+    _same_bits(a, run_gpu(w, "input"))
 
 
 def test_largest_block_window():
