@@ -162,20 +162,21 @@ def kernel_source_hash(root):
 
 def main_stage_kernels(w):
     """The three-pass main stage's kernels as the library launches them: with
-    local entries (B_K = 64, g >= 2) at d <= 128, k_main_mixed where the
-    per-query-block items (KV head, block, 128-row group; in units of four
-    blocks, a whole number per XCD) fill four rounds of its persistent grid
-    (two workgroups per CU on 256 CUs), unless FSA_MAIN_MIXED says otherwise."""
+    local entries (B_K = 64, g >= 2), k_main_mixed (k_main_mixed16 at d = 256)
+    where the per-query-block items (KV head, block, 128-row group; in units of
+    four blocks, a whole number per XCD) fill four rounds of its persistent
+    grid (256 CUs times two workgroups per CU, one at d = 256), unless
+    FSA_MAIN_MIXED says otherwise."""
     B, g, d = w.block_size, w.gqa_group, w.head_dim
     if B != 64 or g < 2:
         return "k_main16" if d == 256 or B == 128 and d == 128 else "k_main"
-    if d == 256:
-        return "k_main_local16+k_main16"
     nb = sum(-(-int(w.cu_seqlens[i + 1] - w.cu_seqlens[i]) // B) for i in range(len(w.cu_seqlens) - 1))
     units = -(-w.num_kv_heads * nb // 4)
     items = -(-units // 8) * 8 * 4 * -(-B * g // 128)
     env = os.environ.get("FSA_MAIN_MIXED")
-    mixed = env == "1" or (env != "0" and items >= 4 * 2 * 256)
+    mixed = env == "1" or (env != "0" and items >= 4 * (1 if d == 256 else 2) * 256)
+    if d == 256:
+        return "k_main_mixed16" if mixed else "k_main_local16+k_main16"
     return "k_main_mixed" if mixed else "k_main_local+k_main"
 
 

@@ -258,8 +258,8 @@ int32_t fsa_selected_attn_fwd_onepass(const fsa_problem* prob, const void* q, co
  * the second half's lie max_pairs * g rows further on, and the reduction adds
  * both.  partial_ws is otherwise private to the library (it also holds the
  * main kernel's work-queue counters after the rows);
- * fsa_selected_attn_reduce reads it as written.  With local entries at
- * d <= 128 the per-query-block work and the block-outer work can run in one
+ * fsa_selected_attn_reduce reads it as written.  With local entries the
+ * per-query-block work and the block-outer work can run in one
  * persistent launch or in two launches in a row; the library picks by the
  * amount of per-query-block work, and the environment variable
  * FSA_MAIN_MIXED (read at each call) forces one launch (1) or two (0).  The

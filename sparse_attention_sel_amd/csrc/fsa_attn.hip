@@ -859,24 +859,42 @@ __device__ __forceinline__ void store_tile16_rows(PT* __restrict__ stage, const 
 // a tile are gathered straight into the B operand of S^T = K Q^T (64
 // contiguous bytes of each row per load), tile i + 1 in flight while tile i
 // computes; O^T is accumulated and stored in two 128-column halves.
+// The LDS of k_main16 (also that of k_main_local16 and k_main_mixed16, whose
+// local items use the first three arrays).
+template <typename T, int D, int BK, typename PT>
+struct Main16Lds {
+  static constexpr int SP = D / 2 + 16 / (int)sizeof(PT);  // stage pitch of store_tile16
+  alignas(16) T Ks[BK * k_ld<D>()];
+  alignas(16) T Vt[D * vt_ld<BK>()];
+  alignas(16) PT Stg[8 * 16 * SP];
+  int ridx[kRowTable], rtok[kRowTable];
+  int s_items[2];
+  int s_local;  // k_main_mixed16: the workgroup's current local item
+};
+
+// k_main16's persistent loop over the block-outer items of the forward list.
 template <typename T, int D, int BK, typename PT, bool SPLIT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_main16(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
-    const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
-    PT* __restrict__ partial, size_t dump_row, size_t half_rows, int H, int g, int NB, int CT, float scale_log2) {
+__device__ __forceinline__ void main16_items(Main16Lds<T, D, BK, PT>& sm, const T* __restrict__ q,
+                                             const T* __restrict__ k, const T* __restrict__ v,
+                                             const int32_t* __restrict__ counts,
+                                             const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx,
+                                             const int4* __restrict__ work, const int32_t* __restrict__ nwork,
+                                             int32_t* __restrict__ queue, const float* __restrict__ lse,
+                                             PT* __restrict__ partial, size_t dump_row, size_t half_rows, int H,
+                                             int g, int NB, int CT, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int NT = 512, NW = NT / 64;
   constexpr int KS = D / 32;   // contraction steps of S^T
   constexpr int KT = BK / 16;  // key tiles of S^T
   constexpr int KK = BK / 32;  // contraction steps of O^T
   constexpr int MH = D / 32;   // 16-column O^T tiles per half
-  constexpr int SP = D / 2 + 16 / (int)sizeof(PT);  // stage pitch of store_tile16
-  __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
-  __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
-  __shared__ __attribute__((aligned(16))) PT Stg[NW * 16 * SP];
-  __shared__ int ridx[kRowTable], rtok[kRowTable];
-  __shared__ int s_items[2];
+  constexpr int SP = Main16Lds<T, D, BK, PT>::SP;
+  T* const Ks = sm.Ks;
+  T* const Vt = sm.Vt;
+  PT* const Stg = sm.Stg;
+  int* const ridx = sm.ridx;
+  int* const rtok = sm.rtok;
+  int* const s_items = sm.s_items;
   ItemChain ch(queue, SPLIT ? 2 * nwork[2] : nwork[2], s_items);  // the forward list
   const int4* const wl = work + nwork[0];
   if (ch.cur < 0) return;
@@ -946,6 +964,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     ch.advance(after);
   }
+}
+
+template <typename T, int D, int BK, typename PT, bool SPLIT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_main16(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
+    const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
+    PT* __restrict__ partial, size_t dump_row, size_t half_rows, int H, int g, int NB, int CT, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) Main16Lds<T, D, BK, PT> sm;
+  main16_items<T, D, BK, PT, SPLIT>(sm, q, k, v, counts, offsets, qidx, work, nwork, queue, lse, partial, dump_row,
+                                    half_rows, H, g, NB, CT, scale_log2);
 }
 
 // ---- local entries, per query block ---------------------------------------------
@@ -1283,32 +1312,23 @@ __device__ __forceinline__ int claim_local(int32_t* __restrict__ queue, int per_
   return -1;
 }
 
-// A workgroup's loop over local items until none is left; thread 0 claims
-// the next item while the current one runs.
-template <typename T, int D, int BK, typename PT>
-__device__ __forceinline__ void local_items(MainLds<T, D, BK>& sm, int32_t* __restrict__ queue, int per_xcd,
-                                            const T* __restrict__ q, const T* __restrict__ k,
-                                            const T* __restrict__ v, const int32_t* __restrict__ cu,
-                                            const int32_t* __restrict__ gboff, int num_seqs,
-                                            const int32_t* __restrict__ loc, const int32_t* __restrict__ slot,
-                                            const float* __restrict__ lse, PT* __restrict__ partial,
-                                            PT* __restrict__ dump, int N, int H, int g, int Tn, int NB, int groups,
-                                            float scale_log2) {
+// A workgroup's loop over local items until none is left: run(i) for each
+// claimed item i; thread 0 claims the next item while the current one runs.
+// s_local: a __shared__ int of the workgroup.
+template <typename F>
+__device__ __forceinline__ void local_loop(int* s_local, int32_t* __restrict__ queue, int per_xcd, F&& run) {
   int tried = 0;
-  if (threadIdx.x == 0) sm.s_local = claim_local(queue, per_xcd, tried);
+  if (threadIdx.x == 0) *s_local = claim_local(queue, per_xcd, tried);
   __syncthreads();
-  int cur = __builtin_amdgcn_readfirstlane(sm.s_local);
+  int cur = __builtin_amdgcn_readfirstlane(*s_local);
   while (cur >= 0) {
     int nxt = -1;
     if (threadIdx.x == 0) nxt = claim_local(queue, per_xcd, tried);
-    const LocalItem it = local_item(cur, cu, gboff, num_seqs, NB, BK, g, groups, H * NB);
-    if (it.rows > 0)
-      local_main_item<T, D, BK, PT, false>(it, sm.Ks, sm.Vt, sm.Qt, q, k, v, loc, slot, lse, nullptr, partial, dump,
-                                           N, H, g, Tn, scale_log2);
+    run(cur);
     __syncthreads();  // every thread has read the current item
-    if (threadIdx.x == 0) sm.s_local = nxt;
+    if (threadIdx.x == 0) *s_local = nxt;
     __syncthreads();
-    cur = __builtin_amdgcn_readfirstlane(sm.s_local);
+    cur = __builtin_amdgcn_readfirstlane(*s_local);
   }
 }
 
@@ -1332,13 +1352,16 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     int NB, int CT, int groups, int local_per_xcd, int local_first, float scale_log2) {
   __shared__ __attribute__((aligned(16))) MainLds<T, D, BK> sm;
   PT* const dump = partial + dump_row * D;
-  if ((int)(blockIdx.x >> 3) < local_first)
-    local_items<T, D, BK, PT>(sm, queue, local_per_xcd, q, k, v, cu, gboff, num_seqs, loc, slot, lse, partial, dump,
-                              N, H, g, Tn, NB, groups, scale_log2);
+  auto run = [&](int i) {
+    const LocalItem it = local_item(i, cu, gboff, num_seqs, NB, BK, g, groups, H * NB);
+    if (it.rows > 0)
+      local_main_item<T, D, BK, PT, false>(it, sm.Ks, sm.Vt, sm.Qt, q, k, v, loc, slot, lse, nullptr, partial, dump,
+                                           N, H, g, Tn, scale_log2);
+  };
+  if ((int)(blockIdx.x >> 3) < local_first) local_loop(&sm.s_local, queue, local_per_xcd, run);
   main_items<T, D, BK, PT, false>(sm, q, k, v, counts, offsets, qidx, work, nwork, queue, lse, nullptr, partial,
                                   dump_row, H, g, NB, CT, scale_log2);
-  local_items<T, D, BK, PT>(sm, queue, local_per_xcd, q, k, v, cu, gboff, num_seqs, loc, slot, lse, partial, dump, N,
-                            H, g, Tn, NB, groups, scale_log2);
+  local_loop(&sm.s_local, queue, local_per_xcd, run);
 }
 
 // The three-pass local main kernel at d = 256 (k_main_local's items, 128
@@ -1348,23 +1371,20 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
 // k_main16's; the accumulation over the local blocks and the designated-row
 // stores are k_main_local's.
 template <typename T, typename PT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_main_local16(
-    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc,
-    const int32_t* __restrict__ slot, const float* __restrict__ lse, PT* __restrict__ partial,
-    PT* __restrict__ dump, int32_t* __restrict__ queue, int N, int H, int g, int Tn, int NB, int groups,
-    float scale_log2) {
+__device__ __forceinline__ void local16_item(const LocalItem& it, Main16Lds<T, 256, 64, PT>& sm,
+                                             const T* __restrict__ q, const T* __restrict__ k,
+                                             const T* __restrict__ v, const int32_t* __restrict__ loc,
+                                             const int32_t* __restrict__ slot, const float* __restrict__ lse,
+                                             PT* __restrict__ partial, PT* __restrict__ dump, int N, int H, int g,
+                                             int Tn, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int D = 256, BK = 64, NT = 512, NW = NT / 64;
   constexpr int KS = D / 32, KT = BK / 16, MT = D / 16;
-  constexpr int SP = D / 2 + 16 / (int)sizeof(PT);
+  constexpr int SP = Main16Lds<T, D, BK, PT>::SP;
   static_assert(NW * 16 == kLocalRows, "one 16-row tile per wave");
-  __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
-  __shared__ __attribute__((aligned(16))) T Vt[D * vt_ld<BK>()];
-  __shared__ __attribute__((aligned(16))) PT Stg[NW * 16 * SP];
-  if (blockIdx.x == 0) clear_queue(queue);
-  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups, H * NB);
-  if (it.rows == 0) return;
+  T* const Ks = sm.Ks;
+  T* const Vt = sm.Vt;
+  PT* const Stg = sm.Stg;
   const int HQ = H * g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lr = lane & 15, u = lane >> 4;
@@ -1419,6 +1439,43 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     store_tile16_rows<PT, D, D / 2, 0>(stage, o, lane, dst, partial, dump);
     store_tile16_rows<PT, D, D / 2, D / 2>(stage, o + MT / 2, lane, dst, partial, dump);
   }
+}
+
+template <typename T, typename PT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_main_local16(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ gboff, int num_seqs, const int32_t* __restrict__ loc,
+    const int32_t* __restrict__ slot, const float* __restrict__ lse, PT* __restrict__ partial,
+    PT* __restrict__ dump, int32_t* __restrict__ queue, int N, int H, int g, int Tn, int NB, int groups,
+    float scale_log2) {
+  __shared__ __attribute__((aligned(16))) Main16Lds<T, 256, 64, PT> sm;
+  if (blockIdx.x == 0) clear_queue(queue);
+  const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, 64, g, groups, H * NB);
+  if (it.rows == 0) return;
+  local16_item<T, PT>(it, sm, q, k, v, loc, slot, lse, partial, dump, N, H, g, Tn, scale_log2);
+}
+
+// k_main_mixed at d = 256: k_main_local16's items and k_main16's block-outer
+// items (64-key blocks) in one persistent launch.  Here a workgroup fills a
+// CU, so the two kinds share the chip by CUs rather than within one.
+template <typename T, typename PT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k_main_mixed16(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qidx, const int4* __restrict__ work,
+    const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
+    PT* __restrict__ partial, size_t dump_row, const int32_t* __restrict__ cu, const int32_t* __restrict__ gboff,
+    int num_seqs, const int32_t* __restrict__ loc, const int32_t* __restrict__ slot, int N, int H, int g, int Tn,
+    int NB, int CT, int groups, int local_per_xcd, int local_first, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) Main16Lds<T, 256, 64, PT> sm;
+  PT* const dump = partial + dump_row * 256;
+  auto run = [&](int i) {
+    const LocalItem it = local_item(i, cu, gboff, num_seqs, NB, 64, g, groups, H * NB);
+    if (it.rows > 0) local16_item<T, PT>(it, sm, q, k, v, loc, slot, lse, partial, dump, N, H, g, Tn, scale_log2);
+  };
+  if ((int)(blockIdx.x >> 3) < local_first) local_loop(&sm.s_local, queue, local_per_xcd, run);
+  main16_items<T, 256, 64, PT, false>(sm, q, k, v, counts, offsets, qidx, work, nwork, queue, lse, partial, dump_row,
+                                      0, H, g, NB, CT, scale_log2);
+  local_loop(&sm.s_local, queue, local_per_xcd, run);
 }
 
 // ---- reduce -----------------------------------------------------------------
@@ -1676,22 +1733,31 @@ void main_launch(const Geometry& geo, const int32_t* cu, const void* q, const vo
   PT* const dump = part + geo.dump_row * geo.d;
   float2* const st = static_cast<float2*>(st_ws);
   int32_t* const queue = reinterpret_cast<int32_t*>(static_cast<char*>(partial) + geo.partial_queue_off);
-  if constexpr (!FUSED && BK == 64 && D <= 128) {
+  if constexpr (!FUSED && BK == 64 && !SPLIT) {
     int groups = 0;
     const unsigned lgrid = geo.local ? local_grid(geo, &groups) : 0;
-    const unsigned grid =
-        geo.local && geo.max_work > 0 ? persistent_grid(k_main_mixed<T, D, BK, PT>, kAttnThreads, geo.max_work + lgrid)
-                                      : 0;
+    unsigned grid = 0;
+    if (geo.local && geo.max_work > 0) {
+      if constexpr (D == 256) grid = persistent_grid(k_main_mixed16<T, PT>, 512, geo.max_work + lgrid);
+      else grid = persistent_grid(k_main_mixed<T, D, BK, PT>, kAttnThreads, geo.max_work + lgrid);
+    }
     const int ov = mixed_main_override();
     if (grid > 0 && (ov == 1 || (ov != 0 && lgrid >= kMixedMinRounds * grid))) {
       // both kinds of items in one persistent launch (see k_main_mixed); the
       // clear kernel zeroes the counters of both
       hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(256), 0, stream, queue);
-      hipLaunchKernelGGL((k_main_mixed<T, D, BK, PT>), dim3(grid), dim3(kAttnThreads), 0, stream,
-                         static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), p.counts,
-                         p.offsets, p.qidx, p.work, p.nwork, queue, lse, part, (size_t)geo.dump_row, cu, p.gboff,
-                         geo.num_seqs, p.loc, idx.slot, geo.N, geo.H, geo.g, geo.T, geo.NB, geo.chunk_tokens, groups,
-                         (int)(lgrid / 8), (int)(grid / 8 / kLocalFirstShare), sl2);
+      const int per_xcd = (int)(lgrid / 8), first = (int)(grid / 8 / kLocalFirstShare);
+      if constexpr (D == 256)
+        hipLaunchKernelGGL((k_main_mixed16<T, PT>), dim3(grid), dim3(512), 0, stream, static_cast<const T*>(q),
+                           static_cast<const T*>(k), static_cast<const T*>(v), p.counts, p.offsets, p.qidx, p.work,
+                           p.nwork, queue, lse, part, (size_t)geo.dump_row, cu, p.gboff, geo.num_seqs, p.loc, idx.slot,
+                           geo.N, geo.H, geo.g, geo.T, geo.NB, geo.chunk_tokens, groups, per_xcd, first, sl2);
+      else
+        hipLaunchKernelGGL((k_main_mixed<T, D, BK, PT>), dim3(grid), dim3(kAttnThreads), 0, stream,
+                           static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), p.counts,
+                           p.offsets, p.qidx, p.work, p.nwork, queue, lse, part, (size_t)geo.dump_row, cu, p.gboff,
+                           geo.num_seqs, p.loc, idx.slot, geo.N, geo.H, geo.g, geo.T, geo.NB, geo.chunk_tokens,
+                           groups, per_xcd, first, sl2);
       return;
     }
   }

@@ -124,3 +124,10 @@ def test_main_stage_kernel_names(monkeypatch):
     assert bench.main_stage_kernels(big) == "k_main_local+k_main"
     small.gqa_group = 1
     assert bench.main_stage_kernels(small) == "k_main"
+    monkeypatch.delenv("FSA_MAIN_MIXED")
+    big.head_dim = 256
+    assert bench.main_stage_kernels(big) == "k_main_mixed16"
+    big.num_kv_heads = 1  # 2048 local items: at least four rounds of 256 workgroups
+    assert bench.main_stage_kernels(big) == "k_main_mixed16"
+    big.cu_seqlens = np.array([0, 8192], dtype=np.int32)  # 128 blocks, 4 groups: 512 items
+    assert bench.main_stage_kernels(big) == "k_main_local16+k_main16"
