@@ -106,6 +106,9 @@ def pretty(name: str) -> str:
     if a and len(a) == 5:
         split = ", two 64-key halves" if a[4] == "true" else ""
         return f"`k_main16<{t(a[0])}, d={a[1]}, B_K={a[2]}, partial={t(a[3])}{split}>`"
+    a = _template_args(name, "k_main_mixed16")
+    if a and len(a) == 2:
+        return f"`k_main_mixed16<{t(a[0])}, d=256, B_K=64, partial={t(a[1])}>`"
     a = _template_args(name, "k_main_mixed")
     if a and len(a) == 4:
         return f"`k_main_mixed<{t(a[0])}, d={a[1]}, B_K={a[2]}, partial={t(a[3])}>`"

@@ -78,6 +78,8 @@ def test_profile_summary_on_rocprof_csv(tmp_path):
         "`k_main_local16<fp16, d=256, B_K=64, partial=fp32>`"
     assert ps.pretty("_ZN3fsa12_GLOBAL__N_112k_main_mixedIDF16bLi128ELi64EDF16bEEvPKT_S4_S4_PKi") == \
         "`k_main_mixed<bf16, d=128, B_K=64, partial=bf16>`"
+    assert ps.pretty("_ZN3fsa12_GLOBAL__N_114k_main_mixed16IDF16bDF16bEEvPKT_S4_S4_PKiS6_S6_PK4int4S6_PiPKfPS3_m") == \
+        "`k_main_mixed16<bf16, d=256, B_K=64, partial=bf16>`"
     hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
 
     def pmc(d, counter, rows):
