@@ -308,6 +308,10 @@ template <int D, int BK, bool FUSED>
 constexpr bool main16() { return !FUSED && ((D == 256 && BK == 64) || (D == 128 && BK == 128)); }
 template <int D, int BK>
 constexpr int stats_local_waves_per_eu() { return stats_gather_b<D, BK>() ? 2 : attn_waves_per_eu<D, BK>(); }
+// k_stats_local stages its up to three key blocks at once (d <= 128, 64-key
+// blocks: 52 KB of LDS at d = 128).
+template <int D, int BK>
+constexpr bool stats_local_all() { return D <= 128 && BK == 64; }
 
 // Every key of the block is visible to every row of the tile: the block lies
 // entirely before each row's token (rows of a chunk are in token order, so
@@ -1142,10 +1146,15 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(st
     int Tn, int NB, int groups, float scale_log2) {
   using V8 = typename Vec8<T>::type;
   constexpr int KS = D / 16, KT = BK / 32;
-  // wide tiles keep the Q tile as the B operand in registers (no LDS tile),
-  // as the statistics kernel does
-  constexpr bool FRAG = stats_gather_b<D, BK>();
-  __shared__ __attribute__((aligned(16))) T Ks[BK * k_ld<D>()];
+  // ALL (d <= 128): the item's up to three key blocks are loaded at once and
+  // staged side by side, so the item waits for memory once instead of once
+  // per block; the Q tile is then kept as the B operand in registers (the
+  // three blocks fill the LDS that its tile would take).  Wide tiles keep
+  // the Q tile in registers as well, as the statistics kernel does.
+  constexpr bool ALL = stats_local_all<D, BK>();
+  constexpr bool FRAG = ALL || stats_gather_b<D, BK>();
+  constexpr int KB = BK * k_ld<D>();  // one staged key block
+  __shared__ __attribute__((aligned(16))) T Ks[(ALL ? 3 : 1) * KB];
   __shared__ __attribute__((aligned(16))) T Qt[FRAG ? 8 : kWaves * 32 * tile_ld<D>()];
   if (blockIdx.x == 0) clear_queue(queue);
   const LocalItem it = local_item(blockIdx.x, cu, gboff, num_seqs, NB, BK, g, groups, H * NB);
@@ -1156,6 +1165,40 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(st
   const bool busy = wave * 32 < it.rows;
   T* const qt = Qt + (FRAG ? 0 : wave * 32 * tile_ld<D>());
   const int kinds = min(it.e, 2) + 1;
+  if constexpr (ALL) {
+    BlockStage<T, D, BK, false> b0, b1, b2;
+    b0.load(k, nullptr, H, it.h, it.bs, it.ntok);
+    if (kinds > 1) b1.load(k, nullptr, H, it.h, it.seq_lo + local_block(1, it.e) * BK, BK);
+    if (kinds > 2) b2.load(k, nullptr, H, it.h, it.seq_lo + local_block(2, it.e) * BK, BK);
+    V8 qv[KS];
+    if (busy) load_q_local_frag<T, D>(q, it, wave, lr, hl, g, HQ, qv);
+    const int row = wave * 32 + lr;
+    const int qrow = local_qrow(it, row, g, HQ);
+    const int tok = row < it.rows ? qrow / HQ : -1;
+    const unsigned word = tok >= 0 ? (unsigned)loc[(size_t)it.h * N + tok] : 0u;
+    b0.commit(Ks, nullptr);
+    if (kinds > 1) b1.commit(Ks + KB, nullptr);
+    if (kinds > 2) b2.commit(Ks + 2 * KB, nullptr);
+    __syncthreads();
+    if (!busy) return;
+    // the blocks merge in the order own, previous, first, as below
+    float M = -INFINITY, L = 0.f;
+    for (int kind = 0; kind < kinds; ++kind) {
+      f32x16 s[KT];
+      qk_frag<T, D, BK>(Ks + kind * KB, qv, lr, hl, s);
+      const int lim = local_lim<BK>(tok, word, kind, it.seq_lo + local_block(kind, it.e) * BK);
+      const float2 ml = kind == 0 ? row_stats<BK, true>(s, hl, lim, scale_log2)
+                                  : row_stats<BK, false>(s, hl, 0, scale_log2);
+      if (lim >= 0) {
+        const float mn = fmaxf(M, ml.x);
+        L = L * __builtin_amdgcn_exp2f(M - mn) + ml.y * __builtin_amdgcn_exp2f(ml.x - mn);
+        M = mn;
+      }
+    }
+    const int64_t dst = local_dst(it, row, tok, word, slot, N, Tn, g);
+    if (hl == 0 && dst >= 0) st[dst] = make_float2(M, L);
+    return;
+  }
   // every load of the item's start goes out here: the own block's K, the Q
   // tile and the row's local word
   BlockStage<T, D, BK, false> pre;
