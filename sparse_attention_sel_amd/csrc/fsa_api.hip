@@ -188,7 +188,7 @@ int32_t compute_geometry(const fsa_problem* p, Geometry* geo) {
 
 namespace {
 
-int32_t check_index(const Geometry& geo, const fsa_index* idx) {
+int32_t check_index(const fsa_index* idx) {
   if (idx == nullptr || idx->counts == nullptr || idx->offsets == nullptr || idx->qidx == nullptr ||
       idx->slot == nullptr || idx->aux == nullptr)
     return FSA_ERR_NULL;
@@ -216,7 +216,7 @@ bool data(const void* p, const Geometry& geo) { return p != nullptr || geo.N == 
 int32_t check_main_args(const Geometry& geo, const void* q, const void* k, const void* v, const fsa_index* idx,
                         const float* lse, const void* partial, size_t partial_bytes) {
   if (!data(q, geo) || !data(k, geo) || !data(v, geo) || !data(lse, geo) || partial == nullptr) return FSA_ERR_NULL;
-  int32_t st = check_index(geo, idx);
+  int32_t st = check_index(idx);
   if (st != FSA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(lse, 4) || !aligned(partial, 16))
     return FSA_ERR_ALIGN;
@@ -227,7 +227,7 @@ int32_t check_main_args(const Geometry& geo, const void* q, const void* k, const
 int32_t check_reduce_args(const Geometry& geo, const fsa_index* idx, const void* partial, size_t partial_bytes,
                           const void* out) {
   if (partial == nullptr || !data(out, geo)) return FSA_ERR_NULL;
-  int32_t st = check_index(geo, idx);
+  int32_t st = check_index(idx);
   if (st != FSA_OK) return st;
   if (!aligned(partial, 16) || !aligned(out, 16)) return FSA_ERR_ALIGN;
   if (partial_bytes < geo.partial_ws_bytes) return FSA_ERR_WORKSPACE;
@@ -289,7 +289,7 @@ int32_t fsa_build_index(const fsa_problem* prob, const int32_t* sel, const fsa_i
   int32_t st = prepare(prob, &geo);
   if (st != FSA_OK) return st;
   if (!data(sel, geo) || ws == nullptr) return FSA_ERR_NULL;
-  st = check_index(geo, idx);
+  st = check_index(idx);
   if (st != FSA_OK) return st;
   if (!aligned(sel, 4) || !aligned(ws, 256)) return FSA_ERR_ALIGN;
   if (ws_bytes < geo.build_ws_bytes) return FSA_ERR_WORKSPACE;
@@ -301,7 +301,7 @@ int32_t fsa_build_index_noalloc(const fsa_problem* prob, const int32_t* sel, con
   int32_t st = prepare(prob, &geo);
   if (st != FSA_OK) return st;
   if (!data(sel, geo)) return FSA_ERR_NULL;
-  st = check_index(geo, idx);
+  st = check_index(idx);
   if (st != FSA_OK) return st;
   if (!aligned(sel, 4)) return FSA_ERR_ALIGN;
   if (geo.build_ws_bytes > (size_t)FSA_NOALLOC_BUILD_SCRATCH_BYTES) return FSA_ERR_SCRATCH;
@@ -317,7 +317,7 @@ int32_t fsa_softmax_stats(const fsa_problem* prob, const void* q, const void* k,
   int32_t st = prepare(prob, &geo);
   if (st != FSA_OK) return st;
   if (!data(q, geo) || !data(k, geo) || !data(row_max, geo) || !data(lse, geo) || ws == nullptr) return FSA_ERR_NULL;
-  st = check_index(geo, idx);
+  st = check_index(idx);
   if (st != FSA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(row_max, 4) || !aligned(lse, 4) || !aligned(ws, 16))
     return FSA_ERR_ALIGN;
@@ -397,7 +397,7 @@ int32_t fsa_selected_attn_bwd(const fsa_problem* prob, const void* q, const void
   if (!data(q, geo) || !data(k, geo) || !data(v, geo) || !data(out, geo) || !data(dout, geo) || !data(lse, geo) ||
       !data(dq, geo) || !data(dk, geo) || !data(dv, geo) || ws == nullptr)
     return FSA_ERR_NULL;
-  st = check_index(geo, idx);
+  st = check_index(idx);
   if (st != FSA_OK) return st;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(dout, 16) ||
       !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(lse, 4) || !aligned(ws, 256))

@@ -73,21 +73,10 @@ __device__ __forceinline__ f32x4 mfma_k32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_k32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma_k16(bf16x4 a, bf16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0,
-                                                   0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_k16(f16x4 a, f16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
 
 template <typename T>
 __device__ __forceinline__ typename Vec8<T>::type bld8(const T* p) {
   return *reinterpret_cast<const typename Vec8<T>::type*>(p);
-}
-template <typename T>
-__device__ __forceinline__ typename Vec4<T>::type bld4(const T* p) {
-  return *reinterpret_cast<const typename Vec4<T>::type*>(p);
 }
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
 // i % 4 of the 8-byte chunks addressed by lanes i / 4, i / 4 + 4, i / 4 + 8
@@ -104,10 +93,6 @@ __device__ __forceinline__ typename Vec4<T>::type read_tr4(const T* p) {
 template <typename V4>
 __device__ __forceinline__ auto cat8(V4 a, V4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-template <typename T>
-__device__ __forceinline__ uint32_t bbits(T x) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, x);
 }
 
 // LDS pitches (elements).  K: [B_K][D + 8]; Q, dO tiles: [32][D + 8]; dS:

@@ -278,8 +278,8 @@ constexpr int kScanItems = 4;
 // k_hist gathered (queries of the block and of the next one); none when the
 // problem does not use the local path.
 __device__ __forceinline__ int segment_local(int f, int count, const int32_t* __restrict__ nloc,
-                                             const int32_t* __restrict__ cu, const int32_t* __restrict__ gboff,
-                                             int num_seqs, int NB, int BK, int use_local) {
+                                             const int32_t* __restrict__ gboff, int num_seqs, int NB,
+                                             int use_local) {
   if (count == 0 || !use_local) return 0;
   const int gb = f % NB;
   const int s = seq_of_block(gboff, num_seqs, gb);
@@ -288,9 +288,8 @@ __device__ __forceinline__ int segment_local(int f, int count, const int32_t* __
 
 __global__ __launch_bounds__(kScanThreads) void k_offsets(const int32_t* __restrict__ counts,
                                                           const int32_t* __restrict__ nloc, int M, int CT,
-                                                          const int32_t* __restrict__ cu,
                                                           const int32_t* __restrict__ gboff, int num_seqs,
-                                                          int NB, int BK, int32_t* __restrict__ offsets,
+                                                          int NB, int32_t* __restrict__ offsets,
                                                           int32_t* __restrict__ cb_full,
                                                           int32_t* __restrict__ cb_fwd, int32_t* __restrict__ nwork,
                                                           int32_t* __restrict__ buckets, int nbuckets, int use_local) {
@@ -305,7 +304,7 @@ __global__ __launch_bounds__(kScanThreads) void k_offsets(const int32_t* __restr
     for (int i = 0; i < kScanItems; ++i) {
       const int f = base + tid * kScanItems + i;
       c[i] = f < M ? counts[f] : 0;
-      cf[i] = c[i] - segment_local(f, c[i], nloc, cu, gboff, num_seqs, NB, BK, use_local);
+      cf[i] = c[i] - segment_local(f, c[i], nloc, gboff, num_seqs, NB, use_local);
       local += ((int64_t)c[i] << 32) + (c[i] + CT - 1) / CT;
       local_f += (cf[i] + CT - 1) / CT;
     }
@@ -393,7 +392,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(
       cursor[i] = tb[i];
       mark[i] = mark[win_max + i] = 0u;
       segoff[i] = offsets[f];
-      lstart[i] = segment_local(f, counts[f], nloc, cu, gboff, num_seqs, NB, BK, use_local);
+      lstart[i] = segment_local(f, counts[f], nloc, gboff, num_seqs, NB, use_local);
     }
   }
   const int RS = row_stride(T);
@@ -492,7 +491,7 @@ __device__ __forceinline__ bool list_item(const ListArgs& a, int w, int4* it, in
   const int gb = f % a.NB;
   const int s = seq_of_block(a.gboff, a.num_seqs, gb);
   const int first =
-      fwd ? segment_local(f, a.counts[f], a.nloc, a.cu, a.gboff, a.num_seqs, a.NB, a.BK, a.use_local) : 0;
+      fwd ? segment_local(f, a.counts[f], a.nloc, a.gboff, a.num_seqs, a.NB, a.use_local) : 0;
   *it = make_int4(f, first + (w - cb[f]) * a.CT, a.cu[s] + (gb - a.gboff[s]) * a.BK, a.cu[s + 1]);
   *bucket0 = fwd ? a.nbuckets : 0;
   return true;
@@ -574,9 +573,8 @@ hipError_t launch_build_index(const Geometry& geo, const int32_t* cu_dev, const 
                        tile_hist, cu_dev, gboff, geo.num_seqs, geo.H, geo.NB, geo.BK, geo.tile_tokens, geo.ntiles,
                        idx.counts);
   }
-  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(kScanThreads), 0, stream, idx.counts, nloc, M, geo.chunk_tokens, cu_dev,
-                     gboff, geo.num_seqs, NB1, geo.BK, idx.offsets, cb_full, cb_fwd, nwork, buckets, nbk,
-                     (int)geo.local);
+  hipLaunchKernelGGL(k_offsets, dim3(1), dim3(kScanThreads), 0, stream, idx.counts, nloc, M, geo.chunk_tokens,
+                     gboff, geo.num_seqs, NB1, idx.offsets, cb_full, cb_fwd, nwork, buckets, nbk, (int)geo.local);
   if (geo.N > 0) {
     int Tp = 1;
     while (Tp < geo.T) Tp <<= 1;
