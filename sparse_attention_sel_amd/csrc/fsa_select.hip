@@ -22,7 +22,8 @@
 // to its next best; it rescans below the winner only when it wins a fourth
 // time.  Groups of 64 blocks wholly past the own block are skipped
 // (wave-uniform).  Rows of up to 64 * kSelRegs candidates keep their keys in
-// registers; longer rows rescan from memory.
+// registers; longer rows rescan from memory.  A row's score loads are all
+// issued before its first key is built.
 #include "fsa_internal.h"
 
 namespace fsa {
@@ -39,10 +40,18 @@ __device__ __forceinline__ uint32_t score_order(uint32_t u) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ uint64_t cand_key(const float* __restrict__ row_scores, int e) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, row_scores[e]);
-  return ((uint64_t)score_order(u) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+// Key of block e from the bit pattern of its score.
+__device__ __forceinline__ uint64_t cand_key(uint32_t score_bits, int e) {
+  return ((uint64_t)score_order(score_bits) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
 }
+
+__device__ __forceinline__ uint32_t score_bits(const float* __restrict__ row_scores, int e) {
+  return __builtin_bit_cast(uint32_t, row_scores[e]);
+}
+
+// Rows past kSelRegBlocks blocks stream their scores in batches of
+// kSelBatch groups of 64, every load of a batch issued before its first use.
+constexpr int kSelBatch = 8;
 
 // One step of a wave-wide unsigned maximum: the DPP-moved neighbour's value
 // (0, the identity, in rows outside ROW_MASK) against the lane's own; the
@@ -111,19 +120,40 @@ __global__ __launch_bounds__(kSelWaves * 64) void k_select(const float* __restri
       second = lo1 > second ? lo1 : second;
       third = lo2 > third ? lo2 : third;
     };
-    if constexpr (IN_REGS) {
+    // every score load of the row goes out before the first key is built
+    // (a key built right after its load would wait for each group in turn)
+    auto scan = [&](uint64_t below) {  // offers the candidate keys < below
+      for (int e0 = 0; e0 <= own; e0 += 64 * kSelBatch) {
+        uint32_t raw[kSelBatch];
 #pragma unroll
-      for (int j = 0; j < kSelRegs; ++j) {
-        keys[j] = 0;
-        if (64 * j <= own) {  // wave-uniform: groups wholly past the own block cost nothing
-          const int e = lane + 64 * j;
-          keys[j] = candidate(e) ? cand_key(rs, e) : 0;
-          offer(keys[j]);
+        for (int u = 0; u < kSelBatch; ++u) {
+          const int e = e0 + lane + 64 * u;
+          raw[u] = candidate(e) ? score_bits(rs, e) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kSelBatch; ++u) {
+          const int e = e0 + lane + 64 * u;
+          const uint64_t k = candidate(e) ? cand_key(raw[u], e) : 0;
+          offer(k < below ? k : 0);
         }
       }
+    };
+    if constexpr (IN_REGS) {
+      uint32_t raw[kSelRegs];
+#pragma unroll
+      for (int j = 0; j < kSelRegs; ++j) {
+        const int e = lane + 64 * j;
+        // groups wholly past the own block load nothing (wave-uniform)
+        raw[j] = 64 * j <= own && candidate(e) ? score_bits(rs, e) : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kSelRegs; ++j) {
+        const int e = lane + 64 * j;
+        keys[j] = 64 * j <= own && candidate(e) ? cand_key(raw[j], e) : 0;
+        if (64 * j <= own) offer(keys[j]);
+      }
     } else {
-      for (int e = lane; e <= own; e += 64)
-        if (candidate(e)) offer(cand_key(rs, e));
+      scan(~uint64_t(0));
     }
     int exact = 2;  // how many of (second, third) are the lane's next keys below best
     for (; picked < want; ++picked) {
@@ -151,11 +181,7 @@ __global__ __launch_bounds__(kSelWaves * 64) void k_select(const float* __restri
             for (int j = 0; j < kSelRegs; ++j)
               if (64 * j <= own) offer(keys[j] < win ? keys[j] : 0);
           } else {
-            for (int e = lane; e <= own; e += 64)
-              if (candidate(e)) {
-                const uint64_t k = cand_key(rs, e);
-                offer(k < win ? k : 0);
-              }
+            scan(win);
           }
           exact = 2;
         }
