@@ -1,8 +1,9 @@
 """The forward captured in a HIP graph (torch.cuda.CUDAGraph over the C-ABI
 calls): the library allocates nothing and clears its own work-queue counters
-with kernels, so a captured index build + statistics + forward (and the
-one-pass forward) replays to the eager result, bit for bit, on every replay,
-with other eager work between replays."""
+with kernels, so a captured index build + statistics + forward (with the main
+stage in one or two launches, and the one-pass forward) replays to the eager
+result, bit for bit, on every replay, with other eager work between
+replays."""
 
 import numpy as np
 import pytest
@@ -15,8 +16,13 @@ from sparse_attention_sel_amd.inputs import make_workload
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("onepass", [False, True])
-def test_forward_graph_replays_match_eager(onepass):
+@pytest.mark.parametrize("mode", ["three_pass", "three_pass_mixed", "one_pass"])
+def test_forward_graph_replays_match_eager(mode, monkeypatch):
+    # the second mode forces the main stage's mixed launch (per-query-block
+    # and block-outer items in one persistent kernel), whose two counter sets
+    # a captured clear kernel zeroes before every replay
+    onepass = mode == "one_pass"
+    monkeypatch.setenv("FSA_MAIN_MIXED", "1" if mode == "three_pass_mixed" else "0")
     w = make_workload("n8k_h4_g2_d128_t16_bf16")
     dev = torch.device("cuda:0")
     prob = problem_for(w, "input")
