@@ -1380,11 +1380,14 @@ __device__ __forceinline__ void local_loop(int* s_local, int32_t* __restrict__ q
 // A local item walks up to three dependent blocks and is bound by latency; a
 // block-outer item is bound by its Q gather and partial-row traffic.  Run
 // side by side, the local items' latency hides under the block-outer items'
-// traffic instead of filling a launch of its own.  Workgroups with
-// (b >> 3) < local_first start on the local items, the others on the
-// block-outer items, and each goes on to the other kind when its first kind
-// runs out, so neither kind waits on the other.  The counters of both kinds
-// are cleared by the launch before this one.
+// traffic instead of filling a launch of its own.  Workgroup b starts on the
+// local items when its place in its XCD's share, b >> 3, is a multiple of
+// local_every, the others on the block-outer items, and each goes on to the
+// other kind when its first kind runs out, so neither kind waits on the
+// other.  With every other workgroup starting local, a CU's two workgroups
+// hold one of each kind whatever order the dispatcher fills CUs in (taking
+// the first half of each share instead measured 0.3-1% slower).  The
+// counters of both kinds are cleared by the launch before this one.
 template <typename T, int D, int BK, typename PT>
 __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<D, BK>()))) void k_main_mixed(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ counts,
@@ -1392,7 +1395,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
     const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
     PT* __restrict__ partial, size_t dump_row, const int32_t* __restrict__ cu, const int32_t* __restrict__ gboff,
     int num_seqs, const int32_t* __restrict__ loc, const int32_t* __restrict__ slot, int N, int H, int g, int Tn,
-    int NB, int CT, int groups, int local_per_xcd, int local_first, float scale_log2) {
+    int NB, int CT, int groups, int local_per_xcd, int local_every, float scale_log2) {
   __shared__ __attribute__((aligned(16))) MainLds<T, D, BK> sm;
   PT* const dump = partial + dump_row * D;
   auto run = [&](int i) {
@@ -1401,7 +1404,7 @@ __global__ __launch_bounds__(kAttnThreads) __attribute__((amdgpu_waves_per_eu(at
       local_main_item<T, D, BK, PT, false>(it, sm.Ks, sm.Vt, sm.Qt, q, k, v, loc, slot, lse, nullptr, partial, dump,
                                            N, H, g, Tn, scale_log2);
   };
-  if ((int)(blockIdx.x >> 3) < local_first) local_loop(&sm.s_local, queue, local_per_xcd, run);
+  if ((int)(blockIdx.x >> 3) % local_every == 0) local_loop(&sm.s_local, queue, local_per_xcd, run);
   main_items<T, D, BK, PT, false>(sm, q, k, v, counts, offsets, qidx, work, nwork, queue, lse, nullptr, partial,
                                   dump_row, H, g, NB, CT, scale_log2);
   local_loop(&sm.s_local, queue, local_per_xcd, run);
@@ -1508,14 +1511,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int32_t* __restrict__ nwork, int32_t* __restrict__ queue, const float* __restrict__ lse,
     PT* __restrict__ partial, size_t dump_row, const int32_t* __restrict__ cu, const int32_t* __restrict__ gboff,
     int num_seqs, const int32_t* __restrict__ loc, const int32_t* __restrict__ slot, int N, int H, int g, int Tn,
-    int NB, int CT, int groups, int local_per_xcd, int local_first, float scale_log2) {
+    int NB, int CT, int groups, int local_per_xcd, int local_every, float scale_log2) {
   __shared__ __attribute__((aligned(16))) Main16Lds<T, 256, 64, PT> sm;
   PT* const dump = partial + dump_row * 256;
   auto run = [&](int i) {
     const LocalItem it = local_item(i, cu, gboff, num_seqs, NB, 64, g, groups, H * NB);
     if (it.rows > 0) local16_item<T, PT>(it, sm, q, k, v, loc, slot, lse, partial, dump, N, H, g, Tn, scale_log2);
   };
-  if ((int)(blockIdx.x >> 3) < local_first) local_loop(&sm.s_local, queue, local_per_xcd, run);
+  if ((int)(blockIdx.x >> 3) % local_every == 0) local_loop(&sm.s_local, queue, local_per_xcd, run);
   main16_items<T, 256, 64, PT, false>(sm, q, k, v, counts, offsets, qidx, work, nwork, queue, lse, partial, dump_row,
                                       0, H, g, NB, CT, scale_log2);
   local_loop(&sm.s_local, queue, local_per_xcd, run);
@@ -1716,7 +1719,8 @@ inline Ptrs<int> index_ptrs(const Geometry& geo, const fsa_index& idx) {
 // before it (the local kernels clear them otherwise).
 __global__ __launch_bounds__(256) void k_clear_queue(int32_t* __restrict__ queue) { clear_queue(queue); }
 
-// One workgroup of k_main_mixed in kLocalFirstShare starts on the local items.
+// One workgroup of k_main_mixed in kLocalFirstShare (every other one) starts
+// on the local items.
 // The mixed launch is taken where the local items fill at least
 // kMixedMinRounds rounds of its workgroups; with fewer, both kinds take about
 // one round each and the two launches in a row measured faster (at 8K tokens,
@@ -1789,18 +1793,19 @@ void main_launch(const Geometry& geo, const int32_t* cu, const void* q, const vo
       // both kinds of items in one persistent launch (see k_main_mixed); the
       // clear kernel zeroes the counters of both
       hipLaunchKernelGGL(k_clear_queue, dim3(1), dim3(256), 0, stream, queue);
-      const int per_xcd = (int)(lgrid / 8), first = (int)(grid / 8 / kLocalFirstShare);
+      const int per_xcd = (int)(lgrid / 8);
       if constexpr (D == 256)
         hipLaunchKernelGGL((k_main_mixed16<T, PT>), dim3(grid), dim3(512), 0, stream, static_cast<const T*>(q),
                            static_cast<const T*>(k), static_cast<const T*>(v), p.counts, p.offsets, p.qidx, p.work,
                            p.nwork, queue, lse, part, (size_t)geo.dump_row, cu, p.gboff, geo.num_seqs, p.loc, idx.slot,
-                           geo.N, geo.H, geo.g, geo.T, geo.NB, geo.chunk_tokens, groups, per_xcd, first, sl2);
+                           geo.N, geo.H, geo.g, geo.T, geo.NB, geo.chunk_tokens, groups, per_xcd,
+                           kLocalFirstShare, sl2);
       else
         hipLaunchKernelGGL((k_main_mixed<T, D, BK, PT>), dim3(grid), dim3(kAttnThreads), 0, stream,
                            static_cast<const T*>(q), static_cast<const T*>(k), static_cast<const T*>(v), p.counts,
                            p.offsets, p.qidx, p.work, p.nwork, queue, lse, part, (size_t)geo.dump_row, cu, p.gboff,
                            geo.num_seqs, p.loc, idx.slot, geo.N, geo.H, geo.g, geo.T, geo.NB, geo.chunk_tokens,
-                           groups, per_xcd, first, sl2);
+                           groups, per_xcd, kLocalFirstShare, sl2);
       return;
     }
   }
