@@ -435,9 +435,9 @@ __global__ __launch_bounds__((stats_threads<D, BK>())) __attribute__((amdgpu_wav
 // One thread per (token, query head): merge the token's local (max, sum) pair
 // (at the row of its designated local entry) and the per-block pairs of its
 // other selecting entries, in slot order, into the row max and lse (stored in
-// natural-log units).  Slots are read 8 at a time and the pairs loaded
-// unconditionally (row 0 stands in for empty and local slots) so that the
-// loads are independent.
+// natural-log units).  Slots are read 8 at a time and their pairs loaded
+// together, the loads of empty and local slots masked off (a stand-in load of
+// one fixed row from every thread would make that row a hot spot).
 __global__ __launch_bounds__(256) void k_stats_combine(const int32_t* __restrict__ slot,
                                                        const float2* __restrict__ st,
                                                        const int32_t* __restrict__ loc,
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(256) void k_stats_combine(const int32_t* __restrict
 #pragma unroll
     for (int u = 0; u < 8; ++u) sv[u] = j0 + u < T && !local_entry(word, j0 + u) ? sl[j0 + u] : -1;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = st[(size_t)max(sv[u], 0) * g + j];
+    for (int u = 0; u < 8; ++u) v[u] = sv[u] >= 0 ? st[(size_t)sv[u] * g + j] : float2{};
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (sv[u] >= 0) {
@@ -1560,7 +1560,9 @@ struct Part8<_Float16> {
 // g*D outputs.  With LOCAL (the forward), the sum starts from the item's local
 // partial row group and skips the local slots; the backward's dQ reduction
 // sums every slot.  Slots are taken 8 at a time; the 8 partial loads are
-// issued together (row 0 stands in for empty slots) and summed in slot order.
+// issued together, those of empty and local slots masked off (loading row 0
+// in their place made that row a hot spot: 64K g = 4 reduction 0.728 ->
+// 0.707 ms), and summed in slot order.
 // FUSED (the one-pass forward): the partial rows are per-block softmax
 // averages o_b with (max, sum) pairs (m_b, l_b); O = sum_b l_b 2^(m_b - m) o_b
 // / l with the row's merged (m, l), also written out as row max and lse.
@@ -1611,8 +1613,8 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __rest
         for (int u = 0; u < 8; ++u) sv[u] = LOCAL && local_entry(word, j0 + u) ? -1 : raw[u];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          v[u] = st[(size_t)max(sv[u], 0) * g + j];
-          x[u] = Part8<PT>::load(partial + (size_t)max(sv[u], 0) * GD + vec * 8);
+          v[u] = sv[u] >= 0 ? st[(size_t)sv[u] * g + j] : float2{};
+          x[u] = sv[u] >= 0 ? Part8<PT>::load(partial + (size_t)sv[u] * GD + vec * 8) : typename Part8<PT>::type{};
         }
         if (LOCAL && j0 == 0 && word != 0u) {
           int lrow = 0;
@@ -1655,12 +1657,14 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const int32_t* __rest
 #pragma unroll
         for (int u = 0; u < 8; ++u) sv[u] = LOCAL && local_entry(word, j0 + u) ? -1 : raw[u];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = Part8<PT>::load(partial + (size_t)max(sv[u], 0) * GD + vec * 8);
+        for (int u = 0; u < 8; ++u)
+          x[u] = sv[u] >= 0 ? Part8<PT>::load(partial + (size_t)sv[u] * GD + vec * 8) : typename Part8<PT>::type{};
         if constexpr (SPLIT) {
           typename Part8<PT>::type y[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u)
-            y[u] = Part8<PT>::load(partial + half_elems + (size_t)max(sv[u], 0) * GD + vec * 8);
+            y[u] = sv[u] >= 0 ? Part8<PT>::load(partial + half_elems + (size_t)sv[u] * GD + vec * 8)
+                              : typename Part8<PT>::type{};
 #pragma unroll
           for (int u = 0; u < 8; ++u)
 #pragma unroll
