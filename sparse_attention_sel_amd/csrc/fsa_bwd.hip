@@ -132,10 +132,10 @@ __global__ __launch_bounds__(256) void k_bwd_delta(const T* __restrict__ out, co
 // One row tile's gather data in registers: this thread's Q / dO vectors
 // (zero for rows past the chunk) and, for threads < kBwdRows, its row's lse
 // and D.
-// Every load is unconditional (rows past the chunk read row 0) and nothing
-// consumes a loaded value before put(), so the loads stay in flight while
-// the previous tile computes; the row mask and the base-2 scaling of lse are
-// applied in put().
+// Rows past the chunk load nothing (masked off, rather than a stand-in row
+// that every workgroup's tail tile would read) and nothing consumes a loaded
+// value before put(), so the loads stay in flight while the previous tile
+// computes; the row mask and the base-2 scaling of lse are applied in put().
 template <typename T, int D, int NT>
 struct BwdTile {
   using V8 = typename Vec8<T>::type;
@@ -158,16 +158,18 @@ struct BwdTile {
       const int r = tile * kBwdRows + row;
       const int t = rtok[r];
       const size_t qrow = t >= 0 ? (size_t)t * HQ + h * g + r % g : 0;
-      x[i] = bld8((tensor == 0 ? q : dout) + qrow * D + c * 8);
+      x[i] = t >= 0 ? bld8((tensor == 0 ? q : dout) + qrow * D + c * 8) : V8{};
       ok[i] = t >= 0;
     }
-    // threads >= 16 load row 0's values too (unused): no branch around the loads
+    // threads < kBwdRows keep the lse and D of tile row threadIdx.x; the
+    // others load a row's values too (unused), so no branch surrounds the
+    // loads; rows past the chunk load nothing
     const int r = tile * kBwdRows + (threadIdx.x & (kBwdRows - 1));
     const int t = rtok[r];
     live = t >= 0;
     const size_t qrow = live ? (size_t)t * HQ + h * g + r % g : 0;
-    lraw = lse[qrow];
-    draw = delta[qrow];
+    lraw = live ? lse[qrow] : 0.f;
+    draw = live ? delta[qrow] : 0.f;
   }
 
   __device__ __forceinline__ void put(T* __restrict__ Qs, T* __restrict__ Ds, float* __restrict__ tab_l,
